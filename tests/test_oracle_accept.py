@@ -1,0 +1,351 @@
+"""Pins of the oracle's accept walk: the pages' worked examples, exact
+enumeration of the rejection sampler, and target-only equivalence of greedy
+speculative decoding on tiny deterministic models."""
+import json
+import os
+import zlib
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import accept as oacc
+from oracle import topk as otopk
+from oracle import tree as otree
+import workloads
+
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def chain_tree(root, proposals, prefix_len=0):
+    n = len(proposals) + 1
+    tokens = np.array([root] + list(proposals), np.int32)
+    parent = np.arange(-1, n - 1, dtype=np.int32)
+    depth = np.arange(n, dtype=np.int32)
+    t = otree.verify_arrays(tokens, parent, depth, np.ones(n, np.float32),
+                            np.array(list(range(n - 1)) + [-1], np.int32), prefix_len, 0)
+    return {k: v[None] for k, v in t.items()}
+
+
+def onehot_rows(choices, V):
+    rows = np.zeros((len(choices), V), np.float32)
+    for i, c in enumerate(choices):
+        rows[i, c] = 1.0
+    return rows
+
+
+# ------------------------------------------------------------ greedy pins
+
+def test_greedy_worked_example(golden_dir):
+    g = _golden(golden_dir, "greedy_worked_example.json")
+    props = g["proposals"]
+    t = chain_tree(0, props)
+    # rows beyond the first mismatch hold arbitrary choices; they must not matter
+    choices = g["target_choices"] + [5] * (len(props) + 1 - len(g["target_choices"]))
+    for filler in (5, 1):
+        choices[2:] = [filler] * (len(choices) - 2)
+        r = oacc.verify_greedy(t, onehot_rows(choices, 8)[None], S=len(props))
+        n = r["commit_len"][0]
+        assert r["commit_tokens"][0, :n].tolist() == g["expected_commit"]
+        assert r["accept_len"][0] == g["expected_accept_len"]
+        assert r["next_root"][0] == g["expected_commit"][-1]
+        assert r["accept_path"][0].tolist() == [0, 1, -1, -1]
+
+
+def test_row_alignment_quiz(golden_dir):
+    """Prefix 5, draft 3: rows 4, 5, 6 verify, row 7 picks the bonus."""
+    g = _golden(golden_dir, "row_alignment.json")
+    L, k = g["prefix_len"], g["draft_len"]
+    V = 64
+    full_rows = onehot_rows([20 + r for r in range(L + k)], V)     # row r chooses 20 + r
+    props = [20 + r for r in g["verify_rows"]]                     # every draft accepted
+    # the root is the last committed token, so the cached prefix is L - 1 tokens
+    t = chain_tree(3, props, prefix_len=L - 1)
+    assert t["positions"][0].tolist() == g["verify_rows"] + [g["bonus_row"]]
+    target = full_rows[t["positions"][0]][None]
+    r = oacc.verify_greedy(t, target, S=k)
+    assert r["accept_len"][0] == k
+    assert r["commit_tokens"][0].tolist() == props + [20 + g["bonus_row"]]
+
+
+def test_greedy_on_hand_tree(golden_dir):
+    g = _golden(golden_dir, "hand_tree_k2s3.json")
+    t = otree.build_tree(np.array([g["topk_p"]], np.float32), np.array([g["topk_id"]], np.int32),
+                         np.array([g["root_token"]]), np.array([g["prefix_len"]]), 2, 3, 6)
+    target = onehot_rows(g["greedy"]["argmax_per_node"], 128)[None]
+    r = oacc.verify_greedy(t, target, S=3)
+    a = r["accept_len"][0]
+    assert r["accept_path"][0, :a + 1].tolist() == g["greedy"]["expected_accept_path"]
+    assert r["commit_tokens"][0, :r["commit_len"][0]].tolist() == g["greedy"]["expected_commit"]
+
+
+def test_budget_and_eos():
+    t = chain_tree(0, [1, 2, 3])
+    target = onehot_rows([1, 2, 3, 4], 8)[None]
+    r = oacc.verify_greedy(t, target, S=3, remaining=np.array([0]))
+    assert r["commit_len"][0] == 0 and r["accept_len"][0] == 0 and r["next_root"][0] == -1
+    r = oacc.verify_greedy(t, target, S=3, remaining=np.array([2]))
+    assert r["commit_tokens"][0, :2].tolist() == [1, 2] and r["commit_len"][0] == 2
+    assert r["accept_len"][0] == 2          # both matched drafts keep their KV
+    r = oacc.verify_greedy(t, target, S=3, eos_id=2)
+    assert r["commit_tokens"][0, :2].tolist() == [1, 2] and r["commit_len"][0] == 2
+    r = oacc.verify_greedy(t, target, S=3)
+    assert r["commit_tokens"][0].tolist() == [1, 2, 3, 4] and r["accept_len"][0] == 3
+
+
+# --------------------------------------------- target-only equivalence
+
+class TinyLM:
+    """Deterministic float64 next-token logits of a prefix: random embeddings
+    mixed over a short window, optionally plus prefix-seeded noise."""
+
+    def __init__(self, V, seed, noise=0.0, noise_seed=0, window=3, d=16):
+        rng = np.random.default_rng(seed)
+        self.E = rng.standard_normal((V, d))
+        self.W = rng.standard_normal((d, V)) * 1.5
+        self.V, self.noise, self.noise_seed, self.window = V, noise, noise_seed, window
+
+    def logits(self, seq):
+        h = np.zeros(self.E.shape[1])
+        for w, tok in enumerate(reversed(seq[-self.window:])):
+            h += (0.6 ** w) * self.E[tok]
+        out = np.tanh(h) @ self.W
+        if self.noise:
+            key = zlib.crc32(np.asarray(seq, np.int64).tobytes()) ^ self.noise_seed
+            out = out + self.noise * np.random.default_rng(key).standard_normal(self.V)
+        return out
+
+    def probs(self, seq):
+        z = self.logits(seq)
+        e = np.exp(z - z.max())
+        return (e / e.sum()).astype(np.float32)
+
+
+def speculative_round(target, draft, seq, k, S, N, remaining=None, eos_id=-1):
+    tb = otree.TreeBuilder(k, S)
+    p0, i0 = otopk.draft_topk(draft.probs(seq)[None], k)
+    tb.start(p0[0], i0[0])
+    for _ in range(1, S):
+        rows_p, rows_i = [], []
+        for e in tb.frontier:
+            p, i = otopk.draft_topk(draft.probs(seq + tb.path_tokens(e))[None], k)
+            rows_p.append(p[0])
+            rows_i.append(i[0])
+        tb.expand(rows_p, rows_i)
+    t = tb.finalize(N, seq[-1], len(seq) - 1)
+    rows = []
+    for u in range(N):
+        path, v = [], u
+        while v > 0:
+            path.append(int(t["tokens"][v]))
+            v = int(t["parent"][v])
+        rows.append(target.logits(seq + path[::-1]))
+    tree = {key: val[None] for key, val in t.items()}
+    rem = None if remaining is None else np.array([remaining])
+    r = oacc.verify_greedy(tree, np.array(rows)[None], S=S, eos_id=eos_id, remaining=rem)
+    return r["commit_tokens"][0, :r["commit_len"][0]].tolist(), int(r["accept_len"][0])
+
+
+@pytest.mark.parametrize("k,S,N,V,noise", [(1, 4, 5, 16, 0.3), (2, 3, 6, 32, 0.5),
+                                           (4, 3, 10, 48, 0.8), (3, 4, 12, 64, 0.2),
+                                           (8, 2, 9, 24, 1.0)])
+def test_greedy_speculation_equals_target_only(k, S, N, V, noise):
+    target = TinyLM(V, seed=V + k)
+    draft = TinyLM(V, seed=V + k, noise=noise, noise_seed=7)
+    prompt = [1, 2, 3]
+    budget = 40
+    ref = list(prompt)
+    while len(ref) < len(prompt) + budget:
+        ref.append(int(np.argmax(target.logits(ref))))
+    seq = list(prompt)
+    accepted = 0
+    while len(seq) < len(prompt) + budget:
+        out, a = speculative_round(target, draft, seq, k, S, N,
+                                   remaining=len(prompt) + budget - len(seq))
+        assert 1 <= len(out) <= S + 1
+        seq += out
+        accepted += a
+    assert seq == ref
+    assert accepted > 0          # the draft is good enough to be accepted sometimes
+
+
+def test_greedy_speculation_with_eos_stops_like_target_only():
+    V = 20
+    target = TinyLM(V, seed=3)
+    draft = TinyLM(V, seed=3, noise=0.3, noise_seed=1)
+    ref = [4]
+    while True:
+        ref.append(int(np.argmax(target.logits(ref))))
+        if len(ref) > 60:
+            break
+    eos = ref[10]                 # some token the target emits
+    stop = ref.index(eos, 1)
+    seq = [4]
+    while seq[-1] != eos or len(seq) == 1:
+        out, _ = speculative_round(target, draft, seq, 2, 3, 6, eos_id=eos)
+        seq += out
+        if eos in out:
+            assert out[-1] == eos
+            break
+    assert seq == ref[:stop + 1]
+
+
+# --------------------------------------------------- stochastic: exact
+
+def _one_child_tree(y):
+    t = otree.verify_arrays(np.array([0, y], np.int32), np.array([-1, 0], np.int32),
+                            np.array([0, 1], np.int32), np.ones(2, np.float32),
+                            np.array([0, -1], np.int32), 0, 0)
+    return {k: v[None] for k, v in t.items()}
+
+
+def _first_token(p, q, y, ka, kd):
+    V = len(p)
+    t = _one_child_tree(y)
+    prow = np.stack([np.asarray(p, np.float32), np.full(V, 1.0 / V, np.float32)])[None]
+    u_acc = np.array([[0.0, ka * 2.0 ** -24]], np.float32)
+    u_draw = np.array([[kd * 2.0 ** -24, 0.0]], np.float32)
+    r = oacc.verify_stochastic(t, prow, np.asarray(q, np.float32)[None, None], u_acc, u_draw, S=1)
+    return int(r["commit_tokens"][0, 0]), int(r["accept_len"][0])
+
+
+def _first_monotone_change(f, lo, hi):
+    """Least x in (lo, hi] with f(x) != f(lo) for a monotone step function f
+    (once it leaves f(lo) it never returns); hi + 1 if none."""
+    base = f(lo)
+    if f(hi) == base:
+        return hi + 1
+    a, b = lo, hi
+    while b - a > 1:
+        m = (a + b) // 2
+        if f(m) == base:
+            a = m
+        else:
+            b = m
+    return b
+
+
+def enumerate_first_token(p, q_exact, y_support):
+    """Exact P(first committed token = v), y ~ q (rational), all 2**24 x 2**24
+    uniform pairs, using that acceptance is monotone in u_accept and the draw
+    is monotone in u_draw (both follow from the sampling contract)."""
+    V = len(p)
+    q32 = np.array([float(x) for x in q_exact], np.float32)
+    tot = {v: Fraction(0) for v in range(V)}
+    n = 1 << 24
+    for y in y_support:
+        n_acc = _first_monotone_change(lambda ka: _first_token(p, q32, y, ka, 0)[1], 0, n - 1)
+        if _first_token(p, q32, y, 0, 0)[1] == 0:
+            n_acc = 0
+        # the draw after a rejection: boundaries of the non-decreasing token map
+        counts = {}
+        if n_acc < n:
+            ka = n_acc
+            lo = 0
+            while lo < n:
+                v = _first_token(p, q32, y, ka, lo)[0]
+                nxt = _first_monotone_change(lambda kd: _first_token(p, q32, y, ka, kd)[0], lo, n - 1)
+                counts[v] = counts.get(v, 0) + (nxt - lo)
+                lo = nxt
+        w = Fraction(q_exact[y])
+        tot[y] += w * Fraction(n_acc, n)
+        for v, c in counts.items():
+            tot[v] += w * Fraction(n - n_acc, n) * Fraction(c, n)
+    return tot
+
+
+def test_page_two_token_example_exact(golden_dir):
+    g = _golden(golden_dir, "stochastic_two_token.json")
+    q = [Fraction(4, 5), Fraction(1, 5)]
+    tot = enumerate_first_token(g["p"], q, [0, 1])
+    assert tot[0] == Fraction(*g["expected"]["0"])
+    assert tot[1] == Fraction(*g["expected"]["1"])
+
+
+def test_planted_resample_from_p_is_caught(golden_dir, monkeypatch):
+    """Planting the page's wrong variant (redraw from p after a rejection) in
+    the oracle moves the output distribution to 14/25, 11/25."""
+    g = _golden(golden_dir, "stochastic_two_token.json")
+    monkeypatch.setattr(oacc, "_rejection_draw_masses", lambda p_u, t, last: oacc.masses(p_u))
+    tot = enumerate_first_token(g["p"], [Fraction(4, 5), Fraction(1, 5)], [0, 1])
+    assert tot[0] != Fraction(*g["expected"]["0"])
+    assert abs(float(tot[0]) - 14 / 25) < 1e-6
+    assert abs(float(tot[1]) - 11 / 25) < 1e-6
+
+
+@pytest.mark.parametrize("p,q", [
+    ([Fraction(1, 4), Fraction(1, 2), Fraction(1, 4)], [Fraction(1, 2), Fraction(1, 4), Fraction(1, 4)]),
+    ([Fraction(3, 8), Fraction(5, 8)], [Fraction(1, 2), Fraction(1, 2)]),
+    ([Fraction(1, 16), Fraction(7, 16), Fraction(5, 16), Fraction(3, 16)],
+     [Fraction(1, 4), Fraction(1, 4), Fraction(1, 4), Fraction(1, 4)]),
+    ([Fraction(0), Fraction(1, 2), Fraction(1, 2)], [Fraction(1, 2), Fraction(0), Fraction(1, 2)]),
+    ([Fraction(1, 2), Fraction(1, 2), Fraction(0)], [Fraction(1, 4), Fraction(1, 4), Fraction(1, 2)]),
+])
+def test_rejection_sampling_preserves_p_dyadic(p, q):
+    """Dyadic p, power-of-two q: the sampled first token is distributed exactly as p."""
+    support = [y for y in range(len(q)) if q[y] > 0]
+    tot = enumerate_first_token([float(x) for x in p], q, support)
+    assert [tot[v] for v in range(len(p))] == list(p)
+
+
+def test_rejection_sampling_preserves_p_random_within_quantisation():
+    rng = np.random.default_rng(11)
+    for _ in range(3):
+        V = 4
+        p = workloads.softmax_rows(rng.standard_normal((1, V)).astype(np.float32) * 2)[0]
+        q = workloads.softmax_rows(rng.standard_normal((1, V)).astype(np.float32) * 2)[0]
+        qf = [Fraction(float(x)) for x in q]
+        s = sum(qf)
+        qf = [x / s for x in qf]
+        tot = enumerate_first_token(p, qf, list(range(V)))
+        for v in range(V):
+            assert abs(float(tot[v]) - float(p[v])) < 1e-6
+
+
+def test_sampling_primitives():
+    # masses are exact fixed point; S sums in any order
+    r = np.array([0.5, 2.0 ** -30, 0.25, 0.0], np.float32)
+    R = oacc.masses(r)
+    assert R.tolist() == [1 << 39, 1 << 10, 1 << 38, 0]
+    # draw: T = floor(kk * S / 2**24); least i whose running mass exceeds T
+    R = np.array([3, 0, 5], np.uint64)
+    assert oacc.inverse_cdf(R, 0.0) == 0
+    kk = (3 << 24) // 8                       # T = floor(kk * 8 / 2**24) = 3 -> index 2
+    assert oacc.inverse_cdf(R, np.float32(kk * 2.0 ** -24)) == 2
+    assert oacc.inverse_cdf(R, np.float32(((1 << 24) - 1) * 2.0 ** -24)) == 2
+    # accept test is strict: u * q == t rejects
+    assert not oacc.accept_test(np.float32(0.5), np.float32(0.8), np.float32(0.4))
+    assert oacc.accept_test(np.float32(0.5 - 2 ** -24), np.float32(0.8), np.float32(0.4))
+
+
+# --------------------------------------------------- stochastic invariants
+
+def test_stochastic_invariants_on_configs():
+    for name in ("c2", "c4"):
+        cfg = workloads.get_config(name, V=300, B=6)
+        inp = workloads.generate(cfg, with_attention=False)
+        # plant agreement so that walks go deep: p rows = q rows of the parent
+        tp, ti = otopk.draft_topk(inp["draft_probs"], cfg.k)
+        t = otree.build_tree(tp, ti, inp["root_token"], inp["prefix_len"], cfg.k, cfg.S, cfg.N)
+        for planted in (False, True):
+            p = inp["target"].copy()
+            if planted:
+                for b in range(cfg.B):
+                    for u in range(cfg.N):
+                        if t["q_row"][b, u] >= 0:
+                            p[b, u] = inp["draft_probs"][b, t["q_row"][b, u]]
+            r = oacc.verify_stochastic(t, p, inp["draft_probs"], inp["u_accept"], inp["u_draw"], S=cfg.S)
+            for b in range(cfg.B):
+                a = r["accept_len"][b]
+                path = r["accept_path"][b, :a + 1]
+                assert r["commit_len"][b] == a + 1
+                assert path[0] == 0
+                for d in range(1, a + 1):
+                    assert t["parent"][b, path[d]] == path[d - 1]
+                    assert r["commit_tokens"][b, d - 1] == t["tokens"][b, path[d]]
+                assert r["next_root"][b] == r["commit_tokens"][b, a]
+            if planted:
+                assert r["accept_len"].mean() > 1

@@ -1,0 +1,194 @@
+"""Pins of the oracle's draft top-k and tree build against facts outside it."""
+import functools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import topk as otopk
+from oracle import tree as otree
+import workloads
+
+
+# ------------------------------------------------------------------ top-k
+
+def test_topk_k1_is_library_argmax():
+    rng = np.random.default_rng(1)
+    p = rng.random((50, 333)).astype(np.float32)
+    p[7, 10] = p[7, 200] = 2.0                     # a tie: the lower id wins
+    vals, ids = otopk.draft_topk(p, 1)
+    assert np.array_equal(ids[:, 0], np.argmax(p, axis=1))
+    assert ids[7, 0] == 10
+    assert np.array_equal(vals[:, 0], p.max(axis=1))
+
+
+def test_topk_matches_python_sorted_with_ties():
+    rng = np.random.default_rng(2)
+    # few distinct values -> many ties
+    p = (rng.integers(0, 6, size=(40, 57)) / 8.0).astype(np.float32)
+    for k in (1, 2, 5, 8, 57):
+        vals, ids = otopk.draft_topk(p, k)
+        for r in range(p.shape[0]):
+            want = sorted(range(p.shape[1]), key=lambda i: (-float(p[r, i]), i))[:k]
+            assert ids[r].tolist() == want
+            assert vals[r].tolist() == [float(p[r, i]) for i in want]
+
+
+def test_topk_rejects_bad_k():
+    with pytest.raises(ValueError):
+        otopk.draft_topk(np.zeros((1, 4), np.float32), 5)
+
+
+# ------------------------------------------------------------------- tree
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("N", [6, 7])
+def test_tree_hand_worked_example(golden_dir, N):
+    g = _golden(golden_dir, "hand_tree_k2s3.json")
+    tp = np.array([g["topk_p"]], np.float32)
+    ti = np.array([g["topk_id"]], np.int32)
+    t = otree.build_tree(tp, ti, np.array([g["root_token"]]), np.array([g["prefix_len"]]),
+                         g["k"], g["S"], N)
+    want = g["N%d" % N]
+    for key in ("tokens", "parent", "depth", "q_row", "next_token", "next_sibling"):
+        assert t[key][0].tolist() == want[key], key
+    assert t["score"][0].tolist() == want["score"]
+    if "positions" in want:
+        assert t["positions"][0].tolist() == want["positions"]
+    if "mask_rows" in want:
+        for i, row in enumerate(want["mask_rows"]):
+            assert np.flatnonzero(t["mask"][0, i]).tolist() == row
+    assert t["retrieve_index"][0].tolist() == list(range(N))
+
+
+def test_exercise_frontier_count(golden_dir):
+    """num_steps=3, topk=4: the steps expand 4+4+4 = 12 frontier candidates."""
+    g = _golden(golden_dir, "exercise_candidates.json")
+    k, S = g["topk"], g["num_steps"]
+    rng = np.random.default_rng(3)
+    probs = workloads.softmax_rows(rng.standard_normal((1, 1 + (S - 1) * k, 64)).astype(np.float32))
+    tp, ti = otopk.draft_topk(probs, k)
+    tb = otree.TreeBuilder(k, S)
+    tb.start(tp[0, 0], ti[0, 0])
+    frontiers = [list(tb.frontier)]
+    for _ in range(1, S):
+        rows = tb.frontier_rows()
+        tb.expand([tp[0, r] for r in rows], [ti[0, r] for r in rows])
+        frontiers.append(list(tb.frontier))
+    assert sum(len(f) for f in frontiers) == g["expanded_candidates"]
+    # draft passes: one per step plus the draft extend; the verify is one target pass
+    assert S + 1 == g["draft_passes"]
+    # the root's row and one row per frontier slot of every step but the last
+    assert workloads.num_draft_rows(k, S) == 1 + (S - 1) * k
+
+
+def test_k1_is_a_chain():
+    """topk=1: the tree is the chain of top-1 tokens, N = S + 1."""
+    rng = np.random.default_rng(4)
+    S = 5
+    probs = workloads.softmax_rows(rng.standard_normal((3, S, 100)).astype(np.float32))
+    tp, ti = otopk.draft_topk(probs, 1)
+    t = otree.build_tree(tp, ti, np.array([1, 2, 3]), np.array([10, 20, 30]), 1, S, S + 1)
+    for b in range(3):
+        assert t["parent"][b].tolist() == [-1] + list(range(S))
+        assert t["tokens"][b, 1:].tolist() == [int(np.argmax(probs[b, r])) for r in range(S)]
+        assert t["depth"][b].tolist() == list(range(S + 1))
+        assert t["positions"][b].tolist() == [10 * (b + 1) + d for d in range(S + 1)]
+        assert t["q_row"][b].tolist() == list(range(S)) + [-1]
+
+
+def _brute_tree(tp, ti, k, S, N):
+    """Independent restatement on paths: a candidate carries the list of draft
+    probabilities along its path from the root; its score is the left fold of
+    fp32 products over that list; its pool key is (step, parent's frontier
+    slot, child rank)."""
+    def score(cand):
+        return functools.reduce(lambda a, x: np.float32(a * np.float32(x)), cand[1], np.float32(1.0))
+
+    cands = []   # (key, path probabilities, token, parent key)
+    level = [((0, 0, c), [tp[0][c]], int(ti[0][c]), None) for c in range(k)]
+    cands.extend(level)
+    for i in range(1, S):
+        ranked = sorted(level, key=lambda e: (-float(score(e)), e[0]))[:k]
+        nxt = []
+        for j, par in enumerate(ranked):
+            row = 1 + (i - 1) * k + j
+            for c in range(k):
+                nxt.append(((i, j, c), par[1] + [tp[row][c]], int(ti[row][c]), par[0]))
+        cands.extend(nxt)
+        level = nxt
+    chosen = sorted(cands, key=lambda e: (-float(score(e)), e[0]))[:N - 1]
+    chosen.sort(key=lambda e: e[0])
+    return [(c[0], score(c), c[2], c[3]) for c in chosen]
+
+
+@pytest.mark.parametrize("k,S,N,seed", [(2, 3, 6, 0), (2, 3, 11, 1), (3, 3, 9, 2), (4, 4, 32, 3),
+                                        (8, 3, 40, 4), (2, 5, 19, 5), (3, 2, 13, 6)])
+def test_tree_matches_brute_force_on_paths(k, S, N, seed):
+    rng = np.random.default_rng(seed)
+    R = 1 + (S - 1) * k
+    # coarse probabilities -> frequent score ties
+    probs = (rng.integers(1, 9, size=(1, R, 24)) / 16.0).astype(np.float32)
+    tp, ti = otopk.draft_topk(probs, k)
+    t = otree.build_tree(tp, ti, np.array([5]), np.array([0]), k, S, N)
+    chosen = _brute_tree(tp[0], ti[0], k, S, N)
+    assert t["tokens"][0, 1:].tolist() == [c[2] for c in chosen]
+    assert t["score"][0, 1:].tolist() == [float(c[1]) for c in chosen]
+    assert t["depth"][0, 1:].tolist() == [c[0][0] + 1 for c in chosen]
+    key_to_node = {c[0]: i + 1 for i, c in enumerate(chosen)}
+    assert t["parent"][0, 1:].tolist() == [0 if c[3] is None else key_to_node[c[3]] for c in chosen]
+
+
+def test_tree_invariants_on_config_shapes():
+    """Ancestor closure, depth, mask = reflexive-transitive closure of parent,
+    retrieve lists = children in ascending order, scores = path products."""
+    for name in ("c1", "c3", "c4"):
+        cfg = workloads.get_config(name, V=512, B=3)
+        inp = workloads.generate(cfg, with_attention=False)
+        tp, ti = otopk.draft_topk(inp["draft_probs"], cfg.k)
+        t = otree.build_tree(tp, ti, inp["root_token"], inp["prefix_len"], cfg.k, cfg.S, cfg.N)
+        for b in range(cfg.B):
+            par = t["parent"][b]
+            for i in range(1, cfg.N):
+                assert 0 <= par[i] < i
+                assert t["depth"][b, i] == t["depth"][b, par[i]] + 1
+                # the node's token is one of its parent's draft row's top-k, and
+                # its score is parent score x that probability (fp32)
+                r = t["q_row"][b, par[i]]
+                c = ti[b, r].tolist().index(t["tokens"][b, i])
+                assert t["score"][b, i] == np.float32(t["score"][b, par[i]] * tp[b, r, c])
+                anc = set()
+                j = i
+                while j >= 0:
+                    anc.add(j)
+                    j = par[j]
+                assert set(np.flatnonzero(t["mask"][b, i]).tolist()) == anc
+                assert t["mask"][b, i].sum() == t["depth"][b, i] + 1
+                for j in range(cfg.N):
+                    bit = (int(t["mask_bits"][b, i, j // 32]) >> (j % 32)) & 1
+                    assert bit == t["mask"][b, i, j]
+            for u in range(cfg.N):
+                kids = [i for i in range(1, cfg.N) if par[i] == u]
+                walk, c = [], t["next_token"][b, u]
+                while c >= 0:
+                    walk.append(int(c))
+                    c = t["next_sibling"][b, c]
+                assert walk == kids
+                if kids:
+                    assert t["q_row"][b, u] >= 0
+            assert t["depth"][b].max() <= cfg.S
+
+
+def test_full_pool_tree_structure():
+    """N - 1 = M: the tree is every expansion; k=2, S=2 -> a full binary tree."""
+    rng = np.random.default_rng(9)
+    probs = workloads.softmax_rows(rng.standard_normal((1, 3, 50)).astype(np.float32))
+    tp, ti = otopk.draft_topk(probs, 2)
+    t = otree.build_tree(tp, ti, np.array([0]), np.array([0]), 2, 2, 7)
+    assert t["parent"][0].tolist() == [-1, 0, 0, 1, 1, 2, 2]
+    assert sorted(t["depth"][0].tolist()) == [0, 1, 1, 2, 2, 2, 2]
