@@ -1,0 +1,281 @@
+/*
+ * sdv.h -- C ABI of the MI355X (gfx950) library for the draft-tree build and
+ * target-side verify step of EAGLE-style speculative decoding.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers named "device" point to HIP device memory; pointers named "host"
+ *   to host memory.  The caller owns every buffer; the library never frees
+ *   caller memory and allocates nothing on these calls.  Scratch memory comes
+ *   from a caller buffer `ws` of at least the bytes the matching
+ *   `*_workspace_size` reports (NULL allowed when that size is 0).
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream) and performs no host synchronisation.  Outputs are valid once
+ *   the stream reaches the call.  Calls are thread-safe; calls that share a
+ *   workspace must not overlap on different streams.
+ * - Arrays are dense, row-major, with the shapes given in brackets.  Token
+ *   ids, positions, tree indices, slots and pages are int32.  bf16 values are
+ *   passed as their raw 16-bit patterns (uint16_t).
+ * - Inputs never alias outputs, except the documented in/out buffers of
+ *   sdv_compact_kv.
+ * - Return value: SDV_OK, or a negative status.  On error nothing has been
+ *   enqueued, and sdv_last_error() returns a message for the calling thread.
+ *   Shape checks run on the host; the kernels additionally clamp or skip
+ *   out-of-range indices read from device arrays instead of faulting (the
+ *   results of such inputs are unspecified).
+ *
+ * Notation: B requests, k = topk, S = draft steps, N = tree size (root
+ * included), V vocabulary, R = 1 + (S-1)*k draft-distribution rows per
+ * request, M = k + (S-1)*k*k candidates per request.
+ */
+#ifndef SDV_H
+#define SDV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SDV_OK = 0,
+  SDV_E_NULL = -1,        /* a required pointer is NULL */
+  SDV_E_SHAPE = -2,       /* inconsistent shape (e.g. N-1 > M, Hq % Hkv != 0, k > V) */
+  SDV_E_UNSUPPORTED = -3, /* a size outside what the kernels implement */
+  SDV_E_WORKSPACE = -4,   /* workspace missing or too small */
+  SDV_E_HIP = -5          /* the HIP runtime reported an error */
+};
+
+enum { SDV_ACCEPT_GREEDY = 0, SDV_ACCEPT_STOCHASTIC = 1 };
+
+/* Message describing the last error of the calling thread ("" if none). */
+const char *sdv_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int32_t sdv_version(void);
+
+/* ------------------------------------------------------------------------
+ * A1  Draft vocabulary top-k.
+ * "[SGLang] Multi-Layer EAGLE", section 3 (draft extend): the per-step softmax
+ * is reduced by fast_topk(probs, topk) to topk_p / topk_index.
+ *
+ * For every row r of probs (device, [rows, V] fp32, no NaN) writes the k
+ * largest values in descending order to topk_p (device, [rows, k] fp32) and
+ * their column ids to topk_id (device, [rows, k] int32).  Equal values are
+ * ordered by ascending id.  1 <= k <= 32, k <= V, V < 2^31.
+ * ---------------------------------------------------------------------- */
+size_t sdv_draft_topk_workspace_size(int64_t rows, int32_t V, int32_t k);
+int32_t sdv_draft_topk(const float *probs, int64_t rows, int32_t V, int32_t k,
+                       float *topk_p, int32_t *topk_id, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
+ * A2-A4  Candidate tree, positions, mask and retrieve arrays.
+ * "[SGLang] Multi-Layer EAGLE", section 2 (select_top_k_tokens builds
+ * tree_info = scores, tokens, parents with cumulative scores);
+ * "EAGLE speculative decoding in four parts", "Drafting, verification and
+ * slots" (build_eagle_tree expands the candidates into a tree and produces
+ * the attention mask and positions) and "Exercises" (topk*S expansions plus
+ * the root); zero-to-sglang ch.10 section 5.2 (verify input: draft tokens,
+ * positions, custom mask, retrieve arrays).
+ *
+ * Inputs (device): topk_p / topk_id [B, R, k] -- row 0 is the root's top-k,
+ * row 1 + i*k + j the top-k after frontier slot j of draft step i;
+ * root_token [B]; prefix_len [B] (tokens whose KV is cached).
+ * Step 0 pools the root's k children (score = prob).  Step i >= 1 pools the k
+ * children of every frontier slot j (score = fp32 product parent*prob, pool
+ * index = step, slot, child rank); the next frontier is the best k of them.
+ * The tree is node 0 = root plus the best N-1 pool entries (score desc, pool
+ * index asc) in ascending pool index.  topk_p must lie in [0, 1].
+ * Outputs (device, [B, N] unless noted):
+ *   tokens, parent (-1 for the root), depth, positions = prefix_len + depth,
+ *   score (fp32, root 1.0), q_row (draft row of the node's children; -1 if
+ *   the node was never expanded; 0 for the root),
+ *   mask [B, N, N] uint8 (1 iff column j is the row's node or an ancestor;
+ *   NULL to skip), mask_bits [B, N, ceil(N/32)] uint32 (bit j%32 of word j/32;
+ *   NULL to skip), retrieve_index (b*N + i), retrieve_next_token (smallest
+ *   child or -1), retrieve_next_sibling (next larger sibling or -1).
+ * Limits: 1 <= k <= 32, S >= 1, 1 <= N <= min(M + 1, 256), M <= 2048.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t B, k, S, N;
+} sdv_tree_shape;
+
+int32_t sdv_build_tree(sdv_tree_shape shape, const float *topk_p, const int32_t *topk_id,
+                       const int32_t *root_token, const int32_t *prefix_len, int32_t *tokens,
+                       int32_t *parent, int32_t *depth, int32_t *positions, float *score,
+                       int32_t *q_row, uint8_t *mask, uint32_t *mask_bits,
+                       int32_t *retrieve_index, int32_t *retrieve_next_token,
+                       int32_t *retrieve_next_sibling, void *stream);
+
+/* ------------------------------------------------------------------------
+ * A5  Tree-verify attention.
+ * "EAGLE speculative decoding in four parts": verification is one target
+ * forward over 1 + candidates tokens per request with a tree attention mask
+ * ("Self-test" answer 1, "Exercises" question 1, "Design trade-offs");
+ * "[SGLang] Multi-Layer EAGLE" section 6 (TARGET_VERIFY with the custom mask).
+ *
+ * For request b, node i, query head h: attends to every prefix key (logical
+ * positions 0 .. prefix_len[b]-1) and to tree key j (logical position
+ * prefix_len[b] + j) iff bit j of mask_bits[b, i] is set;
+ * out = softmax(sm_scale * q.k) v over those keys, KV head h / (Hq/Hkv).
+ * q: device [B, N, Hq, D] bf16.  k_pool, v_pool: device [num_slots, Hkv, D]
+ * bf16 (token-major).  page_table: device [B, max_pages] int32; logical
+ * position p lives in slot page_table[b][p / page] * page + p % page
+ * (page == 1: a slot map).  prefix_len: device [B], with
+ * prefix_len + N <= max_pages * page.  mask_bits: device [B, N, ceil(N/32)].
+ * out: device [B, N, Hq, D] bf16; lse: device [B, N, Hq] fp32 natural-log
+ * sum of exp(sm_scale * q.k) (NULL to skip).  sm_scale <= 0 selects
+ * 1/sqrt(D).  Limits: D in {64, 128}, 1 <= N <= 256, Hq % Hkv == 0,
+ * Hq/Hkv <= 16.  Keys whose page id falls outside the pool are skipped.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t B, N, Hq, Hkv, D, page, max_pages;
+  int64_t num_slots;
+} sdv_attn_shape;
+
+size_t sdv_tree_verify_attention_workspace_size(sdv_attn_shape shape);
+int32_t sdv_tree_verify_attention(sdv_attn_shape shape, float sm_scale, const uint16_t *q,
+                                  const uint16_t *k_pool, const uint16_t *v_pool,
+                                  const int32_t *page_table, const int32_t *prefix_len,
+                                  const uint32_t *mask_bits, uint16_t *out, float *lse,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * A6-A7  Target row reductions and the accept walk.
+ * zero-to-sglang ch.10: section 3.3 (row alignment: a node's target row
+ * verifies its children; the last row picks the bonus), section 4.1
+ * (greedy_commit: commit the target's choice, stop at the first mismatch, at
+ * EOS or when the budget is used up; bonus after a full match), section 5.1
+ * (accept y with probability min(1, p[y]/q[y]); on rejection draw from the
+ * normalised positive residual; bonus from p); "EAGLE speculative decoding
+ * in four parts", "Drafting, verification and slots" (the verification
+ * kernels walk each request's tree to its longest accepted path).
+ *
+ * Tree inputs (device, [B, N]): tokens, next_token, next_sibling (as written
+ * by sdv_build_tree), q_row (stochastic only).  target: device [B, N, V] fp32,
+ * row u = the target after node u (GREEDY: logits; STOCHASTIC: processed
+ * probabilities p).  draft_probs: device [B, R, V] fp32 processed draft
+ * distributions (STOCHASTIC only; may be NULL for GREEDY).  u_accept, u_draw:
+ * device [B, N] fp32 uniforms of the form kk * 2^-24 (STOCHASTIC only):
+ * u_accept[b, c] decides child node c, u_draw[b, u] is the draw at node u.
+ * eos_id: token that ends a request (-1: none).  remaining: device [B]
+ * output budgets (NULL: unlimited).
+ * Greedy: at node u take t = argmax(row u) (lowest id on ties), commit t,
+ * stop on EOS or budget, move to the child carrying t or stop.
+ * Stochastic: t := p_u; for the children in sibling order accept child c iff
+ * double(u_accept) * double(q[y]) < double(t[y]); on rejection
+ * r = max(t - q, 0) (fp32), masses floor(r * 2^40) (uint64, sum S), and
+ * t := fp32(double(r) / (double(S) * 2^-40)) when S > 0.  All children
+ * rejected: draw from the last residual's masses; leaf: draw from
+ * floor(p * 2^40); draw T = floor(kk * S / 2^24), token = least i whose
+ * running mass exceeds T; zero total mass: argmax of t.
+ * Outputs (device): accept_len [B]; accept_path [B, S+1] (tree indices, root
+ * first, -1 padded); commit_tokens [B, S+1] (-1 padded); commit_len [B];
+ * next_root [B] (last committed token, -1 if none).
+ * Limits: V < 2^31 - 4, N <= 256, S + 1 <= 64.  The walk runs as one
+ * cooperative launch; calls that share a workspace must not overlap.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t B, N, S, V, R, mode;
+} sdv_accept_shape;
+
+size_t sdv_verify_accept_workspace_size(sdv_accept_shape shape);
+int32_t sdv_verify_accept(sdv_accept_shape shape, int32_t eos_id, const int32_t *remaining,
+                          const int32_t *tokens, const int32_t *next_token,
+                          const int32_t *next_sibling, const int32_t *q_row, const float *target,
+                          const float *draft_probs, const float *u_accept, const float *u_draw,
+                          int32_t *accept_len, int32_t *accept_path, int32_t *commit_tokens,
+                          int32_t *commit_len, int32_t *next_root, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* ------------------------------------------------------------------------
+ * A8  KV compaction of the accepted path and release of the rest.
+ * "EAGLE speculative decoding in four parts": slots for every candidate are
+ * reserved before drafting; after verification only the accepted path's
+ * slots are kept and the rest freed, and with page size > 1 the last page is
+ * copied ("Self-test" answer 3, "Drafting, verification and slots",
+ * "Design trade-offs"); zero-to-sglang ch.10 section 5.2 (the cache returns
+ * to the committed path; the correction or bonus token has no KV yet).
+ *
+ * Tree of request b: logical positions L .. L+N-1 (node j at L + j, L =
+ * prefix_len[b]).  accept_len [B] = a, accept_path [B, S+1] = path (path[0]
+ * = 0, strictly increasing, < N), both device.  Position L + d must end up
+ * holding node path[d]'s KV, d = 0..a; new_len[b] = L + a + 1.
+ * page == 1: page_table (device [B, max_pages], in/out) is a slot map;
+ * entries L + d are remapped, L+a+1 .. L+N-1 set to -1, no KV bytes move,
+ * and the rejected nodes' old slots are freed in ascending node order.
+ * page > 1: the K and V rows [Hkv, D] of every layer are copied from
+ * position L + path[d] to L + d (all reads of a request happen before its
+ * writes); logical pages ceil(new_len/page) .. (L+N-1)/page are set to -1
+ * in page_table and their page ids freed in page order.
+ * k_pools, v_pools: HOST arrays of `layers` device pointers to
+ * [num_slots, Hkv, D] bf16 pools (in/out; unused when page == 1).
+ * freed: device [B*N] int32, the freed ids of all requests in batch order;
+ * num_freed: device [1] int32.  new_len: device [B].
+ * Limits: N <= 256, layers <= 128, (Hkv * D) % 8 == 0 when page > 1.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t B, N, S, page, Hkv, D, layers, max_pages;
+  int64_t num_slots;
+} sdv_kv_shape;
+
+size_t sdv_compact_kv_workspace_size(sdv_kv_shape shape);
+int32_t sdv_compact_kv(sdv_kv_shape shape, uint16_t *const *k_pools, uint16_t *const *v_pools,
+                       int32_t *page_table, const int32_t *prefix_len, const int32_t *accept_len,
+                       const int32_t *accept_path, int32_t *new_len, int32_t *freed,
+                       int32_t *num_freed, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * A9  TLI pruned draft LM head.
+ * sglang PR #22883 "TLI (Token-Level Intersection)", "Modifications": the
+ * draft LM head becomes a compact [intersection_size x hidden_dim] matrix,
+ * turning the dominant draft matmul from O(B*V_draft*H) into O(B*K*H).
+ *
+ * logits[b, j] = sum_h hidden[b, h] * weight[j, h] with fp32 accumulation.
+ * hidden: device [B, H] bf16; weight: device [K, H] bf16 (row j belongs to
+ * draft id intersection_draft_ids[j]); logits: device [B, K] fp32.
+ * Limits: H % 32 == 0, B >= 1, K >= 1.
+ * ---------------------------------------------------------------------- */
+int32_t sdv_tli_lm_head(int32_t B, int32_t H, int32_t K, const uint16_t *hidden,
+                        const uint16_t *weight, float *logits, void *stream);
+
+/* ------------------------------------------------------------------------
+ * A10  TLI vocabulary maps, logit constraint and distribution scatter.
+ * sglang PR #22883, "Modifications": constrain_draft_logits (logits outside
+ * the intersection -> -inf), map_target_to_draft_ids,
+ * map_draft_to_target_ids, sorted intersection_draft_ids, EOS fallback for
+ * models without an unknown token; the target's rejection sampling is
+ * unchanged.
+ *
+ * sdv_tli_build_maps: from K pairs (inter_ids[j] draft id, tgt_ids[j] target
+ * id; device [K] each, in range, distinct) writes d2t (device [V_draft], -1
+ * outside the intersection) and t2d (device [V_target], `fallback` outside).
+ * sdv_tli_map_ids: out[i] = table[ids[i]] (device arrays; ids outside
+ * [0, table_len) give -1) -- map_target_to_draft_ids with t2d,
+ * map_draft_to_target_ids with d2t.
+ * sdv_tli_constrain_draft_logits: full[b, inter_ids[j]] = pruned[b, j], -inf
+ * elsewhere; pruned device [B, K] fp32, inter_ids device [K] sorted
+ * ascending, full device [B, V_draft] fp32.
+ * sdv_tli_q_scatter: q_target[r, tgt_ids[j]] = q_pruned[r, j], 0 elsewhere;
+ * q_pruned device [rows, K] fp32, q_target device [rows, V_target] fp32;
+ * the workspace holds the inverse of tgt_ids.
+ * ---------------------------------------------------------------------- */
+int32_t sdv_tli_build_maps(int32_t K, const int32_t *inter_ids, const int32_t *tgt_ids,
+                           int32_t V_draft, int32_t V_target, int32_t fallback, int32_t *d2t,
+                           int32_t *t2d, void *stream);
+int32_t sdv_tli_map_ids(const int32_t *table, int32_t table_len, const int32_t *ids, int64_t n,
+                        int32_t *out, void *stream);
+int32_t sdv_tli_constrain_draft_logits(int32_t B, int32_t K, int32_t V_draft, const float *pruned,
+                                       const int32_t *inter_ids, float *full, void *stream);
+size_t sdv_tli_q_scatter_workspace_size(int32_t V_target);
+int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, const float *q_pruned,
+                          const int32_t *tgt_ids, float *q_target, void *ws, size_t ws_bytes,
+                          void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDV_H */

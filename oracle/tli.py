@@ -41,11 +41,13 @@ def build_maps(inter_ids, tgt_ids, V_draft: int, V_target: int, fallback: int):
 
 
 def map_ids(table, ids):
-    """out[i] = table[ids[i]] (ids must lie inside the table)."""
+    """out[i] = table[ids[i]]; an id outside the table maps to -1."""
     ids = np.asarray(ids, np.int64)
-    if ids.size and (ids.min() < 0 or ids.max() >= len(table)):
-        raise IndexError("id outside the map")
-    return np.asarray(table, np.int32)[ids]
+    table = np.asarray(table, np.int32)
+    out = np.full(ids.shape, -1, np.int32)
+    ok = (ids >= 0) & (ids < len(table))
+    out[ok] = table[ids[ok]]
+    return out
 
 
 def constrain_logits(pruned, inter_ids, V_draft: int):

@@ -1,0 +1,24 @@
+"""EAGLE-style draft-tree build and target-side verify on MI355X (gfx950).
+
+The compute lives in libsdv.so (HIP kernels behind the C ABI of
+include/sdv.h); this package holds the kernels' sources (``csrc/``), the
+in-tree build (``build``) and a thin torch binding (``binding``) whose
+functions carry the C entry points' names.  Importing the package does not
+open the library; the first binding call does, and fails loudly if it has
+not been built.
+"""
+from .binding import (  # noqa: F401
+    GREEDY,
+    STOCHASTIC,
+    SdvError,
+    sdv_build_tree,
+    sdv_compact_kv,
+    sdv_draft_topk,
+    sdv_tli_build_maps,
+    sdv_tli_constrain_draft_logits,
+    sdv_tli_lm_head,
+    sdv_tli_map_ids,
+    sdv_tli_q_scatter,
+    sdv_tree_verify_attention,
+    sdv_verify_accept,
+)

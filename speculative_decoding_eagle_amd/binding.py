@@ -1,0 +1,276 @@
+"""Thin torch-tensor binding of the C ABI in include/sdv.h.
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: it checks dtypes, devices and contiguity, allocates outputs and
+workspaces that the caller did not pass (torch device memory), and passes raw
+pointers plus the current HIP stream.  All computation happens in the HIP
+kernels; a non-zero status raises ``SdvError`` with the library's message.
+bf16 tensors may be given as torch.bfloat16 or as int16/uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import AcceptShape, AttnShape, KVShape, TreeShape
+
+GREEDY, STOCHASTIC = 0, 1
+
+
+class SdvError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = _lib.lib().sdv_last_error().decode(errors="replace")
+        raise SdvError("%s failed (status %d): %s" % (what, rc, msg))
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor", allow_none=False) -> int:
+    if t is None:
+        if allow_none:
+            return 0
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    return t.data_ptr()
+
+
+BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return 0, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace too small: %d bytes needed" % nbytes)
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _keep(*_):
+    """Holds references until the call returns (workspaces live on the stream)."""
+
+
+# ---------------------------------------------------------------------- A1
+
+def sdv_draft_topk(probs: torch.Tensor, k: int, topk_p=None, topk_id=None, ws=None):
+    """Top-k of every row of ``probs`` [..., V] fp32 -> (topk_p, topk_id) [..., k]."""
+    V = probs.shape[-1]
+    rows = probs.numel() // V if V else 0
+    dev = probs.device
+    if topk_p is None:
+        topk_p = torch.empty(probs.shape[:-1] + (k,), dtype=torch.float32, device=dev)
+    if topk_id is None:
+        topk_id = torch.empty(probs.shape[:-1] + (k,), dtype=torch.int32, device=dev)
+    L = _lib.lib()
+    need = L.sdv_draft_topk_workspace_size(rows, V, k)
+    wp, wb = _workspace(need, dev, ws)
+    _check(L.sdv_draft_topk(_ptr(probs, torch.float32, "probs"), rows, V, k, _ptr(topk_p, torch.float32, "topk_p"),
+                            _ptr(topk_id, torch.int32, "topk_id"), wp, wb, _stream(dev)), "sdv_draft_topk")
+    return topk_p, topk_id
+
+
+# -------------------------------------------------------------------- A2-A4
+
+TREE_OUTPUTS = ("tokens", "parent", "depth", "positions", "score", "q_row", "mask", "mask_bits",
+                "retrieve_index", "next_token", "next_sibling")
+
+
+def sdv_build_tree(topk_p, topk_id, root_token, prefix_len, k: int, S: int, N: int, out=None,
+                   with_mask: bool = True):
+    """Candidate tree and verify arrays; returns a dict of device tensors."""
+    B = topk_p.shape[0]
+    dev = topk_p.device
+    out = dict(out or {})
+    W = (N + 31) // 32
+
+    def get(name, shape, dtype):
+        if name not in out:
+            out[name] = torch.empty(shape, dtype=dtype, device=dev)
+        return out[name]
+
+    i32 = torch.int32
+    tokens = get("tokens", (B, N), i32)
+    parent = get("parent", (B, N), i32)
+    depth = get("depth", (B, N), i32)
+    positions = get("positions", (B, N), i32)
+    score = get("score", (B, N), torch.float32)
+    q_row = get("q_row", (B, N), i32)
+    mask = get("mask", (B, N, N), torch.uint8) if with_mask else None
+    bits = get("mask_bits", (B, N, W), torch.int32)
+    ri = get("retrieve_index", (B, N), i32)
+    nt = get("next_token", (B, N), i32)
+    ns = get("next_sibling", (B, N), i32)
+    shape = TreeShape(B, k, S, N)
+    _check(_lib.lib().sdv_build_tree(
+        shape, _ptr(topk_p, torch.float32, "topk_p"), _ptr(topk_id, i32, "topk_id"),
+        _ptr(root_token, i32, "root_token"), _ptr(prefix_len, i32, "prefix_len"),
+        _ptr(tokens), _ptr(parent), _ptr(depth), _ptr(positions), _ptr(score), _ptr(q_row),
+        _ptr(mask, torch.uint8, "mask", allow_none=True), _ptr(bits, (torch.int32, torch.uint32), "mask_bits"),
+        _ptr(ri), _ptr(nt), _ptr(ns), _stream(dev)), "sdv_build_tree")
+    return out
+
+
+# ---------------------------------------------------------------------- A5
+
+def sdv_tree_verify_attention(q, k_pool, v_pool, page_table, prefix_len, mask_bits, page: int = 1,
+                              sm_scale: float = 0.0, out=None, lse=None, want_lse: bool = False, ws=None):
+    """Tree-masked attention; returns (out [B,N,Hq,D] bf16, lse or None)."""
+    B, N, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    shape = AttnShape(B, N, Hq, Hkv, D, page, page_table.shape[1], k_pool.shape[0])
+    L = _lib.lib()
+    wp, wb = _workspace(L.sdv_tree_verify_attention_workspace_size(shape), dev, ws)
+    _check(L.sdv_tree_verify_attention(
+        shape, float(sm_scale), _ptr(q, BF16, "q"), _ptr(k_pool, BF16, "k_pool"), _ptr(v_pool, BF16, "v_pool"),
+        _ptr(page_table, torch.int32, "page_table"), _ptr(prefix_len, torch.int32, "prefix_len"),
+        _ptr(mask_bits, (torch.int32, torch.uint32), "mask_bits"), _ptr(out, BF16, "out"),
+        _ptr(lse, torch.float32, "lse", allow_none=True), wp, wb, _stream(dev)), "sdv_tree_verify_attention")
+    return out, lse
+
+
+# -------------------------------------------------------------------- A6-A7
+
+def sdv_verify_accept(mode: int, tree, target, S: int, eos_id: int = -1, remaining=None, draft_probs=None,
+                      u_accept=None, u_draw=None, out=None, ws=None):
+    """Accept walk; ``tree`` holds tokens/next_token/next_sibling/q_row [B,N].
+    Returns dict accept_len, accept_path, commit_tokens, commit_len, next_root."""
+    tokens = tree["tokens"]
+    B, N = tokens.shape
+    V = target.shape[-1]
+    R = draft_probs.shape[1] if draft_probs is not None else 0
+    dev = tokens.device
+    out = dict(out or {})
+    i32 = torch.int32
+    for name, shape in (("accept_len", (B,)), ("accept_path", (B, S + 1)), ("commit_tokens", (B, S + 1)),
+                        ("commit_len", (B,)), ("next_root", (B,))):
+        if name not in out:
+            out[name] = torch.empty(shape, dtype=i32, device=dev)
+    shape = AcceptShape(B, N, S, V, R, mode)
+    L = _lib.lib()
+    wp, wb = _workspace(L.sdv_verify_accept_workspace_size(shape), dev, ws)
+    _check(L.sdv_verify_accept(
+        shape, eos_id, _ptr(remaining, i32, "remaining", allow_none=True), _ptr(tokens, i32, "tokens"),
+        _ptr(tree["next_token"], i32, "next_token"), _ptr(tree["next_sibling"], i32, "next_sibling"),
+        _ptr(tree.get("q_row"), i32, "q_row", allow_none=True), _ptr(target, torch.float32, "target"),
+        _ptr(draft_probs, torch.float32, "draft_probs", allow_none=True),
+        _ptr(u_accept, torch.float32, "u_accept", allow_none=True),
+        _ptr(u_draw, torch.float32, "u_draw", allow_none=True),
+        _ptr(out["accept_len"]), _ptr(out["accept_path"]), _ptr(out["commit_tokens"]), _ptr(out["commit_len"]),
+        _ptr(out["next_root"]), wp, wb, _stream(dev)), "sdv_verify_accept")
+    return out
+
+
+# ---------------------------------------------------------------------- A8
+
+def sdv_compact_kv(page_table, prefix_len, accept_len, accept_path, N: int, S: int, page: int,
+                   k_pools: Sequence[torch.Tensor] = (), v_pools: Sequence[torch.Tensor] = (),
+                   new_len=None, freed=None, num_freed=None, ws=None):
+    """Compaction in place (page_table and, for page > 1, the pools).
+    Returns (new_len [B], freed [B*N], num_freed [1])."""
+    B, max_pages = page_table.shape
+    dev = page_table.device
+    i32 = torch.int32
+    if new_len is None:
+        new_len = torch.empty(B, dtype=i32, device=dev)
+    if freed is None:
+        freed = torch.empty(max(1, B * N), dtype=i32, device=dev)
+    if num_freed is None:
+        num_freed = torch.empty(1, dtype=i32, device=dev)
+    layers = len(k_pools)
+    if page > 1 and (layers == 0 or len(v_pools) != layers):
+        raise ValueError("page > 1 needs matching K and V pools")
+    Hkv = k_pools[0].shape[1] if layers else 0
+    D = k_pools[0].shape[2] if layers else 0
+    slots = k_pools[0].shape[0] if layers else 0
+    kp = (ctypes.c_void_p * max(1, layers))(*[_ptr(t, BF16, "k_pool") for t in k_pools])
+    vp = (ctypes.c_void_p * max(1, layers))(*[_ptr(t, BF16, "v_pool") for t in v_pools])
+    shape = KVShape(B, N, S, page, Hkv, D, layers, max_pages, slots)
+    L = _lib.lib()
+    wp, wb = _workspace(L.sdv_compact_kv_workspace_size(shape), dev, ws)
+    _check(L.sdv_compact_kv(
+        shape, ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p),
+        _ptr(page_table, i32, "page_table"), _ptr(prefix_len, i32, "prefix_len"),
+        _ptr(accept_len, i32, "accept_len"), _ptr(accept_path, i32, "accept_path"), _ptr(new_len, i32, "new_len"),
+        _ptr(freed, i32, "freed"), _ptr(num_freed, i32, "num_freed"), wp, wb, _stream(dev)), "sdv_compact_kv")
+    return new_len, freed, num_freed
+
+
+# ------------------------------------------------------------------- A9-A10
+
+def sdv_tli_lm_head(hidden, weight, logits=None):
+    B, H = hidden.shape
+    K = weight.shape[0]
+    if logits is None:
+        logits = torch.empty((B, K), dtype=torch.float32, device=hidden.device)
+    _check(_lib.lib().sdv_tli_lm_head(B, H, K, _ptr(hidden, BF16, "hidden"), _ptr(weight, BF16, "weight"),
+                                      _ptr(logits, torch.float32, "logits"), _stream(hidden.device)),
+           "sdv_tli_lm_head")
+    return logits
+
+
+def sdv_tli_build_maps(inter_ids, tgt_ids, V_draft: int, V_target: int, fallback: int, d2t=None, t2d=None):
+    dev = inter_ids.device
+    if d2t is None:
+        d2t = torch.empty(V_draft, dtype=torch.int32, device=dev)
+    if t2d is None:
+        t2d = torch.empty(V_target, dtype=torch.int32, device=dev)
+    _check(_lib.lib().sdv_tli_build_maps(inter_ids.numel(), _ptr(inter_ids, torch.int32, "inter_ids"),
+                                         _ptr(tgt_ids, torch.int32, "tgt_ids"), V_draft, V_target, int(fallback),
+                                         _ptr(d2t), _ptr(t2d), _stream(dev)), "sdv_tli_build_maps")
+    return d2t, t2d
+
+
+def sdv_tli_map_ids(table, ids, out=None):
+    if out is None:
+        out = torch.empty_like(ids, dtype=torch.int32)
+    _check(_lib.lib().sdv_tli_map_ids(_ptr(table, torch.int32, "table"), table.numel(), _ptr(ids, torch.int32, "ids"),
+                                      ids.numel(), _ptr(out, torch.int32, "out"), _stream(ids.device)),
+           "sdv_tli_map_ids")
+    return out
+
+
+def sdv_tli_constrain_draft_logits(pruned, inter_ids, V_draft: int, full=None):
+    B, K = pruned.shape
+    if full is None:
+        full = torch.empty((B, V_draft), dtype=torch.float32, device=pruned.device)
+    _check(_lib.lib().sdv_tli_constrain_draft_logits(B, K, V_draft, _ptr(pruned, torch.float32, "pruned"),
+                                                     _ptr(inter_ids, torch.int32, "inter_ids"),
+                                                     _ptr(full, torch.float32, "full"), _stream(pruned.device)),
+           "sdv_tli_constrain_draft_logits")
+    return full
+
+
+def sdv_tli_q_scatter(q_pruned, tgt_ids, V_target: int, q_target=None, ws=None):
+    K = q_pruned.shape[-1]
+    rows = q_pruned.numel() // K
+    dev = q_pruned.device
+    if q_target is None:
+        q_target = torch.empty(q_pruned.shape[:-1] + (V_target,), dtype=torch.float32, device=dev)
+    L = _lib.lib()
+    wp, wb = _workspace(L.sdv_tli_q_scatter_workspace_size(V_target), dev, ws)
+    _check(L.sdv_tli_q_scatter(rows, K, V_target, _ptr(q_pruned, torch.float32, "q_pruned"),
+                               _ptr(tgt_ids, torch.int32, "tgt_ids"), _ptr(q_target, torch.float32, "q_target"),
+                               wp, wb, _stream(dev)), "sdv_tli_q_scatter")
+    return q_target

@@ -1,0 +1,83 @@
+// Shared host/device helpers of the gfx950 library: status reporting, launch
+// checks, workspace carving and a few wave-level primitives.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/sdv.h"
+
+namespace sdv {
+
+// ---------------------------------------------------------------- host side
+
+// Records `msg` as the calling thread's last error and returns `code`.
+int32_t fail(int32_t code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Checks the launch that was just enqueued.
+int32_t check_launch(const char *what);
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Carves consecutive 256-byte aligned regions out of a caller workspace.
+struct Carver {
+  char *base;
+  size_t used = 0;
+  explicit Carver(void *p) : base(static_cast<char *>(p)) {}
+  template <typename T>
+  T *take(size_t count) {
+    used = align_up(used, 256);
+    T *p = base ? reinterpret_cast<T *>(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+  size_t bytes() const { return align_up(used, 256); }
+};
+
+// Number of compute units of the current device (cached per device).
+int num_cus();
+
+#define SDV_REQUIRE(cond, code, ...)          \
+  do {                                        \
+    if (!(cond)) return ::sdv::fail((code), __VA_ARGS__); \
+  } while (0)
+
+// ---------------------------------------------------------------- device side
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Strict total order used by every top-k / argmax: larger value first, then
+// lower index.
+__device__ __forceinline__ bool better(float v, int i, float w, int j) {
+  return v > w || (v == w && i < j);
+}
+
+// Wave-wide reduction to the best (value, index) pair; every lane gets it.
+__device__ __forceinline__ void wave_best(float &v, int &i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float ov = __shfl_xor(v, off, kWave);
+    int oi = __shfl_xor(i, off, kWave);
+    if (better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+}  // namespace sdv

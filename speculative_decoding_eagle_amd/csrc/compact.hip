@@ -1,0 +1,232 @@
+// A8: keep the accepted path's KV and release the rest of the tree's
+// allocation ("EAGLE speculative decoding in four parts", "Self-test"
+// answer 3 and "Drafting, verification and slots"; zero-to-sglang ch.10
+// section 5.2).
+//
+// page == 1: an index remap of the slot map (one block per request), no KV
+// bytes move.  page > 1: a coalesced copy of the moved K/V rows (16-byte
+// vectors, one block per request x layer x pool, all reads of a batch of
+// rows before its writes, batches in increasing destination order), then a
+// per-request kernel that clears the released tail pages and lists them.
+// The freed lists of all requests are laid out in batch order; each block
+// finds its offset from the accept lengths of the requests before it.
+#include "common.hpp"
+
+namespace sdv {
+namespace {
+
+constexpr int kCmpThreads = 256;
+constexpr int kMaxLayers = 128;
+constexpr int kCopyBatch = 4;     // 16-byte vectors per thread per batch
+
+struct PoolPtrs {
+  uint16_t *k[kMaxLayers];
+  uint16_t *v[kMaxLayers];
+};
+
+__device__ __forceinline__ int clamp_accept(int a, int S, int N) {
+  const int hi = min(S, N - 1);
+  return a < 0 ? 0 : (a > hi ? hi : a);
+}
+
+// Released ids of request r.
+__device__ __forceinline__ int released(int r, const int *prefix_len, const int *accept_len, int S, int N,
+                                        int page) {
+  const int a = clamp_accept(accept_len[r], S, N);
+  if (page == 1) return N - 1 - a;
+  const int L = prefix_len[r];
+  const int first_free = (L + a + 1 + page - 1) / page;
+  const int last_used = (L + N - 1) / page;
+  return last_used >= first_free ? last_used - first_free + 1 : 0;
+}
+
+// Sum of released(r) over r < upto (all threads get it).
+__device__ int released_before(int upto, const int *prefix_len, const int *accept_len, int S, int N,
+                               int page) {
+  __shared__ int s_part[kCmpThreads];
+  int acc = 0;
+  for (int r = threadIdx.x; r < upto; r += kCmpThreads) acc += released(r, prefix_len, accept_len, S, N, page);
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  int tot = 0;
+  for (int j = 0; j < kCmpThreads; ++j) tot += s_part[j];
+  __syncthreads();
+  return tot;
+}
+
+__global__ void __launch_bounds__(kCmpThreads)
+remap_slots_kernel(int B, int N, int S, int max_pages, int *__restrict__ table,
+                   const int *__restrict__ prefix_len, const int *__restrict__ accept_len,
+                   const int *__restrict__ accept_path, int *__restrict__ new_len, int *__restrict__ freed,
+                   int *__restrict__ num_freed) {
+  __shared__ int s_old[256];
+  __shared__ int s_kept[256];
+  __shared__ int s_scan[256];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int L = prefix_len[b];
+  const int a = clamp_accept(accept_len[b], S, N);
+  int *row = table + static_cast<int64_t>(b) * max_pages;
+  const bool ok = L >= 0 && L + N <= max_pages;
+  const int base = released_before(b, prefix_len, accept_len, S, N, 1);
+  if (b == 0) {
+    const int tot = released_before(B, prefix_len, accept_len, S, N, 1);
+    if (tid == 0) *num_freed = tot;
+  }
+  if (tid < N) {
+    s_old[tid] = ok ? row[L + tid] : -1;
+    s_kept[tid] = 0;
+  }
+  __syncthreads();
+  if (tid <= a) {
+    int pj = accept_path[static_cast<int64_t>(b) * (S + 1) + tid];
+    pj = pj < 0 ? 0 : (pj >= N ? N - 1 : pj);
+    s_kept[pj] = 1;
+  }
+  __syncthreads();
+  // exclusive scan of the not-kept flags gives each released slot its place
+  const int flag = (tid < N && !s_kept[tid]) ? 1 : 0;
+  s_scan[tid] = flag;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += add;
+    __syncthreads();
+  }
+  if (flag) freed[base + s_scan[tid] - 1] = s_old[tid];
+  if (ok && tid < N) {
+    int v = -1;
+    if (tid <= a) {
+      int pj = accept_path[static_cast<int64_t>(b) * (S + 1) + tid];
+      pj = pj < 0 ? 0 : (pj >= N ? N - 1 : pj);
+      v = s_old[pj];
+    }
+    row[L + tid] = v;
+  }
+  if (tid == 0) new_len[b] = L + a + 1;
+}
+
+__global__ void __launch_bounds__(kCmpThreads)
+copy_rows_kernel(PoolPtrs pools, int layers, int N, int S, int page, int max_pages, int64_t num_slots,
+                 int row16, const int *__restrict__ table, const int *__restrict__ prefix_len,
+                 const int *__restrict__ accept_len, const int *__restrict__ accept_path) {
+  const int b = blockIdx.x / (2 * layers);
+  const int rest = blockIdx.x % (2 * layers);
+  const int layer = rest >> 1;
+  uint4 *pool = reinterpret_cast<uint4 *>((rest & 1) ? pools.v[layer] : pools.k[layer]);
+  const int L = prefix_len[b];
+  const int a = clamp_accept(accept_len[b], S, N);
+  if (a == 0 || L < 0 || L + N > max_pages * page) return;
+  const int *path = accept_path + static_cast<int64_t>(b) * (S + 1);
+  const int *trow = table + static_cast<int64_t>(b) * max_pages;
+  const int items = a * row16;                 // rows d = 1..a
+  for (int first = 0; first < items; first += kCopyBatch * kCmpThreads) {
+    uint4 buf[kCopyBatch];
+    int64_t dst[kCopyBatch];
+#pragma unroll
+    for (int j = 0; j < kCopyBatch; ++j) {
+      const int x = first + j * kCmpThreads + threadIdx.x;
+      dst[j] = -1;
+      if (x < items) {
+        const int d = 1 + x / row16;
+        const int c16 = x % row16;
+        int pd = path[d];
+        pd = pd < 0 ? 0 : (pd >= N ? N - 1 : pd);
+        if (pd != d) {
+          const int ps = L + pd, pdst = L + d;
+          const int64_t ss = static_cast<int64_t>(trow[ps / page]) * page + ps % page;
+          const int64_t sd = static_cast<int64_t>(trow[pdst / page]) * page + pdst % page;
+          if (ss >= 0 && ss < num_slots && sd >= 0 && sd < num_slots) {
+            buf[j] = pool[ss * row16 + c16];
+            dst[j] = sd * row16 + c16;
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCopyBatch; ++j)
+      if (dst[j] >= 0) pool[dst[j]] = buf[j];
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(kCmpThreads)
+release_pages_kernel(int B, int N, int S, int page, int max_pages, int *__restrict__ table,
+                     const int *__restrict__ prefix_len, const int *__restrict__ accept_len,
+                     int *__restrict__ new_len, int *__restrict__ freed, int *__restrict__ num_freed) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int L = prefix_len[b];
+  const int a = clamp_accept(accept_len[b], S, N);
+  const int base = released_before(b, prefix_len, accept_len, S, N, page);
+  if (b == 0) {
+    const int tot = released_before(B, prefix_len, accept_len, S, N, page);
+    if (tid == 0) *num_freed = tot;
+  }
+  const int first_free = (L + a + 1 + page - 1) / page;
+  const int last_used = (L + N - 1) / page;
+  int *row = table + static_cast<int64_t>(b) * max_pages;
+  for (int pg = first_free + tid; pg <= last_used; pg += kCmpThreads) {
+    const bool in = pg >= 0 && pg < max_pages;
+    freed[base + pg - first_free] = in ? row[pg] : -1;
+    if (in) row[pg] = -1;
+  }
+  if (tid == 0) new_len[b] = L + a + 1;
+}
+
+}  // namespace
+}  // namespace sdv
+
+using namespace sdv;
+
+extern "C" size_t sdv_compact_kv_workspace_size(sdv_kv_shape) { return 0; }
+
+extern "C" int32_t sdv_compact_kv(sdv_kv_shape sh, uint16_t *const *k_pools, uint16_t *const *v_pools,
+                                  int32_t *page_table, const int32_t *prefix_len,
+                                  const int32_t *accept_len, const int32_t *accept_path,
+                                  int32_t *new_len, int32_t *freed, int32_t *num_freed, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  clear_error();
+  SDV_REQUIRE(sh.B >= 0 && sh.N >= 1 && sh.S >= 0 && sh.page >= 1 && sh.max_pages >= 1, SDV_E_SHAPE,
+              "compact_kv: need B >= 0, N >= 1, S >= 0, page >= 1, max_pages >= 1");
+  SDV_REQUIRE(sh.N <= 256, SDV_E_UNSUPPORTED, "compact_kv: N=%d above 256", sh.N);
+  if (sh.B == 0) return SDV_OK;
+  SDV_REQUIRE(page_table && prefix_len && accept_len && accept_path && new_len && freed && num_freed,
+              SDV_E_NULL, "compact_kv: NULL pointer");
+  hipStream_t st = as_stream(stream);
+  if (sh.page == 1) {
+    hipLaunchKernelGGL(remap_slots_kernel, dim3(sh.B), dim3(kCmpThreads), 0, st, sh.B, sh.N, sh.S,
+                       sh.max_pages, page_table, prefix_len, accept_len, accept_path, new_len, freed,
+                       num_freed);
+    return check_launch("remap_slots_kernel");
+  }
+  SDV_REQUIRE(sh.layers >= 1 && sh.layers <= kMaxLayers, SDV_E_UNSUPPORTED,
+              "compact_kv: layers=%d outside [1, %d]", sh.layers, kMaxLayers);
+  SDV_REQUIRE(sh.Hkv >= 1 && sh.D >= 1 && (static_cast<int64_t>(sh.Hkv) * sh.D) % 8 == 0, SDV_E_UNSUPPORTED,
+              "compact_kv: Hkv*D must be a multiple of 8");
+  SDV_REQUIRE(k_pools && v_pools, SDV_E_NULL, "compact_kv: NULL pool array");
+  PoolPtrs pp;
+  for (int l = 0; l < sh.layers; ++l) {
+    SDV_REQUIRE(k_pools[l] && v_pools[l], SDV_E_NULL, "compact_kv: NULL pool of layer %d", l);
+    SDV_REQUIRE(reinterpret_cast<uintptr_t>(k_pools[l]) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(v_pools[l]) % 16 == 0,
+                SDV_E_SHAPE, "compact_kv: pools must be 16-byte aligned");
+    pp.k[l] = k_pools[l];
+    pp.v[l] = v_pools[l];
+  }
+  for (int l = sh.layers; l < kMaxLayers; ++l) pp.k[l] = pp.v[l] = nullptr;
+  const int row16 = static_cast<int>(static_cast<int64_t>(sh.Hkv) * sh.D / 8);
+  const int64_t blocks = static_cast<int64_t>(sh.B) * sh.layers * 2;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCmpThreads), 0, st, pp,
+                     sh.layers, sh.N, sh.S, sh.page, sh.max_pages, sh.num_slots, row16, page_table,
+                     prefix_len, accept_len, accept_path);
+  int32_t rc = check_launch("copy_rows_kernel");
+  if (rc != SDV_OK) return rc;
+  hipLaunchKernelGGL(release_pages_kernel, dim3(sh.B), dim3(kCmpThreads), 0, st, sh.B, sh.N, sh.S, sh.page,
+                     sh.max_pages, page_table, prefix_len, accept_len, new_len, freed, num_freed);
+  return check_launch("release_pages_kernel");
+}

@@ -1,0 +1,233 @@
+// A9-A10: Token-Level Intersection for heterogeneous vocabularies (sglang PR
+// #22883 "TLI (Token-Level Intersection)", "Modifications"): the pruned
+// draft LM head, the vocabulary maps, the logit constraint and the scatter
+// of the draft distribution into the target vocabulary.
+//
+// The pruned LM head is a skinny GEMM (B ~ 64 rows) that streams the
+// [K, H] bf16 weight once from HBM: each 4-wave block owns 64 weight rows,
+// each wave 16 of them, and runs bf16 MFMA 16x16x32 with fp32 accumulators
+// over all B rows; the small hidden matrix is re-read from L1/L2.  The remap
+// kernels are coalesced gathers/scatters.
+#include <cmath>
+
+#include "common.hpp"
+
+namespace sdv {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kGemmThreads = 256;
+constexpr int kRowsPerBlock = 64;   // weight rows (output columns) per block
+constexpr int kMaxMBlocks = 8;      // hidden rows handled per pass: 8 x 16 = 128
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  bf16x8 r;
+  __builtin_memcpy(&r, &u, sizeof(r));
+  return r;
+}
+
+// logits[b, j] = sum_h hidden[b, h] * weight[j, h]
+template <int MB>
+__global__ void __launch_bounds__(kGemmThreads)
+lm_head_kernel(int B, int H, int K, const uint16_t *__restrict__ hidden,
+               const uint16_t *__restrict__ weight, float *__restrict__ logits) {
+  const int wave = threadIdx.x / kWave;
+  const int l = lane_id();
+  const int n0 = blockIdx.x * kRowsPerBlock + wave * 16;        // first weight row of this wave
+  const int m0 = blockIdx.y * (MB * 16);                         // first hidden row of this pass
+  const int nrow = min(n0 + (l & 15), K - 1);                     // clamp the tail (never stored)
+  const int kofs = 8 * (l >> 4);
+  const uint16_t *wp = weight + static_cast<int64_t>(nrow) * H + kofs;
+  const uint16_t *hp[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int mrow = min(m0 + mb * 16 + (l & 15), B - 1);
+    hp[mb] = hidden + static_cast<int64_t>(mrow) * H + kofs;
+  }
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    const bf16x8 bw = load_bf16x8(wp + k0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const bf16x8 ah = load_bf16x8(hp[mb] + k0);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[mb], 0, 0, 0);
+    }
+  }
+  // D[m][n]: lane l holds rows 4*(l/16)+i of the 16x16 block, column l%16
+  const int ncol = n0 + (l & 15);
+  if (ncol < K) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + mb * 16 + 4 * (l >> 4) + i;
+        if (m < B) logits[static_cast<int64_t>(m) * K + ncol] = acc[mb][i];
+      }
+  }
+}
+
+__global__ void fill_i32_kernel(int *p, int64_t n, int v) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void scatter_maps_kernel(int K, const int *__restrict__ inter, const int *__restrict__ tgt,
+                                    int Vd, int Vt, int *__restrict__ d2t, int *__restrict__ t2d) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  const int d = inter[j], t = tgt[j];
+  if (d >= 0 && d < Vd) d2t[d] = (t >= 0 && t < Vt) ? t : -1;
+  if (t >= 0 && t < Vt && d >= 0 && d < Vd) t2d[t] = d;
+}
+
+__global__ void map_ids_kernel(const int *__restrict__ table, int len, const int *__restrict__ ids, int64_t n,
+                               int *__restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int x = ids[i];
+  out[i] = (x >= 0 && x < len) ? table[x] : -1;
+}
+
+// Position of v in the sorted list, or -1.
+__device__ __forceinline__ int find_sorted(const int *__restrict__ a, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return (lo < n && a[lo] == v) ? lo : -1;
+}
+
+__global__ void constrain_kernel(int B, int K, int Vd, const float *__restrict__ pruned,
+                                 const int *__restrict__ inter, float *__restrict__ full) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= Vd) return;
+  const int j = find_sorted(inter, K, v);
+  for (int b = 0; b < B; ++b)
+    full[static_cast<int64_t>(b) * Vd + v] = j >= 0 ? pruned[static_cast<int64_t>(b) * K + j] : -INFINITY;
+}
+
+__global__ void inverse_kernel(int K, const int *__restrict__ tgt, int Vt, int *__restrict__ inv) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  const int t = tgt[j];
+  if (t >= 0 && t < Vt) inv[t] = j;
+}
+
+__global__ void q_scatter_kernel(int64_t rows, int K, int Vt, const float *__restrict__ q,
+                                 const int *__restrict__ inv, float *__restrict__ out) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = blockIdx.y;
+  if (v >= Vt || r >= rows) return;
+  const int j = inv[v];
+  out[r * Vt + v] = j >= 0 ? q[r * K + j] : 0.0f;
+}
+
+inline unsigned nblk(int64_t n, int t) { return static_cast<unsigned>((n + t - 1) / t); }
+
+}  // namespace
+}  // namespace sdv
+
+using namespace sdv;
+
+extern "C" int32_t sdv_tli_lm_head(int32_t B, int32_t H, int32_t K, const uint16_t *hidden,
+                                   const uint16_t *weight, float *logits, void *stream) {
+  clear_error();
+  SDV_REQUIRE(B >= 0 && H >= 0 && K >= 0, SDV_E_SHAPE, "tli_lm_head: negative size");
+  SDV_REQUIRE(H % 32 == 0, SDV_E_UNSUPPORTED, "tli_lm_head: H=%d must be a multiple of 32", H);
+  if (B == 0 || K == 0) return SDV_OK;
+  SDV_REQUIRE(hidden && weight && logits, SDV_E_NULL, "tli_lm_head: NULL pointer");
+  SDV_REQUIRE(reinterpret_cast<uintptr_t>(hidden) % 16 == 0 && reinterpret_cast<uintptr_t>(weight) % 16 == 0,
+              SDV_E_SHAPE, "tli_lm_head: hidden and weight must be 16-byte aligned");
+  if (H == 0) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(static_cast<int64_t>(B) * K, 256)), dim3(256), 0,
+                       as_stream(stream), reinterpret_cast<int *>(logits), static_cast<int64_t>(B) * K, 0);
+    return check_launch("fill_i32_kernel");
+  }
+  const int mpass = kMaxMBlocks * 16;
+  dim3 grid(nblk(K, kRowsPerBlock), nblk(B, mpass));
+  if (B <= 16) {
+    hipLaunchKernelGGL(lm_head_kernel<1>, grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
+                       weight, logits);
+  } else if (B <= 32) {
+    hipLaunchKernelGGL(lm_head_kernel<2>, grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
+                       weight, logits);
+  } else if (B <= 64) {
+    hipLaunchKernelGGL(lm_head_kernel<4>, grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
+                       weight, logits);
+  } else {
+    hipLaunchKernelGGL(lm_head_kernel<kMaxMBlocks>, grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K,
+                       hidden, weight, logits);
+  }
+  return check_launch("lm_head_kernel");
+}
+
+extern "C" int32_t sdv_tli_build_maps(int32_t K, const int32_t *inter_ids, const int32_t *tgt_ids,
+                                      int32_t V_draft, int32_t V_target, int32_t fallback, int32_t *d2t,
+                                      int32_t *t2d, void *stream) {
+  clear_error();
+  SDV_REQUIRE(K >= 0 && V_draft >= 1 && V_target >= 1, SDV_E_SHAPE, "tli_build_maps: bad sizes");
+  SDV_REQUIRE(d2t && t2d && (K == 0 || (inter_ids && tgt_ids)), SDV_E_NULL, "tli_build_maps: NULL pointer");
+  hipStream_t st = as_stream(stream);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(V_draft, 256)), dim3(256), 0, st, d2t,
+                     static_cast<int64_t>(V_draft), -1);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(V_target, 256)), dim3(256), 0, st, t2d,
+                     static_cast<int64_t>(V_target), fallback);
+  if (K > 0)
+    hipLaunchKernelGGL(scatter_maps_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, inter_ids, tgt_ids,
+                       V_draft, V_target, d2t, t2d);
+  return check_launch("tli_build_maps");
+}
+
+extern "C" int32_t sdv_tli_map_ids(const int32_t *table, int32_t table_len, const int32_t *ids, int64_t n,
+                                   int32_t *out, void *stream) {
+  clear_error();
+  SDV_REQUIRE(n >= 0 && table_len >= 0, SDV_E_SHAPE, "tli_map_ids: negative size");
+  if (n == 0) return SDV_OK;
+  SDV_REQUIRE(table && ids && out, SDV_E_NULL, "tli_map_ids: NULL pointer");
+  hipLaunchKernelGGL(map_ids_kernel, dim3(nblk(n, 256)), dim3(256), 0, as_stream(stream), table, table_len, ids,
+                     n, out);
+  return check_launch("map_ids_kernel");
+}
+
+extern "C" int32_t sdv_tli_constrain_draft_logits(int32_t B, int32_t K, int32_t V_draft, const float *pruned,
+                                                  const int32_t *inter_ids, float *full, void *stream) {
+  clear_error();
+  SDV_REQUIRE(B >= 0 && K >= 0 && V_draft >= 1 && K <= V_draft, SDV_E_SHAPE, "tli_constrain: bad sizes");
+  if (B == 0) return SDV_OK;
+  SDV_REQUIRE(full && (K == 0 || (pruned && inter_ids)), SDV_E_NULL, "tli_constrain: NULL pointer");
+  hipLaunchKernelGGL(constrain_kernel, dim3(nblk(V_draft, 256)), dim3(256), 0, as_stream(stream), B, K, V_draft,
+                     pruned, inter_ids, full);
+  return check_launch("constrain_kernel");
+}
+
+extern "C" size_t sdv_tli_q_scatter_workspace_size(int32_t V_target) {
+  return V_target > 0 ? align_up(static_cast<size_t>(V_target) * sizeof(int), 256) : 0;
+}
+
+extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, const float *q_pruned,
+                                     const int32_t *tgt_ids, float *q_target, void *ws, size_t ws_bytes,
+                                     void *stream) {
+  clear_error();
+  SDV_REQUIRE(rows >= 0 && K >= 0 && V_target >= 1 && K <= V_target, SDV_E_SHAPE, "tli_q_scatter: bad sizes");
+  SDV_REQUIRE(rows <= 65535, SDV_E_UNSUPPORTED, "tli_q_scatter: rows above 65535");
+  if (rows == 0) return SDV_OK;
+  SDV_REQUIRE(q_target && (K == 0 || (q_pruned && tgt_ids)), SDV_E_NULL, "tli_q_scatter: NULL pointer");
+  const size_t need = sdv_tli_q_scatter_workspace_size(V_target);
+  SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "tli_q_scatter: workspace of %zu bytes needed", need);
+  int *inv = static_cast<int *>(ws);
+  hipStream_t st = as_stream(stream);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(V_target, 256)), dim3(256), 0, st, inv,
+                     static_cast<int64_t>(V_target), -1);
+  if (K > 0)
+    hipLaunchKernelGGL(inverse_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, tgt_ids, V_target, inv);
+  hipLaunchKernelGGL(q_scatter_kernel, dim3(nblk(V_target, 256), static_cast<unsigned>(rows)), dim3(256), 0, st,
+                     rows, K, V_target, q_pruned, inv, q_target);
+  return check_launch("q_scatter_kernel");
+}

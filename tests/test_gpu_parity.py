@@ -1,0 +1,359 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle on the same
+seeded inputs.  Integer and index outputs must match bit for bit; attention
+and the pruned LM head must lie within max |err| <= 2e-2 and
+||err||_2 <= 1e-2 ||ref||_2."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_eagle_amd as sdv
+import workloads
+from oracle import accept as oacc
+from oracle import attention as oatt
+from oracle import compact as ocmp
+from oracle import tli as otli
+from oracle import topk as otopk
+from oracle import tree as otree
+from _helpers import (assert_attention_close, bf16_to_f64, dev, host, oracle_tree, plant_greedy,
+                      plant_stochastic)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    say("device", torch.cuda.get_device_name(0))
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------- A1
+
+@pytest.mark.parametrize("rows,V,k,coarse", [(10, 1000, 2, False), (64, 4099, 8, False), (33, 128256, 8, False),
+                                             (1100, 2048, 8, True), (200, 5000, 13, True), (5, 64, 32, True),
+                                             (3, 7, 7, True), (1, 1, 1, False), (17, 40000, 4, True)])
+def test_topk_bit_exact(rows, V, k, coarse):
+    rng = np.random.default_rng(rows * 131 + V + k)
+    if coarse:
+        p = (rng.integers(0, 9, size=(rows, V)) / 16.0).astype(np.float32)   # many ties
+    else:
+        p = workloads.softmax_rows(rng.standard_normal((rows, V)).astype(np.float32) * 3)
+    say("topk", rows, V, k)
+    gp, gi = sdv.sdv_draft_topk(dev(p), k)
+    torch.cuda.synchronize()
+    op, oi = otopk.draft_topk(p, k)
+    assert np.array_equal(host(gi), oi)
+    assert np.array_equal(host(gp), op)
+
+
+# -------------------------------------------------------------------- A2-A4
+
+TREE_KEYS = ("tokens", "parent", "depth", "positions", "score", "q_row", "mask", "mask_bits", "retrieve_index",
+             "next_token", "next_sibling")
+
+
+def _gpu_tree(tp, ti, root, plen, k, S, N):
+    t = sdv.sdv_build_tree(dev(tp), dev(ti), dev(root), dev(plen), k, S, N)
+    torch.cuda.synchronize()
+    out = {key: host(v) for key, v in t.items()}
+    out["mask_bits"] = out["mask_bits"].view(np.uint32)
+    return out
+
+
+def _assert_tree_equal(g, o):
+    for key in TREE_KEYS:
+        assert np.array_equal(g[key], o[key].astype(g[key].dtype)), key
+
+
+@pytest.mark.parametrize("name,V", [("c1", None), ("c2", 2000), ("c3", 3000), ("c4", 3000)])
+def test_build_tree_bit_exact(name, V):
+    cfg = workloads.get_config(name, **({"V": V} if V else {}))
+    inp = workloads.generate(cfg, with_attention=False)
+    say("build_tree", name, cfg.B, cfg.k, cfg.S, cfg.N)
+    tp, ti = otopk.draft_topk(inp["draft_probs"], cfg.k)
+    g = _gpu_tree(tp, ti, inp["root_token"], inp["prefix_len"], cfg.k, cfg.S, cfg.N)
+    o = otree.build_tree(tp, ti, inp["root_token"], inp["prefix_len"], cfg.k, cfg.S, cfg.N)
+    _assert_tree_equal(g, o)
+
+
+@pytest.mark.parametrize("k,S,N", [(2, 3, 6), (3, 4, 30), (8, 5, 64), (4, 6, 120), (16, 2, 200), (1, 9, 10),
+                                   (2, 1, 3), (5, 3, 1), (8, 5, 256)])
+def test_build_tree_ties_and_shapes(k, S, N):
+    rng = np.random.default_rng(k * 100 + S * 10 + N)
+    B = 5
+    R = 1 + (S - 1) * k
+    probs = (rng.integers(1, 9, size=(B, R, 40)) / 16.0).astype(np.float32)   # coarse -> score ties
+    tp, ti = otopk.draft_topk(probs, k)
+    root = rng.integers(0, 40, size=B).astype(np.int32)
+    plen = rng.integers(0, 1000, size=B).astype(np.int32)
+    say("build_tree ties", k, S, N)
+    g = _gpu_tree(tp, ti, root, plen, k, S, N)
+    o = otree.build_tree(tp, ti, root, plen, k, S, N)
+    _assert_tree_equal(g, o)
+
+
+# -------------------------------------------------------------------- A6-A7
+
+def _gpu_accept(mode, tree, target, S, **kw):
+    gt = {key: dev(tree[key]) for key in ("tokens", "next_token", "next_sibling", "q_row")}
+    args = {}
+    for key in ("draft_probs", "u_accept", "u_draw", "remaining"):
+        if kw.get(key) is not None:
+            args[key] = dev(kw[key])
+    r = sdv.sdv_verify_accept(mode, gt, dev(target), S, eos_id=kw.get("eos_id", -1), **args)
+    torch.cuda.synchronize()
+    return {key: host(v) for key, v in r.items()}
+
+
+def _assert_accept_equal(g, o):
+    for key in ("accept_len", "accept_path", "commit_tokens", "commit_len", "next_root"):
+        assert np.array_equal(g[key], o[key]), key
+
+
+@pytest.mark.parametrize("name,V,planted", [("c1", None, False), ("c1", None, True), ("c3", 5000, True),
+                                            ("c3", 128256, True), ("c4", 4097, True)])
+def test_accept_greedy_bit_exact(name, V, planted):
+    cfg = workloads.get_config(name, **({"V": V} if V else {}))
+    if name == "c3" and V == 128256:
+        cfg = cfg.replace(B=8)
+    inp = workloads.generate(cfg, with_attention=False)
+    tree = oracle_tree(inp, cfg)
+    target = inp["target"]          # stochastic configs: the p rows serve as logits
+    if planted:
+        target = plant_greedy(target, tree, workloads.extra_rng(cfg, 1), cfg.S)
+    say("accept greedy", name, cfg.B, cfg.V, planted)
+    g = _gpu_accept(sdv.GREEDY, tree, target, cfg.S)
+    o = oacc.verify_greedy(tree, target, cfg.S)
+    _assert_accept_equal(g, o)
+    if planted:
+        assert o["accept_len"].max() > 0
+
+
+def test_accept_greedy_budget_and_eos():
+    cfg = workloads.get_config("c3", V=3000, B=12)
+    inp = workloads.generate(cfg, with_attention=False)
+    tree = oracle_tree(inp, cfg)
+    rng = workloads.extra_rng(cfg, 2)
+    target = plant_greedy(inp["target"], tree, rng, cfg.S)
+    remaining = rng.integers(0, 4, size=cfg.B).astype(np.int32)
+    say("accept greedy budget")
+    g = _gpu_accept(sdv.GREEDY, tree, target, cfg.S, remaining=remaining)
+    _assert_accept_equal(g, oacc.verify_greedy(tree, target, cfg.S, remaining=remaining))
+    o0 = oacc.verify_greedy(tree, target, cfg.S)
+    eos = int(o0["commit_tokens"][0, 0])
+    say("accept greedy eos", eos)
+    g = _gpu_accept(sdv.GREEDY, tree, target, cfg.S, eos_id=eos)
+    _assert_accept_equal(g, oacc.verify_greedy(tree, target, cfg.S, eos_id=eos))
+
+
+@pytest.mark.parametrize("name,V,B,planted", [("c2", None, None, False), ("c2", 3001, None, True),
+                                              ("c4", 4096, 16, False), ("c4", 4096, 16, True),
+                                              ("c4", 128256, 8, True), ("c1", None, None, True)])
+def test_accept_stochastic_bit_exact(name, V, B, planted):
+    over = {}
+    if V:
+        over["V"] = V
+    if B:
+        over["B"] = B
+    cfg = workloads.get_config(name, **over)
+    if cfg.mode != "stochastic":
+        cfg = cfg.replace(mode="stochastic")
+    inp = workloads.generate(cfg, with_attention=False)
+    tree = oracle_tree(inp, cfg)
+    p = inp["target"]
+    if planted:
+        p = plant_stochastic(p, inp["draft_probs"], tree, workloads.extra_rng(cfg, 3), cfg.S)
+    say("accept stochastic", name, cfg.B, cfg.V, planted)
+    g = _gpu_accept(sdv.STOCHASTIC, tree, p, cfg.S, draft_probs=inp["draft_probs"], u_accept=inp["u_accept"],
+                    u_draw=inp["u_draw"])
+    o = oacc.verify_stochastic(tree, p, inp["draft_probs"], inp["u_accept"], inp["u_draw"], cfg.S)
+    _assert_accept_equal(g, o)
+
+
+def test_accept_stochastic_degenerate_rows():
+    """A leaf row with zero mass takes the argmax; tiny masses below 2^-40 too."""
+    cfg = workloads.get_config("c2", V=1000, B=4)
+    inp = workloads.generate(cfg, with_attention=False)
+    tree = oracle_tree(inp, cfg)
+    p = plant_stochastic(inp["target"], inp["draft_probs"], tree, workloads.extra_rng(cfg, 4), cfg.S)
+    # every node accepted up to the leaf, whose row is (nearly) empty
+    for b in range(cfg.B):
+        u = 0
+        while tree["next_token"][b, u] >= 0:
+            p[b, u] = inp["draft_probs"][b, tree["q_row"][b, u]]
+            u = tree["next_token"][b, u]
+        p[b, u] = 0.0
+        if b % 2:
+            p[b, u, 17 + b] = np.float32(2.0 ** -45)
+    say("accept stochastic degenerate")
+    g = _gpu_accept(sdv.STOCHASTIC, tree, p, cfg.S, draft_probs=inp["draft_probs"], u_accept=inp["u_accept"],
+                    u_draw=inp["u_draw"])
+    o = oacc.verify_stochastic(tree, p, inp["draft_probs"], inp["u_accept"], inp["u_draw"], cfg.S)
+    _assert_accept_equal(g, o)
+
+
+# ---------------------------------------------------------------------- A8
+
+def _accept_paths(rng, B, N, S, tree=None):
+    acc_len = np.zeros(B, np.int32)
+    acc_path = np.full((B, S + 1), -1, np.int32)
+    for b in range(B):
+        a = int(rng.integers(0, min(S, N - 1) + 1))
+        path = [0] + sorted(rng.choice(np.arange(1, N), size=a, replace=False).tolist())
+        acc_len[b] = a
+        acc_path[b, :a + 1] = path
+    return acc_len, acc_path
+
+
+@pytest.mark.parametrize("page,layers,B,N,S", [(1, 1, 6, 12, 4), (1, 1, 32, 64, 5), (16, 3, 9, 32, 4),
+                                               (4, 2, 7, 12, 6), (16, 1, 64, 32, 4), (8, 2, 5, 256, 9)])
+def test_compaction_bit_exact(page, layers, B, N, S):
+    rng = np.random.default_rng(page * 1000 + layers * 100 + N)
+    Hkv, D = 2, 16
+    L = rng.integers(0, 300, size=B).astype(np.int32)
+    need = (L + N + page - 1) // page
+    total = int(need.sum()) + 5
+    perm = rng.permutation(total).astype(np.int32)
+    table = np.full((B, int(need.max()) + 2), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    kps = [rng.integers(0, 65535, size=(total * page, Hkv, D)).astype(np.uint16) for _ in range(layers)]
+    vps = [rng.integers(0, 65535, size=(total * page, Hkv, D)).astype(np.uint16) for _ in range(layers)]
+    a, path = _accept_paths(rng, B, N, S)
+    say("compact", page, layers, B, N, S)
+    gt = dev(table)
+    gk = [dev(x) for x in kps] if page > 1 else []
+    gv = [dev(x) for x in vps] if page > 1 else []
+    new_len, freed, nf = sdv.sdv_compact_kv(gt, dev(L), dev(a), dev(path), N, S, page, gk, gv)
+    torch.cuda.synchronize()
+    t2, k2, v2, nl, fr = ocmp.compact_kv(table, kps, vps, L, a, path, N, page)
+    assert np.array_equal(host(gt), t2)
+    assert np.array_equal(host(new_len), nl)
+    n = int(host(nf)[0])
+    assert n == len(fr)
+    assert np.array_equal(host(freed)[:n], fr)
+    if page > 1:
+        for x, y in zip(gk + gv, k2 + v2):
+            assert np.array_equal(host(x).view(np.uint16), y)
+
+
+# ---------------------------------------------------------------------- A5
+
+def _attn_case(cfg, inp, requests=None, want_lse=True):
+    t = oracle_tree(inp, cfg)
+    W = (cfg.N + 31) // 32
+    say("attention", cfg.name, cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.page)
+    out, lse = sdv.sdv_tree_verify_attention(dev(inp["q"]), dev(inp["k_pool"]), dev(inp["v_pool"]),
+                                             dev(inp["page_table"]), dev(inp["prefix_len"]),
+                                             dev(t["mask_bits"].view(np.int32)), page=cfg.page, want_lse=want_lse)
+    torch.cuda.synchronize()
+    assert t["mask_bits"].shape[-1] == W
+    ro, rl = oatt.tree_verify_attention(inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                                        inp["prefix_len"], t["mask"], page=cfg.page, requests=requests)
+    got = bf16_to_f64(out)
+    sel = list(range(cfg.B)) if requests is None else list(requests)
+    assert_attention_close(got[sel], ro[sel])
+    if want_lse:
+        assert np.abs(host(lse)[sel] - rl[sel]).max() < 2e-3
+
+
+def test_attention_c1_full():
+    cfg = workloads.get_config("c1")
+    _attn_case(cfg, workloads.generate(cfg))
+
+
+@pytest.mark.parametrize("over", [dict(B=3, L_min=100, L_max=300), dict(B=2, N=13, Hq=6, Hkv=2, D=64, L_min=1, L_max=70),
+                                  dict(B=2, N=40, Hq=8, Hkv=8, D=128, L_min=0, L_max=0),
+                                  dict(B=2, N=256, k=8, S=6, Hq=4, Hkv=1, D=64, L_min=30, L_max=90)])
+def test_attention_small_shapes(over):
+    cfg = workloads.get_config("c3", V=256, **over)
+    _attn_case(cfg, workloads.generate(cfg))
+
+
+def test_attention_paged_small():
+    cfg = workloads.get_config("c4", V=256, B=3, L_min=40, L_max=200)
+    _attn_case(cfg, workloads.generate(cfg))
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_attention_full_config_sampled(name):
+    cfg = workloads.get_config(name, V=256)
+    inp = workloads.generate(cfg)
+    _attn_case(cfg, inp, requests=[0, cfg.B // 2, cfg.B - 1])
+
+
+# ------------------------------------------------------------------- A9-A10
+
+def test_tli_maps_and_remaps_bit_exact():
+    cfg = workloads.get_config("c5")
+    inp = workloads.generate(cfg, with_rows=False)
+    say("tli maps")
+    gd2t, gt2d = sdv.sdv_tli_build_maps(dev(inp["inter_ids"]), dev(inp["tgt_ids"]), cfg.V_draft, cfg.V,
+                                        int(inp["fallback"]))
+    torch.cuda.synchronize()
+    d2t, t2d = otli.build_maps(inp["inter_ids"], inp["tgt_ids"], cfg.V_draft, cfg.V, int(inp["fallback"]))
+    assert np.array_equal(host(gd2t), d2t) and np.array_equal(host(gt2d), t2d)
+    rng = workloads.extra_rng(cfg, 5)
+    ids_t = np.concatenate([rng.integers(0, cfg.V, 5000), [-1, cfg.V, 2 ** 30]]).astype(np.int32)
+    ids_d = np.concatenate([rng.integers(0, cfg.V_draft, 5000), [-5, cfg.V_draft]]).astype(np.int32)
+    assert np.array_equal(host(sdv.sdv_tli_map_ids(gt2d, dev(ids_t))), otli.map_ids(t2d, ids_t))
+    assert np.array_equal(host(sdv.sdv_tli_map_ids(gd2t, dev(ids_d))), otli.map_ids(d2t, ids_d))
+
+
+def test_tli_constrain_and_scatter_bit_exact():
+    cfg = workloads.get_config("c5")
+    inp = workloads.generate(cfg)
+    rng = workloads.extra_rng(cfg, 6)
+    pruned = rng.standard_normal((cfg.B, cfg.K_inter)).astype(np.float32)
+    say("tli constrain")
+    full = sdv.sdv_tli_constrain_draft_logits(dev(pruned), dev(inp["inter_ids"]), cfg.V_draft)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(full), otli.constrain_logits(pruned, inp["inter_ids"], cfg.V_draft))
+    say("tli q_scatter")
+    q = inp["q_pruned"]
+    qt = sdv.sdv_tli_q_scatter(dev(q), dev(inp["tgt_ids"]), cfg.V)
+    torch.cuda.synchronize()
+    want = otli.q_scatter(q.reshape(-1, cfg.K_inter), inp["tgt_ids"], cfg.V).reshape(cfg.B, cfg.R, cfg.V)
+    assert np.array_equal(host(qt), want)
+
+
+@pytest.mark.parametrize("B,H,K", [(64, 896, 60000), (5, 64, 1000), (17, 96, 77), (130, 32, 513)])
+def test_tli_lm_head_within_tolerance(B, H, K):
+    rng = np.random.default_rng(B + H + K)
+    hidden = workloads.to_bf16_bits(rng.standard_normal((B, H)).astype(np.float32))
+    w = workloads.to_bf16_bits((rng.standard_normal((K, H)) * 0.02).astype(np.float32))
+    say("lm_head", B, H, K)
+    g = sdv.sdv_tli_lm_head(dev(hidden), dev(w))
+    torch.cuda.synchronize()
+    ref = otli.lm_head(hidden, w)
+    assert_attention_close(host(g), ref)
+    assert np.abs(host(g) - ref).max() < 1e-3
+
+
+def test_tli_pipeline_c5():
+    """Scatter q into the target vocabulary, take its top-1 chain, verify."""
+    cfg = workloads.get_config("c5")
+    inp = workloads.generate(cfg)
+    say("tli pipeline")
+    qt = sdv.sdv_tli_q_scatter(dev(inp["q_pruned"]), dev(inp["tgt_ids"]), cfg.V)
+    tp, ti = sdv.sdv_draft_topk(qt, 1)
+    t = sdv.sdv_build_tree(tp, ti, dev(inp["root_token"]), dev(inp["prefix_len"]), 1, cfg.S, cfg.N)
+    r = sdv.sdv_verify_accept(sdv.STOCHASTIC, t, dev(inp["target"]), cfg.S, draft_probs=qt,
+                              u_accept=dev(inp["u_accept"]), u_draw=dev(inp["u_draw"]))
+    torch.cuda.synchronize()
+    q_host = otli.q_scatter(inp["q_pruned"].reshape(-1, cfg.K_inter), inp["tgt_ids"], cfg.V).reshape(cfg.B, cfg.R, cfg.V)
+    otp, oti = otopk.draft_topk(q_host, 1)
+    ot = otree.build_tree(otp, oti, inp["root_token"], inp["prefix_len"], 1, cfg.S, cfg.N)
+    o = oacc.verify_stochastic(ot, inp["target"], q_host, inp["u_accept"], inp["u_draw"], cfg.S)
+    for key in o:
+        assert np.array_equal(host(r[key]), o[key]), key

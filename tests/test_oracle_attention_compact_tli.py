@@ -216,8 +216,7 @@ def test_tli_maps_are_inverse_on_the_intersection():
     outside_t = np.setdiff1d(np.arange(250), tgt)
     assert (otli.map_ids(t2d, outside_t) == fb).all()
     assert (otli.map_ids(d2t, np.setdiff1d(np.arange(300), inter)) == -1).all()
-    with pytest.raises(IndexError):
-        otli.map_ids(d2t, np.array([300]))
+    assert otli.map_ids(d2t, np.array([300, -1, inter[0]])).tolist() == [-1, -1, tgt[0]]
 
 
 def test_tli_pruned_head_equals_full_head_columns():
