@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Throughput of the draft-tree build and target-side verify path on one GPU.
+
+One step = one pass of the whole path over one batch with every input
+resident in HBM: draft top-k -> tree build (scores, parents, positions, mask,
+retrieve arrays) -> tree-verify attention -> accept walk -> KV compaction
+(c5 instead: pruned LM head -> logit constraint -> distribution scatter ->
+top-1 -> tree -> stochastic accept -> target-to-draft id remap).
+
+Prints one JSON line: metric "verified draft tokens/s" (B * N tree tokens per
+step, root included), a roofline entry for the step's dominant kernel (HIP
+events on the launch stream) and, on rank 0 at N=1, the CPU oracle timed on
+a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+                    [--accept literal|planted] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+WORKLOAD_NAMES = {
+    "c1": "tiny EAGLE tree verify (B=2, topk=2, S=3, N=6, V=1000, Hq=Hkv=4, D=64, L=256, greedy)",
+    "c2": "linear stochastic verify (B=16, topk=1, S=4, N=5, V=128256, T=1.0)",
+    "c3": "EAGLE-2 tree verify, Llama-3-8B attention shape (B=32, topk=8, S=5, N=64, V=128256, "
+          "Hq=32, Hkv=8, D=128, page 1, L~U[512,4096], greedy, slot compaction)",
+    "c4": "paged tree verify (B=64, topk=4, S=4, N=32, V=128256, Hq=32, Hkv=8, D=128, page 16, "
+          "L~U[1024,8192], stochastic T=0.7, page-16 compaction)",
+    "c5": "TLI draft step + linear verify (B=64, H=896, K=60000, V_draft=151936, V_target=128256, "
+          "topk=1, S=4, N=5, stochastic)",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--accept", default="literal", choices=["literal", "planted"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU oracle sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- GPU path
+
+class Pipeline:
+    """Preallocated device buffers and the per-stage calls of one step."""
+
+    def __init__(self, cfg, inp, n_tables, accept_mode):
+        import torch
+        import speculative_decoding_eagle_amd as sdv
+        self.torch, self.sdv, self.cfg = torch, sdv, cfg
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+        self.d = {k: dev(v) for k, v in inp.items() if isinstance(v, np.ndarray) and v.ndim > 0}
+        self.fallback = int(inp.get("fallback", 0))
+        B, N, k, S = cfg.B, cfg.N, cfg.k, cfg.S
+        d = self.d
+        if cfg.is_tli:
+            self.q_target = torch.empty((B, cfg.R, cfg.V), dtype=torch.float32, device="cuda")
+            self.logits = torch.empty((B, cfg.K_inter), dtype=torch.float32, device="cuda")
+            self.full = torch.empty((B, cfg.V_draft), dtype=torch.float32, device="cuda")
+            self.d2t, self.t2d = sdv.sdv_tli_build_maps(d["inter_ids"], d["tgt_ids"], cfg.V_draft, cfg.V,
+                                                        self.fallback)
+            self.scatter_ws = torch.empty(cfg.V * 4 + 256, dtype=torch.uint8, device="cuda")
+            self.remap_out = torch.empty((B, S + 1), dtype=torch.int32, device="cuda")
+            self.draft_rows = self.q_target
+        else:
+            self.draft_rows = d["draft_probs"]
+        rows = B * cfg.R
+        self.topk_p = torch.empty((B, cfg.R, k), dtype=torch.float32, device="cuda")
+        self.topk_id = torch.empty((B, cfg.R, k), dtype=torch.int32, device="cuda")
+        ws = sdv._lib.lib().sdv_draft_topk_workspace_size(rows, cfg.V, k)
+        self.topk_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+        self.tree = {}
+        self.acc = {}
+        self.acc_ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+        self.mode = sdv.STOCHASTIC if cfg.mode == "stochastic" else sdv.GREEDY
+        if cfg.has_attention:
+            self.attn_out = torch.empty((B, N, cfg.Hq, cfg.D), dtype=torch.bfloat16, device="cuda")
+            self.tables = [d["page_table"].clone() for _ in range(n_tables)]
+            self.new_len = torch.empty(B, dtype=torch.int32, device="cuda")
+            self.freed = torch.empty(B * N, dtype=torch.int32, device="cuda")
+            self.num_freed = torch.empty(1, dtype=torch.int32, device="cuda")
+        self.target = d["target"]
+        # warm build, used to plant acceptance when asked
+        self.run_all(0)
+        torch.cuda.synchronize()
+        if accept_mode == "planted":
+            self._plant()
+
+    def _plant(self):
+        """Make the target accept a random-length path of first children
+        (setup only; the same planted rows are then used by every step)."""
+        cfg, torch = self.cfg, self.torch
+        rng = workloads.extra_rng(cfg, 99)
+        nt = self.tree["next_token"].cpu().numpy()
+        tok = self.tree["tokens"].cpu().numpy()
+        qr = self.tree["q_row"].cpu().numpy()
+        t = self.target
+        for b in range(cfg.B):
+            a = int(rng.integers(0, cfg.S + 1))
+            u = 0
+            for _ in range(a):
+                c = int(nt[b, u])
+                if c < 0:
+                    break
+                if self.mode == self.sdv.GREEDY:
+                    t[b, u, int(tok[b, c])] = t[b, u].max() + 1.0
+                else:
+                    t[b, u] = self.draft_rows[b, int(qr[b, u])]
+                u = c
+        torch.cuda.synchronize()
+
+    # ---- stages
+    def s_tli(self):
+        sdv, d, cfg = self.sdv, self.d, self.cfg
+        sdv.sdv_tli_lm_head(d["hidden"][0], d["weight"], logits=self.logits)
+        sdv.sdv_tli_constrain_draft_logits(self.logits, d["inter_ids"], cfg.V_draft, full=self.full)
+        sdv.sdv_tli_q_scatter(d["q_pruned"], d["tgt_ids"], cfg.V, q_target=self.q_target, ws=self.scatter_ws)
+
+    def s_topk(self):
+        self.sdv.sdv_draft_topk(self.draft_rows, self.cfg.k, topk_p=self.topk_p, topk_id=self.topk_id,
+                                ws=self.topk_ws)
+
+    def s_tree(self):
+        cfg = self.cfg
+        self.tree = self.sdv.sdv_build_tree(self.topk_p, self.topk_id, self.d["root_token"], self.d["prefix_len"],
+                                            cfg.k, cfg.S, cfg.N, out=self.tree)
+
+    def s_attn(self, i):
+        cfg = self.cfg
+        self.sdv.sdv_tree_verify_attention(self.d["q"], self.d["k_pool"], self.d["v_pool"], self.tables[i],
+                                           self.d["prefix_len"], self.tree["mask_bits"], page=cfg.page,
+                                           out=self.attn_out)
+
+    def s_accept(self):
+        d = self.d
+        kw = {}
+        if self.mode == self.sdv.STOCHASTIC:
+            kw = dict(draft_probs=self.draft_rows, u_accept=d["u_accept"], u_draw=d["u_draw"])
+        self.acc = self.sdv.sdv_verify_accept(self.mode, self.tree, self.target, self.cfg.S, out=self.acc,
+                                              ws=self.acc_ws, **kw)
+
+    def s_compact(self, i):
+        cfg, d = self.cfg, self.d
+        pools = ([d["k_pool"]], [d["v_pool"]]) if cfg.page > 1 else ([], [])
+        self.sdv.sdv_compact_kv(self.tables[i], d["prefix_len"], self.acc["accept_len"], self.acc["accept_path"],
+                                cfg.N, cfg.S, cfg.page, pools[0], pools[1], new_len=self.new_len, freed=self.freed,
+                                num_freed=self.num_freed)
+
+    def s_remap(self):
+        self.sdv.sdv_tli_map_ids(self.t2d, self.acc["commit_tokens"], out=self.remap_out)
+
+    def stages(self, i):
+        cfg = self.cfg
+        st = []
+        if cfg.is_tli:
+            st.append(("tli_head_mask_scatter", self.s_tli))
+        st += [("draft_topk", self.s_topk), ("build_tree", self.s_tree)]
+        if cfg.has_attention:
+            st.append(("tree_attention", lambda: self.s_attn(i)))
+        st.append(("accept", self.s_accept))
+        if cfg.has_attention:
+            st.append(("compact_kv", lambda: self.s_compact(i)))
+        if cfg.is_tli:
+            st.append(("t2d_remap", self.s_remap))
+        return st
+
+    def run_all(self, i):
+        for _, fn in self.stages(i):
+            fn()
+
+
+def algorithmic_work(cfg, inp, pipe):
+    """Bytes / flops the method must move or compute per launch, per stage."""
+    B, N, V, R, k = cfg.B, cfg.N, cfg.V, cfg.R, cfg.k
+    out = {"draft_topk": dict(bytes=B * R * V * 4 + B * R * k * 8, flops=0)}
+    if cfg.has_attention:
+        L = inp["prefix_len"].astype(np.int64)
+        depth = pipe.tree["depth"].cpu().numpy().astype(np.int64)
+        W = (N + 31) // 32
+        kv = int(((L + N) * cfg.Hkv * cfg.D * 2 * 2).sum())
+        qo = B * N * cfg.Hq * cfg.D * 2 * 2
+        idx = int(((L + N) * 4).sum()) + B * N * W * 4 + B * 4
+        vis = (L[:, None] + depth + 1).sum()
+        out["tree_attention"] = dict(bytes=kv + qo + idx, flops=int(vis) * cfg.Hq * cfg.D * 4)
+    acc_len = pipe.acc["accept_len"].cpu().numpy().astype(np.int64)
+    commit = pipe.acc["commit_len"].cpu().numpy().astype(np.int64)
+    rows = int(np.maximum(commit, 1).sum())     # visited nodes = committed tokens
+    per_row = V * 4 * (2 if cfg.mode == "stochastic" else 1)
+    out["accept"] = dict(bytes=rows * per_row, flops=0, accepted=int(acc_len.sum()))
+    if cfg.is_tli:
+        H = cfg.H_draft
+        out["tli_head_mask_scatter"] = dict(
+            bytes=cfg.K_inter * H * 2 + B * H * 2 + B * cfg.K_inter * 4          # GEMM
+            + B * cfg.K_inter * 4 + B * cfg.V_draft * 4 + cfg.K_inter * 4       # constrain
+            + B * R * cfg.K_inter * 4 + B * R * V * 4 + cfg.K_inter * 4,        # scatter
+            flops=2 * B * H * cfg.K_inter)
+    return out
+
+
+# --------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(cfg, inp, n_req):
+    """The oracle, as it stands, on the first n_req requests of the same
+    workload, BLAS pinned to one thread; scaled to verified tokens/s."""
+    from threadpoolctl import threadpool_limits
+    import oracle.accept as oacc
+    import oracle.attention as oatt
+    import oracle.compact as ocmp
+    import oracle.tli as otli
+    import oracle.topk as otopk
+    import oracle.tree as otree
+    n = min(n_req, cfg.B)
+    sl = slice(0, n)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        if cfg.is_tli:
+            h = inp["hidden"][0][sl]
+            logits = otli.lm_head(h, inp["weight"])
+            otli.constrain_logits(logits.astype(np.float32), inp["inter_ids"], cfg.V_draft)
+            rows = otli.q_scatter(inp["q_pruned"][sl].reshape(-1, cfg.K_inter), inp["tgt_ids"], cfg.V)
+            rows = rows.reshape(n, cfg.R, cfg.V)
+        else:
+            rows = inp["draft_probs"][sl]
+        tp, ti = otopk.draft_topk(rows, cfg.k)
+        tree = otree.build_tree(tp, ti, inp["root_token"][sl], inp["prefix_len"][sl], cfg.k, cfg.S, cfg.N)
+        if cfg.has_attention:
+            oatt.tree_verify_attention(inp["q"][sl], inp["k_pool"], inp["v_pool"], inp["page_table"][sl],
+                                       inp["prefix_len"][sl], tree["mask"], page=cfg.page)
+        if cfg.mode == "greedy":
+            acc = oacc.verify_greedy(tree, inp["target"][sl], cfg.S)
+        else:
+            acc = oacc.verify_stochastic(tree, inp["target"][sl], rows, inp["u_accept"][sl], inp["u_draw"][sl],
+                                         cfg.S)
+        if cfg.has_attention:
+            ocmp.compact_kv(inp["page_table"][sl], [], [], inp["prefix_len"][sl], acc["accept_len"],
+                            acc["accept_path"], cfg.N, cfg.page) if cfg.page == 1 else \
+                ocmp.compact_kv(inp["page_table"][sl], [inp["k_pool"]], [inp["v_pool"]], inp["prefix_len"][sl],
+                                acc["accept_len"], acc["accept_path"], cfg.N, cfg.page)
+        dt = time.perf_counter() - t0
+    return {"value": n * cfg.N / dt, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of %d requests of %s, every stage of the step (oracle, numpy, BLAS on 1 thread), "
+                      "%.2f s" % (n, cfg.B, cfg.name, dt)}
+
+
+# --------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only (the path is measured at one GPU's share; "
+              "multi-GPU sharding is described in DESIGN.md but not built). Got --gpus %d." % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    cfg = workloads.get_config(args.config)
+    log("generating inputs of %s" % cfg.name)
+    t_gen = time.perf_counter()
+    inp = workloads.generate(cfg)
+    t_gen = time.perf_counter() - t_gen
+    log("inputs ready in %.1f s; uploading and warming up" % t_gen)
+    pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept)
+    stages = [name for name, _ in pipe.stages(0)]
+
+    for i in range(args.warmup):
+        pipe.run_all(1 + i)
+    torch.cuda.synchronize()
+    base = 1 + args.warmup
+
+    # whole-step throughput (no events inside the timed region)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        pipe.run_all(base + i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-stage times with HIP events on the launch stream (same work again)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        st = pipe.stages(base + i)
+        ev[i][0].record()
+        for j, (_, fn) in enumerate(st):
+            fn()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, name in enumerate(stages)}
+
+    log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
+    work = algorithmic_work(cfg, inp, pipe)
+    dom = max((s for s in stages if s in work), key=lambda s: stage_ms[s])
+    w = work[dom]
+    t_s = stage_ms[dom] * 1e-3
+    gbs = w["bytes"] / t_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "algorithmic_bytes": int(w["bytes"]), "avg_ms": round(stage_ms[dom], 4)}
+    if w.get("flops"):
+        roofline["mfma_tflops"] = round(w["flops"] / t_s / 1e12, 2)
+        roofline["mfma_frac"] = round(w["flops"] / t_s / 1e12 / BF16_PEAK_TFLOPS, 4)
+
+    tokens = cfg.B * cfg.N
+    value = tokens / (ms_step * 1e-3)
+    line = {
+        "metric": "verified draft tokens/s (build+tree-attn+accept)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[cfg.name], "name": cfg.name, "batch": cfg.B, "tree_tokens": cfg.N,
+                   "accept": args.accept},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_gbs": {k: round(work[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9, 1) for k in stages if k in work},
+        "accepted_tokens": work["accept"]["accepted"],
+        "roofline": roofline,
+        "device": torch.cuda.get_device_name(0),
+        "input_generation_s": round(t_gen, 2),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -156,18 +156,24 @@ def _streams(seed: int) -> Dict[str, np.random.Generator]:
     return {name: np.random.Generator(np.random.PCG64(ss)) for name, ss in zip(_STREAMS, children)}
 
 
-def softmax_rows(logits: np.ndarray, temperature: float = 1.0, chunk_rows: int = 256) -> np.ndarray:
+def softmax_rows(logits: np.ndarray, temperature: float = 1.0, chunk_rows: int = 32) -> np.ndarray:
     """Processed distribution handed to the verify step: softmax(logits / T)
     along the last axis, evaluated in float64 and rounded once to fp32."""
     x = np.asarray(logits, dtype=np.float32)
     flat = x.reshape(-1, x.shape[-1])
     out = np.empty(flat.shape, dtype=np.float32)
+    buf = np.empty((min(chunk_rows, max(1, flat.shape[0])), flat.shape[1]), dtype=np.float64)
+    inv_t = 1.0 / float(temperature)
     for s in range(0, flat.shape[0], chunk_rows):
-        z = flat[s:s + chunk_rows].astype(np.float64) / float(temperature)
+        n = min(chunk_rows, flat.shape[0] - s)
+        z = buf[:n]
+        z[...] = flat[s:s + n]
+        if inv_t != 1.0:
+            z *= inv_t
         z -= z.max(axis=1, keepdims=True)
         np.exp(z, out=z)
         z /= z.sum(axis=1, keepdims=True)
-        out[s:s + chunk_rows] = z
+        out[s:s + n] = z
     return out.reshape(x.shape)
 
 
