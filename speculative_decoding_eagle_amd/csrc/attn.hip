@@ -3,21 +3,32 @@
 // parts", "Self-test" answer 1, "Exercises" question 1 and "Design
 // trade-offs"; "[SGLang] Multi-Layer EAGLE" section 6, TARGET_VERIFY).
 //
-// Layout of the work.  GQA packs the Hq/Hkv query heads that share a KV head
+// Work layout.  GQA packs the G = Hq/Hkv query heads that share a KV head
 // with the N tree nodes into N*G query rows (row = node*G + g).  A block of
 // four waves owns 64 of those rows of one (request, KV head) and streams the
-// request's keys in tiles of 64 positions through LDS:
-//   * K tile [64 keys][D] (row-padded) and V tile transposed to [D][64 keys],
-//     gathered through the page table (page size 1: a slot map);
-//   * wave w takes keys 16w..16w+15 of every tile for all 64 rows (the
-//     waves split the key axis, so each K/V byte is read from LDS once);
-//   * S^T = K Q^T with bf16 MFMA 16x16x32 (Q fragments stay in registers),
-//     online softmax in fp32 with exp2, O^T += V^T P^T with MFMA 16x16x16,
-//     so every lane keeps the statistics of its own query row;
-//   * at the end the four waves' (max, sum, O) are merged through LDS in a
-//     fixed order (deterministic) and written as bf16.
-// Row blocks of one (request, KV head) are placed on one XCD (the dispatcher
-// deals blocks round-robin over the 8 XCDs) so they share that XCD's L2.
+// request's keys in tiles of 64 positions.  Wave (rh, kh) computes rows
+// 32*rh .. +31 against keys 32*kh .. +31 of every tile, so each wave holds a
+// 32 x D fp32 accumulator and two row blocks of Q fragments in registers.
+//   * Both K and V tiles are staged through LDS (double buffered; the next
+//     tile's 16-byte chunks are fetched into registers while the current one
+//     is computed and written to the other buffer at the end of the
+//     iteration; page-table entries are fetched one tile further ahead).
+//   * S^T = K Q^T on bf16 MFMA 16x16x32 (K rows padded to 68 dwords so the
+//     16-byte fragment reads are bank-conflict free).
+//   * O^T += V^T P^T on MFMA 16x16x16: V rows (padded to 72 dwords) are read
+//     as 8-byte words holding 4 consecutive d of one key; four keys' words
+//     are repacked into the A operands of four MFMAs, output row m of block
+//     (dq, r) standing for d = 64*dq + 4*m + r.  P is rounded to bf16.
+//   * Every lane keeps the softmax state of its own query row; scores are
+//     scaled into log2 units and exponentiated with exp2; the reference max
+//     moves only when a score exceeds it by more than 2^8, so the O rescale
+//     is rare.
+//   * The two key-half waves of a row half are merged through LDS in a fixed
+//     order (deterministic) and the 64 x D tile is stored as bf16.
+// Scheduling: a small kernel ranks requests by prefix length (longest
+// first); blocks are dealt round-robin over the 8 XCDs, so units are
+// interleaved over XCDs in that order while the row blocks of one unit stay
+// on one XCD and share its L2.
 #include <cmath>
 
 #include "common.hpp"
@@ -42,86 +53,106 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 template <int D>
-struct AttnSmem {
-  static constexpr int kKStride = D + 8;          // bf16 elements per K row (16-byte pad)
-  static constexpr int kVStride = kTile + 8;      // bf16 elements per transposed V row
-  static constexpr int kKBytes = kTile * kKStride * 2;
-  static constexpr int kVBytes = D * kVStride * 2;
-  static constexpr int kMergeBytes = 2 * kRows * D * 4;   // two fp32 O tiles
-  static constexpr int kBytes = (kKBytes + kVBytes) > kMergeBytes ? (kKBytes + kVBytes) : kMergeBytes;
+struct AttnCfg {
+  static constexpr int CPK = D / 8;                       // 16-byte chunks per key row
+  static constexpr int KPP = kAttnThreads / CPK;          // keys per load pass
+  static constexpr int NL = kTile / KPP;                  // K (and V) chunks per thread per tile
+  static constexpr int DS = D / 32;                       // k-steps of QK^T
+  static constexpr int DQ = D / 64;                       // 64-wide d groups of PV
+  static constexpr int NO = DQ * 4;                       // O^T accumulator blocks per row block
+  static constexpr int KSTRIDE = D + 8;                   // bf16 per K row in LDS (68 / 36 dwords)
+  static constexpr int VSTRIDE = D + 16;                  // bf16 per V row in LDS (72 / 40 dwords)
+  static constexpr int KBYTES = kTile * KSTRIDE * 2;
+  static constexpr int VBYTES = kTile * VSTRIDE * 2;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int MERGE = kRows * D * 4;             // fp32 O of the 64 rows
+  static constexpr int SMEM = (2 * STAGE) > MERGE ? (2 * STAGE) : MERGE;
 };
+
+// Requests ranked by prefix length (longest first, then lower index).
+__global__ void attn_order_kernel(int B, const int *__restrict__ prefix_len, int *__restrict__ order) {
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int Lb = prefix_len[b];
+    int r = 0;
+    for (int o = 0; o < B; ++o) {
+      const int Lo = prefix_len[o];
+      r += (Lo > Lb) || (Lo == Lb && o < b);
+    }
+    order[r] = b;
+  }
+}
 
 template <int D>
 __global__ void __launch_bounds__(kAttnThreads, 2)
-tree_attn_kernel(int B, int N, int Hq, int Hkv, int page, int max_pages, int64_t num_slots, float scale_log2,
-                 int nrb, int units_total, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
-                 const uint16_t *__restrict__ vpool, const int *__restrict__ table,
-                 const int *__restrict__ prefix_len, const uint32_t *__restrict__ mask_bits,
-                 uint16_t *__restrict__ out, float *__restrict__ lse) {
-  using Sm = AttnSmem<D>;
-  constexpr int DS = D / 32;        // k-steps of the QK^T contraction
-  constexpr int DB = D / 16;        // 16-wide d blocks of the output
-  constexpr int RB = kRows / 16;    // 16-row blocks per wave
-  __shared__ __attribute__((aligned(16))) unsigned char smem[Sm::kBytes];
-  __shared__ float s_m[4][kRows];
-  __shared__ float s_l[4][kRows];
-  __shared__ uint32_t s_mask[kRows / 1][8];
+tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64_t num_slots, float scale_log2,
+                 int nrb, const int *__restrict__ order, const uint16_t *__restrict__ q,
+                 const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
+                 const int *__restrict__ table, const int *__restrict__ prefix_len,
+                 const uint32_t *__restrict__ mask_bits, uint16_t *__restrict__ out, float *__restrict__ lse) {
+  using C = AttnCfg<D>;
+  constexpr int RB = 2;                       // 16-row blocks per wave
+  constexpr int KB = 2;                       // 16-key blocks per wave per tile
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ float s_m[2][kRows];
+  __shared__ float s_l[2][kRows];
+  __shared__ uint32_t s_mask[kRows][8];
 
-  // XCD-aware placement: blocks x, x+8, x+16, ... run on one XCD; give them
-  // consecutive logical indices so the row blocks of a unit share an L2.
-  const int nblocks = gridDim.x;
-  const int per_xcd = nblocks / kXcds;
-  const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (logical >= units_total * nrb) return;
-  const int unit = logical / nrb;
-  const int rblk = logical % nrb;
-  const int b = unit / Hkv;
-  const int kvh = unit % Hkv;
+  // hardware block h runs on XCD h % 8 as that XCD's (h / 8)-th block
+  const int xcd = blockIdx.x % kXcds;
+  const int slot_in_xcd = blockIdx.x / kXcds;
+  const int rank = (slot_in_xcd / nrb) * kXcds + xcd;       // unit rank, longest requests first
+  const int rblk = slot_in_xcd % nrb;
+  if (rank >= B * Hkv) return;
+  const int b = order[rank / Hkv];
+  const int kvh = rank % Hkv;
   const int G = Hq / Hkv;
   const int W = (N + 31) / 32;
+  const int pmask = (1 << pshift) - 1;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
+  const int rh = wave >> 1, kh = wave & 1;
   const int l = lane_id();
   const int l16 = l & 15;
   const int g4 = l >> 4;
 
   const int L = prefix_len[b];
-  const int total_keys = L + N;
+  const int total = L + N;
   const int *trow = table + static_cast<int64_t>(b) * max_pages;
-  const bool req_ok = L >= 0 && static_cast<int64_t>(total_keys) <= static_cast<int64_t>(max_pages) * page;
+  const bool req_ok = L >= 0 && static_cast<int64_t>(total) <= (static_cast<int64_t>(max_pages) << pshift);
+  const int ntiles = req_ok ? (total + kTile - 1) / kTile : 0;
 
-  // tree mask rows of the nodes this block covers
   const int row0 = rblk * kRows;
   const int node0 = row0 / G;
-  const int nodes_here = min(N - node0, (kRows + G - 1) / G + 1);
   for (int x = tid; x < kRows * 8; x += kAttnThreads) {
     const int nn = x / 8, w = x % 8;
     uint32_t v = 0;
-    if (nn < nodes_here && w < W) v = mask_bits[(static_cast<int64_t>(b) * N + node0 + nn) * W + w];
+    if (node0 + nn < N && w < W) v = mask_bits[(static_cast<int64_t>(b) * N + node0 + nn) * W + w];
     s_mask[nn][w] = v;
   }
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][8*g4 .. +7] of k-step ds
-  bf16x8 qf[RB][DS];
+  // this lane's rows: row0 + 32*rh + 16*rb + l16
+  int nrel[RB];
+  bf16x8 qf[RB][C::DS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int r = row0 + rb * 16 + l16;
+    const int r = row0 + 32 * rh + 16 * rb + l16;
     const int node = r / G, g = r % G;
+    nrel[rb] = node - node0;
     const bool ok = node < N;
     const uint16_t *qp = q + ((static_cast<int64_t>(b) * N + (ok ? node : 0)) * Hq + kvh * G + g) * D;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
+    for (int ds = 0; ds < C::DS; ++ds) {
       uint4 u = ok ? *reinterpret_cast<const uint4 *>(qp + ds * 32 + 8 * g4) : make_uint4(0, 0, 0, 0);
       __builtin_memcpy(&qf[rb][ds], &u, 16);
     }
   }
 
-  f32x4 o[RB][DB];
+  f32x4 o[RB][C::NO];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::NO; ++j) o[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[RB], l_run[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -129,116 +160,161 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int page, int max_pages, int64_t
     l_run[rb] = 0.f;
   }
 
-  uint16_t *k_lds = reinterpret_cast<uint16_t *>(smem);
-  uint16_t *v_lds = reinterpret_cast<uint16_t *>(smem + Sm::kKBytes);
-  const int chunks_per_key = D / 8;
+  // tile loading: thread owns 16-byte column `lcol` of keys lkey0 + j*KPP
+  const int lcol = tid % C::CPK;
+  const int lkey0 = tid / C::CPK;
+  int pg[C::NL];
+  uint4 kst[C::NL], vst[C::NL];
 
-  const int ntiles = req_ok ? (total_keys + kTile - 1) / kTile : 0;
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int pos0 = tile * kTile;
-    __syncthreads();
-    // ---- K tile: 16-byte chunks, consecutive lanes along one key row
-    for (int c = tid; c < kTile * chunks_per_key; c += kAttnThreads) {
-      const int kk = c / chunks_per_key, col = c % chunks_per_key;
-      const int pos = pos0 + kk;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (pos < total_keys) {
-        const int64_t slot = static_cast<int64_t>(trow[pos / page]) * page + pos % page;
-        if (slot >= 0 && slot < num_slots)
-          u = *reinterpret_cast<const uint4 *>(kpool + (slot * Hkv + kvh) * D + col * 8);
-      }
-      *reinterpret_cast<uint4 *>(k_lds + kk * Sm::kKStride + col * 8) = u;
-    }
-    // ---- V tile, transposed: a thread takes two adjacent keys of one 8-wide d chunk
-    for (int c = tid; c < (kTile / 2) * chunks_per_key; c += kAttnThreads) {
-      const int kp = c % (kTile / 2), col = c / (kTile / 2);
-      uint4 u[2];
+  auto fetch_pages = [&](int t) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int pos = pos0 + 2 * kp + h;
-        u[h] = make_uint4(0, 0, 0, 0);
-        if (pos < total_keys) {
-          const int64_t slot = static_cast<int64_t>(trow[pos / page]) * page + pos % page;
-          if (slot >= 0 && slot < num_slots)
-            u[h] = *reinterpret_cast<const uint4 *>(vpool + (slot * Hkv + kvh) * D + col * 8);
-        }
-      }
-      const uint16_t *e0 = reinterpret_cast<const uint16_t *>(&u[0]);
-      const uint16_t *e1 = reinterpret_cast<const uint16_t *>(&u[1]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t pair = static_cast<uint32_t>(e0[j]) | (static_cast<uint32_t>(e1[j]) << 16);
-        *reinterpret_cast<uint32_t *>(v_lds + (col * 8 + j) * Sm::kVStride + 2 * kp) = pair;
-      }
+    for (int j = 0; j < C::NL; ++j) {
+      const int pos = t * kTile + lkey0 + j * C::KPP;
+      pg[j] = pos < total ? trow[pos >> pshift] : -1;
     }
-    __syncthreads();
+  };
+  auto fetch_data = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < C::NL; ++j) {
+      const int pos = t * kTile + lkey0 + j * C::KPP;
+      const int64_t sl = (static_cast<int64_t>(pg[j]) << pshift) + (pos & pmask);
+      const bool ok = pg[j] >= 0 && sl < num_slots;
+      const int64_t off = (sl * Hkv + kvh) * D + lcol * 8;
+      kst[j] = ok ? *reinterpret_cast<const uint4 *>(kpool + off) : make_uint4(0, 0, 0, 0);
+      vst[j] = ok ? *reinterpret_cast<const uint4 *>(vpool + off) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_stage = [&](int t) {
+    unsigned char *st = smem + (t & 1) * C::STAGE;
+    uint16_t *kb = reinterpret_cast<uint16_t *>(st);
+    uint16_t *vb = reinterpret_cast<uint16_t *>(st + C::KBYTES);
+#pragma unroll
+    for (int j = 0; j < C::NL; ++j) {
+      const int key = lkey0 + j * C::KPP;
+      *reinterpret_cast<uint4 *>(kb + key * C::KSTRIDE + lcol * 8) = kst[j];
+      *reinterpret_cast<uint4 *>(vb + key * C::VSTRIDE + lcol * 8) = vst[j];
+    }
+  };
 
-    // ---- S^T for this wave's 16 keys: A = K[key][d] from LDS, B = Q^T
-    const int key_base = wave * 16;
-    f32x4 s[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      bf16x8 kf;
-      __builtin_memcpy(&kf, k_lds + (key_base + l16) * Sm::kKStride + ds * 32 + 8 * g4, 16);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], s[rb], 0, 0, 0);
-    }
-
-    // ---- mask, online softmax (lane: row l16 of each row block; keys 4*g4+i)
-    s16x4 pf[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r = row0 + rb * 16 + l16;
-      const int nn = r / G - node0;
-      float v[4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = pos0 + key_base + 4 * g4 + i;
-        bool vis = pos < L;
-        if (!vis && pos < total_keys) {
-          const int j = pos - L;
-          vis = (nn >= 0 && nn < kRows) && ((s_mask[nn][j >> 5] >> (j & 31)) & 1u);
-        }
-        v[i] = vis ? s[rb][i] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, v[i]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run[rb], tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[rb] - m_use);
-      m_run[rb] = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(v[i] - m_use);
-        psum += p;
-        pf[rb][i] = static_cast<short>(f32_to_bf16_rne(p));
-      }
-      l_run[rb] = l_run[rb] * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        o[rb][db][0] *= alpha;
-        o[rb][db][1] *= alpha;
-        o[rb][db][2] *= alpha;
-        o[rb][db][3] *= alpha;
-      }
-    }
-
-    // ---- O^T += V^T P^T: A = V^T[d][keys 4*g4..+3] (LDS), B = P^T (registers)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      s16x4 vf;
-      __builtin_memcpy(&vf, v_lds + (db * 16 + l16) * Sm::kVStride + key_base + 4 * g4, 8);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[rb], o[rb][db], 0, 0, 0);
-    }
+  if (ntiles > 0) {
+    fetch_pages(0);
+    fetch_data(0);
+    fetch_pages(1);
+    store_stage(0);
   }
 
-  // ---- merge the four waves (fixed order) and write
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      fetch_data(t + 1);
+      fetch_pages(t + 2);
+    }
+    const unsigned char *st = smem + (t & 1) * C::STAGE;
+    const uint16_t *kb = reinterpret_cast<const uint16_t *>(st);
+    const uint16_t *vb = reinterpret_cast<const uint16_t *>(st + C::KBYTES);
+
+    // ---- S^T: A = K[key][d] (LDS), B = Q^T (registers)
+    f32x4 s[KB][RB];
+#pragma unroll
+    for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[k2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+#pragma unroll
+      for (int k2 = 0; k2 < KB; ++k2) {
+        bf16x8 kf;
+        __builtin_memcpy(&kf, kb + (32 * kh + 16 * k2 + l16) * C::KSTRIDE + ds * 32 + 8 * g4, 16);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[k2][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], s[k2][rb], 0, 0, 0);
+      }
+    }
+
+    // ---- mask + online softmax (lane: its row per rb; keys 16*k2 + 4*g4 + i)
+    const int kpos0 = t * kTile + 32 * kh + 4 * g4;
+    const bool all_prefix = (t + 1) * kTile <= L;
+    s16x4 pf[KB][RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float v[KB][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bool vis = true;
+          if (!all_prefix) {
+            const int pos = kpos0 + 16 * k2 + i;
+            const int j = pos - L;
+            vis = pos < L || (j < N && ((s_mask[nrel[rb]][j >> 5] >> (j & 31)) & 1u));
+          }
+          v[k2][i] = vis ? s[k2][rb][i] * scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, v[k2][i]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const bool need = tmax > m_run[rb] + 8.0f;
+      if (__any(need)) {
+        const float newm = need ? tmax : m_run[rb];
+        const float alpha = need ? exp2f(m_run[rb] - newm) : 1.0f;   // -inf - -inf must not reach exp2
+        m_run[rb] = newm;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int j = 0; j < C::NO; ++j) {
+          o[rb][j][0] *= alpha;
+          o[rb][j][1] *= alpha;
+          o[rb][j][2] *= alpha;
+          o[rb][j][3] *= alpha;
+        }
+      }
+      const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+      float psum = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(v[k2][i] - m_use);
+          psum += p;
+          pf[k2][rb][i] = static_cast<short>(f32_to_bf16_rne(p));
+        }
+      l_run[rb] += psum;
+    }
+
+    // ---- O^T += V^T P^T: 8-byte LDS words = 4 consecutive d of one key
+#pragma unroll
+    for (int k2 = 0; k2 < KB; ++k2) {
+      const uint16_t *vrow = vb + (32 * kh + 16 * k2 + 4 * g4) * C::VSTRIDE + 4 * l16;
+#pragma unroll
+      for (int dq = 0; dq < C::DQ; ++dq) {
+        uint2 w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint2 *>(vrow + j * C::VSTRIDE + dq * 64);
+        // a[r] = (key0, key1, key2, key3) at d = 64*dq + 4*l16 + r
+        s16x4 a[4];
+        {
+          const uint2 p0 = make_uint2((w[0].x & 0xffffu) | (w[1].x << 16), (w[2].x & 0xffffu) | (w[3].x << 16));
+          const uint2 p1 = make_uint2((w[0].x >> 16) | (w[1].x & 0xffff0000u), (w[2].x >> 16) | (w[3].x & 0xffff0000u));
+          const uint2 p2 = make_uint2((w[0].y & 0xffffu) | (w[1].y << 16), (w[2].y & 0xffffu) | (w[3].y << 16));
+          const uint2 p3 = make_uint2((w[0].y >> 16) | (w[1].y & 0xffff0000u), (w[2].y >> 16) | (w[3].y & 0xffff0000u));
+          __builtin_memcpy(&a[0], &p0, 8);
+          __builtin_memcpy(&a[1], &p1, 8);
+          __builtin_memcpy(&a[2], &p2, 8);
+          __builtin_memcpy(&a[3], &p3, 8);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            o[rb][dq * 4 + r] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[r], pf[k2][rb], o[rb][dq * 4 + r], 0, 0, 0);
+      }
+    }
+    if (more) store_stage(t + 1);
+  }
+
+  // ---- merge the two key halves of each row half (fixed order) and write
   __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -246,21 +322,18 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int page, int max_pages, int64_t
     lt += __shfl_xor(lt, 16, kWave);
     lt += __shfl_xor(lt, 32, kWave);
     if (g4 == 0) {
-      s_m[wave][rb * 16 + l16] = m_run[rb];
-      s_l[wave][rb * 16 + l16] = lt;
+      s_m[kh][32 * rh + 16 * rb + l16] = m_run[rb];
+      s_l[kh][32 * rh + 16 * rb + l16] = lt;
     }
   }
   __syncthreads();
-  float fac[RB];
-  float mrow[RB], lrow[RB];
+  float fac[RB], mrow[RB], lrow[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int r = rb * 16 + l16;
-    float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][r]);
+    const int r = 32 * rh + 16 * rb + l16;
+    const float M = fmaxf(s_m[0][r], s_m[1][r]);
     const float Mu = M == -INFINITY ? 0.f : M;
-    float Lsum = 0.f;
-    for (int w = 0; w < 4; ++w) Lsum += s_l[w][r] * exp2f(s_m[w][r] - Mu);
+    const float Lsum = s_l[0][r] * exp2f(s_m[0][r] - Mu) + s_l[1][r] * exp2f(s_m[1][r] - Mu);
     fac[rb] = Lsum > 0.f ? exp2f(m_run[rb] - Mu) / Lsum : 0.f;
     mrow[rb] = Mu;
     lrow[rb] = Lsum;
@@ -268,58 +341,55 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int page, int max_pages, int64_t
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int j = 0; j < C::NO; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[rb][db][i] *= fac[rb];
+      for (int i = 0; i < 4; ++i) o[rb][j][i] *= fac[rb];
 
-  // O^T fragment: lane holds d = db*16 + 4*g4 + i of row rb*16 + l16
-  float *mbuf = reinterpret_cast<float *>(smem);            // two [kRows][D] fp32 tiles
-  auto put = [&](int which) {
+  // accumulator o[rb][dq*4+r][i] holds row 32*rh+16*rb+l16 at d = 64*dq + 16*g4 + 4*i + r
+  float *mbuf = reinterpret_cast<float *>(smem);
+  if (kh == 1) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int dq = 0; dq < C::DQ; ++dq)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          mbuf[(which * kRows + rb * 16 + l16) * D + db * 16 + 4 * g4 + i] = o[rb][db][i];
-  };
-  auto add = [&](int which) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[rb][db][i] += mbuf[(which * kRows + rb * 16 + l16) * D + db * 16 + 4 * g4 + i];
-  };
-  if (wave >= 2) put(wave - 2);
-  __syncthreads();
-  if (wave < 2) add(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
-  __syncthreads();
-  if (wave == 0) {
-    add(0);
-    put(0);
+          *reinterpret_cast<float4 *>(mbuf + (32 * rh + 16 * rb + l16) * D + dq * 64 + 16 * g4 + 4 * i) =
+              make_float4(o[rb][dq * 4 + 0][i], o[rb][dq * 4 + 1][i], o[rb][dq * 4 + 2][i], o[rb][dq * 4 + 3][i]);
   }
   __syncthreads();
-  // coalesced bf16 store of the 64 x D tile: 8 values (16 bytes) per item
+  if (kh == 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int dq = 0; dq < C::DQ; ++dq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float4 *p4 = reinterpret_cast<float4 *>(mbuf + (32 * rh + 16 * rb + l16) * D + dq * 64 + 16 * g4 + 4 * i);
+          const float4 x = *p4;
+          *p4 = make_float4(o[rb][dq * 4 + 0][i] + x.x, o[rb][dq * 4 + 1][i] + x.y, o[rb][dq * 4 + 2][i] + x.z,
+                            o[rb][dq * 4 + 3][i] + x.w);
+        }
+  }
+  __syncthreads();
   for (int x = tid; x < kRows * (D / 8); x += kAttnThreads) {
     const int r = x / (D / 8), c8 = x % (D / 8);
     const int gr = row0 + r;
     const int node = gr / G, g = gr % G;
     if (node >= N) continue;
-    uint16_t h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = f32_to_bf16_rne(mbuf[r * D + c8 * 8 + j]);
-    uint4 u;
-    __builtin_memcpy(&u, h, 16);
-    *reinterpret_cast<uint4 *>(out + ((static_cast<int64_t>(b) * N + node) * Hq + kvh * G + g) * D + c8 * 8) = u;
+    const float4 a0 = *reinterpret_cast<const float4 *>(mbuf + r * D + c8 * 8);
+    const float4 a1 = *reinterpret_cast<const float4 *>(mbuf + r * D + c8 * 8 + 4);
+    const uint32_t w0 = f32_to_bf16_rne(a0.x) | (static_cast<uint32_t>(f32_to_bf16_rne(a0.y)) << 16);
+    const uint32_t w1 = f32_to_bf16_rne(a0.z) | (static_cast<uint32_t>(f32_to_bf16_rne(a0.w)) << 16);
+    const uint32_t w2 = f32_to_bf16_rne(a1.x) | (static_cast<uint32_t>(f32_to_bf16_rne(a1.y)) << 16);
+    const uint32_t w3 = f32_to_bf16_rne(a1.z) | (static_cast<uint32_t>(f32_to_bf16_rne(a1.w)) << 16);
+    *reinterpret_cast<uint4 *>(out + ((static_cast<int64_t>(b) * N + node) * Hq + kvh * G + g) * D + c8 * 8) =
+        make_uint4(w0, w1, w2, w3);
   }
-  if (lse && wave == 0 && g4 == 0) {
+  if (lse && kh == 0 && g4 == 0) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int gr = row0 + rb * 16 + l16;
+      const int gr = row0 + 32 * rh + 16 * rb + l16;
       const int node = gr / G, g = gr % G;
       if (node < N)
         lse[(static_cast<int64_t>(b) * N + node) * Hq + kvh * G + g] =
@@ -328,20 +398,41 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int page, int max_pages, int64_t
   }
 }
 
+template <int D>
+int32_t launch_attn(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb,
+                    const int *order, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                    const int32_t *page_table, const int32_t *prefix_len, const uint32_t *mask_bits, uint16_t *out,
+                    float *lse) {
+  const size_t lds = AttnCfg<D>::SMEM;
+  static thread_local int configured_dev = -1;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "tree_verify_attention: no device");
+  if (configured_dev != dev) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(tree_attn_kernel<D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return fail(SDV_E_HIP, "tree_verify_attention: LDS attribute: %s", hipGetErrorString(e));
+    configured_dev = dev;
+  }
+  hipLaunchKernelGGL(tree_attn_kernel<D>, dim3(static_cast<unsigned>(blocks)), dim3(kAttnThreads), lds, st, sh.B,
+                     sh.N, sh.Hq, sh.Hkv, pshift, sh.max_pages, sh.num_slots, scale_log2, nrb, order, q, k_pool,
+                     v_pool, page_table, prefix_len, mask_bits, out, lse);
+  return check_launch("tree_attn_kernel");
+}
+
 }  // namespace
 }  // namespace sdv
 
 using namespace sdv;
 
-extern "C" size_t sdv_tree_verify_attention_workspace_size(sdv_attn_shape) { return 0; }
+extern "C" size_t sdv_tree_verify_attention_workspace_size(sdv_attn_shape sh) {
+  return sh.B > 0 ? align_up(static_cast<size_t>(sh.B) * sizeof(int), 256) : 0;
+}
 
 extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, const uint16_t *q,
                                              const uint16_t *k_pool, const uint16_t *v_pool,
                                              const int32_t *page_table, const int32_t *prefix_len,
                                              const uint32_t *mask_bits, uint16_t *out, float *lse, void *ws,
                                              size_t ws_bytes, void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   clear_error();
   SDV_REQUIRE(sh.B >= 0 && sh.N >= 1 && sh.Hq >= 1 && sh.Hkv >= 1 && sh.page >= 1 && sh.max_pages >= 1 &&
                   sh.num_slots >= 0,
@@ -350,28 +441,38 @@ extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, 
   SDV_REQUIRE(sh.D == 64 || sh.D == 128, SDV_E_UNSUPPORTED, "tree_verify_attention: D=%d not in {64,128}", sh.D);
   SDV_REQUIRE(sh.N <= 256 && sh.Hq / sh.Hkv <= 16, SDV_E_UNSUPPORTED,
               "tree_verify_attention: N <= 256 and Hq/Hkv <= 16 required");
+  SDV_REQUIRE((sh.page & (sh.page - 1)) == 0 && sh.page <= (1 << 20), SDV_E_UNSUPPORTED,
+              "tree_verify_attention: page=%d must be a power of two", sh.page);
   if (sh.B == 0) return SDV_OK;
   SDV_REQUIRE(q && k_pool && v_pool && page_table && prefix_len && mask_bits && out, SDV_E_NULL,
               "tree_verify_attention: NULL pointer");
   SDV_REQUIRE(reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(k_pool) % 16 == 0 &&
                   reinterpret_cast<uintptr_t>(v_pool) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0,
               SDV_E_SHAPE, "tree_verify_attention: q, pools and out must be 16-byte aligned");
+  const size_t need = sdv_tree_verify_attention_workspace_size(sh);
+  SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "tree_verify_attention: workspace of %zu bytes needed",
+              need);
+  int pshift = 0;
+  while ((1 << pshift) < sh.page) ++pshift;
   const int G = sh.Hq / sh.Hkv;
   const int nrb = (sh.N * G + kRows - 1) / kRows;
-  const int units = sh.B * sh.Hkv;
-  int64_t blocks = static_cast<int64_t>(units) * nrb;
-  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  const int64_t units = static_cast<int64_t>(sh.B) * sh.Hkv;
+  const int64_t units_pad = (units + kXcds - 1) / kXcds * kXcds;
+  const int64_t blocks = units_pad * nrb;
   SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tree_verify_attention: grid too large");
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(sh.D));
   const float scale_log2 = scale * 1.4426950408889634f;
+  int *order = static_cast<int *>(ws);
   hipStream_t st = as_stream(stream);
+  hipLaunchKernelGGL(attn_order_kernel, dim3(1), dim3(256), 0, st, sh.B, prefix_len, order);
+  int32_t rc = check_launch("attn_order_kernel");
+  if (rc != SDV_OK) return rc;
   if (sh.D == 64)
-    hipLaunchKernelGGL(tree_attn_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(kAttnThreads), 0, st, sh.B,
-                       sh.N, sh.Hq, sh.Hkv, sh.page, sh.max_pages, sh.num_slots, scale_log2, nrb, units, q, k_pool,
-                       v_pool, page_table, prefix_len, mask_bits, out, lse);
+    rc = launch_attn<64>(blocks, st, sh, pshift, scale_log2, nrb, order, q, k_pool, v_pool, page_table, prefix_len,
+                         mask_bits, out, lse);
   else
-    hipLaunchKernelGGL(tree_attn_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(kAttnThreads), 0, st, sh.B,
-                       sh.N, sh.Hq, sh.Hkv, sh.page, sh.max_pages, sh.num_slots, scale_log2, nrb, units, q, k_pool,
-                       v_pool, page_table, prefix_len, mask_bits, out, lse);
+    rc = launch_attn<128>(blocks, st, sh, pshift, scale_log2, nrb, order, q, k_pool, v_pool, page_table, prefix_len,
+                          mask_bits, out, lse);
+  if (rc != SDV_OK) return rc;
   return check_launch("tree_attn_kernel");
 }

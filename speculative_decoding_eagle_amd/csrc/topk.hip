@@ -1,12 +1,12 @@
 // A1: per-row top-k of the draft distributions (fast_topk after the per-step
 // softmax, "[SGLang] Multi-Layer EAGLE" section 3).
 //
-// HBM-bound streaming reduction.  Each 256-thread block scans one slice of
-// one row with 16-byte loads (four in flight per thread), every thread keeping
-// a sorted register list of its K best (value desc, id asc); the block then
-// merges those lists in K rounds of block-wide argmax.  Short-row batches are
-// split over several blocks per row, and a one-wave kernel merges the
-// per-slice lists.
+// HBM-bound streaming reduction under the strict order (value desc, id asc).
+// Each 256-thread block scans one slice of one row; each of its waves streams
+// a contiguous quarter of the slice with 16-byte loads (four in flight per
+// lane) through a per-wave threshold filter (below), and wave 0 merges the
+// four per-wave lists.  Short-row batches are split over several blocks per
+// row, and a one-wave kernel merges the per-slice lists.
 #include <climits>
 #include <cmath>
 
@@ -59,55 +59,109 @@ struct SortedK {
   }
 };
 
-template <int K>
-__device__ __forceinline__ void consume4(SortedK<K> &L, float4 a, int e) {
-  const float m = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
-  if (m >= L.v[K - 1]) {
-    L.insert(a.x, e);
-    L.insert(a.y, e + 1);
-    L.insert(a.z, e + 2);
-    L.insert(a.w, e + 3);
-  }
-}
+// Per-wave candidate filter.  A wave keeps its current best K (value, id)
+// sorted in LDS and a threshold = the K-th of them; elements that beat the
+// threshold are appended to a per-wave LDS buffer (ballot + prefix count)
+// and the buffer is folded into the best-K list whenever it fills up.  After
+// the first fold the threshold is high enough that almost no element passes,
+// so the scan is one compare and one ballot per 16-byte load.
+constexpr int kCap = 512;                     // candidate slots per wave
 
-// Block-wide K rounds of argmax over the threads' sorted lists; thread 0
-// receives the merged list in (ov, oi).
 template <int K>
-__device__ void block_merge(SortedK<K> &L, float *ov, int *oi) {
-  __shared__ float sv[kTopkThreads / kWave];
-  __shared__ int si[kTopkThreads / kWave];
-  const int w = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
-  for (int r = 0; r < K; ++r) {
-    float bv = L.v[0];
-    int bi = L.i[0];
-    wave_best(bv, bi);
-    if (lane_id() == 0) {
-      sv[w] = bv;
-      si[w] = bi;
+struct WaveFilter {
+  float *cv;            // [kCap] candidate values (this wave's slice of LDS)
+  int *ci;              // [kCap] candidate ids
+  float *tv;            // [K] best values, sorted best first
+  int *ti;              // [K] best ids
+  int cnt;              // candidates buffered (wave-uniform)
+  float thr_v;          // K-th best value so far (wave-uniform)
+  int thr_i;
+
+  __device__ void init(float *v, int *i, float *bv, int *bi) {
+    cv = v;
+    ci = i;
+    tv = bv;
+    ti = bi;
+    cnt = 0;
+    thr_v = -INFINITY;
+    thr_i = INT_MAX;
+    if (lane_id() < K) {
+      tv[lane_id()] = -INFINITY;
+      ti[lane_id()] = INT_MAX;
     }
-    __syncthreads();
-    float gv = sv[0];
-    int gi = si[0];
-    for (int x = 1; x < nw; ++x)
-      if (better(sv[x], si[x], gv, gi)) {
-        gv = sv[x];
-        gi = si[x];
-      }
-    if (L.i[0] == gi && L.v[0] == gv && gi != INT_MAX) L.pop_front();
-    if (threadIdx.x == 0) {
-      ov[r] = gv;
-      oi[r] = gi;
-    }
-    __syncthreads();
   }
-}
+
+  // Folds the buffered candidates into the best-K list.
+  __device__ void fold() {
+    __builtin_amdgcn_wave_barrier();   // candidate stores of every lane precede the reads
+    SortedK<K> L;
+    L.init();
+    const int n = cnt + K;
+    for (int x = lane_id(); x < n; x += kWave) {
+      const float v = x < K ? tv[x] : cv[x - K];
+      const int i = x < K ? ti[x] : ci[x - K];
+      L.insert(v, i);
+    }
+    float keep_v = -INFINITY;
+    int keep_i = INT_MAX;
+    for (int r = 0; r < K; ++r) {
+      float bv = L.v[0];
+      int bi = L.i[0];
+      wave_best(bv, bi);
+      if (L.i[0] == bi && L.v[0] == bv && bi != INT_MAX) L.pop_front();
+      if (lane_id() == r) {
+        keep_v = bv;
+        keep_i = bi;
+      }
+    }
+    if (lane_id() < K) {
+      tv[lane_id()] = keep_v;
+      ti[lane_id()] = keep_i;
+    }
+    thr_v = __shfl(keep_v, K - 1, kWave);
+    thr_i = __shfl(keep_i, K - 1, kWave);
+    cnt = 0;
+  }
+
+  __device__ __forceinline__ void push(bool pred, float v, int i) {
+    const unsigned long long m = __ballot(pred);
+    if (m == 0ull) return;
+    const int before = __popcll(m & ((1ull << lane_id()) - 1ull));
+    if (pred) {
+      cv[cnt + before] = v;
+      ci[cnt + before] = i;
+    }
+    cnt += __popcll(m);
+  }
+
+  // Elements e .. e+3 (valid = false: this lane has none).
+  __device__ __forceinline__ void consume4(float4 a, int e, bool valid = true) {
+    const float m = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+    // conservative pre-test: an element can only beat the threshold if m >= thr_v
+    if (__ballot(valid && m >= thr_v) == 0ull) return;
+    push(valid && better(a.x, e, thr_v, thr_i), a.x, e);
+    push(valid && better(a.y, e + 1, thr_v, thr_i), a.y, e + 1);
+    push(valid && better(a.z, e + 2, thr_v, thr_i), a.z, e + 2);
+    push(valid && better(a.w, e + 3, thr_v, thr_i), a.w, e + 3);
+    if (cnt > kCap - 4 * kWave) fold();
+  }
+
+  __device__ __forceinline__ void consume1(float a, int e, bool valid) {
+    push(valid && better(a, e, thr_v, thr_i), a, e);
+    if (cnt > kCap - kWave) fold();
+  }
+};
 
 template <int K>
 __global__ void __launch_bounds__(kTopkThreads)
 topk_slice_kernel(const float *__restrict__ probs, int64_t rows, int V, int splits, int chunk,
                   int k, bool vec, float *__restrict__ out_v, int *__restrict__ out_i,
                   float *__restrict__ part_v, int *__restrict__ part_i) {
+  constexpr int NW = kTopkThreads / kWave;
+  __shared__ float s_cv[NW][kCap];
+  __shared__ int s_ci[NW][kCap];
+  __shared__ float s_tv[NW][K];
+  __shared__ int s_ti[NW][K];
   const int64_t bid = blockIdx.x;
   const int64_t row = bid / splits;
   const int split = static_cast<int>(bid % splits);
@@ -115,39 +169,67 @@ topk_slice_kernel(const float *__restrict__ probs, int64_t rows, int V, int spli
   const float *rp = probs + row * static_cast<int64_t>(V);
   const int lo = split * chunk;
   const int hi = min(V, lo + chunk);
-
-  SortedK<K> L;
-  L.init();
   const int tid = threadIdx.x;
+  const int w = tid / kWave;
+
+  WaveFilter<K> F;
+  F.init(s_cv[w], s_ci[w], s_tv[w], s_ti[w]);
   if (vec) {
-    const int step = 4 * kTopkThreads;
-    int e = lo + 4 * tid;
-    for (; e + 3 * step < hi; e += 4 * step) {
+    // each wave streams its own quarter of the slice (16-byte loads, four in flight)
+    const int per = ((hi - lo) / 4 + NW - 1) / NW * 4;
+    const int wlo = min(hi, lo + w * per);
+    const int whi = min(hi, wlo + per);
+    const int step = 4 * kWave;
+    int e = wlo + 4 * lane_id();
+    int base = wlo;                         // wave-uniform: every lane leaves the loop together
+    for (; base + 4 * step <= whi; base += 4 * step, e += 4 * step) {
       const float4 a0 = *reinterpret_cast<const float4 *>(rp + e);
       const float4 a1 = *reinterpret_cast<const float4 *>(rp + e + step);
       const float4 a2 = *reinterpret_cast<const float4 *>(rp + e + 2 * step);
       const float4 a3 = *reinterpret_cast<const float4 *>(rp + e + 3 * step);
-      consume4(L, a0, e);
-      consume4(L, a1, e + step);
-      consume4(L, a2, e + 2 * step);
-      consume4(L, a3, e + 3 * step);
+      F.consume4(a0, e);
+      F.consume4(a1, e + step);
+      F.consume4(a2, e + 2 * step);
+      F.consume4(a3, e + 3 * step);
     }
-    for (; e < hi; e += step) consume4(L, *reinterpret_cast<const float4 *>(rp + e), e);
+    for (; e - 4 * lane_id() < whi; e += step) {
+      const bool in = e < whi;
+      const float4 a = in ? *reinterpret_cast<const float4 *>(rp + e)
+                          : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      F.consume4(a, e, in);
+    }
   } else {
-    for (int e = lo + tid; e < hi; e += kTopkThreads) L.insert(rp[e], e);
-  }
-
-  __shared__ float mv[K];
-  __shared__ int mi[K];
-  block_merge<K>(L, mv, mi);
-  if (splits == 1) {
-    if (tid < k) {
-      out_v[row * k + tid] = mv[tid];
-      out_i[row * k + tid] = mi[tid];
+    for (int e0 = lo + w * kWave; e0 < hi; e0 += NW * kWave) {
+      const int e = e0 + lane_id();
+      const bool in = e < hi;
+      F.consume1(in ? rp[e] : -INFINITY, e, in);
     }
-  } else if (tid < K) {
-    part_v[bid * K + tid] = mv[tid];
-    part_i[bid * K + tid] = mi[tid];
+  }
+  F.fold();
+  __syncthreads();
+
+  // wave 0 merges the four per-wave lists
+  if (w == 0) {
+    SortedK<K> L;
+    L.init();
+    for (int x = lane_id(); x < NW * K; x += kWave) L.insert(s_tv[x / K][x % K], s_ti[x / K][x % K]);
+    for (int r = 0; r < K; ++r) {
+      float bv = L.v[0];
+      int bi = L.i[0];
+      wave_best(bv, bi);
+      if (L.i[0] == bi && L.v[0] == bv && bi != INT_MAX) L.pop_front();
+      if (lane_id() == 0) {
+        if (splits == 1) {
+          if (r < k) {
+            out_v[row * k + r] = bv;
+            out_i[row * k + r] = bi;
+          }
+        } else {
+          part_v[bid * K + r] = bv;
+          part_i[bid * K + r] = bi;
+        }
+      }
+    }
   }
 }
 
