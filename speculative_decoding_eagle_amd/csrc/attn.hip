@@ -5,31 +5,35 @@
 //
 // Work layout.  GQA packs the G = Hq/Hkv query heads that share a KV head
 // with the N tree nodes into N*G query rows (row = node*G + g).  A block of
-// four waves owns 64 of those rows of one (request, KV head) and streams the
-// request's keys in tiles of 64 positions.  Wave (rh, kh) computes rows
+// eight waves owns 128 of those rows of one (request, KV head) and streams
+// the request's keys in tiles of 64 positions.  Wave (rh, kh) computes rows
 // 32*rh .. +31 against keys 32*kh .. +31 of every tile, so each wave holds a
 // 32 x D fp32 accumulator and two row blocks of Q fragments in registers.
-//   * Both K and V tiles are staged through LDS (double buffered; the next
-//     tile's 16-byte chunks are fetched into registers while the current one
-//     is computed and written to the other buffer at the end of the
-//     iteration; page-table entries are fetched one tile further ahead).
-//   * S^T = K Q^T on bf16 MFMA 16x16x32 (K rows padded to 68 dwords so the
-//     16-byte fragment reads are bank-conflict free).
-//   * O^T += V^T P^T on MFMA 16x16x16: V rows (padded to 72 dwords) are read
-//     as 8-byte words holding 4 consecutive d of one key; four keys' words
-//     are repacked into the A operands of four MFMAs, output row m of block
-//     (dq, r) standing for d = 64*dq + 4*m + r.  P is rounded to bf16.
+//   * K and V tiles go from the paged pool straight into LDS with
+//     global_load_lds_dwordx4 (16 bytes per lane, a wave fills 1 KB per
+//     instruction) through a ring of four stages: while tile t is computed,
+//     tiles t+1 .. t+3 are in flight.  No registers stage the data.
+//   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled per row so that
+//     the MFMA fragment reads below hit distinct banks.
+//   * S^T = K Q^T on bf16 MFMA 16x16x32.  O^T += V^T P^T on MFMA 16x16x16:
+//     V is read as 8-byte words holding 4 consecutive d of one key; four
+//     keys' words are repacked into the A operands of four MFMAs, output row
+//     m of block (dq, r) standing for d = 64*dq + 4*m + r.  P is rounded to
+//     bf16.
 //   * Every lane keeps the softmax state of its own query row; scores are
 //     scaled into log2 units and exponentiated with exp2; the reference max
 //     moves only when a score exceeds it by more than 2^8, so the O rescale
 //     is rare.
-//   * The two key-half waves of a row half are merged through LDS in a fixed
-//     order (deterministic) and the 64 x D tile is stored as bf16.
+//   * Page ids come from an LDS copy of the request's page-table row,
+//     refreshed once per window of kPageCache pages.
+//   * The two key-half waves of a row quarter are merged through LDS in a
+//     fixed order (deterministic) and the 128 x D tile is stored as bf16.
 // Scheduling: a small kernel ranks requests by prefix length (longest
 // first); blocks are dealt round-robin over the 8 XCDs, so units are
 // interleaved over XCDs in that order while the row blocks of one unit stay
 // on one XCD and share its L2.
 #include <cmath>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -38,12 +42,15 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-constexpr int kAttnThreads = 256;
-constexpr int kRows = 64;          // query rows per block
-constexpr int kTile = 64;          // key positions per tile
+constexpr int kAttnThreads = 512;
+constexpr int kRows = 128;          // query rows per block
+constexpr int kTile = 64;           // key positions per tile
+constexpr int kStages = 4;          // LDS ring: three tiles in flight
 constexpr int kXcds = 8;
+constexpr int kPageCache = 4096;    // page-table entries cached in LDS
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -54,23 +61,57 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 template <int D>
 struct AttnCfg {
-  static constexpr int CPK = D / 8;                       // 16-byte chunks per key row
-  static constexpr int KPP = kAttnThreads / CPK;          // keys per load pass
-  static constexpr int NL = kTile / KPP;                  // K (and V) chunks per thread per tile
+  static constexpr int ROW = 2 * D;                       // bytes per key row
+  static constexpr int CHUNKS = D / 8;                    // 16-byte chunks per row
+  static constexpr int KPI = 64 / CHUNKS;                 // key rows per DMA instruction (1 KB)
+  static constexpr int IPW = 8 / KPI;                     // DMA instructions per wave per tile and tensor
   static constexpr int DS = D / 32;                       // k-steps of QK^T
   static constexpr int DQ = D / 64;                       // 64-wide d groups of PV
   static constexpr int NO = DQ * 4;                       // O^T accumulator blocks per row block
-  static constexpr int KSTRIDE = D + 8;                   // bf16 per K row in LDS (68 / 36 dwords)
-  static constexpr int VSTRIDE = D + 16;                  // bf16 per V row in LDS (72 / 40 dwords)
-  static constexpr int KBYTES = kTile * KSTRIDE * 2;
-  static constexpr int VBYTES = kTile * VSTRIDE * 2;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int MERGE = kRows * D * 4;             // fp32 O of the 64 rows
-  static constexpr int SMEM = (2 * STAGE) > MERGE ? (2 * STAGE) : MERGE;
+  static constexpr int TILE_BYTES = kTile * ROW;
+  static constexpr int STAGE = 2 * TILE_BYTES;            // K then V
+  static constexpr int SMEM = kStages * STAGE;            // also holds the fp32 merge buffer
+  static_assert(kRows * D * 4 <= SMEM, "merge buffer must fit");
 };
 
-// Requests ranked by prefix length (longest first, then lower index).
-__global__ void attn_order_kernel(int B, const int *__restrict__ prefix_len, int *__restrict__ order) {
+// Chunk swizzle of key row r: the 16 rows read by one quarter-wave map a
+// fixed chunk to 16 distinct chunks (K fragments), and rows r, r+4 land in
+// different halves of the row (V words).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    r &= 15;
+    return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
+  } else {
+    return (r >> 1) & 7;
+  }
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane L writes LDS
+// bytes lds_addr + 16*L .. +15 (lds_addr is wave-uniform, via M0).  Issued
+// as inline assembly so that the compiler does not add its conservative
+// "wait for every LDS DMA before any LDS read"; the kernel waits explicitly
+// (wait_vmcnt) and the memory clobber keeps LDS reads from moving across.
+__device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
+}
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Requests ranked by prefix length (longest first, then lower index); also
+// clears the 256-byte zero block that out-of-range key positions read.
+__global__ void attn_order_kernel(int B, const int *__restrict__ prefix_len, int *__restrict__ order,
+                                  int *__restrict__ zero_block) {
+  if (threadIdx.x < 64) zero_block[threadIdx.x] = 0;
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
     const int Lb = prefix_len[b];
     int r = 0;
@@ -85,10 +126,11 @@ __global__ void attn_order_kernel(int B, const int *__restrict__ prefix_len, int
 template <int D>
 __global__ void __launch_bounds__(kAttnThreads, 2)
 tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64_t num_slots, float scale_log2,
-                 int nrb, const int *__restrict__ order, const uint16_t *__restrict__ q,
-                 const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
-                 const int *__restrict__ table, const int *__restrict__ prefix_len,
-                 const uint32_t *__restrict__ mask_bits, uint16_t *__restrict__ out, float *__restrict__ lse) {
+                 int nrb, const int *__restrict__ order, const uint16_t *__restrict__ zero16,
+                 const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+                 const uint16_t *__restrict__ vpool, const int *__restrict__ table,
+                 const int *__restrict__ prefix_len, const uint32_t *__restrict__ mask_bits,
+                 uint16_t *__restrict__ out, float *__restrict__ lse) {
   using C = AttnCfg<D>;
   constexpr int RB = 2;                       // 16-row blocks per wave
   constexpr int KB = 2;                       // 16-key blocks per wave per tile
@@ -96,6 +138,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   __shared__ float s_m[2][kRows];
   __shared__ float s_l[2][kRows];
   __shared__ uint32_t s_mask[kRows][8];
+  __shared__ int s_page[kPageCache];
 
   // hardware block h runs on XCD h % 8 as that XCD's (h / 8)-th block
   const int xcd = blockIdx.x % kXcds;
@@ -111,7 +154,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
-  const int rh = wave >> 1, kh = wave & 1;
+  const int rh = wave >> 1, kh = wave & 1;    // rows 32*rh .. +31, keys 32*kh .. +31
   const int l = lane_id();
   const int l16 = l & 15;
   const int g4 = l >> 4;
@@ -121,6 +164,8 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   const int *trow = table + static_cast<int64_t>(b) * max_pages;
   const bool req_ok = L >= 0 && static_cast<int64_t>(total) <= (static_cast<int64_t>(max_pages) << pshift);
   const int ntiles = req_ok ? (total + kTile - 1) / kTile : 0;
+  const int total_pages = (total + pmask) >> pshift;
+  const int win_tiles = (kPageCache << pshift) / kTile;     // tiles covered by one page window
 
   const int row0 = rblk * kRows;
   const int node0 = row0 / G;
@@ -147,7 +192,6 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       __builtin_memcpy(&qf[rb][ds], &u, 16);
     }
   }
-
   f32x4 o[RB][C::NO];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -160,59 +204,77 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
     l_run[rb] = 0.f;
   }
 
-  // tile loading: thread owns 16-byte column `lcol` of keys lkey0 + j*KPP
-  const int lcol = tid % C::CPK;
-  const int lkey0 = tid / C::CPK;
-  int pg[C::NL];
-  uint4 kst[C::NL], vst[C::NL];
-
-  auto fetch_pages = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < C::NL; ++j) {
-      const int pos = t * kTile + lkey0 + j * C::KPP;
-      pg[j] = pos < total ? trow[pos >> pshift] : -1;
-    }
-  };
-  auto fetch_data = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < C::NL; ++j) {
-      const int pos = t * kTile + lkey0 + j * C::KPP;
-      const int64_t sl = (static_cast<int64_t>(pg[j]) << pshift) + (pos & pmask);
-      const bool ok = pg[j] >= 0 && sl < num_slots;
-      const int64_t off = (sl * Hkv + kvh) * D + lcol * 8;
-      kst[j] = ok ? *reinterpret_cast<const uint4 *>(kpool + off) : make_uint4(0, 0, 0, 0);
-      vst[j] = ok ? *reinterpret_cast<const uint4 *>(vpool + off) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_stage = [&](int t) {
-    unsigned char *st = smem + (t & 1) * C::STAGE;
-    uint16_t *kb = reinterpret_cast<uint16_t *>(st);
-    uint16_t *vb = reinterpret_cast<uint16_t *>(st + C::KBYTES);
-#pragma unroll
-    for (int j = 0; j < C::NL; ++j) {
-      const int key = lkey0 + j * C::KPP;
-      *reinterpret_cast<uint4 *>(kb + key * C::KSTRIDE + lcol * 8) = kst[j];
-      *reinterpret_cast<uint4 *>(vb + key * C::VSTRIDE + lcol * 8) = vst[j];
-    }
+  auto refresh_pages = [&](int first_tile) {
+    const int p0 = (first_tile * kTile) >> pshift;
+    for (int x = tid; x < kPageCache; x += kAttnThreads)
+      s_page[x] = (p0 + x < total_pages) ? trow[p0 + x] : -1;
   };
 
+  // DMA of tile t into stage S: wave w moves key rows 8w .. 8w+7 of K and V.
+  // Lane L of an instruction fills LDS chunk L % CHUNKS of row L / CHUNKS,
+  // so it fetches logical chunk (L % CHUNKS) ^ swz(row); the element offset
+  // of that chunk within a slot is fixed per lane and instruction.  Positions
+  // outside the request read the zero block (the instruction is always
+  // issued, which keeps the per-wave count of loads in flight fixed).
+  const int64_t slot_stride = static_cast<int64_t>(Hkv) * D;
+  int dma_row[C::IPW];
+  int dma_col[C::IPW];
+#pragma unroll
+  for (int i = 0; i < C::IPW; ++i) {
+    dma_row[i] = wave * 8 + i * C::KPI + l / C::CHUNKS;
+    dma_col[i] = kvh * D + (((l % C::CHUNKS) ^ swz<D>(dma_row[i])) << 3);
+  }
+  auto dma_tile = [&](int t, auto STG) {
+    constexpr int stg = decltype(STG)::value;
+    unsigned char *kst = smem + stg * C::STAGE;
+    unsigned char *vst = kst + C::TILE_BYTES;
+    const int wbase = ((t / win_tiles) * win_tiles * kTile) >> pshift;
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) {
+      const int pos = t * kTile + dma_row[i];
+      int idx = (pos >> pshift) - wbase;
+      idx = idx < 0 ? 0 : (idx >= kPageCache ? kPageCache - 1 : idx);
+      const int pid = s_page[idx];
+      const int64_t sl = (static_cast<int64_t>(pid) << pshift) + (pos & pmask);
+      const bool ok = pos < total && pid >= 0 && sl < num_slots;
+      const int64_t off = sl * slot_stride + dma_col[i];
+      const uint16_t *ka = ok ? kpool + off : zero16;
+      const uint16_t *va = ok ? vpool + off : zero16;
+      const int lrow = wave * 8 + i * C::KPI;                    // first row of this 1 KB block
+      dma16(ka, __builtin_amdgcn_readfirstlane(lds_offset(kst + lrow * C::ROW)));
+      dma16(va, __builtin_amdgcn_readfirstlane(lds_offset(vst + lrow * C::ROW)));
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+
+  refresh_pages(0);
+  __syncthreads();
+  // the Q fragments and the page copy land here once, not inside the key loop
+  __builtin_amdgcn_s_waitcnt(0);
   if (ntiles > 0) {
-    fetch_pages(0);
-    fetch_data(0);
-    fetch_pages(1);
-    store_stage(0);
+    dma_tile(0, S0{});
+    dma_tile(1, S1{});
+    dma_tile(2, S2{});
   }
 
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    const bool more = t + 1 < ntiles;
-    if (more) {
-      fetch_data(t + 1);
-      fetch_pages(t + 2);
+  // one tile: tile t sits in stage STG = t % 4; tile t+3 goes to stage (t+3) % 4
+  auto tile_step = [&](int t, auto STG) {
+    constexpr int stg = decltype(STG)::value;
+    wait_vmcnt<4 * C::IPW>();            // this wave's DMAs of tile t are done (t+1, t+2 may fly)
+    __syncthreads();                     // everyone's are; and stage (t+3)%4 is no longer read
+    if (t + 3 < ntiles && (t + 3) % win_tiles == 0) {   // block-uniform: next page window
+      refresh_pages(t + 3);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
-    const unsigned char *st = smem + (t & 1) * C::STAGE;
-    const uint16_t *kb = reinterpret_cast<const uint16_t *>(st);
-    const uint16_t *vb = reinterpret_cast<const uint16_t *>(st + C::KBYTES);
+    dma_tile(t + 3, std::integral_constant<int, (stg + 3) % kStages>{});
+
+    const unsigned char *kb = smem + stg * C::STAGE;
+    const unsigned char *vb = kb + C::TILE_BYTES;
 
     // ---- S^T: A = K[key][d] (LDS), B = Q^T (registers)
     f32x4 s[KB][RB];
@@ -221,44 +283,52 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) s[k2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
+    for (int k2 = 0; k2 < KB; ++k2) {
+      const int kr = 32 * kh + 16 * k2 + l16;
+      const int sk = swz<D>(kr);
 #pragma unroll
-      for (int k2 = 0; k2 < KB; ++k2) {
+      for (int ds = 0; ds < C::DS; ++ds) {
         bf16x8 kf;
-        __builtin_memcpy(&kf, kb + (32 * kh + 16 * k2 + l16) * C::KSTRIDE + ds * 32 + 8 * g4, 16);
+        __builtin_memcpy(&kf, kb + kr * C::ROW + (((ds * 4 + g4) ^ sk) << 4), 16);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           s[k2][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], s[k2][rb], 0, 0, 0);
       }
     }
 
-    // ---- mask + online softmax (lane: its row per rb; keys 16*k2 + 4*g4 + i)
+    // ---- mask + online softmax (lane: its row per rb; keys 16*k2 + 4*g4 + i).
+    // Max on raw scores, then p = exp2(s * scale_log2 - m) as one FMA and a
+    // bare v_exp_f32; P goes to bf16 with the hardware pack instruction.
     const int kpos0 = t * kTile + 32 * kh + 4 * g4;
     const bool all_prefix = (t + 1) * kTile <= L;
     s16x4 pf[KB][RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float v[KB][4];
-      float tmax = -INFINITY;
+      float rmax = -INFINITY;
 #pragma unroll
       for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bool vis = true;
           if (!all_prefix) {
-            const int pos = kpos0 + 16 * k2 + i;
-            const int j = pos - L;
-            vis = pos < L || (j < N && ((s_mask[nrel[rb]][j >> 5] >> (j & 31)) & 1u));
+            // Branch-free on purpose: a short-circuit form here becomes
+            // divergent control flow whose -inf write lands in the MFMA
+            // result register for every tree lane, visible ones included.
+            const int j = kpos0 + 16 * k2 + i - L;
+            const uint32_t w = s_mask[nrel[rb]][(j >> 5) & 7];
+            vis = (j < 0) | ((static_cast<unsigned>(j) < static_cast<unsigned>(N)) & ((w >> (j & 31)) & 1u));
           }
-          v[k2][i] = vis ? s[k2][rb][i] * scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, v[k2][i]);
+          v[k2][i] = vis ? s[k2][rb][i] : -INFINITY;
+          rmax = fmaxf(rmax, v[k2][i]);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 16, kWave));
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
+      const float tmax = rmax * scale_log2;
       const bool need = tmax > m_run[rb] + 8.0f;
       if (__any(need)) {
         const float newm = need ? tmax : m_run[rb];
-        const float alpha = need ? exp2f(m_run[rb] - newm) : 1.0f;   // -inf - -inf must not reach exp2
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run[rb] - newm) : 1.0f;   // never -inf - -inf
         m_run[rb] = newm;
         l_run[rb] *= alpha;
 #pragma unroll
@@ -269,28 +339,41 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
           o[rb][j][3] *= alpha;
         }
       }
-      const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+      const float mneg = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
       float psum = 0.f;
 #pragma unroll
-      for (int k2 = 0; k2 < KB; ++k2)
+      for (int k2 = 0; k2 < KB; ++k2) {
+        float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(v[k2][i] - m_use);
-          psum += p;
-          pf[k2][rb][i] = static_cast<short>(f32_to_bf16_rne(p));
+          p[i] = __builtin_amdgcn_exp2f(fmaf(v[k2][i], scale_log2, mneg));
+          psum += p[i];
         }
+        bf16x2 h01, h23;
+        h01[0] = static_cast<__bf16>(p[0]);
+        h01[1] = static_cast<__bf16>(p[1]);
+        h23[0] = static_cast<__bf16>(p[2]);
+        h23[1] = static_cast<__bf16>(p[3]);
+        uint2 packed;
+        __builtin_memcpy(&packed.x, &h01, 4);
+        __builtin_memcpy(&packed.y, &h23, 4);
+        __builtin_memcpy(&pf[k2][rb], &packed, 8);
+      }
       l_run[rb] += psum;
     }
 
     // ---- O^T += V^T P^T: 8-byte LDS words = 4 consecutive d of one key
 #pragma unroll
     for (int k2 = 0; k2 < KB; ++k2) {
-      const uint16_t *vrow = vb + (32 * kh + 16 * k2 + 4 * g4) * C::VSTRIDE + 4 * l16;
 #pragma unroll
       for (int dq = 0; dq < C::DQ; ++dq) {
         uint2 w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint2 *>(vrow + j * C::VSTRIDE + dq * 64);
+        for (int j = 0; j < 4; ++j) {
+          const int vr = 32 * kh + 16 * k2 + 4 * g4 + j;
+          const int c = (dq * 8 + (l16 >> 1)) ^ swz<D>(vr);
+          w[j] = *reinterpret_cast<const uint2 *>(vb + vr * C::ROW + (c << 4) + ((l16 & 1) << 3));
+        }
         // a[r] = (key0, key1, key2, key3) at d = 64*dq + 4*l16 + r
         s16x4 a[4];
         {
@@ -311,10 +394,17 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
                 __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[r], pf[k2][rb], o[rb][dq * 4 + r], 0, 0, 0);
       }
     }
-    if (more) store_stage(t + 1);
+  };
+
+  for (int t = 0; t < ntiles; t += kStages) {
+    tile_step(t, S0{});
+    if (t + 1 < ntiles) tile_step(t + 1, S1{});
+    if (t + 2 < ntiles) tile_step(t + 2, S2{});
+    if (t + 3 < ntiles) tile_step(t + 3, S3{});
   }
 
-  // ---- merge the two key halves of each row half (fixed order) and write
+  // ---- merge the two key halves of each row quarter (fixed order) and write
+  __builtin_amdgcn_s_waitcnt(0);         // trailing DMAs (zero blocks) must land before reuse
   __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -400,7 +490,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
 
 template <int D>
 int32_t launch_attn(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb,
-                    const int *order, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                    const int *order, const uint16_t *zero16, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                     const int32_t *page_table, const int32_t *prefix_len, const uint32_t *mask_bits, uint16_t *out,
                     float *lse) {
   const size_t lds = AttnCfg<D>::SMEM;
@@ -414,7 +504,7 @@ int32_t launch_attn(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, in
     configured_dev = dev;
   }
   hipLaunchKernelGGL(tree_attn_kernel<D>, dim3(static_cast<unsigned>(blocks)), dim3(kAttnThreads), lds, st, sh.B,
-                     sh.N, sh.Hq, sh.Hkv, pshift, sh.max_pages, sh.num_slots, scale_log2, nrb, order, q, k_pool,
+                     sh.N, sh.Hq, sh.Hkv, pshift, sh.max_pages, sh.num_slots, scale_log2, nrb, order, zero16, q, k_pool,
                      v_pool, page_table, prefix_len, mask_bits, out, lse);
   return check_launch("tree_attn_kernel");
 }
@@ -425,7 +515,7 @@ int32_t launch_attn(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, in
 using namespace sdv;
 
 extern "C" size_t sdv_tree_verify_attention_workspace_size(sdv_attn_shape sh) {
-  return sh.B > 0 ? align_up(static_cast<size_t>(sh.B) * sizeof(int), 256) : 0;
+  return sh.B > 0 ? align_up(static_cast<size_t>(sh.B) * sizeof(int), 256) + 256 : 0;
 }
 
 extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, const uint16_t *q,
@@ -463,15 +553,17 @@ extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, 
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(sh.D));
   const float scale_log2 = scale * 1.4426950408889634f;
   int *order = static_cast<int *>(ws);
+  int *zero_block = reinterpret_cast<int *>(static_cast<char *>(ws) + align_up(static_cast<size_t>(sh.B) * sizeof(int), 256));
+  const uint16_t *zero16 = reinterpret_cast<const uint16_t *>(zero_block);
   hipStream_t st = as_stream(stream);
-  hipLaunchKernelGGL(attn_order_kernel, dim3(1), dim3(256), 0, st, sh.B, prefix_len, order);
+  hipLaunchKernelGGL(attn_order_kernel, dim3(1), dim3(256), 0, st, sh.B, prefix_len, order, zero_block);
   int32_t rc = check_launch("attn_order_kernel");
   if (rc != SDV_OK) return rc;
   if (sh.D == 64)
-    rc = launch_attn<64>(blocks, st, sh, pshift, scale_log2, nrb, order, q, k_pool, v_pool, page_table, prefix_len,
+    rc = launch_attn<64>(blocks, st, sh, pshift, scale_log2, nrb, order, zero16, q, k_pool, v_pool, page_table, prefix_len,
                          mask_bits, out, lse);
   else
-    rc = launch_attn<128>(blocks, st, sh, pshift, scale_log2, nrb, order, q, k_pool, v_pool, page_table, prefix_len,
+    rc = launch_attn<128>(blocks, st, sh, pshift, scale_log2, nrb, order, zero16, q, k_pool, v_pool, page_table, prefix_len,
                           mask_bits, out, lse);
   if (rc != SDV_OK) return rc;
   return check_launch("tree_attn_kernel");
