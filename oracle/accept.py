@@ -17,7 +17,7 @@ slots": the verification kernels walk the tree to each request's longest
 accepted path.  sglang PR #22883 ("Modifications"): the acceptance criterion
 is unchanged under TLI.
 
-Readings (listed in DESIGN.md):
+Readings where the pages leave a step open:
 * Target row u of request b is the target's distribution after tree node u
   (greedy: raw logits; stochastic: processed p).  The draft distribution that
   produced u's children is draft row q_row[u].

@@ -8,7 +8,7 @@ page is copied too ("Self-test" answer 3; "Drafting, verification and slots";
 ch.10, section 5.2: after a rejection the cache is restored to the committed
 path, and the correction or bonus token has no KV of its own yet.
 
-Readings (listed in DESIGN.md):
+Readings where the pages leave a step open:
 * The tree of request b occupies logical positions L_b .. L_b+N-1 of the
   request's own chain (node j at L_b + j), starting inside the prefix's partial
   last page when the page size P > 1.

@@ -12,7 +12,7 @@ Follows sglang PR #22883 "TLI (Token-Level Intersection)", "Modifications":
 * the target's rejection-sampling step is unchanged, which keeps TLI lossless
   ("Motivation"; "Accuracy Tests").
 
-Readings (listed in the design doc): the intersection is given as pairs
+Readings where the pages leave a step open: the intersection is given as pairs
 (inter_ids[j], tgt_ids[j]) -- draft id and target id of the same normalised
 token -- with inter_ids sorted; the pruned weight is row-major [K, H] with row
 j belonging to draft id inter_ids[j]; a draft id outside the intersection maps

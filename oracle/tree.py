@@ -12,7 +12,7 @@ Follows
 * zero-to-sglang ch.10, section 5.2: the verify input carries the draft tokens,
   their positions, the custom mask and the retrieve arrays.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 1. Pool.  Step 0 puts the root's k children in the pool with score = prob.
    Each later step expands every frontier slot j of the previous step into its
    k children with score = fl32(score(parent) * prob); all of them join the

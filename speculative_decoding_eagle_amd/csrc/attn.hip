@@ -28,8 +28,8 @@
 //     refreshed once per window of kPageCache pages.
 //   * The two key-half waves of a row quarter are merged through LDS in a
 //     fixed order (deterministic) and the 128 x D tile is stored as bf16.
-// Scheduling: a small kernel ranks requests by prefix length (longest
-// first); blocks are dealt round-robin over the 8 XCDs, so units are
+// Scheduling: each block ranks the requests by prefix length (longest
+// first) and takes its unit by rank; blocks are dealt round-robin over the 8 XCDs, so units are
 // interleaved over XCDs in that order while the row blocks of one unit stay
 // on one XCD and share its L2.
 #include <cmath>
@@ -107,27 +107,37 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Requests ranked by prefix length (longest first, then lower index); also
-// clears the 256-byte zero block that out-of-range key positions read.
-__global__ void attn_order_kernel(int B, const int *__restrict__ prefix_len, int *__restrict__ order,
-                                  int *__restrict__ zero_block) {
-  if (threadIdx.x < 64) zero_block[threadIdx.x] = 0;
-  for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int Lb = prefix_len[b];
-    int r = 0;
+// Source of the DMA for key positions outside the request: 256 zero bytes,
+// never written.
+__device__ __attribute__((aligned(256))) uint16_t g_zero16[128];
+
+constexpr int kRankMax = 1024;      // requests ranked in-kernel; larger batches keep their order
+
+// The request of rank r when requests are ranked by prefix length (longest
+// first, then lower index).  Every block ranks the (small) batch itself from
+// an LDS copy of the prefix lengths; s_len is LDS scratch of B ints.
+__device__ int request_of_rank(int r, int B, const int *__restrict__ prefix_len, int *s_len, int *s_pick) {
+  if (B > kRankMax) return r;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < B; i += kAttnThreads) s_len[i] = prefix_len[i];
+  __syncthreads();
+  for (int c = tid; c < B; c += kAttnThreads) {
+    const int Lc = s_len[c];
+    int rk = 0;
     for (int o = 0; o < B; ++o) {
-      const int Lo = prefix_len[o];
-      r += (Lo > Lb) || (Lo == Lb && o < b);
+      const int Lo = s_len[o];
+      rk += (Lo > Lc) | ((Lo == Lc) & (o < c));
     }
-    order[r] = b;
+    if (rk == r) *s_pick = c;
   }
+  __syncthreads();
+  return *s_pick;
 }
 
 template <int D>
 __global__ void __launch_bounds__(kAttnThreads, 2)
 tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64_t num_slots, float scale_log2,
-                 int nrb, const int *__restrict__ order, const uint16_t *__restrict__ zero16,
-                 const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+                 int nrb, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
                  const uint16_t *__restrict__ vpool, const int *__restrict__ table,
                  const int *__restrict__ prefix_len, const uint32_t *__restrict__ mask_bits,
                  uint16_t *__restrict__ out, float *__restrict__ lse) {
@@ -139,6 +149,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   __shared__ float s_l[2][kRows];
   __shared__ uint32_t s_mask[kRows][8];
   __shared__ int s_page[kPageCache];
+  __shared__ int s_pick;
 
   // hardware block h runs on XCD h % 8 as that XCD's (h / 8)-th block
   const int xcd = blockIdx.x % kXcds;
@@ -146,7 +157,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   const int rank = (slot_in_xcd / nrb) * kXcds + xcd;       // unit rank, longest requests first
   const int rblk = slot_in_xcd % nrb;
   if (rank >= B * Hkv) return;
-  const int b = order[rank / Hkv];
+  const int b = request_of_rank(rank / Hkv, B, prefix_len, reinterpret_cast<int *>(smem), &s_pick);
   const int kvh = rank % Hkv;
   const int G = Hq / Hkv;
   const int W = (N + 31) / 32;
@@ -238,8 +249,8 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       const int64_t sl = (static_cast<int64_t>(pid) << pshift) + (pos & pmask);
       const bool ok = pos < total && pid >= 0 && sl < num_slots;
       const int64_t off = sl * slot_stride + dma_col[i];
-      const uint16_t *ka = ok ? kpool + off : zero16;
-      const uint16_t *va = ok ? vpool + off : zero16;
+      const uint16_t *ka = ok ? kpool + off : g_zero16;
+      const uint16_t *va = ok ? vpool + off : g_zero16;
       const int lrow = wave * 8 + i * C::KPI;                    // first row of this 1 KB block
       dma16(ka, __builtin_amdgcn_readfirstlane(lds_offset(kst + lrow * C::ROW)));
       dma16(va, __builtin_amdgcn_readfirstlane(lds_offset(vst + lrow * C::ROW)));
@@ -490,7 +501,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
 
 template <int D>
 int32_t launch_attn(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb,
-                    const int *order, const uint16_t *zero16, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                    const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                     const int32_t *page_table, const int32_t *prefix_len, const uint32_t *mask_bits, uint16_t *out,
                     float *lse) {
   const size_t lds = AttnCfg<D>::SMEM;
@@ -504,7 +515,7 @@ int32_t launch_attn(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, in
     configured_dev = dev;
   }
   hipLaunchKernelGGL(tree_attn_kernel<D>, dim3(static_cast<unsigned>(blocks)), dim3(kAttnThreads), lds, st, sh.B,
-                     sh.N, sh.Hq, sh.Hkv, pshift, sh.max_pages, sh.num_slots, scale_log2, nrb, order, zero16, q, k_pool,
+                     sh.N, sh.Hq, sh.Hkv, pshift, sh.max_pages, sh.num_slots, scale_log2, nrb, q, k_pool,
                      v_pool, page_table, prefix_len, mask_bits, out, lse);
   return check_launch("tree_attn_kernel");
 }
@@ -515,7 +526,8 @@ int32_t launch_attn(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, in
 using namespace sdv;
 
 extern "C" size_t sdv_tree_verify_attention_workspace_size(sdv_attn_shape sh) {
-  return sh.B > 0 ? align_up(static_cast<size_t>(sh.B) * sizeof(int), 256) + 256 : 0;
+  (void)sh;
+  return 0;
 }
 
 extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, const uint16_t *q,
@@ -539,9 +551,8 @@ extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, 
   SDV_REQUIRE(reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(k_pool) % 16 == 0 &&
                   reinterpret_cast<uintptr_t>(v_pool) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0,
               SDV_E_SHAPE, "tree_verify_attention: q, pools and out must be 16-byte aligned");
-  const size_t need = sdv_tree_verify_attention_workspace_size(sh);
-  SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "tree_verify_attention: workspace of %zu bytes needed",
-              need);
+  (void)ws;
+  (void)ws_bytes;
   int pshift = 0;
   while ((1 << pshift) < sh.page) ++pshift;
   const int G = sh.Hq / sh.Hkv;
@@ -552,18 +563,13 @@ extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, 
   SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tree_verify_attention: grid too large");
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(sh.D));
   const float scale_log2 = scale * 1.4426950408889634f;
-  int *order = static_cast<int *>(ws);
-  int *zero_block = reinterpret_cast<int *>(static_cast<char *>(ws) + align_up(static_cast<size_t>(sh.B) * sizeof(int), 256));
-  const uint16_t *zero16 = reinterpret_cast<const uint16_t *>(zero_block);
   hipStream_t st = as_stream(stream);
-  hipLaunchKernelGGL(attn_order_kernel, dim3(1), dim3(256), 0, st, sh.B, prefix_len, order, zero_block);
-  int32_t rc = check_launch("attn_order_kernel");
-  if (rc != SDV_OK) return rc;
+  int32_t rc;
   if (sh.D == 64)
-    rc = launch_attn<64>(blocks, st, sh, pshift, scale_log2, nrb, order, zero16, q, k_pool, v_pool, page_table, prefix_len,
+    rc = launch_attn<64>(blocks, st, sh, pshift, scale_log2, nrb, q, k_pool, v_pool, page_table, prefix_len,
                          mask_bits, out, lse);
   else
-    rc = launch_attn<128>(blocks, st, sh, pshift, scale_log2, nrb, order, zero16, q, k_pool, v_pool, page_table, prefix_len,
+    rc = launch_attn<128>(blocks, st, sh, pshift, scale_log2, nrb, q, k_pool, v_pool, page_table, prefix_len,
                           mask_bits, out, lse);
   if (rc != SDV_OK) return rc;
   return check_launch("tree_attn_kernel");
