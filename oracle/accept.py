@@ -27,7 +27,10 @@ Readings where the pages leave a step open:
   in sibling order; a rejected child replaces t by the normalised residual
   (t - q_u)+ with q_u held fixed; the first accepted child is moved to; if all
   are rejected the correction is drawn from the last residual; at a leaf the
-  bonus is drawn from p_u.
+  bonus is drawn from p_u.  This is the multi-candidate speculative sampling
+  of SpecInfer (Miao et al., 2023), which commits exactly p when the
+  candidates are i.i.d. draws from q (pinned by exact enumeration); for the
+  deterministic top-k children of a draft tree no output law is claimed.
 * An EOS or budget stop on a token that matched a child counts that child as
   accepted, with no further token.
 * Sampling arithmetic (makes the walk bit-exact across devices):

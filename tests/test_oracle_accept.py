@@ -321,6 +321,97 @@ def test_sampling_primitives():
     assert oacc.accept_test(np.float32(0.5 - 2 ** -24), np.float32(0.8), np.float32(0.4))
 
 
+# ------------------------------------- stochastic: siblings (tree, k = 2)
+#
+# The walk's treatment of several children -- try them in sibling order, each
+# rejection replacing t by the normalised residual (t - q)+ with q fixed, the
+# correction drawn from the last residual -- is the multi-candidate
+# ("multi-step") speculative sampling of SpecInfer (Miao et al., 2023).  Its
+# theorem: when the candidates are drawn i.i.d. from q the committed token is
+# distributed exactly as p.  The exact enumeration below feeds the oracle every
+# pair (y1, y2) of i.i.d. draws as a two-child tree and every uniform.
+
+def _two_child_tree(y1, y2):
+    t = otree.verify_arrays(np.array([0, y1, y2], np.int32), np.array([-1, 0, 0], np.int32),
+                            np.array([0, 1, 1], np.int32), np.ones(3, np.float32),
+                            np.array([0, -1, -1], np.int32), 0, 0)
+    return {k: v[None] for k, v in t.items()}
+
+
+def _first_token_two(p, q32, y1, y2, ka1, ka2, kd):
+    V = len(p)
+    t = _two_child_tree(y1, y2)
+    flat = np.full(V, 1.0 / V, np.float32)
+    prow = np.stack([np.asarray(p, np.float32), flat, flat])[None]
+    u_acc = np.array([[0.0, ka1 * 2.0 ** -24, ka2 * 2.0 ** -24]], np.float32)
+    u_draw = np.array([[kd * 2.0 ** -24, 0.0, 0.0]], np.float32)
+    r = oacc.verify_stochastic(t, prow, q32[None, None], u_acc, u_draw, S=1)
+    return int(r["commit_tokens"][0, 0]), int(r["accept_path"][0, 1])
+
+
+def enumerate_first_token_two(p, q_exact):
+    """Exact P(first committed token = v) with y1, y2 ~ q i.i.d. and all
+    uniforms; acceptance of each child is monotone in its own uniform and the
+    draw is monotone in u_draw (sampling contract)."""
+    V = len(p)
+    q32 = np.array([float(x) for x in q_exact], np.float32)
+    n = 1 << 24
+    tot = {v: Fraction(0) for v in range(V)}
+    support = [y for y in range(V) if q_exact[y] > 0]
+    for y1 in support:
+        for y2 in support:
+            w = Fraction(q_exact[y1]) * Fraction(q_exact[y2])
+            f1 = lambda ka: _first_token_two(p, q32, y1, y2, ka, n - 1, 0)[1] == 1   # noqa: E731
+            n1 = 0 if not f1(0) else _first_monotone_change(f1, 0, n - 1)
+            tot[y1] += w * Fraction(n1, n)
+            if n1 == n:
+                continue
+            w1 = w * Fraction(n - n1, n)
+            f2 = lambda ka: _first_token_two(p, q32, y1, y2, n1, ka, 0)[1] == 2     # noqa: E731
+            n2 = 0 if not f2(0) else _first_monotone_change(f2, 0, n - 1)
+            tot[y2] += w1 * Fraction(n2, n)
+            if n2 == n:
+                continue
+            w2 = w1 * Fraction(n - n2, n)
+            lo = 0
+            while lo < n:
+                v = _first_token_two(p, q32, y1, y2, n1, n2, lo)[0]
+                nxt = _first_monotone_change(lambda kd: _first_token_two(p, q32, y1, y2, n1, n2, kd)[0], lo, n - 1)
+                tot[v] += w2 * Fraction(nxt - lo, n)
+                lo = nxt
+    return tot
+
+
+_SIBLING_CASES = [
+    ([Fraction(1, 4), Fraction(1, 2), Fraction(1, 4)], [Fraction(1, 2), Fraction(1, 4), Fraction(1, 4)]),
+    ([Fraction(1, 16), Fraction(7, 16), Fraction(5, 16), Fraction(3, 16)],
+     [Fraction(1, 4), Fraction(1, 4), Fraction(1, 4), Fraction(1, 4)]),
+    ([Fraction(2, 5), Fraction(3, 5)], [Fraction(4, 5), Fraction(1, 5)]),
+    # residual above q on two tokens: skipping the normalisation would matter here
+    ([Fraction(5, 8), Fraction(3, 8), Fraction(0), Fraction(0)],
+     [Fraction(1, 8), Fraction(1, 8), Fraction(1, 4), Fraction(1, 2)]),
+]
+
+
+@pytest.mark.parametrize("p,q", _SIBLING_CASES)
+def test_two_siblings_iid_from_q_preserve_p(p, q):
+    """Within the contract's 2**-24 / 2**-40 quantisation (normalised residuals
+    are rounded to fp32), the committed token of the two-sibling walk is p."""
+    tot = enumerate_first_token_two([float(x) for x in p], q)
+    assert sum(tot.values()) == 1
+    for v in range(len(p)):
+        assert abs(float(tot[v]) - float(p[v])) < 1e-6
+
+
+def test_two_siblings_unnormalised_residual_is_caught(monkeypatch):
+    """Planting a mistake in the oracle -- the next sibling tested against the
+    raw residual instead of the normalised one -- moves the distribution."""
+    p, q = _SIBLING_CASES[3]
+    monkeypatch.setattr(oacc, "normalise", lambda r, S: np.asarray(r, np.float32))
+    tot = enumerate_first_token_two([float(x) for x in p], q)
+    assert max(abs(float(tot[v]) - float(p[v])) for v in range(len(p))) > 1e-3
+
+
 # --------------------------------------------------- stochastic invariants
 
 def test_stochastic_invariants_on_configs():
