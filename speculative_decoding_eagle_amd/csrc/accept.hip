@@ -5,18 +5,35 @@
 //
 // The walk of one request is sequential in depth, but every row it reads is
 // 4*V bytes, so a single wave per request cannot pull HBM bandwidth.  Each
-// request is served by a group of W workgroups, each owning a contiguous
-// slice of the vocabulary.  One cooperative launch keeps all groups
-// resident; a group synchronises through a per-request arrival counter
+// request is served by a group of W workgroups; workgroup c owns the
+// vocabulary slice [c*T*E, (c+1)*T*E) of every row and keeps that slice of
+// the current node's rows in registers (E floats per thread): the target row
+// and, for rejection sampling, the draft row are read from HBM once per
+// visited node, with every load of the slice in flight at once.
+//
+// A launch never holds more workgroups than the device keeps resident at
+// once (larger batches take several launches), so every group is resident
+// together; a group synchronises through a per-request arrival counter
 // (agent-scope release/acquire) whenever the walk needs a row-wide value:
 //   greedy     -- the argmax of the current node's target row;
-//   stochastic -- each rejection's fixed-point residual mass, and the draw.
-// Every workgroup of a group reduces the same W partials in the same order,
-// so all of them take the same decisions without a second barrier.
+//   stochastic -- each rejection's fixed-point residual mass (or, at a leaf,
+//                 the mass of t) and, if it is zero, the argmax of t.
+// Every workgroup reduces the same W partials in the same order, so all of
+// them take the same decisions.  The final inverse-CDF draw needs no extra
+// barrier: the workgroup whose slice holds the crossing finds the token in
+// its registers and writes the request's outputs itself.
+//
+// Rejection levels update t in registers as the pair (r, s): the current
+// residual r = max(t - q, 0) and the scale s = S * 2^-40 of the level's mass,
+// t' = fp32(double(r) / s).  These are the same operations, in the same
+// order, as the single-entry recursion used for the accept test, so both
+// agree bit for bit with each other and with the sampling contract.
+//
 // Partial slots form a ring of two: a workgroup only reaches barrier n+1
-// after every workgroup has consumed barrier n-1's partials.
-// Every spin is bounded; on timeout the kernel records an error flag and
-// carries on, so every wave always exits.
+// after every workgroup has consumed barrier n-1's partials.  Every spin is
+// bounded; on timeout the kernel records an error flag and carries on, so
+// every wave always exits.
+#include <atomic>
 #include <climits>
 #include <cmath>
 
@@ -28,13 +45,13 @@ namespace {
 constexpr int kAccThreads = 256;
 constexpr int kAccWaves = kAccThreads / kWave;
 constexpr int kMaxGroup = 64;          // workgroups per request
+constexpr int kMaxE = 64;              // floats per thread per row slice
 constexpr int kMaxLevels = 256;        // rejections at one node (children of one node)
-constexpr unsigned kSpinLimit = 1u << 26;
+constexpr unsigned kSpinLimit = 1u << 22;
 
 struct AcceptArgs {
   int B, N, S, V, R, mode, eos;
-  int W, chunk, b0;                    // group size, slice length, first request of this launch
-  bool vec;
+  int W, b0;                           // group size, first request of this launch
   const int *remaining;
   const int *tokens, *next_token, *next_sibling, *q_row;
   const float *target, *draft, *u_accept, *u_draw;
@@ -69,14 +86,17 @@ __device__ void group_barrier(unsigned *ctr, unsigned &gen, int W, unsigned *err
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned target = gen * static_cast<unsigned>(W);
+    // poll with relaxed loads (an acquire per poll would invalidate the L2
+    // under every other workgroup's streaming), then acquire once
     unsigned spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
         __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -140,6 +160,14 @@ __device__ unsigned long long block_exclusive_scan(unsigned long long x, unsigne
 
 // ------------------------------------------------------- sampling arithmetic
 
+__device__ __forceinline__ unsigned long long mass(float w) {
+  return static_cast<unsigned long long>(floor(static_cast<double>(w) * 0x1p40));
+}
+
+__device__ __forceinline__ float rescale(float r, double s) {
+  return static_cast<float>(static_cast<double>(r) / s);
+}
+
 // t at one vocabulary entry after `lev` rejections at the current node:
 // t <- fp32(double(max(t - q, 0)) / (double(S_j) * 2^-40)) for every level j
 // whose residual mass S_j was non-zero.
@@ -148,31 +176,135 @@ __device__ __forceinline__ float t_at(float p, float q, const unsigned long long
   for (int j = 0; j < lev; ++j) {
     const unsigned long long Sj = Slev[j];
     if (Sj == 0) continue;
-    const float r = fmaxf(t - q, 0.0f);
-    t = static_cast<float>(static_cast<double>(r) / (static_cast<double>(Sj) * 0x1p-40));
+    t = rescale(fmaxf(t - q, 0.0f), static_cast<double>(Sj) * 0x1p-40);
   }
   return t;
 }
 
-enum MassKind { kResidual = 0, kT = 1 };
+// ---------------------------------------------------------------- row slices
+//
+// Element x of float4 group j of thread tid is vocabulary entry
+// lo + 4*(j*T + tid) + x: each load instruction of a wave covers 1 KB of
+// the row, and a thread's entries ascend with (j, x).
 
-__device__ __forceinline__ unsigned long long mass_of(float p, float q, const unsigned long long *Slev,
-                                                      int lev, int kind) {
-  const float t = t_at(p, q, Slev, lev);
-  const float w = kind == kResidual ? fmaxf(t - q, 0.0f) : t;
-  return static_cast<unsigned long long>(floor(static_cast<double>(w) * 0x1p40));
+template <int E, bool VEC>
+__device__ __forceinline__ void load_slice(const float *__restrict__ row, int lo, int hi, float (&v)[E], float fill) {
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+    float4 x[E / 4];
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+      const int e = lo + 4 * (j * kAccThreads + tid);
+      x[j] = *reinterpret_cast<const float4 *>(row + (e < hi ? e : lo));
+    }
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+      const bool ok = lo + 4 * (j * kAccThreads + tid) < hi;
+      v[4 * j + 0] = ok ? x[j].x : fill;
+      v[4 * j + 1] = ok ? x[j].y : fill;
+      v[4 * j + 2] = ok ? x[j].z : fill;
+      v[4 * j + 3] = ok ? x[j].w : fill;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = lo + 4 * (j * kAccThreads + tid) + k;
+        const float y = row[e < hi ? e : lo];
+        v[4 * j + k] = e < hi ? y : fill;
+      }
+  }
+}
+
+template <int E>
+__device__ __forceinline__ int slice_index(int lo, int n) {
+  return lo + 4 * ((n >> 2) * kAccThreads + static_cast<int>(threadIdx.x)) + (n & 3);
+}
+
+// Best (value, index) of the thread's entries.  Entries ascend with n and the
+// out-of-slice ones come last holding -inf, so keeping the first maximum in
+// n order is the (value desc, index asc) rule; a thread with no entry in the
+// slice reports (-inf, INT_MAX).
+template <int E>
+__device__ __forceinline__ void thread_best(const float (&v)[E], int lo, int hi, float &bv, int &bi) {
+  bv = v[0];
+  int bn = 0;
+#pragma unroll
+  for (int n = 1; n < E; ++n)
+    if (v[n] > bv) {
+      bv = v[n];
+      bn = n;
+    }
+  bi = slice_index<E>(lo, bn);
+  if (bi >= hi) bi = INT_MAX;
 }
 
 // ------------------------------------------------------------------- kernel
 
+__device__ void write_outputs(const AcceptArgs &a, int b, const int *s_path, const int *s_out, int path_len,
+                              int n_out) {
+  for (int j = threadIdx.x; j <= a.S; j += kAccThreads) {
+    a.accept_path[static_cast<int64_t>(b) * (a.S + 1) + j] = j < path_len ? s_path[j] : -1;
+    a.commit_tokens[static_cast<int64_t>(b) * (a.S + 1) + j] = j < n_out ? s_out[j] : -1;
+  }
+  if (threadIdx.x == 0) {
+    a.accept_len[b] = path_len - 1;
+    a.commit_len[b] = n_out;
+    a.next_root[b] = n_out > 0 ? s_out[n_out - 1] : -1;
+  }
+}
+
+// Keeps the compiler from interleaving the fp64 divisions of many entries
+// (each holds about ten registers while in flight).
+__device__ __forceinline__ void one_at_a_time() { __builtin_amdgcn_sched_barrier(0); }
+
+// The group's partials, read by one wave at once: lane x holds workgroup x's.
+__device__ __forceinline__ unsigned long long lane_part(unsigned long long *slot, int W, unsigned long long fill) {
+  const int x = lane_id();
+  return x < W ? load_part(slot + x) : fill;
+}
+
+__device__ __forceinline__ int group_argmax(unsigned long long *slot, int W) {
+  const unsigned long long pk = lane_part(slot, W, pack_best(-INFINITY, INT_MAX));
+  float v = unpack_v(pk);
+  int i = unpack_i(pk);
+  wave_best(v, i);
+  return i;
+}
+
+__device__ __forceinline__ unsigned long long group_total(unsigned long long *slot, int W) {
+  return wave_sum_u64(lane_part(slot, W, 0ull));
+}
+
+// The workgroup whose slice holds the crossing T of the running mass, and the
+// mass of the slices before it.
+__device__ __forceinline__ int group_owner(unsigned long long *slot, int W, unsigned long long T,
+                                           unsigned long long &base) {
+  const unsigned long long px = lane_part(slot, W, 0ull);
+  unsigned long long inc = px;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const unsigned long long y = __shfl_up(inc, off, kWave);
+    if (lane_id() >= off) inc += y;
+  }
+  const unsigned long long hit = __ballot(lane_id() < W && T < inc);
+  const int owner = hit ? __ffsll(static_cast<long long>(hit)) - 1 : W - 1;
+  base = __shfl(inc - px, owner, kWave);
+  return owner;
+}
+
+template <int E, bool STOCH, bool VEC>
 __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
   const int b = a.b0 + static_cast<int>(blockIdx.x) / a.W;
   const int c = static_cast<int>(blockIdx.x) % a.W;
   if (b >= a.B) return;
   const int tid = threadIdx.x;
   const int V = a.V;
-  const int lo = min(V, c * a.chunk);
-  const int hi = min(V, lo + a.chunk);
+  const int N = a.N;
+  constexpr int kChunk = kAccThreads * E;
+  const int lo = min(V, c * kChunk);
+  const int hi = min(V, lo + kChunk);
   unsigned *ctr = a.ctr + b;
   unsigned long long *ring = a.part + static_cast<int64_t>(b) * 2 * kMaxGroup;
   unsigned gen = 0;
@@ -180,50 +312,63 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
   __shared__ int s_path[66];
   __shared__ int s_out[66];
   __shared__ unsigned long long s_Slev[kMaxLevels];
+  __shared__ int s_found;
+  // the request's tree, staged once
+  __shared__ int s_tok[256], s_nxt[256], s_sib[256], s_qr[256];
+  __shared__ float s_ua[256];
+  // children of the current node and their p[y], q[y]
+  __shared__ int s_kid[256];
+  __shared__ float s_py[256], s_qy[256];
+  __shared__ int s_nk;
 
-  const int *tok = a.tokens + static_cast<int64_t>(b) * a.N;
-  const int *nxt = a.next_token + static_cast<int64_t>(b) * a.N;
-  const int *sib = a.next_sibling + static_cast<int64_t>(b) * a.N;
+  for (int i = tid; i < N; i += kAccThreads) {
+    const int64_t g = static_cast<int64_t>(b) * N + i;
+    s_tok[i] = a.tokens[g];
+    s_nxt[i] = a.next_token[g];
+    s_sib[i] = a.next_sibling[g];
+    if constexpr (STOCH) {
+      s_qr[i] = a.q_row[g];
+      s_ua[i] = a.u_accept[g];
+    }
+  }
+  if (tid == 0) s_path[0] = 0;
   int rem = a.remaining ? a.remaining[b] : INT_MAX;
   if (rem < 0) rem = 0;
-  int path_len = 1, n_out = 0;
-  if (tid == 0) s_path[0] = 0;
+  __syncthreads();
 
+  // publishes this workgroup's partial, waits for the group, returns the slot
+  auto exchange = [&](unsigned long long value) -> unsigned long long * {
+    unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
+    if (tid == 0) store_part(slot + c, value);
+    group_barrier(ctr, gen, a.W, a.err);
+    return slot;
+  };
+  auto group_best = [&](float v, int i) -> int {
+    block_best(v, i);
+    return group_argmax(exchange(pack_best(v, i)), a.W);
+  };
+
+  int path_len = 1, n_out = 0;
+  bool writer = c == 0;
   int u = 0;
   const int max_out = a.S + 1;
   while (rem > 0 && n_out < max_out) {
-    const float *prow = a.target + (static_cast<int64_t>(b) * a.N + u) * V;
-    if (a.mode == SDV_ACCEPT_GREEDY) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-      if (a.vec) {
-        for (int e = lo + 4 * tid; e < hi; e += 4 * kAccThreads) {
-          const float4 x = *reinterpret_cast<const float4 *>(prow + e);
-          if (better(x.x, e, bv, bi)) { bv = x.x; bi = e; }
-          if (better(x.y, e + 1, bv, bi)) { bv = x.y; bi = e + 1; }
-          if (better(x.z, e + 2, bv, bi)) { bv = x.z; bi = e + 2; }
-          if (better(x.w, e + 3, bv, bi)) { bv = x.w; bi = e + 3; }
-        }
-      } else {
-        for (int e = lo + tid; e < hi; e += kAccThreads)
-          if (better(prow[e], e, bv, bi)) { bv = prow[e]; bi = e; }
-      }
-      block_best(bv, bi);
-      unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
-      if (tid == 0) store_part(slot + c, pack_best(bv, bi));
-      group_barrier(ctr, gen, a.W, a.err);
-      float gv = -INFINITY;
-      int gi = INT_MAX;
-      for (int x = 0; x < a.W; ++x) {
-        const unsigned long long pk = load_part(slot + x);
-        if (better(unpack_v(pk), unpack_i(pk), gv, gi)) { gv = unpack_v(pk); gi = unpack_i(pk); }
-      }
-      const int t = gi;
+    const float *prow = a.target + (static_cast<int64_t>(b) * N + u) * V;
+    if constexpr (!STOCH) {
+      float p[E];
+      load_slice<E, VEC>(prow, lo, hi, p, -INFINITY);
+      float bv;
+      int bi;
+      thread_best<E>(p, lo, hi, bv, bi);
+      const int t = group_best(bv, bi);
       int match = -1;
-      int cc = nxt[u];
-      for (int hops = 0; cc > 0 && cc < a.N && hops < a.N; ++hops) {
-        if (tok[cc] == t) { match = cc; break; }
-        cc = sib[cc];
+      int cc = s_nxt[u];
+      for (int hops = 0; cc > 0 && cc < N && hops < N; ++hops) {
+        if (s_tok[cc] == t) {
+          match = cc;
+          break;
+        }
+        cc = s_sib[cc];
       }
       if (tid == 0) s_out[n_out] = t;
       ++n_out;
@@ -234,177 +379,185 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
       if (t == a.eos || n_out == rem || match < 0) break;
       u = match;
       continue;
-    }
+    } else {
+      // ---------------- stochastic: t is held as (r, s); level 0 is t = p
+      const int qr = s_qr[u];
+      const bool has_kids = s_nxt[u] > 0 && s_nxt[u] < N && qr >= 0 && qr < a.R;
+      const float *qrow = has_kids ? a.draft + (static_cast<int64_t>(b) * a.R + qr) * V : prow;
+      if (tid == 0) {
+        int nk = 0;
+        int cc = has_kids ? s_nxt[u] : -1;
+        for (int hops = 0; cc > 0 && cc < N && hops < N && nk < kMaxLevels; ++hops) {
+          s_kid[nk++] = cc;
+          cc = s_sib[cc];
+        }
+        s_nk = nk;
+      }
+      __syncthreads();
+      const int nk = s_nk;
+      for (int i = tid; i < nk; i += kAccThreads) {
+        int y = s_tok[s_kid[i]];
+        y = y < 0 ? 0 : (y >= V ? V - 1 : y);
+        s_py[i] = prow[y];
+        s_qy[i] = qrow[y];
+      }
+      float r[E], q[E];
+      load_slice<E, VEC>(prow, lo, hi, r, 0.0f);
+      if (has_kids) {
+        load_slice<E, VEC>(qrow, lo, hi, q, 0.0f);
+      } else {
+#pragma unroll
+        for (int n = 0; n < E; ++n) q[n] = 0.0f;
+      }
+      __syncthreads();
+      bool scaled = false;           // t = r / s (else t = r)
+      double s = 1.0;
+      int nlev = 0;
+      int accepted = -1;
+      unsigned long long last_total = 0;
+      unsigned long long *last_slot = nullptr;
+      for (int i = 0; i < nk; ++i) {
+        const int cc = s_kid[i];
+        const float qy = s_qy[i];
+        const float ty = t_at(s_py[i], qy, s_Slev, nlev);
+        if (static_cast<double>(s_ua[cc]) * static_cast<double>(qy) < static_cast<double>(ty)) {
+          accepted = cc;
+          break;
+        }
+        // rejection: r <- max(t - q, 0) and its mass
+        unsigned long long m = 0;
+#pragma unroll
+        for (int n = 0; n < E; ++n) {
+          const float t = scaled ? rescale(r[n], s) : r[n];
+          r[n] = fmaxf(t - q[n], 0.0f);
+          m += mass(r[n]);
+          one_at_a_time();
+        }
+        m = block_sum(m);
+        unsigned long long *slot = exchange(m);
+        const unsigned long long tot = group_total(slot, a.W);
+        if (tid == 0) s_Slev[nlev] = tot;
+        __syncthreads();
+        ++nlev;
+        last_total = tot;
+        last_slot = slot;
+        if (tot > 0) {
+          scaled = true;
+          s = static_cast<double>(tot) * 0x1p-40;
+        } else {
+          // A level of zero mass leaves t as it was, but r already holds its
+          // residual: rebuild t from the row through the levels so far (rare).
+          load_slice<E, VEC>(prow, lo, hi, r, 0.0f);
+#pragma unroll
+          for (int n = 0; n < E; ++n) {
+            r[n] = t_at(r[n], q[n], s_Slev, nlev);
+            one_at_a_time();
+          }
+          scaled = false;
+        }
+      }
+      if (accepted >= 0) {
+        const int y = s_tok[accepted];
+        if (tid == 0) {
+          s_out[n_out] = y;
+          s_path[path_len] = accepted;
+        }
+        ++n_out;
+        ++path_len;
+        if (y == a.eos || n_out == rem) break;
+        u = accepted;
+        __syncthreads();             // s_kid / s_py / s_qy are rewritten for the next node
+        continue;
+      }
 
-    // ---------------- stochastic
-    int qr = a.q_row[static_cast<int64_t>(b) * a.N + u];
-    const bool has_kids = nxt[u] > 0 && nxt[u] < a.N && qr >= 0 && qr < a.R;
-    const float *qrow = has_kids ? a.draft + (static_cast<int64_t>(b) * a.R + qr) * V : prow;
-    int nlev = 0;
-    int accepted = -1;
-    unsigned long long last_total = 0;
-    bool rejected_any = false;
-    int cc = has_kids ? nxt[u] : -1;
-    for (int hops = 0; cc > 0 && cc < a.N && hops < a.N && nlev < kMaxLevels; ++hops) {
-      int y = tok[cc];
-      y = y < 0 ? 0 : (y >= V ? V - 1 : y);
-      const float qy = qrow[y];
-      const float ty = t_at(prow[y], qy, s_Slev, nlev);
-      const float ua = a.u_accept[static_cast<int64_t>(b) * a.N + cc];
-      if (static_cast<double>(ua) * static_cast<double>(qy) < static_cast<double>(ty)) {
-        accepted = cc;
+      // ---- draw the correction (all children rejected) or the bonus (leaf):
+      // from the last residual if its mass is non-zero, else from t
+      const bool from_residual = nlev > 0 && last_total > 0;
+      unsigned long long *mslot;
+      unsigned long long total;
+      if (from_residual) {
+        mslot = last_slot;
+        total = last_total;
+      } else {
+        unsigned long long m = 0;
+#pragma unroll
+        for (int n = 0; n < E; ++n) {
+          m += mass(scaled ? rescale(r[n], s) : r[n]);
+          one_at_a_time();
+        }
+        m = block_sum(m);
+        mslot = exchange(m);
+        total = group_total(mslot, a.W);
+      }
+
+      if (total == 0) {
+        // degenerate: argmax of t, lowest id
+#pragma unroll
+        for (int n = 0; n < E; ++n) {
+          r[n] = scaled ? rescale(r[n], s) : r[n];
+          one_at_a_time();
+        }
+        float bv;
+        int bi;
+        thread_best<E>(r, lo, hi, bv, bi);
+        const int token = group_best(bv, bi);
+        if (tid == 0) s_out[n_out] = token;
+        ++n_out;
         break;
       }
-      // rejection: residual mass of this slice at level nlev
-      unsigned long long m = 0;
-      if (a.vec) {
-        for (int e = lo + 4 * tid; e < hi; e += 4 * kAccThreads) {
-          const float4 p4 = *reinterpret_cast<const float4 *>(prow + e);
-          const float4 q4 = *reinterpret_cast<const float4 *>(qrow + e);
-          m += mass_of(p4.x, q4.x, s_Slev, nlev, kResidual);
-          m += mass_of(p4.y, q4.y, s_Slev, nlev, kResidual);
-          m += mass_of(p4.z, q4.z, s_Slev, nlev, kResidual);
-          m += mass_of(p4.w, q4.w, s_Slev, nlev, kResidual);
-        }
-      } else {
-        for (int e = lo + tid; e < hi; e += kAccThreads) m += mass_of(prow[e], qrow[e], s_Slev, nlev, kResidual);
-      }
-      m = block_sum(m);
-      unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
-      if (tid == 0) store_part(slot + c, m);
-      group_barrier(ctr, gen, a.W, a.err);
-      unsigned long long tot = 0;
-      for (int x = 0; x < a.W; ++x) tot += load_part(slot + x);
-      if (tid == 0) s_Slev[nlev] = tot;
-      __syncthreads();
-      ++nlev;
-      last_total = tot;
-      rejected_any = true;
-      cc = sib[cc];
-    }
-    if (accepted >= 0) {
-      int y = tok[accepted];
-      if (tid == 0) {
-        s_out[n_out] = y;
-        s_path[path_len] = accepted;
-      }
-      ++n_out;
-      ++path_len;
-      if (y == a.eos || n_out == rem) break;
-      u = accepted;
-      continue;
-    }
 
-    // ---- draw the correction (all children rejected) or the bonus (leaf)
-    int kind, lev;
-    unsigned long long total;
-    unsigned long long *mslot;   // slot holding the slice masses of the draw
-    if (rejected_any && last_total > 0) {
-      kind = kResidual;
-      lev = nlev - 1;
-      total = last_total;
-      mslot = ring + ((gen - 1) & 1) * kMaxGroup;
-    } else {
-      kind = kT;
-      lev = nlev;
-      unsigned long long m = 0;
-      for (int e = lo + tid; e < hi; e += kAccThreads) m += mass_of(prow[e], qrow[e], s_Slev, lev, kT);
-      m = block_sum(m);
-      mslot = ring + (gen & 1) * kMaxGroup;
-      if (tid == 0) store_part(mslot + c, m);
-      group_barrier(ctr, gen, a.W, a.err);
-      total = 0;
-      for (int x = 0; x < a.W; ++x) total += load_part(mslot + x);
-    }
-
-    int token;
-    if (total == 0) {
-      // degenerate: argmax of t, lowest id
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-      for (int e = lo + tid; e < hi; e += kAccThreads) {
-        const float t = t_at(prow[e], qrow[e], s_Slev, lev);
-        if (better(t, e, bv, bi)) { bv = t; bi = e; }
-      }
-      block_best(bv, bi);
-      unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
-      if (tid == 0) store_part(slot + c, pack_best(bv, bi));
-      group_barrier(ctr, gen, a.W, a.err);
-      float gv = -INFINITY;
-      int gi = INT_MAX;
-      for (int x = 0; x < a.W; ++x) {
-        const unsigned long long pk = load_part(slot + x);
-        if (better(unpack_v(pk), unpack_i(pk), gv, gi)) { gv = unpack_v(pk); gi = unpack_i(pk); }
-      }
-      token = gi;
-    } else {
-      const float ud = a.u_draw[static_cast<int64_t>(b) * a.N + u];
+      const float ud = a.u_draw[static_cast<int64_t>(b) * N + u];
       const unsigned long long kk = static_cast<unsigned long long>(ud * 16777216.0f);
       const unsigned long long T = kk * (total >> 24) + ((kk * (total & 0xffffffull)) >> 24);
-      // the slice holding the crossing
-      unsigned long long base = 0;
-      int owner = a.W - 1;
-      for (int x = 0; x < a.W; ++x) {
-        const unsigned long long px = load_part(mslot + x);
-        if (T < base + px) { owner = x; break; }
-        base += px;
+      unsigned long long base;
+      const int owner = group_owner(mslot, a.W, T, base);
+      if (c != owner) {
+        writer = false;
+        break;
       }
-      unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
-      if (c == owner) {
-        // scan the slice in tiles of kE entries per thread
-        constexpr int kE = 8;
-        __shared__ int s_found;
-        if (tid == 0) s_found = INT_MAX;
-        __syncthreads();
-        for (int t0 = lo; t0 < hi; t0 += kE * kAccThreads) {
-          const int my0 = t0 + tid * kE;
-          unsigned long long loc[kE];
-          unsigned long long sum = 0;
+      writer = true;
+      // masses of the drawn distribution, scanned in vocabulary order: group j
+      // of every thread, then the next group
+      if (tid == 0) s_found = INT_MAX;
+      __syncthreads();
 #pragma unroll
-          for (int j = 0; j < kE; ++j) {
-            const int e = my0 + j;
-            loc[j] = e < hi ? mass_of(prow[e], qrow[e], s_Slev, lev, kind) : 0ull;
-            sum += loc[j];
-          }
-          unsigned long long tile_total;
-          unsigned long long before = base + block_exclusive_scan(sum, tile_total);
-          if (T < before + sum) {
-            unsigned long long run = before;
+      for (int j = 0; j < E / 4; ++j) {
+        unsigned long long w4[4];
+        unsigned long long sum = 0;
 #pragma unroll
-            for (int j = 0; j < kE; ++j) {
-              run += loc[j];
-              if (T < run) {
-                atomicMin(&s_found, my0 + j);
-                break;
-              }
+        for (int k = 0; k < 4; ++k) {
+          const int n = 4 * j + k;
+          const float w = from_residual ? r[n] : (scaled ? rescale(r[n], s) : r[n]);
+          w4[k] = mass(w);
+          sum += w4[k];
+          one_at_a_time();
+        }
+        unsigned long long grp_total;
+        const unsigned long long before = base + block_exclusive_scan(sum, grp_total);
+        if (T >= before && T < before + sum) {
+          unsigned long long run = before;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            run += w4[k];
+            if (T < run) {
+              s_found = slice_index<E>(lo, 4 * j + k);
+              break;
             }
           }
-          base += tile_total;
-          __syncthreads();
-          if (s_found != INT_MAX) break;
         }
-        if (tid == 0) store_part(slot + c, static_cast<unsigned long long>(s_found == INT_MAX ? hi - 1 : s_found));
+        base += grp_total;
+        __syncthreads();
+        if (s_found != INT_MAX) break;
       }
-      group_barrier(ctr, gen, a.W, a.err);
-      token = static_cast<int>(load_part(slot + owner));
+      const int token = s_found == INT_MAX ? hi - 1 : s_found;
+      if (tid == 0) s_out[n_out] = token;
+      ++n_out;
+      break;
     }
-    if (tid == 0) s_out[n_out] = token;
-    ++n_out;
-    break;
   }
 
   __syncthreads();
-  if (c == 0) {
-    for (int j = tid; j <= a.S; j += kAccThreads) {
-      a.accept_path[static_cast<int64_t>(b) * (a.S + 1) + j] = j < path_len ? s_path[j] : -1;
-      a.commit_tokens[static_cast<int64_t>(b) * (a.S + 1) + j] = j < n_out ? s_out[j] : -1;
-    }
-    if (tid == 0) {
-      a.accept_len[b] = path_len - 1;
-      a.commit_len[b] = n_out;
-      a.next_root[b] = n_out > 0 ? s_out[n_out - 1] : -1;
-    }
-  }
+  if (writer) write_outputs(a, b, s_path, s_out, path_len, n_out);
 }
 
 __global__ void zero_u32_kernel(unsigned *p, int n) {
@@ -413,27 +566,69 @@ __global__ void zero_u32_kernel(unsigned *p, int n) {
 }
 
 struct AcceptPlan {
-  int W, chunk, per_launch;
+  int W, E, per_launch;
 };
 
-int32_t plan_accept(const sdv_accept_shape &sh, AcceptPlan &p) {
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel, kAccThreads, 0);
+template <int E>
+const void *kernel_of(bool stoch, bool vec) {
+  if (stoch)
+    return vec ? reinterpret_cast<const void *>(accept_kernel<E, true, true>)
+               : reinterpret_cast<const void *>(accept_kernel<E, true, false>);
+  return vec ? reinterpret_cast<const void *>(accept_kernel<E, false, true>)
+             : reinterpret_cast<const void *>(accept_kernel<E, false, false>);
+}
+
+const void *accept_kernel_for(int E, bool stoch, bool vec) {
+  switch (E) {
+    case 4: return kernel_of<4>(stoch, vec);
+    case 8: return kernel_of<8>(stoch, vec);
+    case 16: return kernel_of<16>(stoch, vec);
+    case 32: return kernel_of<32>(stoch, vec);
+    default: return kernel_of<64>(stoch, vec);
+  }
+}
+
+// Resident workgroups per CU of one kernel variant, queried once per device.
+int32_t blocks_per_cu(int E, bool stoch, bool vec, int &per_cu) {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cache[kDevices][5][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "verify_accept: no device");
+  int ei = 0;
+  while ((4 << ei) < E) ++ei;
+  std::atomic<int> *slot = dev < kDevices ? &cache[dev][ei][stoch][vec] : nullptr;
+  per_cu = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (per_cu > 0) return SDV_OK;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel_for(E, stoch, vec), kAccThreads, 0);
   if (e != hipSuccess || per_cu <= 0) return fail(SDV_E_HIP, "verify_accept: occupancy query failed");
-  const int64_t resident = static_cast<int64_t>(per_cu) * num_cus();
-  int64_t W = (2LL * num_cus()) / (sh.B > 0 ? sh.B : 1);
-  const int64_t by_len = (sh.V + 1023) / 1024;
-  if (W > by_len) W = by_len;
+  if (slot) slot->store(per_cu, std::memory_order_relaxed);
+  return SDV_OK;
+}
+
+// Group size: enough workgroups to cover 2 per CU over the batch, no more
+// than the vocabulary needs at 4 floats per thread, and at least what it
+// needs at kMaxE floats per thread; the slice width E then follows.
+int32_t plan_accept(const sdv_accept_shape &sh, bool vec, AcceptPlan &p) {
+  const int64_t T = kAccThreads;
+  int64_t W = (2LL * num_cus() + sh.B - 1) / (sh.B > 0 ? sh.B : 1);
+  const int64_t w_small = (sh.V + T * 4 - 1) / (T * 4);
+  const int64_t w_big = (sh.V + T * kMaxE - 1) / (T * kMaxE);
+  if (W > w_small) W = w_small;
   if (W > kMaxGroup) W = kMaxGroup;
-  if (W > resident) W = resident;
+  if (W < w_big) W = w_big;
   if (W < 1) W = 1;
-  int64_t chunk = (sh.V + W - 1) / W;
-  chunk = (chunk + 3) / 4 * 4;
-  p.W = static_cast<int>(W);
-  p.chunk = static_cast<int>(chunk);
+  int E = 4;
+  while (E < kMaxE && T * E * W < sh.V) E <<= 1;
+  int per_cu = 0;
+  const int32_t rc = blocks_per_cu(E, sh.mode == SDV_ACCEPT_STOCHASTIC, vec, per_cu);
+  if (rc != SDV_OK) return rc;
+  const int64_t resident = static_cast<int64_t>(per_cu) * num_cus();
+  if (W > resident) return fail(SDV_E_UNSUPPORTED, "verify_accept: group of %lld workgroups cannot be resident",
+                                static_cast<long long>(W));
   int64_t per = resident / W;
-  if (per < 1) per = 1;
   if (per > sh.B) per = sh.B;
+  p.W = static_cast<int>(W);
+  p.E = E;
   p.per_launch = static_cast<int>(per);
   return SDV_OK;
 }
@@ -464,8 +659,8 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
               "verify_accept: need B >= 0, N >= 1, S >= 0, V >= 1");
   SDV_REQUIRE(sh.mode == SDV_ACCEPT_GREEDY || sh.mode == SDV_ACCEPT_STOCHASTIC, SDV_E_SHAPE,
               "verify_accept: unknown mode %d", sh.mode);
-  SDV_REQUIRE(sh.N <= 256 && sh.S + 1 <= 64 && sh.V < INT_MAX - 4096, SDV_E_UNSUPPORTED,
-              "verify_accept: N <= 256, S+1 <= 64 and V < 2^31-4096 required");
+  SDV_REQUIRE(sh.N <= 256 && sh.S + 1 <= 64 && sh.V <= kMaxGroup * kAccThreads * kMaxE, SDV_E_UNSUPPORTED,
+              "verify_accept: N <= 256, S+1 <= 64 and V <= %d required", kMaxGroup * kAccThreads * kMaxE);
   SDV_REQUIRE(sh.mode == SDV_ACCEPT_GREEDY || sh.R >= 1, SDV_E_SHAPE, "verify_accept: R >= 1 needed");
   if (sh.B == 0) return SDV_OK;
   SDV_REQUIRE(tokens && next_token && next_sibling && target && accept_len && accept_path &&
@@ -476,8 +671,10 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
                 "verify_accept: stochastic mode needs q_row, draft_probs and uniforms");
   const size_t need = sdv_verify_accept_workspace_size(sh);
   SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "verify_accept: workspace of %zu bytes needed", need);
+  const bool vec = (sh.V % 4 == 0) && (reinterpret_cast<uintptr_t>(target) % 16 == 0) &&
+                   (!draft_probs || reinterpret_cast<uintptr_t>(draft_probs) % 16 == 0);
   AcceptPlan p;
-  int32_t rc = plan_accept(sh, p);
+  int32_t rc = plan_accept(sh, vec, p);
   if (rc != SDV_OK) return rc;
 
   Carver cv(ws);
@@ -491,23 +688,20 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
 
   AcceptArgs a;
   a.B = sh.B; a.N = sh.N; a.S = sh.S; a.V = sh.V; a.R = sh.R; a.mode = sh.mode; a.eos = eos_id;
-  a.W = p.W; a.chunk = p.chunk;
-  a.vec = (sh.V % 4 == 0) && (reinterpret_cast<uintptr_t>(target) % 16 == 0) &&
-          (!draft_probs || reinterpret_cast<uintptr_t>(draft_probs) % 16 == 0);
+  a.W = p.W;
   a.remaining = remaining;
   a.tokens = tokens; a.next_token = next_token; a.next_sibling = next_sibling; a.q_row = q_row;
   a.target = target; a.draft = draft_probs; a.u_accept = u_accept; a.u_draw = u_draw;
   a.accept_len = accept_len; a.accept_path = accept_path; a.commit_tokens = commit_tokens;
   a.commit_len = commit_len; a.next_root = next_root;
   a.ctr = ctr; a.part = part; a.err = ctr + sh.B;
+  const void *fn = accept_kernel_for(p.E, sh.mode == SDV_ACCEPT_STOCHASTIC, vec);
   for (int b0 = 0; b0 < sh.B; b0 += p.per_launch) {
     a.b0 = b0;
     const int nb = (sh.B - b0 < p.per_launch ? sh.B - b0 : p.per_launch);
     void *args[] = {&a};
-    hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(accept_kernel),
-                                              dim3(static_cast<unsigned>(nb * p.W)), dim3(kAccThreads),
-                                              args, 0, st);
-    if (e != hipSuccess) return fail(SDV_E_HIP, "verify_accept: cooperative launch: %s", hipGetErrorString(e));
+    hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(nb * p.W)), dim3(kAccThreads), args, 0, st);
+    if (e != hipSuccess) return fail(SDV_E_HIP, "verify_accept: launch: %s", hipGetErrorString(e));
   }
   return SDV_OK;
 }
