@@ -13,15 +13,18 @@
 //
 // A launch never holds more workgroups than the device keeps resident at
 // once (larger batches take several launches), so every group is resident
-// together; a group synchronises through a per-request arrival counter
-// (agent-scope release/acquire) whenever the walk needs a row-wide value:
+// together.  A group exchanges a row-wide value whenever the walk needs one:
 //   greedy     -- the argmax of the current node's target row;
 //   stochastic -- each rejection's fixed-point residual mass (or, at a leaf,
 //                 the mass of t) and, if it is zero, the argmax of t.
-// Every workgroup reduces the same W partials in the same order, so all of
-// them take the same decisions.  The final inverse-CDF draw needs no extra
-// barrier: the workgroup whose slice holds the crossing finds the token in
-// its registers and writes the request's outputs itself.
+// Workgroup c publishes its partial as one 64-bit word that also carries the
+// exchange's sequence tag, with a single agent-scope atomic store; readers
+// poll the W words (lane x of each wave reads workgroup x's) until every tag
+// matches.  Flag and value share one location, so no fence or counter is
+// involved.  Every workgroup reduces the same W partials in the same order,
+// so all of them take the same decisions.  The final inverse-CDF draw needs
+// no extra exchange: the workgroup whose slice holds the crossing finds the
+// token in its registers and writes the request's outputs itself.
 //
 // Rejection levels update t in registers as the pair (r, s): the current
 // residual r = max(t - q, 0) and the scale s = S * 2^-40 of the level's mass,
@@ -29,10 +32,10 @@
 // order, as the single-entry recursion used for the accept test, so both
 // agree bit for bit with each other and with the sampling contract.
 //
-// Partial slots form a ring of two: a workgroup only reaches barrier n+1
-// after every workgroup has consumed barrier n-1's partials.  Every spin is
-// bounded; on timeout the kernel records an error flag and carries on, so
-// every wave always exits.
+// Partial words form a ring of two per request: a workgroup only publishes
+// exchange n+2 after every workgroup has published exchange n+1, which each
+// does only after reading exchange n.  Every poll is bounded; on timeout the
+// kernel records an error flag and carries on, so every wave always exits.
 #include <atomic>
 #include <climits>
 #include <cmath>
@@ -56,19 +59,39 @@ struct AcceptArgs {
   const int *tokens, *next_token, *next_sibling, *q_row;
   const float *target, *draft, *u_accept, *u_draw;
   int *accept_len, *accept_path, *commit_tokens, *commit_len, *next_root;
-  unsigned *ctr;                       // [B] arrival counters (zeroed before the launch)
-  unsigned long long *part;            // [B][2][kMaxGroup]
+  unsigned long long *part;            // [B][2][kMaxGroup] tagged partials (zeroed before the launch)
   unsigned *err;                       // [1] timeout flag
 };
 
-__device__ __forceinline__ unsigned long long pack_best(float v, int i) {
-  return (static_cast<unsigned long long>(__float_as_uint(v)) << 32) | static_cast<unsigned>(i);
+// Tagged partial words.
+//   argmax: value bits [63:32], tag [31:20] (12 bits), index [19:0]
+//           (kNoIndex: the slice is empty);
+//   mass:   tag [63:55] (9 bits), value [54:0] (a slice holds at most 2^14
+//           entries of mass at most 2^40 + 2^17).
+constexpr unsigned kNoIndex = 0xFFFFFu;
+
+__device__ __forceinline__ unsigned long long pack_best(float v, int i, unsigned tag) {
+  const unsigned idx = i == INT_MAX ? kNoIndex : static_cast<unsigned>(i);
+  return (static_cast<unsigned long long>(__float_as_uint(v)) << 32) | ((tag & 0xFFFu) << 20) | idx;
 }
-__device__ __forceinline__ float unpack_v(unsigned long long x) {
-  return __uint_as_float(static_cast<unsigned>(x >> 32));
+__device__ __forceinline__ bool best_tag_is(unsigned long long w, unsigned tag) {
+  return ((w >> 20) & 0xFFFu) == (tag & 0xFFFu);
 }
-__device__ __forceinline__ int unpack_i(unsigned long long x) {
-  return static_cast<int>(static_cast<unsigned>(x & 0xffffffffu));
+__device__ __forceinline__ float unpack_v(unsigned long long w) {
+  return __uint_as_float(static_cast<unsigned>(w >> 32));
+}
+__device__ __forceinline__ int unpack_i(unsigned long long w) {
+  const unsigned idx = static_cast<unsigned>(w) & kNoIndex;
+  return idx == kNoIndex ? INT_MAX : static_cast<int>(idx);
+}
+__device__ __forceinline__ unsigned long long pack_mass(unsigned long long m, unsigned tag) {
+  return (static_cast<unsigned long long>(tag & 0x1FFu) << 55) | m;
+}
+__device__ __forceinline__ bool mass_tag_is(unsigned long long w, unsigned tag) {
+  return (w >> 55) == (tag & 0x1FFu);
+}
+__device__ __forceinline__ unsigned long long unpack_mass(unsigned long long w) {
+  return w & ((1ull << 55) - 1);
 }
 
 __device__ __forceinline__ void store_part(unsigned long long *p, unsigned long long v) {
@@ -78,27 +101,23 @@ __device__ __forceinline__ unsigned long long load_part(unsigned long long *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Arrival barrier of the W workgroups serving one request.  `gen` counts the
-// barriers this workgroup has passed; the n-th barrier completes at n*W.
-__device__ void group_barrier(unsigned *ctr, unsigned &gen, int W, unsigned *err) {
-  __syncthreads();
-  ++gen;
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned target = gen * static_cast<unsigned>(W);
-    // poll with relaxed loads (an acquire per poll would invalidate the L2
-    // under every other workgroup's streaming), then acquire once
-    unsigned spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
+// Lane x < W waits for workgroup x's word of this exchange and returns it;
+// other lanes return `fill`.
+template <bool MASS>
+__device__ __forceinline__ unsigned long long await_part(unsigned long long *slot, int W, unsigned tag,
+                                                         unsigned long long fill, unsigned *err) {
+  const int x = lane_id();
+  if (x >= W) return fill;
+  unsigned spins = 0;
+  for (;;) {
+    const unsigned long long w = load_part(slot + x);
+    if (MASS ? mass_tag_is(w, tag) : best_tag_is(w, tag)) return w;
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return fill;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
-  __syncthreads();
 }
 
 // ------------------------------------------------------------ block reductions
@@ -259,29 +278,10 @@ __device__ void write_outputs(const AcceptArgs &a, int b, const int *s_path, con
 // (each holds about ten registers while in flight).
 __device__ __forceinline__ void one_at_a_time() { __builtin_amdgcn_sched_barrier(0); }
 
-// The group's partials, read by one wave at once: lane x holds workgroup x's.
-__device__ __forceinline__ unsigned long long lane_part(unsigned long long *slot, int W, unsigned long long fill) {
-  const int x = lane_id();
-  return x < W ? load_part(slot + x) : fill;
-}
-
-__device__ __forceinline__ int group_argmax(unsigned long long *slot, int W) {
-  const unsigned long long pk = lane_part(slot, W, pack_best(-INFINITY, INT_MAX));
-  float v = unpack_v(pk);
-  int i = unpack_i(pk);
-  wave_best(v, i);
-  return i;
-}
-
-__device__ __forceinline__ unsigned long long group_total(unsigned long long *slot, int W) {
-  return wave_sum_u64(lane_part(slot, W, 0ull));
-}
-
-// The workgroup whose slice holds the crossing T of the running mass, and the
-// mass of the slices before it.
-__device__ __forceinline__ int group_owner(unsigned long long *slot, int W, unsigned long long T,
+// The workgroup whose slice holds the crossing T of the running mass (lane x
+// holds workgroup x's mass), and the mass of the slices before it.
+__device__ __forceinline__ int group_owner(unsigned long long px, int W, unsigned long long T,
                                            unsigned long long &base) {
-  const unsigned long long px = lane_part(slot, W, 0ull);
   unsigned long long inc = px;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -305,7 +305,6 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
   constexpr int kChunk = kAccThreads * E;
   const int lo = min(V, c * kChunk);
   const int hi = min(V, lo + kChunk);
-  unsigned *ctr = a.ctr + b;
   unsigned long long *ring = a.part + static_cast<int64_t>(b) * 2 * kMaxGroup;
   unsigned gen = 0;
 
@@ -336,16 +335,27 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
   if (rem < 0) rem = 0;
   __syncthreads();
 
-  // publishes this workgroup's partial, waits for the group, returns the slot
-  auto exchange = [&](unsigned long long value) -> unsigned long long * {
-    unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
-    if (tid == 0) store_part(slot + c, value);
-    group_barrier(ctr, gen, a.W, a.err);
-    return slot;
-  };
+  // Exchanges: publish this workgroup's partial, then every wave gathers the
+  // group's partials (lane x: workgroup x).
   auto group_best = [&](float v, int i) -> int {
     block_best(v, i);
-    return group_argmax(exchange(pack_best(v, i)), a.W);
+    unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
+    ++gen;
+    if (tid == 0) store_part(slot + c, pack_best(v, i, gen));
+    const unsigned long long w = await_part<false>(slot, a.W, gen, pack_best(-INFINITY, INT_MAX, gen), a.err);
+    float gv = unpack_v(w);
+    int gi = unpack_i(w);
+    wave_best(gv, gi);
+    return gi;
+  };
+  // returns the group total; `lane_mass` receives workgroup lane_id()'s part
+  auto group_mass = [&](unsigned long long m, unsigned long long &lane_mass) -> unsigned long long {
+    m = block_sum(m);
+    unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
+    ++gen;
+    if (tid == 0) store_part(slot + c, pack_mass(m, gen));
+    lane_mass = unpack_mass(await_part<true>(slot, a.W, gen, pack_mass(0, gen), a.err));
+    return wave_sum_u64(lane_mass);
   };
 
   int path_len = 1, n_out = 0;
@@ -415,7 +425,7 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
       int nlev = 0;
       int accepted = -1;
       unsigned long long last_total = 0;
-      unsigned long long *last_slot = nullptr;
+      unsigned long long last_lane = 0;
       for (int i = 0; i < nk; ++i) {
         const int cc = s_kid[i];
         const float qy = s_qy[i];
@@ -433,14 +443,13 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
           m += mass(r[n]);
           one_at_a_time();
         }
-        m = block_sum(m);
-        unsigned long long *slot = exchange(m);
-        const unsigned long long tot = group_total(slot, a.W);
+        unsigned long long lane_mass;
+        const unsigned long long tot = group_mass(m, lane_mass);
         if (tid == 0) s_Slev[nlev] = tot;
         __syncthreads();
         ++nlev;
         last_total = tot;
-        last_slot = slot;
+        last_lane = lane_mass;
         if (tot > 0) {
           scaled = true;
           s = static_cast<double>(tot) * 0x1p-40;
@@ -473,10 +482,10 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
       // ---- draw the correction (all children rejected) or the bonus (leaf):
       // from the last residual if its mass is non-zero, else from t
       const bool from_residual = nlev > 0 && last_total > 0;
-      unsigned long long *mslot;
+      unsigned long long lane_mass;
       unsigned long long total;
       if (from_residual) {
-        mslot = last_slot;
+        lane_mass = last_lane;
         total = last_total;
       } else {
         unsigned long long m = 0;
@@ -485,9 +494,7 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
           m += mass(scaled ? rescale(r[n], s) : r[n]);
           one_at_a_time();
         }
-        m = block_sum(m);
-        mslot = exchange(m);
-        total = group_total(mslot, a.W);
+        total = group_mass(m, lane_mass);
       }
 
       if (total == 0) {
@@ -510,7 +517,7 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
       const unsigned long long kk = static_cast<unsigned long long>(ud * 16777216.0f);
       const unsigned long long T = kk * (total >> 24) + ((kk * (total & 0xffffffull)) >> 24);
       unsigned long long base;
-      const int owner = group_owner(mslot, a.W, T, base);
+      const int owner = group_owner(lane_mass, a.W, T, base);
       if (c != owner) {
         writer = false;
         break;
@@ -619,6 +626,7 @@ int32_t plan_accept(const sdv_accept_shape &sh, bool vec, AcceptPlan &p) {
   if (W < 1) W = 1;
   int E = 4;
   while (E < kMaxE && T * E * W < sh.V) E <<= 1;
+  W = (sh.V + T * E - 1) / (T * E);       // no empty slices
   int per_cu = 0;
   const int32_t rc = blocks_per_cu(E, sh.mode == SDV_ACCEPT_STOCHASTIC, vec, per_cu);
   if (rc != SDV_OK) return rc;
@@ -641,8 +649,7 @@ using namespace sdv;
 extern "C" size_t sdv_verify_accept_workspace_size(sdv_accept_shape sh) {
   if (sh.B <= 0) return 0;
   Carver c(nullptr);
-  c.take<unsigned>(static_cast<size_t>(sh.B) + 1);
-  c.take<unsigned long long>(static_cast<size_t>(sh.B) * 2 * kMaxGroup);
+  c.take<unsigned long long>(static_cast<size_t>(sh.B) * 2 * kMaxGroup + 1);
   return c.bytes();
 }
 
@@ -659,8 +666,8 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
               "verify_accept: need B >= 0, N >= 1, S >= 0, V >= 1");
   SDV_REQUIRE(sh.mode == SDV_ACCEPT_GREEDY || sh.mode == SDV_ACCEPT_STOCHASTIC, SDV_E_SHAPE,
               "verify_accept: unknown mode %d", sh.mode);
-  SDV_REQUIRE(sh.N <= 256 && sh.S + 1 <= 64 && sh.V <= kMaxGroup * kAccThreads * kMaxE, SDV_E_UNSUPPORTED,
-              "verify_accept: N <= 256, S+1 <= 64 and V <= %d required", kMaxGroup * kAccThreads * kMaxE);
+  SDV_REQUIRE(sh.N <= 256 && sh.S + 1 <= 64 && sh.V < static_cast<int>(kNoIndex), SDV_E_UNSUPPORTED,
+              "verify_accept: N <= 256, S+1 <= 64 and V < %d required", static_cast<int>(kNoIndex));
   SDV_REQUIRE(sh.mode == SDV_ACCEPT_GREEDY || sh.R >= 1, SDV_E_SHAPE, "verify_accept: R >= 1 needed");
   if (sh.B == 0) return SDV_OK;
   SDV_REQUIRE(tokens && next_token && next_sibling && target && accept_len && accept_path &&
@@ -678,11 +685,12 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
   if (rc != SDV_OK) return rc;
 
   Carver cv(ws);
-  unsigned *ctr = cv.take<unsigned>(static_cast<size_t>(sh.B) + 1);
-  unsigned long long *part = cv.take<unsigned long long>(static_cast<size_t>(sh.B) * 2 * kMaxGroup);
+  const size_t words = static_cast<size_t>(sh.B) * 2 * kMaxGroup + 1;
+  unsigned long long *part = cv.take<unsigned long long>(words);
   hipStream_t st = as_stream(stream);
-  const int nz = sh.B + 1;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, st, ctr, nz);
+  const int nz = static_cast<int>(words * 2);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, st, reinterpret_cast<unsigned *>(part),
+                     nz);
   rc = check_launch("zero_u32_kernel");
   if (rc != SDV_OK) return rc;
 
@@ -694,7 +702,8 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
   a.target = target; a.draft = draft_probs; a.u_accept = u_accept; a.u_draw = u_draw;
   a.accept_len = accept_len; a.accept_path = accept_path; a.commit_tokens = commit_tokens;
   a.commit_len = commit_len; a.next_root = next_root;
-  a.ctr = ctr; a.part = part; a.err = ctr + sh.B;
+  a.part = part;
+  a.err = reinterpret_cast<unsigned *>(part + words - 1);
   const void *fn = accept_kernel_for(p.E, sh.mode == SDV_ACCEPT_STOCHASTIC, vec);
   for (int b0 = 0; b0 < sh.B; b0 += p.per_launch) {
     a.b0 = b0;
