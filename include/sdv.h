@@ -128,8 +128,9 @@ int32_t sdv_build_tree(sdv_tree_shape shape, const float *topk_p, const int32_t 
  * out: device [B, N, Hq, D] bf16; lse: device [B, N, Hq] fp32 natural-log
  * sum of exp(sm_scale * q.k) (NULL to skip).  sm_scale <= 0 selects
  * 1/sqrt(D).  Limits: D in {64, 128}, 1 <= N <= 256, Hq % Hkv == 0,
- * Hq/Hkv <= 16, page a power of two.  Keys whose page id falls outside
- * the pool are skipped.  The call needs no workspace: the size query returns
+ * Hq/Hkv <= 16, page a power of two, num_slots + page < 2^31 and
+ * num_slots * Hkv * D * 2 < 2^36 bytes per pool.  Keys whose page id falls
+ * outside the pool are skipped.  The call needs no workspace: the size query returns
  * 0 and ws may be NULL (the arguments stay for a stable ABI).
  * ---------------------------------------------------------------------- */
 typedef struct {

@@ -15,11 +15,9 @@
 //     tiles t+1 .. t+3 are in flight.  No registers stage the data.
 //   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled per row so that
 //     the MFMA fragment reads below hit distinct banks.
-//   * S^T = K Q^T on bf16 MFMA 16x16x32.  O^T += V^T P^T on MFMA 16x16x16:
-//     V is read as 8-byte words holding 4 consecutive d of one key; four
-//     keys' words are repacked into the A operands of four MFMAs, output row
-//     m of block (dq, r) standing for d = 64*dq + 4*m + r.  P is rounded to
-//     bf16.
+//   * S^T = K Q^T on bf16 MFMA 16x16x32.  O^T += V^T P^T on MFMA 16x16x16
+//     with each V^T operand fetched by one transposing LDS read
+//     (ds_read_b64_tr_b16); P is rounded to bf16.
 //   * Every lane keeps the softmax state of its own query row; scores are
 //     scaled into log2 units and exponentiated with exp2; the reference max
 //     moves only when a score exceeds it by more than 2^8, so the O rescale
@@ -66,8 +64,7 @@ struct AttnCfg {
   static constexpr int KPI = 64 / CHUNKS;                 // key rows per DMA instruction (1 KB)
   static constexpr int IPW = 8 / KPI;                     // DMA instructions per wave per tile and tensor
   static constexpr int DS = D / 32;                       // k-steps of QK^T
-  static constexpr int DQ = D / 64;                       // 64-wide d groups of PV
-  static constexpr int NO = DQ * 4;                       // O^T accumulator blocks per row block
+  static constexpr int NO = D / 16;                       // 16-wide d blocks of O^T per row block
   static constexpr int TILE_BYTES = kTile * ROW;
   static constexpr int STAGE = 2 * TILE_BYTES;            // K then V
   static constexpr int SMEM = kStages * STAGE;            // also holds the fp32 merge buffer
@@ -227,18 +224,23 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   // of that chunk within a slot is fixed per lane and instruction.  Positions
   // outside the request read the zero block (the instruction is always
   // issued, which keeps the per-wave count of loads in flight fixed).
-  const int64_t slot_stride = static_cast<int64_t>(Hkv) * D;
+  // Positions are fetched in 16-byte chunks; pool offsets count chunks
+  // (32-bit: the host checks that the pool holds fewer than 2^32 of them).
+  const int row_chunks = Hkv * (D / 8);
+  const unsigned pid_max = static_cast<unsigned>(num_slots >> pshift);   // last page id with a slot
+  const unsigned nslots = static_cast<unsigned>(num_slots);
   int dma_row[C::IPW];
   int dma_col[C::IPW];
 #pragma unroll
   for (int i = 0; i < C::IPW; ++i) {
     dma_row[i] = wave * 8 + i * C::KPI + l / C::CHUNKS;
-    dma_col[i] = kvh * D + (((l % C::CHUNKS) ^ swz<D>(dma_row[i])) << 3);
+    dma_col[i] = kvh * (D / 8) + ((l % C::CHUNKS) ^ swz<D>(dma_row[i]));
   }
-  auto dma_tile = [&](int t, auto STG) {
-    constexpr int stg = decltype(STG)::value;
-    unsigned char *kst = smem + stg * C::STAGE;
-    unsigned char *vst = kst + C::TILE_BYTES;
+  const uint4 *kp16 = reinterpret_cast<const uint4 *>(kpool);
+  const uint4 *vp16 = reinterpret_cast<const uint4 *>(vpool);
+  const uint32_t lds0 = lds_offset(smem);
+  auto dma_tile = [&](int t) {
+    const uint32_t kst = lds0 + (t & (kStages - 1)) * C::STAGE;
     const int wbase = ((t / win_tiles) * win_tiles * kTile) >> pshift;
 #pragma unroll
     for (int i = 0; i < C::IPW; ++i) {
@@ -246,35 +248,47 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       int idx = (pos >> pshift) - wbase;
       idx = idx < 0 ? 0 : (idx >= kPageCache ? kPageCache - 1 : idx);
       const int pid = s_page[idx];
-      const int64_t sl = (static_cast<int64_t>(pid) << pshift) + (pos & pmask);
-      const bool ok = pos < total && pid >= 0 && sl < num_slots;
-      const int64_t off = sl * slot_stride + dma_col[i];
-      const uint16_t *ka = ok ? kpool + off : g_zero16;
-      const uint16_t *va = ok ? vpool + off : g_zero16;
-      const int lrow = wave * 8 + i * C::KPI;                    // first row of this 1 KB block
-      dma16(ka, __builtin_amdgcn_readfirstlane(lds_offset(kst + lrow * C::ROW)));
-      dma16(va, __builtin_amdgcn_readfirstlane(lds_offset(vst + lrow * C::ROW)));
+      const unsigned slot = (static_cast<unsigned>(pid) << pshift) + static_cast<unsigned>(pos & pmask);
+      const bool ok = (pos < total) & (static_cast<unsigned>(pid) <= pid_max) & (slot < nslots);
+      const uint32_t off = slot * static_cast<uint32_t>(row_chunks) + dma_col[i];
+      const void *ka = ok ? static_cast<const void *>(kp16 + off) : static_cast<const void *>(g_zero16);
+      const void *va = ok ? static_cast<const void *>(vp16 + off) : static_cast<const void *>(g_zero16);
+      const uint32_t lrow = (wave * 8 + i * C::KPI) * C::ROW;     // first row of this 1 KB block
+      dma16(ka, __builtin_amdgcn_readfirstlane(kst + lrow));
+      dma16(va, __builtin_amdgcn_readfirstlane(kst + C::TILE_BYTES + lrow));
     }
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
+  // Lane parts of the LDS fragment addresses (per stage: + stage base).
+  // K: row 32*kh + 16*k2 + l16, chunk (4*ds + g4) ^ swz(row).
+  // V^T (transposing read): row 32*kh + 16*k2 + 4*g4 + l16/4, 8 bytes at
+  // d = 16*db + 4*(l16 % 4), i.e. chunk (2*db + (l16 % 4)/2) ^ swz(row).
+  uint32_t koff[KB][C::DS], voff[KB][C::NO];
+#pragma unroll
+  for (int k2 = 0; k2 < KB; ++k2) {
+    const int kr = 32 * kh + 16 * k2 + l16;
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) koff[k2][ds] = kr * C::ROW + (((ds * 4 + g4) ^ swz<D>(kr)) << 4);
+    const int vr = 32 * kh + 16 * k2 + 4 * g4 + (l16 >> 2);
+#pragma unroll
+    for (int db = 0; db < C::NO; ++db)
+      voff[k2][db] = C::TILE_BYTES + vr * C::ROW + (((2 * db + ((l16 & 3) >> 1)) ^ swz<D>(vr)) << 4) + ((l16 & 1) << 3);
+  }
 
   refresh_pages(0);
   __syncthreads();
   // the Q fragments and the page copy land here once, not inside the key loop
   __builtin_amdgcn_s_waitcnt(0);
   if (ntiles > 0) {
-    dma_tile(0, S0{});
-    dma_tile(1, S1{});
-    dma_tile(2, S2{});
+    dma_tile(0);
+    dma_tile(1);
+    dma_tile(2);
   }
 
-  // one tile: tile t sits in stage STG = t % 4; tile t+3 goes to stage (t+3) % 4
-  auto tile_step = [&](int t, auto STG) {
-    constexpr int stg = decltype(STG)::value;
+  // One tile: tile t sits in stage t % 4; tile t+3 goes to stage (t+3) % 4.
+  // MASKED: the tile reaches past the prefix, so the tree mask applies.
+  auto tile_step = [&](int t, auto MASKED) {
+    constexpr bool masked = decltype(MASKED)::value;
     wait_vmcnt<4 * C::IPW>();            // this wave's DMAs of tile t are done (t+1, t+2 may fly)
     __syncthreads();                     // everyone's are; and stage (t+3)%4 is no longer read
     if (t + 3 < ntiles && (t + 3) % win_tiles == 0) {   // block-uniform: next page window
@@ -282,10 +296,8 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    dma_tile(t + 3, std::integral_constant<int, (stg + 3) % kStages>{});
-
-    const unsigned char *kb = smem + stg * C::STAGE;
-    const unsigned char *vb = kb + C::TILE_BYTES;
+    dma_tile(t + 3);
+    const uint32_t base = lds0 + (t & (kStages - 1)) * C::STAGE;
 
     // ---- S^T: A = K[key][d] (LDS), B = Q^T (registers)
     f32x4 s[KB][RB];
@@ -295,12 +307,9 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       for (int rb = 0; rb < RB; ++rb) s[k2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k2 = 0; k2 < KB; ++k2) {
-      const int kr = 32 * kh + 16 * k2 + l16;
-      const int sk = swz<D>(kr);
 #pragma unroll
       for (int ds = 0; ds < C::DS; ++ds) {
-        bf16x8 kf;
-        __builtin_memcpy(&kf, kb + kr * C::ROW + (((ds * 4 + g4) ^ sk) << 4), 16);
+        const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(base + koff[k2][ds]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           s[k2][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], s[k2][rb], 0, 0, 0);
@@ -310,29 +319,32 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
     // ---- mask + online softmax (lane: its row per rb; keys 16*k2 + 4*g4 + i).
     // Max on raw scores, then p = exp2(s * scale_log2 - m) as one FMA and a
     // bare v_exp_f32; P goes to bf16 with the hardware pack instruction.
-    const int kpos0 = t * kTile + 32 * kh + 4 * g4;
-    const bool all_prefix = (t + 1) * kTile <= L;
-    s16x4 pf[KB][RB];
+    bf16x8 pb[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float v[KB][4];
-      float rmax = -INFINITY;
 #pragma unroll
       for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bool vis = true;
-          if (!all_prefix) {
-            // Branch-free on purpose: a short-circuit form here becomes
+        for (int i = 0; i < 4; ++i) v[k2][i] = s[k2][rb][i];
+      if constexpr (masked) {
+        const int kpos0 = t * kTile + 32 * kh + 4 * g4;
+#pragma unroll
+        for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // branch-free on purpose: a short-circuit form here becomes
             // divergent control flow whose -inf write lands in the MFMA
-            // result register for every tree lane, visible ones included.
+            // result register for every tree lane, visible ones included
             const int j = kpos0 + 16 * k2 + i - L;
             const uint32_t w = s_mask[nrel[rb]][(j >> 5) & 7];
-            vis = (j < 0) | ((static_cast<unsigned>(j) < static_cast<unsigned>(N)) & ((w >> (j & 31)) & 1u));
+            const bool vis =
+                (j < 0) | ((static_cast<unsigned>(j) < static_cast<unsigned>(N)) & ((w >> (j & 31)) & 1u));
+            v[k2][i] = vis ? v[k2][i] : -INFINITY;
           }
-          v[k2][i] = vis ? s[k2][rb][i] : -INFINITY;
-          rmax = fmaxf(rmax, v[k2][i]);
-        }
+      }
+      float rmax = fmaxf(fmaxf(fmaxf(v[0][0], v[0][1]), fmaxf(v[0][2], v[0][3])),
+                         fmaxf(fmaxf(v[1][0], v[1][1]), fmaxf(v[1][2], v[1][3])));
       rmax = fmaxf(rmax, __shfl_xor(rmax, 16, kWave));
       rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
       const float tmax = rmax * scale_log2;
@@ -352,67 +364,43 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       }
       const float mneg = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
       float psum = 0.f;
+      bf16x8 pk;
 #pragma unroll
-      for (int k2 = 0; k2 < KB; ++k2) {
-        float p[4];
+      for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(v[k2][i], scale_log2, mneg));
-          psum += p[i];
+          const float p = __builtin_amdgcn_exp2f(fmaf(v[k2][i], scale_log2, mneg));
+          psum += p;
+          pk[4 * k2 + i] = static_cast<__bf16>(p);
         }
-        bf16x2 h01, h23;
-        h01[0] = static_cast<__bf16>(p[0]);
-        h01[1] = static_cast<__bf16>(p[1]);
-        h23[0] = static_cast<__bf16>(p[2]);
-        h23[1] = static_cast<__bf16>(p[3]);
-        uint2 packed;
-        __builtin_memcpy(&packed.x, &h01, 4);
-        __builtin_memcpy(&packed.y, &h23, 4);
-        __builtin_memcpy(&pf[k2][rb], &packed, 8);
-      }
+      pb[rb] = pk;
       l_run[rb] += psum;
     }
 
-    // ---- O^T += V^T P^T: 8-byte LDS words = 4 consecutive d of one key
+    // ---- O^T += V^T P^T on MFMA 16x16x32.  MFMA k index 8*g4 + j stands
+    // for key 4*g4 + j (j < 4) or 16 + 4*g4 + (j - 4) of this wave's 32
+    // keys: P holds them in that order, and the V^T operand is the two
+    // transposing reads of the 16-key blocks side by side.  A transposing
+    // read: lane 4j + q of a 16-lane group points at row j, d 4q..4q+3, and
+    // lane i of the group receives d = i of the group's four rows.
 #pragma unroll
-    for (int k2 = 0; k2 < KB; ++k2) {
+    for (int db = 0; db < C::NO; ++db) {
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4 *>(base + voff[0][db]));
+      const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4 *>(base + voff[1][db]));
+      bf16x8 a;
+      __builtin_memcpy(reinterpret_cast<char *>(&a), &a0, 8);
+      __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &a1, 8);
 #pragma unroll
-      for (int dq = 0; dq < C::DQ; ++dq) {
-        uint2 w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int vr = 32 * kh + 16 * k2 + 4 * g4 + j;
-          const int c = (dq * 8 + (l16 >> 1)) ^ swz<D>(vr);
-          w[j] = *reinterpret_cast<const uint2 *>(vb + vr * C::ROW + (c << 4) + ((l16 & 1) << 3));
-        }
-        // a[r] = (key0, key1, key2, key3) at d = 64*dq + 4*l16 + r
-        s16x4 a[4];
-        {
-          const uint2 p0 = make_uint2((w[0].x & 0xffffu) | (w[1].x << 16), (w[2].x & 0xffffu) | (w[3].x << 16));
-          const uint2 p1 = make_uint2((w[0].x >> 16) | (w[1].x & 0xffff0000u), (w[2].x >> 16) | (w[3].x & 0xffff0000u));
-          const uint2 p2 = make_uint2((w[0].y & 0xffffu) | (w[1].y << 16), (w[2].y & 0xffffu) | (w[3].y << 16));
-          const uint2 p3 = make_uint2((w[0].y >> 16) | (w[1].y & 0xffff0000u), (w[2].y >> 16) | (w[3].y & 0xffff0000u));
-          __builtin_memcpy(&a[0], &p0, 8);
-          __builtin_memcpy(&a[1], &p1, 8);
-          __builtin_memcpy(&a[2], &p2, 8);
-          __builtin_memcpy(&a[3], &p3, 8);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            o[rb][dq * 4 + r] =
-                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[r], pf[k2][rb], o[rb][dq * 4 + r], 0, 0, 0);
-      }
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb], o[rb][db], 0, 0, 0);
     }
   };
 
-  for (int t = 0; t < ntiles; t += kStages) {
-    tile_step(t, S0{});
-    if (t + 1 < ntiles) tile_step(t + 1, S1{});
-    if (t + 2 < ntiles) tile_step(t + 2, S2{});
-    if (t + 3 < ntiles) tile_step(t + 3, S3{});
-  }
+  // tiles wholly inside the prefix need no mask
+  const int nfull = min(ntiles, L / kTile);
+  int t = 0;
+  for (; t < nfull; ++t) tile_step(t, std::false_type{});
+  for (; t < ntiles; ++t) tile_step(t, std::true_type{});
 
   // ---- merge the two key halves of each row quarter (fixed order) and write
   __builtin_amdgcn_s_waitcnt(0);         // trailing DMAs (zero blocks) must land before reuse
@@ -446,31 +434,26 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[rb][j][i] *= fac[rb];
 
-  // accumulator o[rb][dq*4+r][i] holds row 32*rh+16*rb+l16 at d = 64*dq + 16*g4 + 4*i + r
+  // accumulator o[rb][db][i] holds row 32*rh+16*rb+l16 at d = 16*db + 4*g4 + i
   float *mbuf = reinterpret_cast<float *>(smem);
   if (kh == 1) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int dq = 0; dq < C::DQ; ++dq)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<float4 *>(mbuf + (32 * rh + 16 * rb + l16) * D + dq * 64 + 16 * g4 + 4 * i) =
-              make_float4(o[rb][dq * 4 + 0][i], o[rb][dq * 4 + 1][i], o[rb][dq * 4 + 2][i], o[rb][dq * 4 + 3][i]);
+      for (int db = 0; db < C::NO; ++db)
+        *reinterpret_cast<float4 *>(mbuf + (32 * rh + 16 * rb + l16) * D + 16 * db + 4 * g4) =
+            make_float4(o[rb][db][0], o[rb][db][1], o[rb][db][2], o[rb][db][3]);
   }
   __syncthreads();
   if (kh == 0) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int dq = 0; dq < C::DQ; ++dq)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float4 *p4 = reinterpret_cast<float4 *>(mbuf + (32 * rh + 16 * rb + l16) * D + dq * 64 + 16 * g4 + 4 * i);
-          const float4 x = *p4;
-          *p4 = make_float4(o[rb][dq * 4 + 0][i] + x.x, o[rb][dq * 4 + 1][i] + x.y, o[rb][dq * 4 + 2][i] + x.z,
-                            o[rb][dq * 4 + 3][i] + x.w);
-        }
+      for (int db = 0; db < C::NO; ++db) {
+        float4 *p4 = reinterpret_cast<float4 *>(mbuf + (32 * rh + 16 * rb + l16) * D + 16 * db + 4 * g4);
+        const float4 x = *p4;
+        *p4 = make_float4(o[rb][db][0] + x.x, o[rb][db][1] + x.y, o[rb][db][2] + x.z, o[rb][db][3] + x.w);
+      }
   }
   __syncthreads();
   for (int x = tid; x < kRows * (D / 8); x += kAttnThreads) {
@@ -561,6 +544,8 @@ extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, 
   const int64_t units_pad = (units + kXcds - 1) / kXcds * kXcds;
   const int64_t blocks = units_pad * nrb;
   SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tree_verify_attention: grid too large");
+  SDV_REQUIRE(sh.num_slots + sh.page < (1LL << 31) && sh.num_slots * sh.Hkv * (sh.D / 8) < (1LL << 32),
+              SDV_E_UNSUPPORTED, "tree_verify_attention: pool too large (2^31 slots, 2^32 16-byte chunks)");
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(sh.D));
   const float scale_log2 = scale * 1.4426950408889634f;
   hipStream_t st = as_stream(stream);
