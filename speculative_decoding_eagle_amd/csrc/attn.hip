@@ -275,21 +275,49 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       voff[k2][db] = C::TILE_BYTES + vr * C::ROW + (((2 * db + ((l16 & 3) >> 1)) ^ swz<D>(vr)) << 4) + ((l16 & 1) << 3);
   }
 
+  // ---- S^T of tile t: A = K[key][d] (LDS), B = Q^T (registers)
+  auto scores = [&](int t, f32x4 (&sc)[KB][RB]) {
+    const uint32_t base = lds0 + (t & (kStages - 1)) * C::STAGE;
+#pragma unroll
+    for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sc[k2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < KB; ++k2) {
+#pragma unroll
+      for (int ds = 0; ds < C::DS; ++ds) {
+        const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(base + koff[k2][ds]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sc[k2][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], sc[k2][rb], 0, 0, 0);
+      }
+    }
+  };
+
   refresh_pages(0);
   __syncthreads();
   // the Q fragments and the page copy land here once, not inside the key loop
   __builtin_amdgcn_s_waitcnt(0);
+  f32x4 s[KB][RB];
   if (ntiles > 0) {
     dma_tile(0);
     dma_tile(1);
     dma_tile(2);
+    wait_vmcnt<4 * C::IPW>();            // tile 0 is in
+    __syncthreads();
+    scores(0, s);
   }
 
-  // One tile: tile t sits in stage t % 4; tile t+3 goes to stage (t+3) % 4.
-  // MASKED: the tile reaches past the prefix, so the tree mask applies.
+  // Step t: softmax and PV of tile t, with the scores of tile t+1 computed
+  // first so that their MFMAs run under the softmax's VALU work.  Tile t
+  // sits in stage t % 4; tile t+3 goes to stage (t+3) % 4, whose K was last
+  // read for tile t-1's scores and whose V for tile t-1's PV (both done by
+  // every wave at this step's barrier).  DMAs go out as K(t), V(t) per step,
+  // so K(t+1) being in means V(t) is in too.
+  // MASKED: tile t reaches past the prefix, so the tree mask applies.
   auto tile_step = [&](int t, auto MASKED) {
     constexpr bool masked = decltype(MASKED)::value;
-    wait_vmcnt<4 * C::IPW>();            // this wave's DMAs of tile t are done (t+1, t+2 may fly)
+    wait_vmcnt<3 * C::IPW>();            // this wave's DMAs through K(t+1) are done
     __syncthreads();                     // everyone's are; and stage (t+3)%4 is no longer read
     if (t + 3 < ntiles && (t + 3) % win_tiles == 0) {   // block-uniform: next page window
       refresh_pages(t + 3);
@@ -299,34 +327,16 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
     dma_tile(t + 3);
     const uint32_t base = lds0 + (t & (kStages - 1)) * C::STAGE;
 
-    // ---- S^T: A = K[key][d] (LDS), B = Q^T (registers)
-    f32x4 s[KB][RB];
-#pragma unroll
-    for (int k2 = 0; k2 < KB; ++k2)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[k2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k2 = 0; k2 < KB; ++k2) {
-#pragma unroll
-      for (int ds = 0; ds < C::DS; ++ds) {
-        const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(base + koff[k2][ds]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          s[k2][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], s[k2][rb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask + online softmax (lane: its row per rb; keys 16*k2 + 4*g4 + i).
-    // Max on raw scores, then p = exp2(s * scale_log2 - m) as one FMA and a
-    // bare v_exp_f32; P goes to bf16 with the hardware pack instruction.
-    bf16x8 pb[RB];
+    // ---- mask, row max and the (rare) rescale of the running state
+    // (lane: its row per rb; keys 16*k2 + 4*g4 + i)
+    float v[RB][KB][4];
+    float mneg[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float v[KB][4];
 #pragma unroll
       for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[k2][i] = s[k2][rb][i];
+        for (int i = 0; i < 4; ++i) v[rb][k2][i] = s[k2][rb][i];
       if constexpr (masked) {
         const int kpos0 = t * kTile + 32 * kh + 4 * g4;
 #pragma unroll
@@ -340,11 +350,11 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
             const uint32_t w = s_mask[nrel[rb]][(j >> 5) & 7];
             const bool vis =
                 (j < 0) | ((static_cast<unsigned>(j) < static_cast<unsigned>(N)) & ((w >> (j & 31)) & 1u));
-            v[k2][i] = vis ? v[k2][i] : -INFINITY;
+            v[rb][k2][i] = vis ? v[rb][k2][i] : -INFINITY;
           }
       }
-      float rmax = fmaxf(fmaxf(fmaxf(v[0][0], v[0][1]), fmaxf(v[0][2], v[0][3])),
-                         fmaxf(fmaxf(v[1][0], v[1][1]), fmaxf(v[1][2], v[1][3])));
+      float rmax = fmaxf(fmaxf(fmaxf(v[rb][0][0], v[rb][0][1]), fmaxf(v[rb][0][2], v[rb][0][3])),
+                         fmaxf(fmaxf(v[rb][1][0], v[rb][1][1]), fmaxf(v[rb][1][2], v[rb][1][3])));
       rmax = fmaxf(rmax, __shfl_xor(rmax, 16, kWave));
       rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
       const float tmax = rmax * scale_log2;
@@ -362,38 +372,84 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
           o[rb][j][3] *= alpha;
         }
       }
-      const float mneg = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
-      float psum = 0.f;
-      bf16x8 pk;
-#pragma unroll
-      for (int k2 = 0; k2 < KB; ++k2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(v[k2][i], scale_log2, mneg));
-          psum += p;
-          pk[4 * k2 + i] = static_cast<__bf16>(p);
-        }
-      pb[rb] = pk;
-      l_run[rb] += psum;
+      mneg[rb] = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
     }
 
-    // ---- O^T += V^T P^T on MFMA 16x16x32.  MFMA k index 8*g4 + j stands
-    // for key 4*g4 + j (j < 4) or 16 + 4*g4 + (j - 4) of this wave's 32
-    // keys: P holds them in that order, and the V^T operand is the two
-    // transposing reads of the 16-key blocks side by side.  A transposing
-    // read: lane 4j + q of a 16-lane group points at row j, d 4q..4q+3, and
-    // lane i of the group receives d = i of the group's four rows.
+    // ---- one straight-line block in a fixed order (in-order issue: an MFMA
+    // runs while the VALU work after it issues).  The scores of tile t+1
+    // (computed even past the last tile: the stage holds in-bounds data and
+    // they go unused) are interleaved with the exponentials of tile t; then
+    // O^T += V^T P^T with each pair of V reads issued one block ahead.
+    const uint32_t nbase = lds0 + ((t + 1) & (kStages - 1)) * C::STAGE;
+    bf16x8 kf[KB][C::DS];
 #pragma unroll
-    for (int db = 0; db < C::NO; ++db) {
-      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+      for (int ds = 0; ds < C::DS; ++ds)
+        kf[k2][ds] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(nbase + koff[k2][ds]);
+    f32x4 sn[KB][RB];
+#pragma unroll
+    for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sn[k2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_sched_barrier(0);
+    float psum[RB] = {0.f, 0.f};
+    bf16x8 pb[RB];
+    constexpr int kSteps = KB * C::DS * RB / 2;          // two score MFMAs per step
+    constexpr int kEps = RB * KB * 4 / kSteps;           // exponentials per step (2 or 4)
+    static_assert(kEps * kSteps == RB * KB * 4 && kEps % 2 == 0, "even split of the exponentials");
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = 2 * st + h;                          // MFMA index: (k2, ds, rb)
+        const int k2 = m / (C::DS * RB), ds = (m / RB) % C::DS, rb = m % RB;
+        sn[k2][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k2][ds], qf[rb][ds], sn[k2][rb], 0, 0, 0);
+      }
+      // exponentials of this lane's elements kEps*st .. +kEps-1 (rb, k2, i)
+#pragma unroll
+      for (int x = 0; x < kEps; x += 2) {
+        const int e = kEps * st + x;
+        const int rb = e / (KB * 4), k2 = (e / 4) % KB, i = e % 4;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(v[rb][k2][i], scale_log2, mneg[rb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(v[rb][k2][i + 1], scale_log2, mneg[rb]));
+        psum[rb] += p0 + p1;
+        pb[rb][4 * k2 + i] = static_cast<__bf16>(p0);
+        pb[rb][4 * k2 + i + 1] = static_cast<__bf16>(p1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_run[rb] += psum[rb];
+
+    // O^T += V^T P^T on MFMA 16x16x32.  MFMA k index 8*g4 + j stands for key
+    // 4*g4 + j (j < 4) or 16 + 4*g4 + (j - 4) of this wave's 32 keys: P holds
+    // them in that order, and the V^T operand is the two transposing reads
+    // of the 16-key blocks side by side.  A transposing read: lane 4j + q of
+    // a 16-lane group points at row j, d 4q..4q+3, and lane i of the group
+    // receives d = i of the group's four rows.
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    auto vread = [&](int db) {
       const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4 *>(base + voff[0][db]));
       const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4 *>(base + voff[1][db]));
       bf16x8 a;
       __builtin_memcpy(reinterpret_cast<char *>(&a), &a0, 8);
       __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &a1, 8);
+      return a;
+    };
+    bf16x8 va = vread(0);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb], o[rb][db], 0, 0, 0);
+    for (int db = 0; db < C::NO; ++db) {
+      const bf16x8 vn = db + 1 < C::NO ? vread(db + 1) : va;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb], o[rb][db], 0, 0, 0);
+      va = vn;
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[k2][rb] = sn[k2][rb];
   };
 
   // tiles wholly inside the prefix need no mask
