@@ -2,10 +2,10 @@
 // softmax, "[SGLang] Multi-Layer EAGLE" section 3).
 //
 // HBM-bound streaming reduction under the strict order (value desc, id asc).
-// Each 256-thread block scans one slice of one row; each of its waves streams
-// a contiguous quarter of the slice with 16-byte loads (four in flight per
-// lane) through a per-wave threshold filter (below), and wave 0 merges the
-// four per-wave lists.  Short-row batches are split over several blocks per
+// Each 256-thread block scans one slice of one row in contiguous 16 KB
+// windows (16-byte non-temporal loads, four in flight per lane); every wave
+// runs a threshold filter (below) over its share, and wave 0 merges the four
+// per-wave lists.  Short-row batches are split over several blocks per
 // row, and a one-wave kernel merges the per-slice lists.
 #include <climits>
 #include <cmath>
@@ -16,6 +16,13 @@ namespace sdv {
 namespace {
 
 constexpr int kTopkThreads = 256;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+// 16-byte load marked non-temporal (the probability rows are read once).
+__device__ __forceinline__ float4 stream_load(const float *p) {
+  const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 template <int K>
 struct SortedK {
@@ -175,27 +182,27 @@ topk_slice_kernel(const float *__restrict__ probs, int64_t rows, int V, int spli
   WaveFilter<K> F;
   F.init(s_cv[w], s_ci[w], s_tv[w], s_ti[w]);
   if (vec) {
-    // each wave streams its own quarter of the slice (16-byte loads, four in flight)
-    const int per = ((hi - lo) / 4 + NW - 1) / NW * 4;
-    const int wlo = min(hi, lo + w * per);
-    const int whi = min(hi, wlo + per);
-    const int step = 4 * kWave;
-    int e = wlo + 4 * lane_id();
-    int base = wlo;                         // wave-uniform: every lane leaves the loop together
-    for (; base + 4 * step <= whi; base += 4 * step, e += 4 * step) {
-      const float4 a0 = *reinterpret_cast<const float4 *>(rp + e);
-      const float4 a1 = *reinterpret_cast<const float4 *>(rp + e + step);
-      const float4 a2 = *reinterpret_cast<const float4 *>(rp + e + 2 * step);
-      const float4 a3 = *reinterpret_cast<const float4 *>(rp + e + 3 * step);
+    // The block reads one contiguous 16 KB window per iteration: load u of
+    // wave w covers 1 KB chunk 4*u + w of the window.  One stream per row
+    // (rather than one per wave) and non-temporal loads (the rows are read
+    // once) keep HBM efficient when a thousand rows stream at once.
+    const int step = 4 * kWave;                   // floats per 1 KB chunk
+    const int win = 4 * NW * step;                // floats per window
+    int base = lo;
+    for (; base + win <= hi; base += win) {
+      const int e = base + w * step + 4 * lane_id();
+      const float4 a0 = stream_load(rp + e);
+      const float4 a1 = stream_load(rp + e + NW * step);
+      const float4 a2 = stream_load(rp + e + 2 * NW * step);
+      const float4 a3 = stream_load(rp + e + 3 * NW * step);
       F.consume4(a0, e);
-      F.consume4(a1, e + step);
-      F.consume4(a2, e + 2 * step);
-      F.consume4(a3, e + 3 * step);
+      F.consume4(a1, e + NW * step);
+      F.consume4(a2, e + 2 * NW * step);
+      F.consume4(a3, e + 3 * NW * step);
     }
-    for (; e - 4 * lane_id() < whi; e += step) {
-      const bool in = e < whi;
-      const float4 a = in ? *reinterpret_cast<const float4 *>(rp + e)
-                          : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    for (int e = base + w * step + 4 * lane_id(); e - 4 * lane_id() < hi; e += NW * step) {
+      const bool in = e < hi;
+      const float4 a = in ? stream_load(rp + e) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       F.consume4(a, e, in);
     }
   } else {
