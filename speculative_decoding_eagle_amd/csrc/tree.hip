@@ -4,8 +4,8 @@
 // slots"), plus positions, the tree mask and the retrieve arrays
 // (zero-to-sglang ch.10 section 5.2).
 //
-// Latency-bound integer work: one 256-thread block per request keeps the
-// whole candidate pool in LDS.  Every selection (each step's frontier and the
+// Latency-bound integer work: one 512-thread block per request keeps its
+// top-k lists and the whole candidate pool in LDS.  Every selection (each step's frontier and the
 // final best N-1) is a rank computation under the strict order
 // (score desc, pool index asc): an entry's rank is the number of entries that
 // beat it, so ranks are unique and the result is deterministic.
@@ -14,15 +14,48 @@
 namespace sdv {
 namespace {
 
-constexpr int kTreeThreads = 256;
+constexpr int kTreeThreads = 512;
+constexpr int kTreeWaves = kTreeThreads / kWave;
 constexpr int kMaxPool = 2048;
 constexpr int kMaxNodes = 256;
 constexpr int kMaxWords = kMaxNodes / 32;
 
-__device__ __forceinline__ bool beats(const float *sc, int a, int b) {
-  return sc[a] > sc[b] || (sc[a] == sc[b] && a < b);
+// Rank of pool entry e among entries [lo, lo + n): the number that beat it
+// under (score desc, pool index asc).  Unrolled so that many LDS reads are in
+// flight; se stays in a register.
+__device__ __forceinline__ int rank_among(const float *sc, int lo, int n, int e) {
+  const float se = sc[e];
+  int r = 0;
+#pragma unroll 8
+  for (int o = lo; o < lo + n; ++o) {
+    const float so = sc[o];
+    r += (so > se) | ((so == se) & (o < e));
+  }
+  return r;
 }
 
+// Exclusive block scan of one int per thread.
+__device__ int block_exclusive_scan(int x) {
+  __shared__ int s_w[kTreeWaves];
+  const int l = lane_id(), w = threadIdx.x / kWave;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(inc, off, kWave);
+    if (l >= off) inc += y;
+  }
+  if (l == kWave - 1) s_w[w] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int j = 0; j < w; ++j) before += s_w[j];
+  __syncthreads();
+  return before + inc - x;
+}
+
+// Pool entry e of a request coincides with entry e of its row-major [R, k]
+// top-k lists: step 0 holds the root's k children (row 0), and entry
+// k + (i-1)*k*k + j*k + c of step i >= 1 is child c of frontier slot j,
+// drawn from row 1 + (i-1)*k + j.
 __global__ void __launch_bounds__(kTreeThreads)
 build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
                   const int *__restrict__ topk_id, const int *__restrict__ root_token,
@@ -34,100 +67,73 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
                   int *__restrict__ o_next_token, int *__restrict__ o_next_sibling) {
   extern __shared__ unsigned char smem[];
   const int M = k + (S - 1) * k * k;
-  const int R = 1 + (S - 1) * k;
-  float *s_score = reinterpret_cast<float *>(smem);
-  int *s_token = reinterpret_cast<int *>(s_score + M);
-  int *s_par = s_token + M;      // pool index of the parent, -1 = root
-  int *s_step = s_par + M;
-  int *s_row = s_step + M;       // draft row of the entry's children, -1
-  int *s_tree = s_row + M;       // tree index, -1 if not selected
+  float *s_tp = reinterpret_cast<float *>(smem);
+  int *s_tok = reinterpret_cast<int *>(s_tp + M);
+  float *s_score = reinterpret_cast<float *>(s_tok + M);
+  int *s_par = reinterpret_cast<int *>(s_score + M);   // pool index of the parent, -1 = root
+  int *s_row = s_par + M;                                // draft row of the entry's children, -1
+  int *s_tree = s_row + M;                               // tree index, -1 if not selected
   __shared__ int s_front[32];
   __shared__ int s_tpar[kMaxNodes];
   __shared__ uint32_t s_bits[kMaxNodes][kMaxWords];
-  __shared__ int s_scan[kTreeThreads];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  const float *tp = topk_p + static_cast<int64_t>(b) * R * k;
-  const int *ti = topk_id + static_cast<int64_t>(b) * R * k;
+  const float *tp = topk_p + static_cast<int64_t>(b) * M;
+  const int *ti = topk_id + static_cast<int64_t>(b) * M;
+  for (int e = tid; e < M; e += kTreeThreads) {
+    s_tp[e] = tp[e];
+    s_tok[e] = ti[e];
+    s_row[e] = -1;
+  }
+  const int L = prefix_len[b];
+  const int root = root_token[b];
+  __syncthreads();
 
-  // step 0: the root's children, in rank order they already form the frontier
+  // step 0: the root's children; their rank order is the first frontier
   for (int c = tid; c < k; c += kTreeThreads) {
-    s_score[c] = tp[c];
-    s_token[c] = ti[c];
+    s_score[c] = s_tp[c];
     s_par[c] = -1;
-    s_step[c] = 0;
-    s_row[c] = -1;
-    s_tree[c] = -1;
   }
   __syncthreads();
-  for (int c = tid; c < k; c += kTreeThreads) {
-    int r = 0;
-    for (int o = 0; o < k; ++o) r += beats(s_score, o, c);
-    s_front[r] = c;
-  }
+  for (int c = tid; c < k; c += kTreeThreads) s_front[rank_among(s_score, 0, k, c)] = c;
   __syncthreads();
 
   // steps 1 .. S-1: expand every frontier slot, keep the best k as the next frontier
   for (int i = 1; i < S; ++i) {
     const int base = k + (i - 1) * k * k;
     for (int x = tid; x < k * k; x += kTreeThreads) {
-      const int j = x / k, c = x % k;
-      const int f = s_front[j];
-      const int row = 1 + (i - 1) * k + j;
+      const int f = s_front[x / k];
       const int e = base + x;
-      s_score[e] = s_score[f] * tp[row * k + c];
-      s_token[e] = ti[row * k + c];
+      s_score[e] = s_score[f] * s_tp[e];
       s_par[e] = f;
-      s_step[e] = i;
-      s_row[e] = -1;
-      s_tree[e] = -1;
     }
     for (int j = tid; j < k; j += kTreeThreads) s_row[s_front[j]] = 1 + (i - 1) * k + j;
     __syncthreads();
     for (int x = tid; x < k * k; x += kTreeThreads) {
       const int e = base + x;
-      int r = 0;
-      for (int o = base; o < base + k * k; ++o) r += beats(s_score, o, e);
+      const int r = rank_among(s_score, base, k * k, e);
       if (r < k) s_front[r] = e;
     }
     __syncthreads();
   }
 
-  // final selection: the best N-1 pool entries
+  // final selection: the best N-1 pool entries, numbered in pool order
   const int per = (M + kTreeThreads - 1) / kTreeThreads;
   const int e0 = tid * per;
   int cnt = 0;
   for (int e = e0; e < min(M, e0 + per); ++e) {
-    int r = 0;
-    for (int o = 0; o < M; ++o) r += beats(s_score, o, e);
-    const bool sel = r < N - 1;
+    const bool sel = rank_among(s_score, 0, M, e) < N - 1;
     s_tree[e] = sel ? 1 : 0;
     cnt += sel;
   }
-  s_scan[tid] = cnt;
-  __syncthreads();
-  // inclusive Hillis-Steele scan of the per-thread counts
-  for (int off = 1; off < kTreeThreads; off <<= 1) {
-    const int add = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += add;
-    __syncthreads();
-  }
-  int t = 1 + s_scan[tid] - cnt;   // tree index of this thread's first selected entry
-  for (int e = e0; e < min(M, e0 + per); ++e) {
-    if (s_tree[e]) {
-      s_tree[e] = t++;
-    } else {
-      s_tree[e] = -1;
-    }
-  }
+  int t = 1 + block_exclusive_scan(cnt);   // tree index of this thread's first selected entry
+  for (int e = e0; e < min(M, e0 + per); ++e) s_tree[e] = s_tree[e] ? t++ : -1;
   __syncthreads();
 
   const int64_t ob = static_cast<int64_t>(b) * N;
-  const int L = prefix_len[b];
   if (tid == 0) {
-    o_tokens[ob] = root_token[b];
+    o_tokens[ob] = root;
     o_parent[ob] = -1;
     o_depth[ob] = 0;
     o_positions[ob] = L;
@@ -140,10 +146,11 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
     if (te < 0) continue;
     const int pe = s_par[e];
     const int tpar = pe < 0 ? 0 : s_tree[pe];   // -1 only if scores broke monotonicity
-    o_tokens[ob + te] = s_token[e];
+    const int step = e < k ? 0 : 1 + (e - k) / (k * k);
+    o_tokens[ob + te] = s_tok[e];
     o_parent[ob + te] = tpar;
-    o_depth[ob + te] = s_step[e] + 1;
-    o_positions[ob + te] = L + s_step[e] + 1;
+    o_depth[ob + te] = step + 1;
+    o_positions[ob + te] = L + step + 1;
     o_score[ob + te] = s_score[e];
     o_qrow[ob + te] = s_row[e];
     s_tpar[te] = tpar;
@@ -169,10 +176,11 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
     }
     int nt = -1, ns = -1;
     const int p = s_tpar[n];
+#pragma unroll 8
     for (int m = n + 1; m < N; ++m) {
       const int pm = s_tpar[m];
-      if (nt < 0 && pm == n) nt = m;
-      if (ns < 0 && p >= 0 && pm == p) ns = m;
+      nt = (nt < 0 && pm == n) ? m : nt;
+      ns = (ns < 0 && p >= 0 && pm == p) ? m : ns;
     }
     o_next_token[ob + n] = nt;
     o_next_sibling[ob + n] = ns;
@@ -213,7 +221,7 @@ extern "C" int32_t sdv_build_tree(sdv_tree_shape sh, const float *topk_p, const 
   SDV_REQUIRE(topk_p && topk_id && root_token && prefix_len && tokens && parent && depth && positions &&
                   score && q_row && retrieve_index && retrieve_next_token && retrieve_next_sibling,
               SDV_E_NULL, "build_tree: NULL pointer");
-  const size_t lds = static_cast<size_t>(M) * 6 * sizeof(int);
+  const size_t lds = static_cast<size_t>(M) * 6 * sizeof(int);   // tp, tok, score, par, row, tree
   hipLaunchKernelGGL(build_tree_kernel, dim3(sh.B), dim3(kTreeThreads), lds, as_stream(stream), sh.k,
                      sh.S, sh.N, topk_p, topk_id, root_token, prefix_len, tokens, parent, depth,
                      positions, score, q_row, mask, mask_bits, retrieve_index, retrieve_next_token,
