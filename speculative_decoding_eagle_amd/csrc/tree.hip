@@ -4,34 +4,52 @@
 // slots"), plus positions, the tree mask and the retrieve arrays
 // (zero-to-sglang ch.10 section 5.2).
 //
-// Latency-bound integer work: one 512-thread block per request keeps its
+// Latency-bound integer work: one 1024-thread block per request keeps its
 // top-k lists and the whole candidate pool in LDS.  Every selection (each step's frontier and the
 // final best N-1) is a rank computation under the strict order
 // (score desc, pool index asc): an entry's rank is the number of entries that
 // beat it, so ranks are unique and the result is deterministic.
+#include <climits>
+
 #include "common.hpp"
 
 namespace sdv {
 namespace {
 
-constexpr int kTreeThreads = 512;
+constexpr int kTreeThreads = 1024;
 constexpr int kTreeWaves = kTreeThreads / kWave;
 constexpr int kMaxPool = 2048;
 constexpr int kMaxNodes = 256;
 constexpr int kMaxWords = kMaxNodes / 32;
 
-// Rank of pool entry e among entries [lo, lo + n): the number that beat it
-// under (score desc, pool index asc).  Unrolled so that many LDS reads are in
-// flight; se stays in a register.
-__device__ __forceinline__ int rank_among(const float *sc, int lo, int n, int e) {
-  const float se = sc[e];
-  int r = 0;
-#pragma unroll 8
-  for (int o = lo; o < lo + n; ++o) {
-    const float so = sc[o];
-    r += (so > se) | ((so == se) & (o < e));
+// Order key of pool entry e: larger key = better under (score desc, pool
+// index asc).  The score's bits are mapped to an unsigned order (-0 is
+// folded into +0 first, so equal scores still tie on the index).
+__device__ __forceinline__ unsigned long long order_key(float score, int e) {
+  const unsigned u = __float_as_uint(score + 0.0f);
+  const unsigned su = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<unsigned long long>(su) << 32) | static_cast<unsigned>(~e);
+}
+
+// Ranks the n entries [lo, lo + n) among themselves (rank = how many beat
+// it).  g lanes share an entry (g a power of two, g * n <= threads, g <= 64)
+// and split its comparisons; f(e, rank) is called by the group's first lane.
+template <typename F>
+__device__ __forceinline__ void rank_block(const unsigned long long *key, int lo, int n, F f) {
+  int g = 1;
+  while (g < kWave && 2 * g * n <= kTreeThreads) g <<= 1;
+  const int per_pass = kTreeThreads / g;
+  for (int ent0 = 0; ent0 < n; ent0 += per_pass) {
+    const int ent = ent0 + static_cast<int>(threadIdx.x) / g, part = static_cast<int>(threadIdx.x) % g;
+    int r = 0;
+    if (ent < n) {
+      const unsigned long long ke = key[lo + ent];
+#pragma unroll 4
+      for (int o = lo + part; o < lo + n; o += g) r += key[o] > ke;
+    }
+    for (int off = 1; off < g; off <<= 1) r += __shfl_xor(r, off, kWave);
+    if (ent < n && part == 0) f(lo + ent, r);
   }
-  return r;
 }
 
 // Exclusive block scan of one int per thread.
@@ -67,7 +85,8 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
                   int *__restrict__ o_next_token, int *__restrict__ o_next_sibling) {
   extern __shared__ unsigned char smem[];
   const int M = k + (S - 1) * k * k;
-  float *s_tp = reinterpret_cast<float *>(smem);
+  unsigned long long *s_key = reinterpret_cast<unsigned long long *>(smem);
+  float *s_tp = reinterpret_cast<float *>(s_key + M);
   int *s_tok = reinterpret_cast<int *>(s_tp + M);
   float *s_score = reinterpret_cast<float *>(s_tok + M);
   int *s_par = reinterpret_cast<int *>(s_score + M);   // pool index of the parent, -1 = root
@@ -75,6 +94,7 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
   int *s_tree = s_row + M;                               // tree index, -1 if not selected
   __shared__ int s_front[32];
   __shared__ int s_tpar[kMaxNodes];
+  __shared__ int s_fc[kMaxNodes], s_ns[kMaxNodes];
   __shared__ uint32_t s_bits[kMaxNodes][kMaxWords];
 
   const int b = blockIdx.x;
@@ -94,9 +114,10 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
   for (int c = tid; c < k; c += kTreeThreads) {
     s_score[c] = s_tp[c];
     s_par[c] = -1;
+    s_key[c] = order_key(s_tp[c], c);
   }
   __syncthreads();
-  for (int c = tid; c < k; c += kTreeThreads) s_front[rank_among(s_score, 0, k, c)] = c;
+  rank_block(s_key, 0, k, [&](int e, int r) { s_front[r] = e; });
   __syncthreads();
 
   // steps 1 .. S-1: expand every frontier slot, keep the best k as the next frontier
@@ -105,28 +126,26 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
     for (int x = tid; x < k * k; x += kTreeThreads) {
       const int f = s_front[x / k];
       const int e = base + x;
-      s_score[e] = s_score[f] * s_tp[e];
+      const float sc = s_score[f] * s_tp[e];
+      s_score[e] = sc;
       s_par[e] = f;
+      s_key[e] = order_key(sc, e);
     }
     for (int j = tid; j < k; j += kTreeThreads) s_row[s_front[j]] = 1 + (i - 1) * k + j;
     __syncthreads();
-    for (int x = tid; x < k * k; x += kTreeThreads) {
-      const int e = base + x;
-      const int r = rank_among(s_score, base, k * k, e);
+    rank_block(s_key, base, k * k, [&](int e, int r) {
       if (r < k) s_front[r] = e;
-    }
+    });
     __syncthreads();
   }
 
   // final selection: the best N-1 pool entries, numbered in pool order
+  rank_block(s_key, 0, M, [&](int e, int r) { s_tree[e] = r < N - 1 ? 1 : 0; });
+  __syncthreads();
   const int per = (M + kTreeThreads - 1) / kTreeThreads;
   const int e0 = tid * per;
   int cnt = 0;
-  for (int e = e0; e < min(M, e0 + per); ++e) {
-    const bool sel = rank_among(s_score, 0, M, e) < N - 1;
-    s_tree[e] = sel ? 1 : 0;
-    cnt += sel;
-  }
+  for (int e = e0; e < min(M, e0 + per); ++e) cnt += s_tree[e];
   int t = 1 + block_exclusive_scan(cnt);   // tree index of this thread's first selected entry
   for (int e = e0; e < min(M, e0 + per); ++e) s_tree[e] = s_tree[e] ? t++ : -1;
   __syncthreads();
@@ -157,6 +176,21 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
   }
   __syncthreads();
 
+  // first child and next sibling: the smallest larger index with the node
+  // as parent / with the same parent, found over all (n, m) pairs
+  for (int n = tid; n < N; n += kTreeThreads) {
+    s_fc[n] = INT_MAX;
+    s_ns[n] = INT_MAX;
+  }
+  __syncthreads();
+  for (int x = tid; x < N * N; x += kTreeThreads) {
+    const int n = x / N, m = x % N;
+    if (m <= n) continue;
+    const int pm = s_tpar[m];
+    if (pm == n) atomicMin(&s_fc[n], m);
+    const int p = s_tpar[n];
+    if (p >= 0 && pm == p) atomicMin(&s_ns[n], m);
+  }
   const int W = (N + 31) / 32;
   for (int n = tid; n < N; n += kTreeThreads) {
     uint32_t bits[kMaxWords];
@@ -174,20 +208,14 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
       s_bits[n][w] = bits[w];
       if (o_bits && w < W) o_bits[(ob + n) * W + w] = bits[w];
     }
-    int nt = -1, ns = -1;
-    const int p = s_tpar[n];
-#pragma unroll 8
-    for (int m = n + 1; m < N; ++m) {
-      const int pm = s_tpar[m];
-      nt = (nt < 0 && pm == n) ? m : nt;
-      ns = (ns < 0 && p >= 0 && pm == p) ? m : ns;
-    }
-    o_next_token[ob + n] = nt;
-    o_next_sibling[ob + n] = ns;
     o_retrieve[ob + n] = static_cast<int>(ob + n);
   }
+  __syncthreads();
+  for (int n = tid; n < N; n += kTreeThreads) {
+    o_next_token[ob + n] = s_fc[n] == INT_MAX ? -1 : s_fc[n];
+    o_next_sibling[ob + n] = s_ns[n] == INT_MAX ? -1 : s_ns[n];
+  }
   if (o_mask) {
-    __syncthreads();
     for (int x = tid; x < N * N; x += kTreeThreads) {
       const int r = x / N, c = x % N;
       o_mask[ob * N + x] = static_cast<uint8_t>((s_bits[r][c / 32] >> (c % 32)) & 1u);
@@ -221,7 +249,7 @@ extern "C" int32_t sdv_build_tree(sdv_tree_shape sh, const float *topk_p, const 
   SDV_REQUIRE(topk_p && topk_id && root_token && prefix_len && tokens && parent && depth && positions &&
                   score && q_row && retrieve_index && retrieve_next_token && retrieve_next_sibling,
               SDV_E_NULL, "build_tree: NULL pointer");
-  const size_t lds = static_cast<size_t>(M) * 6 * sizeof(int);   // tp, tok, score, par, row, tree
+  const size_t lds = static_cast<size_t>(M) * (6 * sizeof(int) + sizeof(uint64_t));   // key, tp, tok, score, par, row, tree
   hipLaunchKernelGGL(build_tree_kernel, dim3(sh.B), dim3(kTreeThreads), lds, as_stream(stream), sh.k,
                      sh.S, sh.N, topk_p, topk_id, root_token, prefix_len, tokens, parent, depth,
                      positions, score, q_row, mask, mask_bits, retrieve_index, retrieve_next_token,
