@@ -242,6 +242,9 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   auto dma_tile = [&](int t) {
     const uint32_t kst = lds0 + (t & (kStages - 1)) * C::STAGE;
     const int wbase = ((t / win_tiles) * win_tiles * kTile) >> pshift;
+    // all K instructions of the tile first, then all V: the waits count on
+    // that order (K(t) landed = everything up to the tile's last K)
+    const void *ka[C::IPW], *va[C::IPW];
 #pragma unroll
     for (int i = 0; i < C::IPW; ++i) {
       const int pos = t * kTile + dma_row[i];
@@ -251,12 +254,15 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       const unsigned slot = (static_cast<unsigned>(pid) << pshift) + static_cast<unsigned>(pos & pmask);
       const bool ok = (pos < total) & (static_cast<unsigned>(pid) <= pid_max) & (slot < nslots);
       const uint32_t off = slot * static_cast<uint32_t>(row_chunks) + dma_col[i];
-      const void *ka = ok ? static_cast<const void *>(kp16 + off) : static_cast<const void *>(g_zero16);
-      const void *va = ok ? static_cast<const void *>(vp16 + off) : static_cast<const void *>(g_zero16);
-      const uint32_t lrow = (wave * 8 + i * C::KPI) * C::ROW;     // first row of this 1 KB block
-      dma16(ka, __builtin_amdgcn_readfirstlane(kst + lrow));
-      dma16(va, __builtin_amdgcn_readfirstlane(kst + C::TILE_BYTES + lrow));
+      ka[i] = ok ? static_cast<const void *>(kp16 + off) : static_cast<const void *>(g_zero16);
+      va[i] = ok ? static_cast<const void *>(vp16 + off) : static_cast<const void *>(g_zero16);
     }
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i)
+      dma16(ka[i], __builtin_amdgcn_readfirstlane(kst + (wave * 8 + i * C::KPI) * C::ROW));
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i)
+      dma16(va[i], __builtin_amdgcn_readfirstlane(kst + C::TILE_BYTES + (wave * 8 + i * C::KPI) * C::ROW));
   };
 
   // Lane parts of the LDS fragment addresses (per stage: + stage base).
@@ -317,7 +323,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   // MASKED: tile t reaches past the prefix, so the tree mask applies.
   auto tile_step = [&](int t, auto MASKED) {
     constexpr bool masked = decltype(MASKED)::value;
-    wait_vmcnt<3 * C::IPW>();            // this wave's DMAs through K(t+1) are done
+    wait_vmcnt<3 * C::IPW>();            // this wave's DMAs through K(t+1) are done (V(t+1), tile t+2 may fly)
     __syncthreads();                     // everyone's are; and stage (t+3)%4 is no longer read
     if (t + 3 < ntiles && (t + 3) % win_tiles == 0) {   // block-uniform: next page window
       refresh_pages(t + 3);
