@@ -11,8 +11,10 @@
 // 32 x D fp32 accumulator and two row blocks of Q fragments in registers.
 //   * K and V tiles go from the paged pool straight into LDS with
 //     global_load_lds_dwordx4 (16 bytes per lane, a wave fills 1 KB per
-//     instruction) through a ring of four stages: while tile t is computed,
-//     tiles t+1 .. t+3 are in flight.  No registers stage the data.
+//     instruction) through a ring of four K tiles and a ring of four V
+//     tiles, the K stream one tile ahead (the scores of tile t+1 are computed
+//     while tile t's softmax runs): every tile's K and V get three steps to
+//     arrive.  No registers stage the data.
 //   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled per row so that
 //     the MFMA fragment reads below hit distinct banks.
 //   * S^T = K Q^T on bf16 MFMA 16x16x32.  O^T += V^T P^T on MFMA 16x16x16
@@ -66,8 +68,7 @@ struct AttnCfg {
   static constexpr int DS = D / 32;                       // k-steps of QK^T
   static constexpr int NO = D / 16;                       // 16-wide d blocks of O^T per row block
   static constexpr int TILE_BYTES = kTile * ROW;
-  static constexpr int STAGE = 2 * TILE_BYTES;            // K then V
-  static constexpr int SMEM = kStages * STAGE;            // also holds the fp32 merge buffer
+  static constexpr int SMEM = 2 * kStages * TILE_BYTES;  // K ring, V ring; also holds the fp32 merge buffer
   static_assert(kRows * D * 4 <= SMEM, "merge buffer must fit");
 };
 
@@ -239,12 +240,12 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   const uint4 *kp16 = reinterpret_cast<const uint4 *>(kpool);
   const uint4 *vp16 = reinterpret_cast<const uint4 *>(vpool);
   const uint32_t lds0 = lds_offset(smem);
-  auto dma_tile = [&](int t) {
-    const uint32_t kst = lds0 + (t & (kStages - 1)) * C::STAGE;
+  // LDS: a ring of four K tiles, then a ring of four V tiles.
+  auto kbase = [&](int t) { return lds0 + (t & (kStages - 1)) * C::TILE_BYTES; };
+  auto vbase = [&](int t) { return lds0 + (kStages + (t & (kStages - 1))) * C::TILE_BYTES; };
+  // Pool addresses of this lane's chunks of tile t (K and V share them).
+  auto tile_addr = [&](int t, const void *(&ka)[C::IPW], const void *(&va)[C::IPW]) {
     const int wbase = ((t / win_tiles) * win_tiles * kTile) >> pshift;
-    // all K instructions of the tile first, then all V: the waits count on
-    // that order (K(t) landed = everything up to the tile's last K)
-    const void *ka[C::IPW], *va[C::IPW];
 #pragma unroll
     for (int i = 0; i < C::IPW; ++i) {
       const int pos = t * kTile + dma_row[i];
@@ -257,12 +258,11 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       ka[i] = ok ? static_cast<const void *>(kp16 + off) : static_cast<const void *>(g_zero16);
       va[i] = ok ? static_cast<const void *>(vp16 + off) : static_cast<const void *>(g_zero16);
     }
+  };
+  auto issue = [&](uint32_t stage, const void *(&ga)[C::IPW]) {
 #pragma unroll
     for (int i = 0; i < C::IPW; ++i)
-      dma16(ka[i], __builtin_amdgcn_readfirstlane(kst + (wave * 8 + i * C::KPI) * C::ROW));
-#pragma unroll
-    for (int i = 0; i < C::IPW; ++i)
-      dma16(va[i], __builtin_amdgcn_readfirstlane(kst + C::TILE_BYTES + (wave * 8 + i * C::KPI) * C::ROW));
+      dma16(ga[i], __builtin_amdgcn_readfirstlane(stage + (wave * 8 + i * C::KPI) * C::ROW));
   };
 
   // Lane parts of the LDS fragment addresses (per stage: + stage base).
@@ -278,12 +278,12 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
     const int vr = 32 * kh + 16 * k2 + 4 * g4 + (l16 >> 2);
 #pragma unroll
     for (int db = 0; db < C::NO; ++db)
-      voff[k2][db] = C::TILE_BYTES + vr * C::ROW + (((2 * db + ((l16 & 3) >> 1)) ^ swz<D>(vr)) << 4) + ((l16 & 1) << 3);
+      voff[k2][db] = vr * C::ROW + (((2 * db + ((l16 & 3) >> 1)) ^ swz<D>(vr)) << 4) + ((l16 & 1) << 3);
   }
 
   // ---- S^T of tile t: A = K[key][d] (LDS), B = Q^T (registers)
   auto scores = [&](int t, f32x4 (&sc)[KB][RB]) {
-    const uint32_t base = lds0 + (t & (kStages - 1)) * C::STAGE;
+    const uint32_t base = kbase(t);
 #pragma unroll
     for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
@@ -305,33 +305,45 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   // the Q fragments and the page copy land here once, not inside the key loop
   __builtin_amdgcn_s_waitcnt(0);
   f32x4 s[KB][RB];
+  // DMA schedule: K runs one tile ahead of V.  Step t issues K(t+4) and
+  // V(t+3) (in that order); K(t+1) and V(t), which step t consumes, went out
+  // together three steps earlier.  K(t+4) lands in the K slot that tile t's
+  // scores (step t-1) last read, V(t+3) in the V slot of tile t-1's PV.
+  const void *ka[C::IPW], *va[C::IPW], *va_next[C::IPW];
   if (ntiles > 0) {
-    dma_tile(0);
-    dma_tile(1);
-    dma_tile(2);
-    wait_vmcnt<4 * C::IPW>();            // tile 0 is in
+    tile_addr(0, ka, va);
+    issue(kbase(0), ka);
+#pragma unroll
+    for (int t0 = 1; t0 <= 3; ++t0) {
+      tile_addr(t0, ka, va_next);
+      issue(kbase(t0), ka);
+      issue(vbase(t0 - 1), va);
+#pragma unroll
+      for (int i = 0; i < C::IPW; ++i) va[i] = va_next[i];
+    }
+    wait_vmcnt<6 * C::IPW>();            // K(0) is in
     __syncthreads();
     scores(0, s);
   }
 
   // Step t: softmax and PV of tile t, with the scores of tile t+1 computed
-  // first so that their MFMAs run under the softmax's VALU work.  Tile t
-  // sits in stage t % 4; tile t+3 goes to stage (t+3) % 4, whose K was last
-  // read for tile t-1's scores and whose V for tile t-1's PV (both done by
-  // every wave at this step's barrier).  DMAs go out as K(t), V(t) per step,
-  // so K(t+1) being in means V(t) is in too.
+  // first so that their MFMAs run under the softmax's VALU work.
   // MASKED: tile t reaches past the prefix, so the tree mask applies.
   auto tile_step = [&](int t, auto MASKED) {
     constexpr bool masked = decltype(MASKED)::value;
-    wait_vmcnt<3 * C::IPW>();            // this wave's DMAs through K(t+1) are done (V(t+1), tile t+2 may fly)
-    __syncthreads();                     // everyone's are; and stage (t+3)%4 is no longer read
-    if (t + 3 < ntiles && (t + 3) % win_tiles == 0) {   // block-uniform: next page window
-      refresh_pages(t + 3);
+    wait_vmcnt<4 * C::IPW>();            // this wave's K(t+1), V(t) are in (steps t-2, t-1 may fly)
+    __syncthreads();                     // everyone's are; and the slots refilled below are no longer read
+    if (t + 4 < ntiles && (t + 4) % win_tiles == 0) {   // block-uniform: next page window
+      refresh_pages(t + 4);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    dma_tile(t + 3);
-    const uint32_t base = lds0 + (t & (kStages - 1)) * C::STAGE;
+    tile_addr(t + 4, ka, va_next);
+    issue(kbase(t + 4), ka);
+    issue(vbase(t + 3), va);
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) va[i] = va_next[i];
+    const uint32_t base = vbase(t);
 
     // ---- mask, row max and the (rare) rescale of the running state
     // (lane: its row per rb; keys 16*k2 + 4*g4 + i)
@@ -386,7 +398,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
     // (computed even past the last tile: the stage holds in-bounds data and
     // they go unused) are interleaved with the exponentials of tile t; then
     // O^T += V^T P^T with each pair of V reads issued one block ahead.
-    const uint32_t nbase = lds0 + ((t + 1) & (kStages - 1)) * C::STAGE;
+    const uint32_t nbase = kbase(t + 1);
     bf16x8 kf[KB][C::DS];
 #pragma unroll
     for (int k2 = 0; k2 < KB; ++k2)
