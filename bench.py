@@ -231,9 +231,9 @@ MEASURED_TRAFFIC = {
     "tree_attention": {
         "workload": "c3",
         "source": "speculative_decoding_eagle_amd/csrc/attn.hip",
-        "sha256": "ebfb0fbe01539b9422ce66fb59c39476ecba49f9592bf530c0e1d7c78b42d46d",
-        "fetch_kib": 183413.4, "fetch_factor": 1.99996,
-        "write_kib": 17408.0, "write_factor": 1.0,
+        "sha256": "ac59c472806bcf90bc6c4f0df1b18801da1de49ae492a6a62038508ecc0ed730",
+        "fetch_kib": 183102.8, "fetch_factor": 1.99996,
+        "write_kib": 16384.0, "write_factor": 1.0,
     },
 }
 
