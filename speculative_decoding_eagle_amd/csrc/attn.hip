@@ -17,13 +17,15 @@
 //     arrive.  No registers stage the data.
 //   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled per row so that
 //     the MFMA fragment reads below hit distinct banks.
-//   * S^T = K Q^T on bf16 MFMA 16x16x32.  O^T += V^T P^T on MFMA 16x16x16
-//     with each V^T operand fetched by one transposing LDS read
-//     (ds_read_b64_tr_b16); P is rounded to bf16.
+//   * S^T = K Q^T and O^T += V^T P^T on bf16 MFMA 16x16x32; each V^T
+//     operand is two transposing LDS reads (ds_read_b64_tr_b16), P is
+//     rounded to bf16.  The scores of tile t+1 are issued interleaved with
+//     the exponentials of tile t (a fixed issue order).
 //   * Every lane keeps the softmax state of its own query row; scores are
 //     scaled into log2 units and exponentiated with exp2; the reference max
 //     moves only when a score exceeds it by more than 2^8, so the O rescale
-//     is rare.
+//     is rare.  Row maxima and sums cross lanes with the row-half swap
+//     instructions, not LDS permutes.
 //   * Page ids come from an LDS copy of the request's page-table row,
 //     refreshed once per window of kPageCache pages.
 //   * The two key-half waves of a row quarter are merged through LDS in a
@@ -42,13 +44,12 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kAttnThreads = 512;
 constexpr int kRows = 128;          // query rows per block
 constexpr int kTile = 64;           // key positions per tile
-constexpr int kStages = 4;          // LDS ring: three tiles in flight
+constexpr int kStages = 4;          // tiles per LDS ring (one ring for K, one for V)
 constexpr int kXcds = 8;
 constexpr int kPageCache = 4096;    // page-table entries cached in LDS
 
@@ -92,6 +93,27 @@ __device__ __forceinline__ int swz(int r) {
 // (wait_vmcnt) and the memory clobber keeps LDS reads from moving across.
 __device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Lane l's value combined with lane l^16's (l^32's): the row-half swap
+// instructions hand every lane the pair {x[l], x[l^16]} ({x[l], x[l^32]}).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
@@ -373,8 +395,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
       }
       float rmax = fmaxf(fmaxf(fmaxf(v[rb][0][0], v[rb][0][1]), fmaxf(v[rb][0][2], v[rb][0][3])),
                          fmaxf(fmaxf(v[rb][1][0], v[rb][1][1]), fmaxf(v[rb][1][2], v[rb][1][3])));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 16, kWave));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
+      rmax = max_xor32(max_xor16(rmax));
       const float tmax = rmax * scale_log2;
       const bool need = tmax > m_run[rb] + 8.0f;
       if (__any(need)) {
@@ -482,8 +503,7 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float lt = l_run[rb];
-    lt += __shfl_xor(lt, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
+    lt = sum_xor32(sum_xor16(lt));
     if (g4 == 0) {
       s_m[kh][32 * rh + 16 * rb + l16] = m_run[rb];
       s_l[kh][32 * rh + 16 * rb + l16] = lt;
