@@ -231,8 +231,8 @@ MEASURED_TRAFFIC = {
     "tree_attention": {
         "workload": "c3",
         "source": "speculative_decoding_eagle_amd/csrc/attn.hip",
-        "sha256": "ac59c472806bcf90bc6c4f0df1b18801da1de49ae492a6a62038508ecc0ed730",
-        "fetch_kib": 183102.8, "fetch_factor": 1.99996,
+        "sha256": "c03bcb8aa03eab0af2aee44001d1a30d86de9013967ed4258b3d04a66896bc76",
+        "fetch_kib": 182761.3, "fetch_factor": 1.99996,
         "write_kib": 16384.0, "write_factor": 1.0,
     },
 }
