@@ -128,10 +128,18 @@ int32_t sdv_build_tree(sdv_tree_shape shape, const float *topk_p, const int32_t 
  * out: device [B, N, Hq, D] bf16; lse: device [B, N, Hq] fp32 natural-log
  * sum of exp(sm_scale * q.k) (NULL to skip).  sm_scale <= 0 selects
  * 1/sqrt(D).  Limits: D in {64, 128}, 1 <= N <= 256, Hq % Hkv == 0,
- * Hq/Hkv <= 16, page a power of two, num_slots + page < 2^31 and
- * num_slots * Hkv * D * 2 < 2^36 bytes per pool.  Keys whose page id falls
- * outside the pool are skipped.  The call needs no workspace: the size query returns
- * 0 and ws may be NULL (the arguments stay for a stable ABI).
+ * Hq/Hkv <= 16, page a power of two, 1 <= num_slots, num_slots + page < 2^31
+ * and num_slots * Hkv * D * 2 < 2^36 bytes per pool.  A page id outside the
+ * pool is an input error: no read leaves the pools and the outputs of the
+ * rows that see such a key are unspecified.
+ * Workspace: when N * Hq/Hkv > 128 (and B * Hkv * ceil(N * Hq/Hkv / 256) <=
+ * 4096) the size query returns the bytes with which a call may split each
+ * unit's keys over two workgroups (few units, many CUs).  ws must then be
+ * 256-byte aligned and zero-filled once before its first use: its first
+ * 32 KiB hold counters that every call leaves at zero, whatever the shape,
+ * and the rest is scratch.  Calls that may overlap need separate
+ * workspaces.  ws = NULL (or fewer bytes) runs without the split.
+ * Otherwise the size query returns 0 and ws is ignored.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t B, N, Hq, Hkv, D, page, max_pages;

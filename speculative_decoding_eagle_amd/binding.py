@@ -129,9 +129,28 @@ def sdv_build_tree(topk_p, topk_id, root_token, prefix_len, k: int, S: int, N: i
 
 # ---------------------------------------------------------------------- A5
 
+_ATTN_WS = {}
+
+
+def _attn_workspace(nbytes: int, device) -> torch.Tensor:
+    """Zero-filled attention workspace, one per (device, stream): every call
+    leaves it zero-filled again, so it is cleared once, when allocated."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    buf = _ATTN_WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _ATTN_WS[key] = buf
+    return buf
+
+
 def sdv_tree_verify_attention(q, k_pool, v_pool, page_table, prefix_len, mask_bits, page: int = 1,
-                              sm_scale: float = 0.0, out=None, lse=None, want_lse: bool = False, ws=None):
-    """Tree-masked attention; returns (out [B,N,Hq,D] bf16, lse or None)."""
+                              sm_scale: float = 0.0, out=None, lse=None, want_lse: bool = False, ws=None,
+                              split_keys: bool = True):
+    """Tree-masked attention; returns (out [B,N,Hq,D] bf16, lse or None).
+
+    ``ws``: a zero-filled workspace of the size query's bytes (kept
+    zero-filled by the calls); by default a cached one.  ``split_keys=False``
+    passes no workspace, which runs without the key split."""
     B, N, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     dev = q.device
@@ -141,12 +160,19 @@ def sdv_tree_verify_attention(q, k_pool, v_pool, page_table, prefix_len, mask_bi
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
     shape = AttnShape(B, N, Hq, Hkv, D, page, page_table.shape[1], k_pool.shape[0])
     L = _lib.lib()
-    wp, wb = _workspace(L.sdv_tree_verify_attention_workspace_size(shape), dev, ws)
+    need = L.sdv_tree_verify_attention_workspace_size(shape)
+    if not split_keys or need == 0:
+        wp, wb = 0, 0
+    else:
+        if ws is None:
+            ws = _attn_workspace(need, dev)
+        wp, wb = _workspace(need, dev, ws)
     _check(L.sdv_tree_verify_attention(
         shape, float(sm_scale), _ptr(q, BF16, "q"), _ptr(k_pool, BF16, "k_pool"), _ptr(v_pool, BF16, "v_pool"),
         _ptr(page_table, torch.int32, "page_table"), _ptr(prefix_len, torch.int32, "prefix_len"),
         _ptr(mask_bits, (torch.int32, torch.uint32), "mask_bits"), _ptr(out, BF16, "out"),
         _ptr(lse, torch.float32, "lse", allow_none=True), wp, wb, _stream(dev)), "sdv_tree_verify_attention")
+    _keep(ws)
     return out, lse
 
 

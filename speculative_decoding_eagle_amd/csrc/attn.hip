@@ -34,125 +34,20 @@
 // first) and takes its unit by rank; blocks are dealt round-robin over the 8 XCDs, so units are
 // interleaved over XCDs in that order while the row blocks of one unit stay
 // on one XCD and share its L2.
-#include <cmath>
 #include <type_traits>
 
-#include "common.hpp"
+#include "attn_common.hpp"
 
 namespace sdv {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-
-constexpr int kAttnThreads = 512;
 constexpr int kRows = 128;          // query rows per block
-constexpr int kTile = 64;           // key positions per tile
-constexpr int kStages = 4;          // tiles per LDS ring (one ring for K, one for V)
-constexpr int kXcds = 8;
-constexpr int kPageCache = 4096;    // page-table entries cached in LDS
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);   // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
 
 template <int D>
-struct AttnCfg {
-  static constexpr int ROW = 2 * D;                       // bytes per key row
-  static constexpr int CHUNKS = D / 8;                    // 16-byte chunks per row
-  static constexpr int KPI = 64 / CHUNKS;                 // key rows per DMA instruction (1 KB)
-  static constexpr int IPW = 8 / KPI;                     // DMA instructions per wave per tile and tensor
-  static constexpr int DS = D / 32;                       // k-steps of QK^T
-  static constexpr int NO = D / 16;                       // 16-wide d blocks of O^T per row block
-  static constexpr int TILE_BYTES = kTile * ROW;
-  static constexpr int SMEM = 2 * kStages * TILE_BYTES;  // K ring, V ring; also holds the fp32 merge buffer
+struct AttnCfg : KvTile<D> {
+  static constexpr int SMEM = KvTile<D>::RINGS;           // K ring, V ring; also holds the fp32 merge buffer
   static_assert(kRows * D * 4 <= SMEM, "merge buffer must fit");
 };
-
-// Chunk swizzle of key row r: the 16 rows read by one quarter-wave map a
-// fixed chunk to 16 distinct chunks (K fragments), and rows r, r+4 land in
-// different halves of the row (V words).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) {
-    r &= 15;
-    return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
-  } else {
-    return (r >> 1) & 7;
-  }
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane L writes LDS
-// bytes lds_addr + 16*L .. +15 (lds_addr is wave-uniform, via M0).  Issued
-// as inline assembly so that the compiler does not add its conservative
-// "wait for every LDS DMA before any LDS read"; the kernel waits explicitly
-// (wait_vmcnt) and the memory clobber keeps LDS reads from moving across.
-__device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
-}
-
-// Lane l's value combined with lane l^16's (l^32's): the row-half swap
-// instructions hand every lane the pair {x[l], x[l^16]} ({x[l], x[l^32]}).
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
-  return a > b ? a : b;
-}
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
-  return a > b ? a : b;
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
-}
-
-// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Source of the DMA for key positions outside the request: 256 zero bytes,
-// never written.
-__device__ __attribute__((aligned(256))) uint16_t g_zero16[128];
-
-constexpr int kRankMax = 1024;      // requests ranked in-kernel; larger batches keep their order
-
-// The request of rank r when requests are ranked by prefix length (longest
-// first, then lower index).  Every block ranks the (small) batch itself from
-// an LDS copy of the prefix lengths; s_len is LDS scratch of B ints.
-__device__ int request_of_rank(int r, int B, const int *__restrict__ prefix_len, int *s_len, int *s_pick) {
-  if (B > kRankMax) return r;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < B; i += kAttnThreads) s_len[i] = prefix_len[i];
-  __syncthreads();
-  for (int c = tid; c < B; c += kAttnThreads) {
-    const int Lc = s_len[c];
-    int rk = 0;
-    for (int o = 0; o < B; ++o) {
-      const int Lo = s_len[o];
-      rk += (Lo > Lc) | ((Lo == Lc) & (o < c));
-    }
-    if (rk == r) *s_pick = c;
-  }
-  __syncthreads();
-  return *s_pick;
-}
 
 template <int D>
 __global__ void __launch_bounds__(kAttnThreads, 2)
@@ -195,8 +90,8 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   const int *trow = table + static_cast<int64_t>(b) * max_pages;
   const bool req_ok = L >= 0 && static_cast<int64_t>(total) <= (static_cast<int64_t>(max_pages) << pshift);
   const int ntiles = req_ok ? (total + kTile - 1) / kTile : 0;
-  const int total_pages = (total + pmask) >> pshift;
-  const int win_tiles = (kPageCache << pshift) / kTile;     // tiles covered by one page window
+  const int total_pages = req_ok ? (total + pmask) >> pshift : 0;   // page-table entries the request owns
+  const int win_tiles = pshift >= 19 ? (1 << 30) : (kPageCache << pshift) / kTile;   // tiles per page window
 
   const int row0 = rblk * kRows;
   const int node0 = row0 / G;
@@ -602,9 +497,17 @@ int32_t launch_attn(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, in
 
 using namespace sdv;
 
+// Units of more than kRows query rows go to the wide kernel; its key split
+// needs a workspace (sized for the split whether or not a call uses it).
+static int wide_row_blocks(const sdv_attn_shape &sh) {
+  const int rows = sh.N * (sh.Hq / sh.Hkv);
+  return rows > kRows ? (rows + 255) / 256 : 0;
+}
+
 extern "C" size_t sdv_tree_verify_attention_workspace_size(sdv_attn_shape sh) {
-  (void)sh;
-  return 0;
+  if (sh.B <= 0 || sh.N < 1 || sh.Hkv < 1 || sh.Hq % sh.Hkv != 0 || (sh.D != 64 && sh.D != 128)) return 0;
+  const int nrb = wide_row_blocks(sh);
+  return nrb ? attn_wide_workspace(static_cast<int64_t>(sh.B) * sh.Hkv * nrb, sh.D) : 0;
 }
 
 extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, const uint16_t *q,
@@ -628,21 +531,33 @@ extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, 
   SDV_REQUIRE(reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(k_pool) % 16 == 0 &&
                   reinterpret_cast<uintptr_t>(v_pool) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0,
               SDV_E_SHAPE, "tree_verify_attention: q, pools and out must be 16-byte aligned");
-  (void)ws;
-  (void)ws_bytes;
+  SDV_REQUIRE(sh.num_slots >= 1, SDV_E_SHAPE, "tree_verify_attention: empty pool");
   int pshift = 0;
   while ((1 << pshift) < sh.page) ++pshift;
+  SDV_REQUIRE(sh.num_slots + sh.page < (1LL << 31) && sh.num_slots * sh.Hkv * (sh.D / 8) < (1LL << 32),
+              SDV_E_UNSUPPORTED, "tree_verify_attention: pool too large (2^31 slots, 2^32 16-byte chunks)");
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(sh.D));
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t st = as_stream(stream);
+  const int wide_nrb = wide_row_blocks(sh);
+  if (wide_nrb > 0) {
+    // split each unit's keys over two workgroups when units alone leave CUs
+    // idle and the caller gave the workspace the split needs
+    const int64_t slots = static_cast<int64_t>(sh.B) * sh.Hkv * wide_nrb;
+    const size_t need = attn_wide_workspace(slots, sh.D);
+    const bool has_ws = need > 0 && ws && ws_bytes >= need;
+    const int nch = has_ws && slots < 2LL * num_cus() ? 2 : 1;
+    SDV_REQUIRE(nch == 1 || reinterpret_cast<uintptr_t>(ws) % 256 == 0, SDV_E_WORKSPACE,
+                "tree_verify_attention: workspace must be 256-byte aligned");
+    return launch_attn_wide(st, sh, pshift, scale_log2, wide_nrb, nch, q, k_pool, v_pool, page_table, prefix_len,
+                            mask_bits, out, lse, ws);
+  }
   const int G = sh.Hq / sh.Hkv;
   const int nrb = (sh.N * G + kRows - 1) / kRows;
   const int64_t units = static_cast<int64_t>(sh.B) * sh.Hkv;
   const int64_t units_pad = (units + kXcds - 1) / kXcds * kXcds;
   const int64_t blocks = units_pad * nrb;
   SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tree_verify_attention: grid too large");
-  SDV_REQUIRE(sh.num_slots + sh.page < (1LL << 31) && sh.num_slots * sh.Hkv * (sh.D / 8) < (1LL << 32),
-              SDV_E_UNSUPPORTED, "tree_verify_attention: pool too large (2^31 slots, 2^32 16-byte chunks)");
-  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(sh.D));
-  const float scale_log2 = scale * 1.4426950408889634f;
-  hipStream_t st = as_stream(stream);
   int32_t rc;
   if (sh.D == 64)
     rc = launch_attn<64>(blocks, st, sh, pshift, scale_log2, nrb, q, k_pool, v_pool, page_table, prefix_len,

@@ -1,0 +1,160 @@
+// Pieces shared by the two tree-verify attention kernels (attn.hip: units of
+// up to 128 query rows; attn_wide.hip: wider units, keys split over
+// workgroups): fragment types, the LDS chunk swizzle, the LDS-DMA issue,
+// cross-lane reductions and the in-kernel longest-first request ranking.
+#pragma once
+
+#include <cmath>
+
+#include "common.hpp"
+
+namespace sdv {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kAttnThreads = 512;   // eight waves per workgroup (both kernels)
+constexpr int kTile = 64;           // key positions per tile
+constexpr int kStages = 4;          // tiles per LDS ring (one ring for K, one for V)
+constexpr int kXcds = 8;
+constexpr int kPageCache = 4096;    // page-table entries cached in LDS
+constexpr int kRankMax = 1024;      // requests ranked in-kernel; larger batches keep their order
+
+// Per head dimension: bytes and 16-byte chunks of a key row, and how the
+// eight waves split one tile's DMA (wave w moves key rows 8w .. 8w+7).
+template <int D>
+struct KvTile {
+  static constexpr int ROW = 2 * D;                       // bytes per key row
+  static constexpr int CHUNKS = D / 8;                    // 16-byte chunks per row
+  static constexpr int KPI = 64 / CHUNKS;                 // key rows per DMA instruction (1 KB)
+  static constexpr int IPW = 8 / KPI;                     // DMA instructions per wave per tile and tensor
+  static constexpr int DS = D / 32;                       // k-steps of QK^T
+  static constexpr int NO = D / 16;                       // 16-wide d blocks of O^T per row block
+  static constexpr int TILE_BYTES = kTile * ROW;
+  static constexpr int RINGS = 2 * kStages * TILE_BYTES;  // K ring, then V ring
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);   // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Chunk swizzle of key row r (depends on r % 16 only): the 16 rows read by
+// one quarter-wave map a fixed chunk to 16 distinct chunks (K fragments),
+// and rows r, r+4 land in different halves of the row (V words).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    r &= 15;
+    return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
+  } else {
+    return (r >> 1) & 7;
+  }
+}
+
+// 4 bytes per lane from global memory straight into LDS (lane L writes LDS
+// bytes lds_addr + 4*L .. +3); same conventions as dma16 below.
+__device__ __forceinline__ void dma4(const void *gaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
+}
+
+// As dma16, addressed as a 64-bit base in scalar registers plus this
+// lane's 32-bit byte offset.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane L writes LDS
+// bytes lds_addr + 16*L .. +15 (lds_addr is wave-uniform, via M0).  Issued
+// as inline assembly so that the compiler does not add its conservative
+// "wait for every LDS DMA before any LDS read"; the kernels wait explicitly
+// (wait_vmcnt) and the memory clobber keeps LDS reads from moving across.
+__device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
+}
+
+// IEEE-754-2019 maximum (NaN propagates): one v_maximum3_f32 on gfx950,
+// with no NaN-quieting of its inputs in front of it as fmaxf needs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Lane l's value combined with lane l^16's (l^32's): the row-half swap
+// instructions hand every lane the pair {x[l], x[l^16]} ({x[l], x[l^32]}).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
+}
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+namespace {
+// Source of the DMA for key positions outside the request: 256 zero bytes,
+// never written.
+__device__ __attribute__((aligned(256))) uint16_t g_zero16[128];
+}  // namespace
+
+// The request of rank r when requests are ranked by prefix length (longest
+// first, then lower index).  Every block ranks the (small) batch itself from
+// an LDS copy of the prefix lengths; s_len is LDS scratch of B ints.
+__device__ __forceinline__ int request_of_rank(int r, int B, const int *__restrict__ prefix_len, int *s_len,
+                                               int *s_pick) {
+  if (B > kRankMax) return r;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < B; i += kAttnThreads) s_len[i] = prefix_len[i];
+  __syncthreads();
+  for (int c = tid; c < B; c += kAttnThreads) {
+    const int Lc = s_len[c];
+    int rk = 0;
+    for (int o = 0; o < B; ++o) {
+      const int Lo = s_len[o];
+      rk += (Lo > Lc) | ((Lo == Lc) & (o < c));
+    }
+    if (rk == r) *s_pick = c;
+  }
+  __syncthreads();
+  return *s_pick;
+}
+
+// The wide kernel's workspace starts with a fixed region of counters (two
+// per unit), the same for every shape, so that what one call leaves there
+// (zeros) is what any later call expects; the partial results follow.
+constexpr int kAttnSyncWords = 8192;
+
+// Workspace of the wide kernel for `slots` (request, KV head, row block)
+// units when its keys are split over two workgroups; 0 when the split is not
+// offered (more than kAttnSyncWords / 2 units).
+size_t attn_wide_workspace(int64_t slots, int D);
+
+// Launches the wide kernel (query rows per unit above 128).  nch: workgroups
+// per unit that split its keys (1 or 2); ws: attn_wide_workspace bytes,
+// zero-filled before first use (calls leave it zero-filled).
+int32_t launch_attn_wide(hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb, int nch,
+                         const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                         const int32_t *page_table, const int32_t *prefix_len, const uint32_t *mask_bits,
+                         uint16_t *out, float *lse, void *ws);
+
+}  // namespace sdv

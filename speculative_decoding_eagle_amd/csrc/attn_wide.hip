@@ -1,0 +1,667 @@
+// A5 for units of more than 128 query rows: tree-verify attention -- one
+// target pass over the prefix plus the candidate tree under the tree mask
+// ("EAGLE speculative decoding in four parts", "Self-test" answer 1,
+// "Exercises" question 1 and "Design trade-offs"; "[SGLang] Multi-Layer
+// EAGLE" section 6, TARGET_VERIFY).  Same operation and arguments as the
+// kernel in attn.hip, another work layout.
+//
+// Work layout.  A unit is one (request, KV head) and its N*G query rows (row
+// = node*G + g).  A workgroup of eight waves owns 256 rows of a unit, wave w
+// rows 32w .. 32w+31 against all 64 keys of every tile, so each K/V tile is
+// copied into LDS once for all of those rows (128-row workgroups would copy
+// every tile twice).  When there are few units, a unit's key tiles are split
+// between two workgroups (chunks) so that 256 CUs get enough pieces of equal
+// size; the workgroup that finishes second merges the two partial softmax
+// states (m, l, O), in chunk order, so the result does not depend on which
+// one finished first.
+//   * K and V tiles move from the paged pool into LDS by DMA
+//     (global_load_lds_dwordx4) through a ring of four K tiles and a ring of
+//     four V tiles, the K stream one tile ahead; the chunk swizzle keeps the
+//     MFMA fragment reads conflict free.
+//   * Per step a wave issues the score MFMAs of tile t+1 and the PV MFMAs of
+//     tile t, with the exponentials of tile t between them and the row
+//     maxima of tile t+1 after the last PV MFMA.  The main loop is unrolled
+//     over the four ring stages: every LDS fragment address is a fixed
+//     per-lane register plus an immediate, and the scores alternate between
+//     two register sets without copies.
+//   * Each wave DMAs the page ids of the tile seven ahead into its own LDS
+//     ring; a key's slot is clamped into the pool, and positions past the
+//     request read its last token (finite data that the mask turns into a
+//     zero weight), so every DMA reads real pool rows.
+//   * The merge protocol: each chunk takes a ticket (an atomic counter per
+//     unit); the first publishes its (m, l, O) in the workspace and bumps a
+//     second counter; the last waits for it (bounded), merges, writes the
+//     output and resets both counters to zero for the next call.
+#include <type_traits>
+
+#include "attn_common.hpp"
+
+namespace sdv {
+namespace {
+
+constexpr int kWideRows = 256;            // query rows per workgroup (32 per wave)
+constexpr unsigned kMergeSpin = 1u << 22; // polls before the merge gives up
+constexpr float kNoMax = -1e30f;          // running max before any visible key (finite: no inf - inf)
+
+template <int D>
+struct WideCfg : KvTile<D> {
+  static constexpr int RB = 2;                             // 16-row blocks per wave
+  static constexpr int KB = 4;                             // 16-key blocks per tile
+  static constexpr int SMEM = KvTile<D>::RINGS;
+  static constexpr size_t PART_O = static_cast<size_t>(kWideRows) * D * 4;   // fp32 partial O
+  static constexpr size_t PART = PART_O + kWideRows * 8;                      // + (m, l) per row
+};
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+// BIG: pools of 4 GiB or more (64-bit addresses per lane); otherwise a
+// 32-bit byte offset per lane from the pool base in scalar registers.
+template <int D, bool BIG>
+__global__ void __launch_bounds__(kAttnThreads, 1)
+tree_attn_wide_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64_t num_slots, float scale_log2,
+                      int nrb, int nch, const uint16_t *__restrict__ q,
+                      const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
+                      const int *__restrict__ table, const int *__restrict__ prefix_len,
+                      const uint32_t *__restrict__ mask_bits, uint16_t *__restrict__ out, float *__restrict__ lse,
+                      unsigned *__restrict__ sync, char *__restrict__ parts) {
+  using C = WideCfg<D>;
+  constexpr int RB = C::RB, KB = C::KB, DS = C::DS, NO = C::NO, IPW = C::IPW;
+  constexpr int ROW = C::ROW, TILE = C::TILE_BYTES;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ uint32_t s_mask[kWideRows][8];
+  __shared__ int s_pid[8][kStages][kTile];   // per wave: page ids of four tiles (ring, by LDS DMA)
+  __shared__ int s_pick;
+  __shared__ unsigned s_ticket;
+  __shared__ int s_ok;
+
+  // hardware block h runs on XCD h % 8 as that XCD's (h / 8)-th block; the
+  // row blocks and chunks of one unit are consecutive there
+  const int per = nrb * nch;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot_in_xcd = blockIdx.x / kXcds;
+  const int rank = (slot_in_xcd / per) * kXcds + xcd;        // unit rank, longest requests first
+  const int sub = slot_in_xcd % per;
+  const int rblk = sub / nch, ch = sub % nch;
+  if (rank >= B * Hkv) return;
+  const int b = request_of_rank(rank / Hkv, B, prefix_len, reinterpret_cast<int *>(smem), &s_pick);
+  const int kvh = rank % Hkv;
+  const int G = Hq / Hkv;
+  const int W = (N + 31) / 32;
+  const int pmask = (1 << pshift) - 1;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int l = lane_id();
+  const int l16 = l & 15;
+  const int g4 = l >> 4;
+
+  const int L = prefix_len[b];
+  const int total = L + N;
+  const int *trow = table + static_cast<int64_t>(b) * max_pages;
+  const bool req_ok = L >= 0 && static_cast<int64_t>(total) <= (static_cast<int64_t>(max_pages) << pshift);
+  const int ntiles = req_ok ? (total + kTile - 1) / kTile : 0;
+  const int tb = static_cast<int>(static_cast<int64_t>(ch) * ntiles / nch);         // this chunk's tiles
+  const int te = static_cast<int>(static_cast<int64_t>(ch + 1) * ntiles / nch);
+  const int total_pages = req_ok ? (total + pmask) >> pshift : 0;   // page-table entries the request owns
+  const int nfull = min(te, L / kTile);     // tiles below nfull lie wholly inside the prefix
+
+  const int row0 = rblk * kWideRows;
+  const int node0 = row0 / G;
+  for (int x = tid; x < kWideRows * 8; x += kAttnThreads) {
+    const int nn = x / 8, w = x % 8;
+    uint32_t v = 0;
+    if (node0 + nn < N && w < W) v = mask_bits[(static_cast<int64_t>(b) * N + node0 + nn) * W + w];
+    s_mask[nn][w] = v;
+  }
+
+  // this lane's rows: row0 + 32*wave + 16*rb + l16
+  int nrel[RB];
+  bf16x8 qf[RB][DS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = row0 + 32 * wave + 16 * rb + l16;
+    const int node = r / G, g = r % G;
+    nrel[rb] = node - node0;
+    const bool ok = node < N;
+    const uint16_t *qp = q + ((static_cast<int64_t>(b) * N + (ok ? node : 0)) * Hq + kvh * G + g) * D;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      uint4 u = ok ? *reinterpret_cast<const uint4 *>(qp + ds * 32 + 8 * g4) : make_uint4(0, 0, 0, 0);
+      __builtin_memcpy(&qf[rb][ds], &u, 16);
+    }
+  }
+  f32x4 o[RB][NO];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < NO; ++j) o[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = kNoMax;
+    l_run[rb] = 0.f;
+  }
+
+  // ---- DMA.  Wave w moves key rows 8w .. 8w+7 of a tile: lane L of an
+  // instruction fills LDS chunk L % CHUNKS of row L / CHUNKS, so it fetches
+  // logical chunk (L % CHUNKS) ^ swz(row).  A key's address is the pool base
+  // plus slot * (bytes per slot) plus this lane's chunk.
+  const uint32_t slot_bytes = static_cast<uint32_t>(Hkv) * D * 2;
+  const unsigned nslots = static_cast<unsigned>(num_slots);
+  const unsigned pid_max = static_cast<unsigned>((num_slots - 1) >> pshift);   // last page id with a slot
+  int dma_row[IPW];
+  uint32_t col_bytes[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    dma_row[i] = wave * 8 + i * C::KPI + l / C::CHUNKS;
+    col_bytes[i] = 16u * (kvh * (D / 8) + ((l % C::CHUNKS) ^ swz<D>(dma_row[i])));
+  }
+  const uint32_t lds0 = lds_offset(smem);
+  const uint32_t m0k = __builtin_amdgcn_readfirstlane(lds0 + wave * 8 * ROW);   // this wave's rows, K ring
+  const uint32_t m0v = m0k + kStages * TILE;                                     // V ring
+  const uint32_t m0p = __builtin_amdgcn_readfirstlane(lds_offset(&s_pid[wave][0][0]));   // page-id ring
+
+  // Page ids of every position of tile t into ring slot u of this wave (one
+  // instruction: lane L takes position 64t + L, clamped to the request's
+  // last token).
+  auto pid_dma = [&](int t, int u) {
+    const int idx = min(t * kTile + l, total - 1) >> pshift;
+    dma4(trow + idx, m0p + u * kTile * 4);
+  };
+  // Page ids of this lane's rows of tile t (ring slot u), then their pool slots.
+  auto read_pids = [&](int u, int (&pid)[IPW]) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) pid[i] = s_pid[wave][u][dma_row[i]];
+  };
+  auto tile_off = [&](int t, const int (&pids)[IPW], uint32_t (&slot)[IPW]) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int pos = min(t * kTile + dma_row[i], total - 1);
+      const unsigned pid = min(static_cast<unsigned>(pids[i]), pid_max);
+      slot[i] = min((pid << pshift) + static_cast<unsigned>(pos & pmask), nslots - 1);
+    }
+  };
+  auto issue = [&](uint32_t m0, const uint16_t *pool, const uint32_t (&slot)[IPW]) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      if constexpr (BIG) {
+        const uint64_t a = reinterpret_cast<uint64_t>(pool) + static_cast<uint64_t>(slot[i]) * slot_bytes + col_bytes[i];
+        dma16(reinterpret_cast<const void *>(a), m0 + i * C::KPI * ROW);
+      } else {
+        dma16s(slot[i] * slot_bytes + col_bytes[i], pool, m0 + i * C::KPI * ROW);
+      }
+    }
+  };
+
+  // ---- LDS fragment addresses: a per-lane register plus an immediate
+  // (ring stage * TILE + key block * 16 rows).
+  // K (A operand of S^T = K Q^T): key row 16*kb + l16, chunk (4*ds + g4) ^ swz(row).
+  // V^T (transposing read): key row 16*kb + 4*g4 + l16/4, 8 bytes at
+  // d = 16*db + 4*(l16 % 4), i.e. chunk (2*db + (l16 % 4)/2) ^ swz(row).
+  uint32_t koff[DS], voff[NO];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) koff[ds] = lds0 + l16 * ROW + (((ds * 4 + g4) ^ swz<D>(l16)) << 4);
+  {
+    const int vr = 4 * g4 + (l16 >> 2);
+#pragma unroll
+    for (int db = 0; db < NO; ++db)
+      voff[db] = lds0 + kStages * TILE + vr * ROW + (((2 * db + ((l16 & 3) >> 1)) ^ swz<D>(vr)) << 4) +
+                 ((l16 & 1) << 3);
+  }
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  auto kread = [&](uint32_t kst, int kb, int ds) {
+    return *reinterpret_cast<const lds_bf16x8 *>(koff[ds] + kst + kb * 16 * ROW);
+  };
+  // V^T operand of 32 keys (key blocks 2kk, 2kk+1) and d block db.  A
+  // transposing read: lane 4j + q of a 16-lane group points at row j, d
+  // 4q..4q+3, and lane i of the group receives d = i of the group's four rows.
+  auto vread = [&](uint32_t vst, int kk, int db) {
+    const s16x4 a0 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4 *>(voff[db] + vst + 2 * kk * 16 * ROW));
+    const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_s16x4 *>(voff[db] + vst + (2 * kk + 1) * 16 * ROW));
+    bf16x8 a;
+    __builtin_memcpy(reinterpret_cast<char *>(&a), &a0, 8);
+    __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &a1, 8);
+    return a;
+  };
+
+  // ---- softmax state.  sc holds one tile's S^T blocks sc[kb][rb] (lane
+  // (g4, l16): keys 16*kb + 4*g4 + i of row block rb's row l16); a step
+  // overwrites them with the next tile's, key block by key block, once the
+  // exponentials that read them have run.
+  static_assert(KB == 4, "the step order below covers four key blocks");
+  f32x4 sc[KB][RB];
+  bf16x8 pb[RB][2];                      // P of the current tile, bf16, one per 32-key PV block
+
+  // mask of key blocks kb, kb+1 of tile t (tiles reaching into the tree)
+  auto mask_pair = [&](int t, int kb0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int kpos0 = t * kTile + 4 * g4 - L;
+#pragma unroll
+      for (int kb = kb0; kb < kb0 + 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // branch-free on purpose: a short-circuit form becomes divergent
+          // control flow whose -inf write can land in the MFMA result
+          // register for every lane
+          const int j = kpos0 + 16 * kb + i;
+          const uint32_t w = s_mask[nrel[rb]][(j >> 5) & 7];
+          const bool vis =
+              (j < 0) | ((static_cast<unsigned>(j) < static_cast<unsigned>(N)) & ((w >> (j & 31)) & 1u));
+          sc[kb][rb][i] = vis ? sc[kb][rb][i] : -INFINITY;
+        }
+    }
+  };
+  // maximum of this lane's 8 values in key blocks kb, kb+1 (3-input
+  // maximum trees, no NaN quieting in between)
+  auto pair_max = [&](int kb0, float (&pm)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x4 &a = sc[kb0][rb], &c = sc[kb0 + 1][rb];
+      pm[rb] = vmax(vmax(vmax(vmax(a[0], a[1]), a[2]), vmax(vmax(a[3], c[0]), c[1])), vmax(c[2], c[3]));
+    }
+  };
+  // Row maxima across the four lane groups, in log2 units.
+  auto row_max = [&](const float (&p0)[RB], const float (&p1)[RB], float (&tmax)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) tmax[rb] = max_xor32(max_xor16(vmax(p0[rb], p1[rb]))) * scale_log2;
+  };
+  // The running state moves to a new reference max only when a score
+  // exceeds the current one by more than 2^8 (rare): m, l and the exponent
+  // here, branch-free; O by rescale_o once its MFMAs are done.
+  auto update_state = [&](const float (&tmax)[RB], float (&alpha)[RB]) {
+    bool anyneed = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool need = tmax[rb] > m_run[rb] + 8.0f;
+      const float newm = need ? tmax[rb] : m_run[rb];
+      alpha[rb] = need ? __builtin_amdgcn_exp2f(m_run[rb] - newm) : 1.0f;   // both finite
+      m_run[rb] = newm;
+      l_run[rb] *= alpha[rb];
+      anyneed |= need;
+    }
+    return anyneed;
+  };
+  auto rescale_o = [&](bool anyneed, const float (&alpha)[RB]) {
+    if (__any(anyneed)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+          o[rb][j][0] *= alpha[rb];
+          o[rb][j][1] *= alpha[rb];
+          o[rb][j][2] *= alpha[rb];
+          o[rb][j][3] *= alpha[rb];
+        }
+    }
+  };
+
+  // Exponentials of this lane's element pair x (0..15) of key block kb:
+  // (rb = x / 2, i = 2 * (x % 2)) -> P in bf16 for PV block kb / 2; the row
+  // sum adds the pair as rounded to bf16 (one dot2 with (1, 1)), the weights
+  // the PV product uses.
+  auto exp_pair = [&](int kb, int x) {
+    const int rb = x / 2, i = 2 * (x % 2), kk = kb / 2, e = 4 * (kb % 2) + i;
+    const float q0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][rb][i], scale_log2, -m_run[rb]));
+    const float q1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][rb][i + 1], scale_log2, -m_run[rb]));
+    bf16x2 pk;
+    pk[0] = static_cast<__bf16>(q0);
+    pk[1] = static_cast<__bf16>(q1);
+    l_run[rb] = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes2, l_run[rb], false);
+    pb[rb][kk][e] = pk[0];
+    pb[rb][kk][e + 1] = pk[1];
+  };
+  // exponential pairs [x0, x1) of the 16 (kb, x) pairs of key blocks kb0 ..
+  auto exps = [&](int kb0, int x0, int x1) {
+#pragma unroll
+    for (int x = x0; x < x1; ++x) exp_pair(kb0 + x / 4, x % 4);
+  };
+  // items 0 .. n-1 spread evenly over `iters` iterations: those of iteration it
+  auto spread = [](int n, int iters, int it, auto &&fn) {
+#pragma unroll
+    for (int x = it * n / iters; x < (it + 1) * n / iters; ++x) fn(x);
+  };
+
+  // ---- scores of key block kb of a tile from K stage kst into sc[kb]
+  // (fragment ds of the block in kf when called; the next block's first
+  // fragment is read into kf on the way out when `more`), VALU work
+  // valu(ds) after each pair of MFMAs
+  auto score_block = [&](uint32_t kst, int kb, bf16x8 &kf, bool more, auto &&valu) {
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const bf16x8 cur = kf;
+      if (ds + 1 < DS)
+        kf = kread(kst, kb, ds + 1);
+      else if (more)
+        kf = kread(kst, kb + 1, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[rb][ds],
+                                                             ds == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[kb][rb], 0, 0,
+                                                             0);
+      valu(ds);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // O^T += V^T P^T for PV block kk from V stage vst (its first operand in va
+  // when called), VALU work valu(db) after each pair of MFMAs
+  auto pv_block = [&](uint32_t vst, int kk, bf16x8 &va, auto &&valu) {
+#pragma unroll
+    for (int db = 0; db < NO; ++db) {
+      const bf16x8 cur = va;
+      if (db + 1 < NO) va = vread(vst, kk, db + 1);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pb[rb][kk], o[rb][db], 0, 0, 0);
+      valu(db);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- one step: softmax and PV of tile t (masked scores in sc, its row
+  // maxima applied), scores and row maxima of tile t+1.  STAGE: ring slot of
+  // tile t.
+  uint32_t offv[IPW];      // V chunk offsets of the tile whose K went out last step
+  // DMA batches: step t issues K(t+4) and V(t+3) (LDS slots of K(t) and
+  // V(t-1), read in step t-1) and the page ids of tile t+7 (ring slot of
+  // tile t+3's, read in step t-1); it needs K(t+1), V(t) and the page ids of
+  // tile t+4, which went out together three steps earlier.
+  constexpr int kBatch = 1 + 2 * IPW;    // vector-memory instructions per step and wave
+  auto step = [&](int t, auto STAGE) {
+    constexpr int S = decltype(STAGE)::value;
+    wait_vmcnt<2 * kBatch>();            // this wave's batch of step t-3 is in (two later ones may fly)
+    __syncthreads();                     // everyone's are; and the slots refilled below are no longer read
+    // This step's DMA batch goes out in pieces between MFMAs (a stalled
+    // issue then overlaps matrix work): K(t+4) after the first score MFMAs,
+    // V(t+3) after the next ones, the page ids of tile t+7 during PV block 0.
+    int pids[IPW];
+    read_pids(S, pids);                  // page ids of tile t+4, in by the wait above
+    uint32_t offn[IPW];
+    auto issue_k = [&]() {
+      tile_off(t + 4, pids, offn);
+      issue(m0k + S * TILE, kpool, offn);                                            // K(t+4)
+    };
+    auto issue_v = [&]() {
+      issue(m0v + ((S + kStages - 1) & (kStages - 1)) * TILE, vpool, offv);          // V(t+3)
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) offv[i] = offn[i];
+    };
+    constexpr uint32_t kst = ((S + 1) & (kStages - 1)) * TILE;    // K(t+1)
+    constexpr uint32_t vst = S * TILE;                             // V(t)
+    const bool next = t + 1 < te;                                  // block-uniform
+    const bool masked_next = t + 1 >= nfull;
+    bf16x8 kf = kread(kst, 0, 0);
+    auto none = [](int) {};
+    // (key block 0's exponentials ran at the end of the last step)
+    // 1.-2. scores of key blocks 0, 1 of tile t+1 | exponentials of key blocks 1, 2 (first half)
+    score_block(kst, 0, kf, true, [&](int ds) {
+      spread(4, DS, ds, [&](int x) { exp_pair(1, x); });
+      if (ds == 0) issue_k();
+    });
+    bf16x8 va = vread(vst, 0, 0);
+    score_block(kst, 1, kf, false, [&](int ds) {
+      spread(2, DS, ds, [&](int x) { exp_pair(2, x); });
+      if (ds == 0) issue_v();
+    });
+    // 3. PV block 0 | exponentials of key block 2 (second half), 3 (first half)
+    kf = kread(kst, 2, 0);
+    pv_block(vst, 0, va, [&](int db) {
+      spread(4, NO, db, [&](int x) { exp_pair(x < 2 ? 2 : 3, (x + 2) % 4); });   // block 2 pairs 2, 3; block 3 pairs 0, 1
+      if (db == 0) pid_dma(t + 7, (S + 3) & (kStages - 1));
+    });
+    va = vread(vst, 1, 0);
+    // 4.-5. scores of key blocks 2, 3 | exponentials of key block 3 (second
+    // half); mask and maxima of key blocks 0, 1 of tile t+1
+    float p0[RB], p1[RB], tmax[RB], alpha[RB];
+    score_block(kst, 2, kf, true, [&](int ds) { spread(2, DS, ds, [&](int x) { exp_pair(3, 2 + x); }); });
+    score_block(kst, 3, kf, false, [&](int ds) {
+      if (ds == 0 && masked_next) mask_pair(t + 1, 0);
+      if (ds == DS - 1) pair_max(0, p0);
+    });
+    // 6. PV block 1 | tile t+1: mask and maxima of key blocks 2, 3, row
+    // maxima, the state update, exponentials of key block 0; then the (rare)
+    // rescale of O
+    if (next) {
+      bool anyneed = false;
+      pv_block(vst, 1, va, [&](int db) {
+        spread(8, NO, db, [&](int x) {
+          switch (x) {
+            case 0: if (masked_next) mask_pair(t + 1, 2); break;
+            case 1: pair_max(2, p1); break;
+            case 2: row_max(p0, p1, tmax); break;
+            case 3: anyneed = update_state(tmax, alpha); break;
+            case 4: exps(0, 0, 1); break;
+            case 5: exps(0, 1, 2); break;
+            case 6: exps(0, 2, 3); break;
+            default: exps(0, 3, 4); break;
+          }
+        });
+      });
+      rescale_o(anyneed, alpha);
+    } else {
+      pv_block(vst, 1, va, none);
+    }
+  };
+
+  // ---- prologue: page ids of tiles tb .. tb+3, K(tb), then three batches
+  // shaped like a step's: page ids of tile tb+4+u, K(tb+1+u), V(tb+u)
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);         // the Q fragments and the mask land here, not in the key loop
+  if (tb < te) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) pid_dma(tb + u, u);
+    wait_vmcnt<0>();
+    uint32_t off[kStages][IPW];
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      int pids[IPW];
+      read_pids(u, pids);
+      tile_off(tb + u, pids, off[u]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);       // page ids read before their slots are refilled
+    issue(m0k, kpool, off[0]);
+#pragma unroll
+    for (int u = 0; u + 1 < kStages; ++u) {
+      issue(m0k + (u + 1) * TILE, kpool, off[u + 1]);
+      issue(m0v + u * TILE, vpool, off[u]);
+      pid_dma(tb + 4 + u, u);
+    }
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) offv[i] = off[kStages - 1][i];
+    wait_vmcnt<3 * kBatch>();            // K(tb) is in
+    __syncthreads();
+    bf16x8 kf = kread(0, 0, 0);
+    auto none = [](int) {};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) score_block(0, kb, kf, kb + 1 < KB, none);
+    float p0[RB], p1[RB], tmax[RB], alpha[RB];
+    if (tb >= nfull) {
+      mask_pair(tb, 0);
+      mask_pair(tb, 2);
+    }
+    pair_max(0, p0);
+    pair_max(2, p1);
+    row_max(p0, p1, tmax);
+    update_state(tmax, alpha);           // O is still zero: nothing to rescale
+    exps(0, 0, 4);
+  }
+
+  // ---- main loop: the step of tile t uses ring stage (t - tb) % 4; the
+  // loop leaves after any step
+  for (int t = tb; t < te;) {
+    step(t, IC<0>{});
+    if (++t >= te) break;
+    step(t, IC<1>{});
+    if (++t >= te) break;
+    step(t, IC<2>{});
+    if (++t >= te) break;
+    step(t, IC<3>{});
+    ++t;
+  }
+  __builtin_amdgcn_s_waitcnt(0);         // trailing DMAs land before the workgroup ends
+
+  // ---- row sums over the four lane groups (m_run is equal across them)
+  float lrow[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) lrow[rb] = sum_xor32(sum_xor16(l_run[rb]));
+  float mfin[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) mfin[rb] = m_run[rb];
+
+  if (nch > 1) {
+    const int64_t uslot = static_cast<int64_t>(rank) * nrb + rblk;
+    unsigned *ticket = sync + 2 * uslot;
+    unsigned *done = ticket + 1;
+    float4 *pO = reinterpret_cast<float4 *>(parts + uslot * C::PART);
+    float2 *pml = reinterpret_cast<float2 *>(parts + uslot * C::PART + C::PART_O);
+    if (tid == 0) s_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_ticket + 1 < static_cast<unsigned>(nch)) {
+      // first: publish (m, l, O) and bump `done` after the stores are visible
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < NO; ++db)
+          pO[((wave * RB + rb) * NO + db) * kWave + l] = make_float4(o[rb][db][0], o[rb][db][1], o[rb][db][2], o[rb][db][3]);
+      if (g4 == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) pml[wave * 32 + 16 * rb + l16] = make_float2(mfin[rb], lrow[rb]);
+      }
+      // every wave's stores complete (stores count in vmcnt), then one
+      // agent-scope release (one L2 write-back for the workgroup) before the
+      // count moves
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // last: wait for the other chunk, then reset both counters for the next call
+    if (tid == 0) {
+      unsigned spins = 0;
+      int ok = 1;
+      while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 < static_cast<unsigned>(nch)) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kMergeSpin) {
+          ok = 0;
+          break;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ok = ok;
+    }
+    __syncthreads();                     // thread 0's acquire covers the workgroup (one CU, one L1)
+    // merge in chunk order (chunk 0's terms first): m = max, l and O summed
+    // with weights 2^(m_c - m)
+    const bool mine0 = ch == 0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float2 ml = pml[wave * 32 + 16 * rb + l16];
+      const float m0 = mine0 ? mfin[rb] : ml.x, m1 = mine0 ? ml.x : mfin[rb];
+      const float l0 = mine0 ? lrow[rb] : ml.y, l1 = mine0 ? ml.y : lrow[rb];
+      const float Mu = fmaxf(m0, m1);      // finite: maxima start at kNoMax
+      const float f0 = exp2f(m0 - Mu), f1 = exp2f(m1 - Mu);
+#pragma unroll
+      for (int db = 0; db < NO; ++db) {
+        const float4 x = pO[((wave * RB + rb) * NO + db) * kWave + l];
+        const float xp[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = mine0 ? o[rb][db][i] : xp[i], x1 = mine0 ? xp[i] : o[rb][db][i];
+          o[rb][db][i] = fmaf(x1, f1, x0 * f0);     // one expression in chunk order
+        }
+      }
+      lrow[rb] = fmaf(l1, f1, l0 * f0);
+      mfin[rb] = Mu;
+      if (!s_ok) lrow[rb] = __builtin_nanf("");
+    }
+  }
+
+  // ---- normalise and store: o[rb][db][i] is row 32*wave + 16*rb + l16 at
+  // d = 16*db + 4*g4 + i
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = row0 + 32 * wave + 16 * rb + l16;
+    const int node = r / G, g = r % G;
+    if (node >= N) continue;
+    const float fac = lrow[rb] > 0.f ? 1.0f / lrow[rb] : (lrow[rb] == 0.f ? 0.f : lrow[rb]);
+    uint16_t *op = out + ((static_cast<int64_t>(b) * N + node) * Hq + kvh * G + g) * D + 4 * g4;
+#pragma unroll
+    for (int db = 0; db < NO; ++db) {
+      const uint32_t w0 = f32_to_bf16_rne(o[rb][db][0] * fac) |
+                          (static_cast<uint32_t>(f32_to_bf16_rne(o[rb][db][1] * fac)) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(o[rb][db][2] * fac) |
+                          (static_cast<uint32_t>(f32_to_bf16_rne(o[rb][db][3] * fac)) << 16);
+      *reinterpret_cast<uint2 *>(op + 16 * db) = make_uint2(w0, w1);
+    }
+    if (lse && g4 == 0)
+      lse[(static_cast<int64_t>(b) * N + node) * Hq + kvh * G + g] =
+          lrow[rb] > 0.f ? (mfin[rb] + log2f(lrow[rb])) * 0.69314718055994531f
+                         : (lrow[rb] == 0.f ? -INFINITY : lrow[rb]);
+  }
+}
+
+template <int D, bool BIG>
+int32_t launch_wide(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb,
+                    int nch, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                    const int32_t *page_table, const int32_t *prefix_len, const uint32_t *mask_bits, uint16_t *out,
+                    float *lse, unsigned *sync, char *parts) {
+  const size_t lds = WideCfg<D>::SMEM;
+  static thread_local int configured_dev = -1;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "tree_verify_attention: no device");
+  if (configured_dev != dev) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(tree_attn_wide_kernel<D, BIG>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return fail(SDV_E_HIP, "tree_verify_attention: LDS attribute: %s", hipGetErrorString(e));
+    configured_dev = dev;
+  }
+  hipLaunchKernelGGL((tree_attn_wide_kernel<D, BIG>), dim3(static_cast<unsigned>(blocks)), dim3(kAttnThreads), lds, st,
+                     sh.B, sh.N, sh.Hq, sh.Hkv, pshift, sh.max_pages, sh.num_slots, scale_log2, nrb, nch,
+                     q, k_pool, v_pool, page_table, prefix_len, mask_bits, out, lse, sync, parts);
+  return check_launch("tree_attn_wide_kernel");
+}
+
+}  // namespace
+
+size_t attn_wide_workspace(int64_t slots, int D) {
+  if (2 * slots > kAttnSyncWords) return 0;          // the key split is not offered for this many units
+  Carver c(nullptr);
+  c.take<unsigned>(kAttnSyncWords);
+  c.take<char>(static_cast<size_t>(slots) * (D == 64 ? WideCfg<64>::PART : WideCfg<128>::PART));
+  return c.bytes();
+}
+
+int32_t launch_attn_wide(hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb, int nch,
+                         const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                         const int32_t *page_table, const int32_t *prefix_len, const uint32_t *mask_bits,
+                         uint16_t *out, float *lse, void *ws) {
+  const int64_t units = static_cast<int64_t>(sh.B) * sh.Hkv;
+  const int64_t units_pad = (units + kXcds - 1) / kXcds * kXcds;
+  const int64_t blocks = units_pad * nrb * nch;
+  SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tree_verify_attention: grid too large");
+  unsigned *sync = nullptr;
+  char *parts = nullptr;
+  if (nch > 1) {
+    Carver c(ws);
+    sync = c.take<unsigned>(kAttnSyncWords);
+    parts = c.take<char>(static_cast<size_t>(units * nrb) * (sh.D == 64 ? WideCfg<64>::PART : WideCfg<128>::PART));
+  }
+  const bool big = static_cast<uint64_t>(sh.num_slots) * sh.Hkv * sh.D * 2 >= (1ull << 32);
+#define SDV_WIDE(DD, BB)                                                                                       \
+  launch_wide<DD, BB>(blocks, st, sh, pshift, scale_log2, nrb, nch, q, k_pool, v_pool, page_table, prefix_len, \
+                      mask_bits, out, lse, sync, parts)
+  if (sh.D == 64) return big ? SDV_WIDE(64, true) : SDV_WIDE(64, false);
+  return big ? SDV_WIDE(128, true) : SDV_WIDE(128, false);
+#undef SDV_WIDE
+}
+
+}  // namespace sdv
