@@ -42,16 +42,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Chunk swizzle of key row r (depends on r % 16 only): the 16 rows read by
-// one quarter-wave map a fixed chunk to 16 distinct chunks (K fragments),
-// and rows r, r+4 land in different halves of the row (V words).
+// Chunk swizzle of key row r (depends on r % 16 only), for two LDS read
+// patterns.  K fragments (16-byte reads): the 16 rows read by one
+// quarter-wave map a fixed chunk to 16 distinct bank groups.  V^T
+// (transposing 8-byte reads): a half-wave reads chunk pair (2db, 2db+1) of
+// rows 0..7 (or 8..15), and swz(r) / 2 differs across those rows, so the 16
+// chunk reads hit distinct bank groups.  (A 256-byte row covers all 64
+// banks: the bank group is the chunk; a 128-byte row covers half, so for
+// D = 64 rows of either parity are told apart separately.)
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (D == 128) {
-    r &= 15;
-    return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
+    return ((r & 7) << 1) | ((r >> 3) & 1);
   } else {
-    return (r >> 1) & 7;
+    return (r & 6) | ((r >> 3) & 1);
   }
 }
 
