@@ -230,22 +230,30 @@ def algorithmic_work(cfg, inp, pipe):
 MEASURED_TRAFFIC = {
     "tree_attention": {
         "workload": "c3",
-        "source": "speculative_decoding_eagle_amd/csrc/attn.hip",
-        "sha256": "c03bcb8aa03eab0af2aee44001d1a30d86de9013967ed4258b3d04a66896bc76",
-        "fetch_kib": 182761.3, "fetch_factor": 1.99996,
-        "write_kib": 16384.0, "write_factor": 1.0,
+        "sources": ["speculative_decoding_eagle_amd/csrc/attn_wide.hip",
+                    "speculative_decoding_eagle_amd/csrc/attn_common.hpp"],
+        "sha256": "8bf14e274c37619e26f5bcb275d23f8cf643592f516690ab45c01edc80917a16",
+        "fetch_kib": 206285.5, "fetch_factor": 1.99996,
+        "write_kib": 63016.0, "write_factor": 1.0,
     },
 }
 
 
-def measured_traffic(stage, workload):
+def sources_sha256(paths):
     import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(stage, workload):
     rec = MEASURED_TRAFFIC.get(stage)
-    if rec is None or rec["workload"] != workload:
+    if rec is None or rec["workload"] != workload or rec["sha256"] is None:
         return None
-    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
-            return None
+    if sources_sha256(rec["sources"]) != rec["sha256"]:
+        return None
     return int(rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"])
 
 

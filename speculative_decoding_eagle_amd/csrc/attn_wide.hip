@@ -165,11 +165,14 @@ tree_attn_wide_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, 
   const uint32_t m0v = m0k + kStages * TILE;                                     // V ring
   const uint32_t m0p = __builtin_amdgcn_readfirstlane(lds_offset(&s_pid[wave][0][0]));   // page-id ring
 
+  // Key position that row r of tile t reads: its own, clamped to the
+  // request's last token; tiles past this chunk (the pipeline runs three
+  // ahead) all read that last token, one row that stays in L2.
+  auto key_pos = [&](int t, int r) { return t < te ? min(t * kTile + r, total - 1) : total - 1; };
   // Page ids of every position of tile t into ring slot u of this wave (one
-  // instruction: lane L takes position 64t + L, clamped to the request's
-  // last token).
+  // instruction: lane L takes key_pos(t, L)).
   auto pid_dma = [&](int t, int u) {
-    const int idx = min(t * kTile + l, total - 1) >> pshift;
+    const int idx = key_pos(t, l) >> pshift;
     dma4(trow + idx, m0p + u * kTile * 4);
   };
   // Page ids of this lane's rows of tile t (ring slot u), then their pool slots.
@@ -180,7 +183,7 @@ tree_attn_wide_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, 
   auto tile_off = [&](int t, const int (&pids)[IPW], uint32_t (&slot)[IPW]) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int pos = min(t * kTile + dma_row[i], total - 1);
+      const int pos = key_pos(t, dma_row[i]);
       const unsigned pid = min(static_cast<unsigned>(pids[i]), pid_max);
       slot[i] = min((pid << pshift) + static_cast<unsigned>(pos & pmask), nslots - 1);
     }
