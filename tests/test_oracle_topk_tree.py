@@ -40,6 +40,104 @@ def test_topk_rejects_bad_k():
         otopk.draft_topk(np.zeros((1, 4), np.float32), 5)
 
 
+# ------------------------------------------- fused softmax + top-k (logits)
+
+import math
+
+
+def test_fused_two_entries_follow_the_logistic_function():
+    """softmax of two logits is the logistic function of their difference."""
+    for a, b, T in [(1.5, -0.25, 1.0), (0.0, 3.0, 0.7), (-2.0, -2.5, 1.3), (10.0, -10.0, 2.0)]:
+        vals, ids = otopk.draft_topk_from_logits(np.array([[a, b]], np.float32), 2, T)
+        hi, lo = (a, b) if a >= b else (b, a)
+        p_hi = 1.0 / (1.0 + math.exp(-(hi - lo) / T))
+        assert ids[0].tolist() == ([0, 1] if a >= b else [1, 0])
+        assert abs(vals[0, 0] - p_hi) < 1e-15 and abs(vals[0, 1] - (1.0 - p_hi)) < 1e-15
+
+
+def test_fused_is_invariant_to_shift_and_to_scaling_logits_with_the_temperature():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((6, 300)) * 3.0).astype(np.float32)
+    v0, i0 = otopk.draft_topk_from_logits(x, 8, 0.8)
+    v1, i1 = otopk.draft_topk_from_logits(x + np.float32(5.0), 8, 0.8)    # the shift rounds in fp32: 1e-5
+    v2, i2 = otopk.draft_topk_from_logits(x * np.float32(2.0), 8, 1.6)    # x*2 is exact in fp32
+    assert np.array_equal(i0, i1) and np.array_equal(i0, i2)
+    assert np.allclose(v0, v1, rtol=1e-5, atol=0) and np.allclose(v0, v2, rtol=1e-13, atol=0)
+
+
+def test_fused_uniform_row_gives_lowest_ids_and_one_over_V():
+    vals, ids = otopk.draft_topk_from_logits(np.full((2, 40), 0.5, np.float32), 5, 1.0)
+    assert ids.tolist() == [[0, 1, 2, 3, 4]] * 2
+    assert np.allclose(vals, 1.0 / 40, rtol=1e-15, atol=0)
+
+
+def test_fused_excluded_entries_get_zero_and_the_rest_renormalise():
+    x = np.full((1, 10), -np.inf, np.float32)
+    x[0, [2, 5, 7]] = [1.0, 3.0, 1.0]
+    vals, ids = otopk.draft_topk_from_logits(x, 5, 1.0)
+    z = math.exp(1.0) * 2 + math.exp(3.0)
+    assert ids[0].tolist() == [5, 2, 7, 0, 1]
+    assert np.allclose(vals[0, :3], [math.exp(3.0) / z, math.exp(1.0) / z, math.exp(1.0) / z], rtol=1e-15)
+    assert vals[0, 3] == 0.0 and vals[0, 4] == 0.0
+
+
+def test_fused_agrees_with_processed_rows_and_the_plain_top_k():
+    """The generator's softmax (an independent float64 evaluation, rounded
+    once to fp32) followed by the plain top-k gives the same ids where the
+    rounded probabilities do not tie, and values within that rounding."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((12, 4099)) * 3.0).astype(np.float32)
+    for T in (1.0, 0.7):
+        pv, pi = otopk.draft_topk_from_logits(x, 8, T)
+        rows = workloads.softmax_rows(x, T)
+        qv, qi = otopk.draft_topk(rows, 9)
+        for r in range(x.shape[0]):
+            if len(set(qv[r].tolist())) == 9:
+                assert pi[r].tolist() == qi[r, :8].tolist()
+        assert np.all(np.abs(pv - qv[:, :8].astype(np.float64)) <= 2.0 ** -24 * pv)
+
+
+def test_fused_orders_by_exact_probability_not_by_rounded_values():
+    """Logits 0 and 2^-30 give fp32 probabilities that round alike, so the
+    plain top-k of the rounded row puts the lower id first; the exact
+    probabilities order the larger logit first."""
+    x = np.full((1, 5000), -30.0, np.float32)
+    x[0, 3] = 0.0
+    x[0, 9] = np.float32(2.0 ** -30)
+    rows = workloads.softmax_rows(x, 1.0)
+    assert rows[0, 3] == rows[0, 9] and otopk.draft_topk(rows, 2)[1][0].tolist() == [3, 9]
+    vals, ids = otopk.draft_topk_from_logits(x, 2, 1.0)
+    assert ids[0].tolist() == [9, 3]
+    assert vals[0, 0] > vals[0, 1]
+
+
+def test_fused_reads_bf16_bit_patterns():
+    bits = np.array([[0x3F80, 0x4000, 0xFF80, 0xBF80]], np.uint16)    # 1, 2, -inf, -1
+    vb, ib = otopk.draft_topk_from_logits(bits, 4, 1.0, bf16=True)
+    vf, iff = otopk.draft_topk_from_logits(np.array([[1.0, 2.0, -np.inf, -1.0]], np.float32), 4, 1.0)
+    assert ib.tolist() == [[1, 0, 3, 2]] and np.array_equal(ib, iff) and np.array_equal(vb, vf)
+
+
+def test_fused_full_row_sums_to_one():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((3, 257)) * 4.0).astype(np.float32)
+    vals, ids = otopk.draft_topk_from_logits(x, 257, 1.1)
+    assert np.allclose(vals.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    for r in range(3):
+        assert ids[r].tolist() == sorted(range(257), key=lambda i: (-float(x[r, i]), i))
+
+
+def test_fused_rejects_bad_input():
+    with pytest.raises(ValueError):
+        otopk.draft_topk_from_logits(np.zeros((1, 4), np.float32), 2, 0.0)
+    with pytest.raises(ValueError):
+        otopk.draft_topk_from_logits(np.array([[0.0, np.nan]], np.float32), 1, 1.0)
+    with pytest.raises(ValueError):
+        otopk.draft_topk_from_logits(np.full((1, 3), -np.inf, np.float32), 1, 1.0)
+    with pytest.raises(ValueError):
+        otopk.draft_topk_from_logits(np.zeros((1, 4), np.float32), 5, 1.0)
+
+
 # ------------------------------------------------------------------- tree
 
 def _golden(golden_dir, name):
