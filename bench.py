@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--accept", default="literal", choices=["literal", "planted"])
+    ap.add_argument("--draft-input", default="probs", choices=["probs", "logits_f32", "logits_bf16"],
+                    help="what the draft top-k reads: the processed probability rows, or the draft logits "
+                         "(fp32 or bf16) with the softmax fused into the top-k (non-TLI workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -68,7 +71,7 @@ def log(msg):
 class Pipeline:
     """Preallocated device buffers and the per-stage calls of one step."""
 
-    def __init__(self, cfg, inp, n_tables, accept_mode):
+    def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs"):
         import torch
         import speculative_decoding_eagle_amd as sdv
         self.torch, self.sdv, self.cfg = torch, sdv, cfg
@@ -88,10 +91,17 @@ class Pipeline:
             self.draft_rows = self.q_target
         else:
             self.draft_rows = d["draft_probs"]
+        self.draft_input = draft_input
+        if draft_input != "probs":
+            # the fused path reads logits; the stochastic accept still reads
+            # the probability rows of the draft distribution
+            lg = d.pop("draft_logits")
+            self.draft_logits = lg.to(torch.bfloat16) if draft_input == "logits_bf16" else lg
         rows = B * cfg.R
         self.topk_p = torch.empty((B, cfg.R, k), dtype=torch.float32, device="cuda")
         self.topk_id = torch.empty((B, cfg.R, k), dtype=torch.int32, device="cuda")
-        ws = sdv._lib.lib().sdv_draft_topk_workspace_size(rows, cfg.V, k)
+        ws = max(sdv._lib.lib().sdv_draft_topk_workspace_size(rows, cfg.V, k),
+                 sdv._lib.lib().sdv_draft_topk_logits_workspace_size(rows, cfg.V, k))
         self.topk_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
         self.tree = {}
         self.acc = {}
@@ -141,8 +151,12 @@ class Pipeline:
         sdv.sdv_tli_q_scatter(d["q_pruned"], d["tgt_ids"], cfg.V, q_target=self.q_target, ws=self.scatter_ws)
 
     def s_topk(self):
-        self.sdv.sdv_draft_topk(self.draft_rows, self.cfg.k, topk_p=self.topk_p, topk_id=self.topk_id,
-                                ws=self.topk_ws)
+        if self.draft_input == "probs":
+            self.sdv.sdv_draft_topk(self.draft_rows, self.cfg.k, topk_p=self.topk_p, topk_id=self.topk_id,
+                                    ws=self.topk_ws)
+        else:
+            self.sdv.sdv_draft_topk_logits(self.draft_logits, self.cfg.k, self.cfg.temperature,
+                                           topk_p=self.topk_p, topk_id=self.topk_id, ws=self.topk_ws)
 
     def s_tree(self):
         cfg = self.cfg
@@ -196,7 +210,8 @@ class Pipeline:
 def algorithmic_work(cfg, inp, pipe):
     """Bytes / flops the method must move or compute per launch, per stage."""
     B, N, V, R, k = cfg.B, cfg.N, cfg.V, cfg.R, cfg.k
-    out = {"draft_topk": dict(bytes=B * R * V * 4 + B * R * k * 8, flops=0)}
+    row_bytes = 2 if pipe.draft_input == "logits_bf16" else 4
+    out = {"draft_topk": dict(bytes=B * R * V * row_bytes + B * R * k * 8, flops=0)}
     if cfg.has_attention:
         L = inp["prefix_len"].astype(np.int64)
         depth = pipe.tree["depth"].cpu().numpy().astype(np.int64)
@@ -337,10 +352,14 @@ def main():
     cfg = workloads.get_config(args.config)
     log("generating inputs of %s" % cfg.name)
     t_gen = time.perf_counter()
-    inp = workloads.generate(cfg)
+    if args.draft_input != "probs" and cfg.is_tli:
+        print("--draft-input %s: the TLI workloads take the draft rows from the pruned head" % args.draft_input,
+              file=sys.stderr)
+        sys.exit(2)
+    inp = workloads.generate(cfg, with_logits=args.draft_input != "probs")
     t_gen = time.perf_counter() - t_gen
     log("inputs ready in %.1f s; uploading and warming up" % t_gen)
-    pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept)
+    pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept, args.draft_input)
     stages = [name for name, _ in pipe.stages(0)]
 
     for i in range(args.warmup):
@@ -397,7 +416,7 @@ def main():
         "dtype": "f32+bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[cfg.name], "name": cfg.name, "batch": cfg.B, "tree_tokens": cfg.N,
-                   "accept": args.accept},
+                   "accept": args.accept, "draft_input": args.draft_input},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_gbs": {k: round(work[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9, 1) for k in stages if k in work},
         "accepted_tokens": work["accept"]["accepted"],

@@ -71,6 +71,30 @@ int32_t sdv_draft_topk(const float *probs, int64_t rows, int32_t V, int32_t k,
                        void *stream);
 
 /* ------------------------------------------------------------------------
+ * A1, fused from logits: the per-step softmax and fast_topk of the draft in
+ * one pass ("[SGLang] Multi-Layer EAGLE", section 3: softmax then fast_topk
+ * after each draft pass; the processed draft distribution is
+ * softmax(logits / T)).  The probability rows are never materialised.
+ *
+ * For every row r of logits (device, [rows, V], dtype SDV_DTYPE_F32 or
+ * SDV_DTYPE_BF16; entries may be -inf, at least one finite per row, no NaN)
+ * writes to topk_p (device, [rows, k] fp32) the k largest values of
+ * p = softmax(logits[r] / temperature), in descending order, and to topk_id
+ * (device, [rows, k] int32) their column ids.  The order is that of the
+ * exact probabilities, i.e. of the logits, lower id first among equal
+ * logits (fp32 rounding of p never reorders).  p is computed in fp32 with
+ * the row's normaliser accumulated in a fixed order (deterministic).
+ * temperature > 0; 1 <= k <= 32, k <= V, V < 2^31.  Scratch: the size query's
+ * bytes (0 when rows alone fill the GPU).
+ * ---------------------------------------------------------------------- */
+enum { SDV_DTYPE_F32 = 0, SDV_DTYPE_BF16 = 1 };
+
+size_t sdv_draft_topk_logits_workspace_size(int64_t rows, int32_t V, int32_t k);
+int32_t sdv_draft_topk_logits(const void *logits, int32_t dtype, int64_t rows, int32_t V, int32_t k,
+                              float temperature, float *topk_p, int32_t *topk_id, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * A2-A4  Candidate tree, positions, mask and retrieve arrays.
  * "[SGLang] Multi-Layer EAGLE", section 2 (select_top_k_tokens builds
  * tree_info = scores, tokens, parents with cumulative scores);

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     sdv_build_tree,
     sdv_compact_kv,
     sdv_draft_topk,
+    sdv_draft_topk_logits,
     sdv_tli_build_maps,
     sdv_tli_constrain_draft_logits,
     sdv_tli_lm_head,

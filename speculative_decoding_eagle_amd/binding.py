@@ -86,6 +86,33 @@ def sdv_draft_topk(probs: torch.Tensor, k: int, topk_p=None, topk_id=None, ws=No
     return topk_p, topk_id
 
 
+def sdv_draft_topk_logits(logits: torch.Tensor, k: int, temperature: float = 1.0, topk_p=None, topk_id=None,
+                          ws=None):
+    """softmax(logits / temperature) top-k of every row of ``logits`` [..., V]
+    (fp32 or bf16) -> (topk_p fp32, topk_id int32) [..., k]."""
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V else 0
+    dev = logits.device
+    if logits.dtype == torch.float32:
+        dtype = 0
+    elif logits.dtype == torch.bfloat16:
+        dtype = 1
+    else:
+        raise ValueError("logits must be float32 or bfloat16, got %s" % logits.dtype)
+    if topk_p is None:
+        topk_p = torch.empty(logits.shape[:-1] + (k,), dtype=torch.float32, device=dev)
+    if topk_id is None:
+        topk_id = torch.empty(logits.shape[:-1] + (k,), dtype=torch.int32, device=dev)
+    L = _lib.lib()
+    need = L.sdv_draft_topk_logits_workspace_size(rows, V, k)
+    wp, wb = _workspace(need, dev, ws)
+    _check(L.sdv_draft_topk_logits(_ptr(logits, (torch.float32, torch.bfloat16), "logits"), dtype, rows, V, k,
+                                   float(temperature), _ptr(topk_p, torch.float32, "topk_p"),
+                                   _ptr(topk_id, torch.int32, "topk_id"), wp, wb, _stream(dev)),
+           "sdv_draft_topk_logits")
+    return topk_p, topk_id
+
+
 # -------------------------------------------------------------------- A2-A4
 
 TREE_OUTPUTS = ("tokens", "parent", "depth", "positions", "score", "q_row", "mask", "mask_bits",

@@ -81,10 +81,6 @@ __device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
 }
 
-// IEEE-754-2019 maximum (NaN propagates): one v_maximum3_f32 on gfx950,
-// with no NaN-quieting of its inputs in front of it as fmaxf needs.
-__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-
 // Lane l's value combined with lane l^16's (l^32's): the row-half swap
 // instructions hand every lane the pair {x[l], x[l^16]} ({x[l], x[l^32]}).
 __device__ __forceinline__ float max_xor16(float x) {

@@ -55,6 +55,10 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// IEEE-754-2019 maximum (NaN propagates): one v_maximum3_f32 on gfx950,
+// with no NaN-quieting of its inputs in front of it as fmaxf needs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Strict total order used by every top-k / argmax: larger value first, then
 // lower index.
 __device__ __forceinline__ bool better(float v, int i, float w, int j) {

@@ -16,13 +16,9 @@ namespace sdv {
 namespace {
 
 constexpr int kTopkThreads = 256;
+constexpr int kLoads = 4;        // 16-byte loads per lane in flight per window
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-// 16-byte load marked non-temporal (the probability rows are read once).
-__device__ __forceinline__ float4 stream_load(const float *p) {
-  const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(p));
-  return make_float4(v.x, v.y, v.z, v.w);
-}
 
 template <int K>
 struct SortedK {
@@ -72,12 +68,10 @@ struct SortedK {
 // and the buffer is folded into the best-K list whenever it fills up.  After
 // the first fold the threshold is high enough that almost no element passes,
 // so the scan is one compare and one ballot per 16-byte load.
-constexpr int kCap = 512;                     // candidate slots per wave
-
-template <int K>
+template <int K, int CAP>
 struct WaveFilter {
-  float *cv;            // [kCap] candidate values (this wave's slice of LDS)
-  int *ci;              // [kCap] candidate ids
+  float *cv;            // [CAP] candidate values (this wave's slice of LDS)
+  int *ci;              // [CAP] candidate ids
   float *tv;            // [K] best values, sorted best first
   int *ti;              // [K] best ids
   int cnt;              // candidates buffered (wave-uniform)
@@ -130,6 +124,26 @@ struct WaveFilter {
     cnt = 0;
   }
 
+  // Raises the threshold, before anything is buffered, to the K-th largest
+  // of the lanes' maxima over a first stretch of the wave's elements.  K of
+  // the wave's elements reach that value, so each of its K best does too;
+  // with the id bound at INT_MAX, elements equal to it still pass.  This
+  // spares the folds that a threshold at -inf would take on the first
+  // elements.
+  __device__ void seed(float lane_max) {
+    float v = lane_max, kth = -INFINITY;
+    for (int r = 0; r < K; ++r) {
+      float m = v;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = vmax(m, __shfl_xor(m, off, kWave));
+      const unsigned long long hit = __ballot(v == m);
+      if (lane_id() == __ffsll(static_cast<long long>(hit)) - 1) v = -INFINITY;
+      kth = m;
+    }
+    thr_v = kth;
+    thr_i = INT_MAX;
+  }
+
   __device__ __forceinline__ void push(bool pred, float v, int i) {
     const unsigned long long m = __ballot(pred);
     if (m == 0ull) return;
@@ -141,82 +155,238 @@ struct WaveFilter {
     cnt += __popcll(m);
   }
 
-  // Elements e .. e+3 (valid = false: this lane has none).
-  __device__ __forceinline__ void consume4(float4 a, int e, bool valid = true) {
-    const float m = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
-    // conservative pre-test: an element can only beat the threshold if m >= thr_v
-    if (__ballot(valid && m >= thr_v) == 0ull) return;
-    push(valid && better(a.x, e, thr_v, thr_i), a.x, e);
-    push(valid && better(a.y, e + 1, thr_v, thr_i), a.y, e + 1);
-    push(valid && better(a.z, e + 2, thr_v, thr_i), a.z, e + 2);
-    push(valid && better(a.w, e + 3, thr_v, thr_i), a.w, e + 3);
-    if (cnt > kCap - 4 * kWave) fold();
-  }
-
-  __device__ __forceinline__ void consume1(float a, int e, bool valid) {
-    push(valid && better(a, e, thr_v, thr_i), a, e);
-    if (cnt > kCap - kWave) fold();
+  // n elements per lane at ids e .. e+n-1 (valid = false: this lane has
+  // none); mx is the largest of them.  Nothing happens unless some lane's
+  // mx reaches the threshold.  With EACH, a ballot on x >= thr_v (one
+  // compare) skips the exact test of element j wherever no lane reaches the
+  // threshold (cheaper when n is large); then the buffer is folded if
+  // another n elements per lane might not fit.
+  template <int n, bool EACH>
+  __device__ __forceinline__ void offer(const float *xs, float mx, int e, bool valid) {
+    if (__ballot(valid && mx >= thr_v) == 0ull) return;
+#pragma unroll
+    for (int j = 0; j < n; ++j) {
+      if (!EACH || __ballot(valid && xs[j] >= thr_v) != 0ull)
+        push(valid && better(xs[j], e + j, thr_v, thr_i), xs[j], e + j);
+    }
+    if (cnt > CAP - n * kWave) fold();
   }
 };
 
-template <int K>
+// What a row holds: probabilities (fp32), or logits (fp32 or bf16) that the
+// kernel turns into softmax(logits / T) of the selected entries.
+enum : int { kInProbs = 0, kInLogitsF32 = 1, kInLogitsBf16 = 2 };
+
+// Running softmax normaliser in log2 units: m = largest logit seen, s = sum
+// of 2^((x - m) * c) with c = log2(e) / T.  Entries at -inf add nothing;
+// m = -inf while nothing finite has been seen (then s = 0).
+struct Norm {
+  float m = -INFINITY, s = 0.f;
+
+  // Adds the n entries of xs, whose largest is mx.  Branch-free: the old sum
+  // is rescaled by 2^((m - m') c) (0 while m = -inf), each term is
+  // 2^(x c - m' c) in one fma and one exp.
+  template <int n>
+  __device__ __forceinline__ void add(const float (&xs)[n], float mx, float c) {
+    const float mn = vmax(m, mx);
+    const float mc = mn == -INFINITY ? 0.f : mn * c;
+    float t0 = __builtin_amdgcn_exp2f(fmaf(xs[0], c, -mc)), t1 = 0.f;
+    if constexpr (n > 1) t1 = __builtin_amdgcn_exp2f(fmaf(xs[1], c, -mc));
+#pragma unroll
+    for (int j = 2; j < n; j += 2) {
+      t0 += __builtin_amdgcn_exp2f(fmaf(xs[j], c, -mc));
+      if (j + 1 < n) t1 += __builtin_amdgcn_exp2f(fmaf(xs[j + 1], c, -mc));
+    }
+    s = fmaf(s, __builtin_amdgcn_exp2f(fmaf(m, c, -mc)), t0 + t1);
+    m = mn;
+  }
+  // this <- this (+) o, this one's terms first
+  __device__ __forceinline__ void merge(float om, float os, float c) {
+    const float M = vmax(m, om);
+    if (M == -INFINITY) return;
+    const float a = m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - M) * c);
+    const float b = om == -INFINITY ? 0.f : os * __builtin_amdgcn_exp2f((om - M) * c);
+    m = M;
+    s = a + b;
+  }
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// One slice [lo, hi) of one row.  IN: what the row holds (above).
+template <int K, int IN>
 __global__ void __launch_bounds__(kTopkThreads)
-topk_slice_kernel(const float *__restrict__ probs, int64_t rows, int V, int splits, int chunk,
-                  int k, bool vec, float *__restrict__ out_v, int *__restrict__ out_i,
-                  float *__restrict__ part_v, int *__restrict__ part_i) {
+topk_slice_kernel(const void *__restrict__ rows_in, int64_t rows, int V, int splits, int chunk,
+                  int k, bool vec, float c2, float *__restrict__ out_v, int *__restrict__ out_i,
+                  float *__restrict__ part_v, int *__restrict__ part_i, float2 *__restrict__ part_n) {
   constexpr int NW = kTopkThreads / kWave;
-  __shared__ float s_cv[NW][kCap];
-  __shared__ int s_ci[NW][kCap];
+  constexpr bool LOGITS = IN != kInProbs;
+  constexpr int EPL = IN == kInLogitsBf16 ? 8 : 4;          // elements per 16-byte load
+  // Software pipelined windows (the next window's loads issued before this
+  // one is processed), filtered element by element (see offer) with a
+  // larger candidate buffer: for bf16 rows, which carry twice the elements
+  // per byte, and for K <= 4, where the second set of load registers still
+  // leaves six workgroups per CU.  Otherwise one window at a time.
+  constexpr bool PIPE = EPL == 8 || K <= 4;
+  constexpr int CAP = PIPE ? 768 : 512;                     // candidate slots per wave
+  __shared__ float s_cv[NW][CAP];
+  __shared__ int s_ci[NW][CAP];
   __shared__ float s_tv[NW][K];
   __shared__ int s_ti[NW][K];
+  __shared__ float2 s_norm[NW];
   const int64_t bid = blockIdx.x;
   const int64_t row = bid / splits;
   const int split = static_cast<int>(bid % splits);
   if (row >= rows) return;
-  const float *rp = probs + row * static_cast<int64_t>(V);
   const int lo = split * chunk;
   const int hi = min(V, lo + chunk);
   const int tid = threadIdx.x;
   const int w = tid / kWave;
+  const float *rp32 = static_cast<const float *>(rows_in) + row * static_cast<int64_t>(V);
+  const uint16_t *rp16 = static_cast<const uint16_t *>(rows_in) + row * static_cast<int64_t>(V);
 
-  WaveFilter<K> F;
+  WaveFilter<K, CAP> F;
   F.init(s_cv[w], s_ci[w], s_tv[w], s_ti[w]);
-  if (vec) {
-    // The block reads one contiguous 16 KB window per iteration: load u of
-    // wave w covers 1 KB chunk 4*u + w of the window.  One stream per row
-    // (rather than one per wave) and non-temporal loads (the rows are read
-    // once) keep HBM efficient when a thousand rows stream at once.
-    const int step = 4 * kWave;                   // floats per 1 KB chunk
-    const int win = 4 * NW * step;                // floats per window
-    int base = lo;
-    for (; base + win <= hi; base += win) {
-      const int e = base + w * step + 4 * lane_id();
-      const float4 a0 = stream_load(rp + e);
-      const float4 a1 = stream_load(rp + e + NW * step);
-      const float4 a2 = stream_load(rp + e + 2 * NW * step);
-      const float4 a3 = stream_load(rp + e + 3 * NW * step);
-      F.consume4(a0, e);
-      F.consume4(a1, e + NW * step);
-      F.consume4(a2, e + 2 * NW * step);
-      F.consume4(a3, e + 3 * NW * step);
+  Norm nm;
+  // one 16-byte load: EPL elements starting at element e
+  auto load = [&](int e) {
+    return IN == kInLogitsBf16 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(rp16 + e))
+                               : __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(rp32 + e));
+  };
+  auto unpack = [&](const f32x4v &u, float *x) {
+    if constexpr (IN == kInLogitsBf16) {
+      const uint32_t wd[4] = {__float_as_uint(u.x), __float_as_uint(u.y), __float_as_uint(u.z),
+                              __float_as_uint(u.w)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf16_to_f32(wd[j] & 0xffffu);
+        x[2 * j + 1] = __uint_as_float(wd[j] & 0xffff0000u);
+      }
+    } else {
+      x[0] = u.x;
+      x[1] = u.y;
+      x[2] = u.z;
+      x[3] = u.w;
     }
-    for (int e = base + w * step + 4 * lane_id(); e - 4 * lane_id() < hi; e += NW * step) {
+  };
+  if (vec) {
+    // The block reads one contiguous window of kLoads * 4 KB per iteration:
+    // load u of wave w covers 1 KB chunk 4*u + w of the window.  One stream per row
+    // (rather than one per wave) and non-temporal loads (the rows are read
+    // once) keep HBM efficient when a thousand rows stream at once.  The
+    // loads are all in flight before the first is used, one ballot
+    // tests the lane maxima of the window against the threshold, and the
+    // normaliser takes the window in one update.
+    constexpr int step = EPL * kWave;             // elements per 1 KB chunk
+    constexpr int win = kLoads * NW * step;       // elements per window
+    // the window at base, its loads in r
+    auto window = [&](int base, const f32x4v (&r)[kLoads]) {
+      const int e = base + w * step + EPL * lane_id();
+      float x[kLoads * EPL];
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) unpack(r[u], x + u * EPL);
+      float lmx[kLoads];
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        lmx[u] = x[u * EPL];
+#pragma unroll
+        for (int j = 1; j < EPL; ++j) lmx[u] = vmax(lmx[u], x[u * EPL + j]);
+      }
+      float mx = lmx[0];
+#pragma unroll
+      for (int u = 1; u < kLoads; ++u) mx = vmax(mx, lmx[u]);
+      if (base == lo) F.seed(mx);                 // the first window's lane maxima
+      if (__ballot(mx >= F.thr_v) != 0ull) {
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) F.template offer<EPL, PIPE>(x + u * EPL, lmx[u], e + u * NW * step, true);
+      }
+      if constexpr (LOGITS) nm.add(x, mx, c2);
+    };
+    auto issue = [&](int base, f32x4v (&r)[kLoads]) {
+      const int e = base + w * step + EPL * lane_id();
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) r[u] = load(e + u * NW * step);
+    };
+    int base = lo;
+    if constexpr (PIPE) {
+      if (base + win <= hi) {
+        // the next window's loads are in flight while this one is processed
+        f32x4v cur[kLoads], nxt[kLoads];
+        issue(base, cur);
+        for (; base + 2 * win <= hi; base += win) {
+          issue(base + win, nxt);
+          __builtin_amdgcn_sched_barrier(0);
+          window(base, cur);
+#pragma unroll
+          for (int u = 0; u < kLoads; ++u) cur[u] = nxt[u];
+        }
+        window(base, cur);
+        base += win;
+      }
+    } else {
+      for (; base + win <= hi; base += win) {
+        f32x4v cur[kLoads];
+        issue(base, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        window(base, cur);
+      }
+    }
+    for (int e = base + w * step + EPL * lane_id(); e - EPL * lane_id() < hi; e += NW * step) {
       const bool in = e < hi;
-      const float4 a = in ? stream_load(rp + e) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      F.consume4(a, e, in);
+      float x[EPL];
+      if (in) {
+        unpack(load(e), x);
+      } else {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) x[j] = -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int j = 1; j < EPL; ++j) mx = vmax(mx, x[j]);
+      F.template offer<EPL, PIPE>(x, mx, e, in);
+      if constexpr (LOGITS) {
+        if (in) nm.add(x, mx, c2);
+      }
     }
   } else {
     for (int e0 = lo + w * kWave; e0 < hi; e0 += NW * kWave) {
       const int e = e0 + lane_id();
       const bool in = e < hi;
-      F.consume1(in ? rp[e] : -INFINITY, e, in);
+      float x[1] = {-INFINITY};
+      if (in) x[0] = IN == kInLogitsBf16 ? bf16_to_f32(rp16[e]) : rp32[e];
+      F.template offer<1, false>(x, x[0], e, in);
+      if constexpr (LOGITS) {
+        if (in) nm.add(x, x[0], c2);
+      }
     }
   }
   F.fold();
+  if constexpr (LOGITS) {
+    // the wave's lanes in butterfly order, then the waves in order
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float om = __shfl_xor(nm.m, off, kWave), os = __shfl_xor(nm.s, off, kWave);
+      if (lane_id() & off) {
+        Norm t;
+        t.m = om;
+        t.s = os;
+        t.merge(nm.m, nm.s, c2);
+        nm = t;
+      } else {
+        nm.merge(om, os, c2);
+      }
+    }
+    if (lane_id() == 0) s_norm[w] = make_float2(nm.m, nm.s);
+  }
   __syncthreads();
 
   // wave 0 merges the four per-wave lists
   if (w == 0) {
+    Norm tot;
+    if constexpr (LOGITS) {
+#pragma unroll
+      for (int x = 0; x < NW; ++x) tot.merge(s_norm[x].x, s_norm[x].y, c2);
+    }
     SortedK<K> L;
     L.init();
     for (int x = lane_id(); x < NW * K; x += kWave) L.insert(s_tv[x / K][x % K], s_ti[x / K][x % K]);
@@ -228,7 +398,7 @@ topk_slice_kernel(const float *__restrict__ probs, int64_t rows, int V, int spli
       if (lane_id() == 0) {
         if (splits == 1) {
           if (r < k) {
-            out_v[row * k + r] = bv;
+            out_v[row * k + r] = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
             out_i[row * k + r] = bi;
           }
         } else {
@@ -237,20 +407,29 @@ topk_slice_kernel(const float *__restrict__ probs, int64_t rows, int V, int spli
         }
       }
     }
+    if (LOGITS && splits > 1 && lane_id() == 0) part_n[bid] = make_float2(tot.m, tot.s);
   }
 }
 
-// One wave per row merges splits*K candidates.
-template <int K>
+// One wave per row merges splits*K candidates (and, for logits, the splits'
+// normalisers in split order).
+template <int K, bool LOGITS>
 __global__ void __launch_bounds__(kWave)
-topk_merge_kernel(int64_t rows, int splits, int k, const float *__restrict__ part_v,
-                  const int *__restrict__ part_i, float *__restrict__ out_v,
+topk_merge_kernel(int64_t rows, int splits, int k, float c2, const float *__restrict__ part_v,
+                  const int *__restrict__ part_i, const float2 *__restrict__ part_n, float *__restrict__ out_v,
                   int *__restrict__ out_i) {
   const int64_t row = blockIdx.x;
   if (row >= rows) return;
   const int n = splits * K;
   const float *pv = part_v + row * n;
   const int *pi = part_i + row * n;
+  Norm tot;
+  if constexpr (LOGITS) {
+    for (int x = 0; x < splits; ++x) {
+      const float2 t = part_n[row * splits + x];
+      tot.merge(t.x, t.y, c2);
+    }
+  }
   SortedK<K> L;
   L.init();
   for (int c = lane_id(); c < n; c += kWave) L.insert(pv[c], pi[c]);
@@ -260,7 +439,7 @@ topk_merge_kernel(int64_t rows, int splits, int k, const float *__restrict__ par
     wave_best(bv, bi);
     if (L.i[0] == bi && L.v[0] == bv && bi != INT_MAX) L.pop_front();
     if (lane_id() == 0) {
-      out_v[row * k + r] = bv;
+      out_v[row * k + r] = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
       out_i[row * k + r] = bi;
     }
   }
@@ -279,24 +458,74 @@ TopkPlan plan_topk(int64_t rows, int V, int k) {
   const int64_t max_splits = V / 4096 > 0 ? V / 4096 : 1;
   if (splits > max_splits) splits = max_splits;
   int64_t chunk = (V + splits - 1) / splits;
-  chunk = (chunk + 3) / 4 * 4;
+  chunk = (chunk + 7) / 8 * 8;                       // whole 16-byte loads of fp32 and bf16
   splits = (V + chunk - 1) / chunk;
   p.splits = static_cast<int>(splits);
   p.chunk = static_cast<int>(chunk);
   return p;
 }
 
-template <int K>
-int32_t launch_topk(const float *probs, int64_t rows, int V, int k, const TopkPlan &p, bool vec,
-                    float *out_v, int *out_i, float *part_v, int *part_i, hipStream_t st) {
+size_t topk_workspace(int64_t rows, int V, int k, bool logits) {
+  const TopkPlan p = plan_topk(rows, V, k);
+  if (p.splits == 1) return 0;
+  Carver c(nullptr);
+  c.take<float>(static_cast<size_t>(rows) * p.splits * p.K);
+  c.take<int>(static_cast<size_t>(rows) * p.splits * p.K);
+  if (logits) c.take<float2>(static_cast<size_t>(rows) * p.splits);
+  return c.bytes();
+}
+
+template <int K, int IN>
+int32_t launch_topk(const void *rows_in, int64_t rows, int V, int k, const TopkPlan &p, bool vec, float c2,
+                    float *out_v, int *out_i, float *part_v, int *part_i, float2 *part_n, hipStream_t st) {
   const int64_t blocks = rows * p.splits;
-  hipLaunchKernelGGL(topk_slice_kernel<K>, dim3(static_cast<unsigned>(blocks)), dim3(kTopkThreads), 0,
-                     st, probs, rows, V, p.splits, p.chunk, k, vec, out_v, out_i, part_v, part_i);
+  hipLaunchKernelGGL((topk_slice_kernel<K, IN>), dim3(static_cast<unsigned>(blocks)), dim3(kTopkThreads), 0,
+                     st, rows_in, rows, V, p.splits, p.chunk, k, vec, c2, out_v, out_i, part_v, part_i, part_n);
   int32_t rc = check_launch("topk_slice_kernel");
   if (rc != SDV_OK || p.splits == 1) return rc;
-  hipLaunchKernelGGL(topk_merge_kernel<K>, dim3(static_cast<unsigned>(rows)), dim3(kWave), 0, st, rows,
-                     p.splits, k, part_v, part_i, out_v, out_i);
+  hipLaunchKernelGGL((topk_merge_kernel<K, IN != kInProbs>), dim3(static_cast<unsigned>(rows)), dim3(kWave), 0,
+                     st, rows, p.splits, k, c2, part_v, part_i, part_n, out_v, out_i);
   return check_launch("topk_merge_kernel");
+}
+
+// Common checks and dispatch of both entry points.
+int32_t run_topk(const char *what, int IN, const void *rows_in, int64_t rows, int32_t V, int32_t k, float c2,
+                 float *topk_p, int32_t *topk_id, void *ws, size_t ws_bytes, void *stream) {
+  SDV_REQUIRE(rows >= 0 && V >= 1 && k >= 1 && k <= V, SDV_E_SHAPE,
+              "%s: need rows >= 0 and 1 <= k <= V (rows=%lld V=%d k=%d)", what, static_cast<long long>(rows), V,
+              k);
+  SDV_REQUIRE(k <= 32, SDV_E_UNSUPPORTED, "%s: k=%d above 32", what, k);
+  SDV_REQUIRE(V < INT_MAX - 4096, SDV_E_UNSUPPORTED, "%s: V too large", what);
+  SDV_REQUIRE(rows <= (1LL << 30), SDV_E_UNSUPPORTED, "%s: too many rows", what);
+  if (rows == 0) return SDV_OK;
+  SDV_REQUIRE(rows_in && topk_p && topk_id, SDV_E_NULL, "%s: NULL pointer", what);
+  const TopkPlan p = plan_topk(rows, V, k);
+  const size_t need = topk_workspace(rows, V, k, IN != kInProbs);
+  SDV_REQUIRE(ws_bytes >= need && (need == 0 || ws), SDV_E_WORKSPACE, "%s: workspace of %zu bytes needed", what,
+              need);
+  Carver c(ws);
+  float *part_v = c.take<float>(static_cast<size_t>(rows) * p.splits * p.K);
+  int *part_i = c.take<int>(static_cast<size_t>(rows) * p.splits * p.K);
+  float2 *part_n = IN != kInProbs ? c.take<float2>(static_cast<size_t>(rows) * p.splits) : nullptr;
+  const int epl = IN == kInLogitsBf16 ? 8 : 4;
+  const bool vec = (V % epl == 0) && (reinterpret_cast<uintptr_t>(rows_in) % 16 == 0);
+  hipStream_t st = as_stream(stream);
+#define SDV_TOPK_IN(KK)                                                                                          \
+  (IN == kInProbs        ? launch_topk<KK, kInProbs>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, part_v,     \
+                                                     part_i, part_n, st)                                         \
+   : IN == kInLogitsF32 ? launch_topk<KK, kInLogitsF32>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, part_v, \
+                                                         part_i, part_n, st)                                     \
+                         : launch_topk<KK, kInLogitsBf16>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id,       \
+                                                          part_v, part_i, part_n, st))
+  switch (p.K) {
+    case 1: return SDV_TOPK_IN(1);
+    case 2: return SDV_TOPK_IN(2);
+    case 4: return SDV_TOPK_IN(4);
+    case 8: return SDV_TOPK_IN(8);
+    case 16: return SDV_TOPK_IN(16);
+    default: return SDV_TOPK_IN(32);
+  }
+#undef SDV_TOPK_IN
 }
 
 }  // namespace
@@ -306,41 +535,30 @@ using namespace sdv;
 
 extern "C" size_t sdv_draft_topk_workspace_size(int64_t rows, int32_t V, int32_t k) {
   if (rows <= 0 || V <= 0 || k <= 0 || k > 32) return 0;
-  const TopkPlan p = plan_topk(rows, V, k);
-  if (p.splits == 1) return 0;
-  Carver c(nullptr);
-  c.take<float>(static_cast<size_t>(rows) * p.splits * p.K);
-  c.take<int>(static_cast<size_t>(rows) * p.splits * p.K);
-  return c.bytes();
+  return topk_workspace(rows, V, k, false);
 }
 
 extern "C" int32_t sdv_draft_topk(const float *probs, int64_t rows, int32_t V, int32_t k,
                                   float *topk_p, int32_t *topk_id, void *ws, size_t ws_bytes,
                                   void *stream) {
   clear_error();
-  SDV_REQUIRE(rows >= 0 && V >= 1 && k >= 1 && k <= V, SDV_E_SHAPE,
-              "draft_topk: need rows >= 0 and 1 <= k <= V (rows=%lld V=%d k=%d)",
-              static_cast<long long>(rows), V, k);
-  SDV_REQUIRE(k <= 32, SDV_E_UNSUPPORTED, "draft_topk: k=%d above 32", k);
-  SDV_REQUIRE(V < INT_MAX - 4096, SDV_E_UNSUPPORTED, "draft_topk: V too large");
-  SDV_REQUIRE(rows <= (1LL << 30), SDV_E_UNSUPPORTED, "draft_topk: too many rows");
-  if (rows == 0) return SDV_OK;
-  SDV_REQUIRE(probs && topk_p && topk_id, SDV_E_NULL, "draft_topk: NULL pointer");
-  const TopkPlan p = plan_topk(rows, V, k);
-  const size_t need = sdv_draft_topk_workspace_size(rows, V, k);
-  SDV_REQUIRE(ws_bytes >= need && (need == 0 || ws), SDV_E_WORKSPACE,
-              "draft_topk: workspace of %zu bytes needed", need);
-  Carver c(ws);
-  float *part_v = c.take<float>(static_cast<size_t>(rows) * p.splits * p.K);
-  int *part_i = c.take<int>(static_cast<size_t>(rows) * p.splits * p.K);
-  const bool vec = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(probs) % 16 == 0);
-  hipStream_t st = as_stream(stream);
-  switch (p.K) {
-    case 1: return launch_topk<1>(probs, rows, V, k, p, vec, topk_p, topk_id, part_v, part_i, st);
-    case 2: return launch_topk<2>(probs, rows, V, k, p, vec, topk_p, topk_id, part_v, part_i, st);
-    case 4: return launch_topk<4>(probs, rows, V, k, p, vec, topk_p, topk_id, part_v, part_i, st);
-    case 8: return launch_topk<8>(probs, rows, V, k, p, vec, topk_p, topk_id, part_v, part_i, st);
-    case 16: return launch_topk<16>(probs, rows, V, k, p, vec, topk_p, topk_id, part_v, part_i, st);
-    default: return launch_topk<32>(probs, rows, V, k, p, vec, topk_p, topk_id, part_v, part_i, st);
-  }
+  return run_topk("draft_topk", kInProbs, probs, rows, V, k, 0.f, topk_p, topk_id, ws, ws_bytes, stream);
+}
+
+extern "C" size_t sdv_draft_topk_logits_workspace_size(int64_t rows, int32_t V, int32_t k) {
+  if (rows <= 0 || V <= 0 || k <= 0 || k > 32) return 0;
+  return topk_workspace(rows, V, k, true);
+}
+
+extern "C" int32_t sdv_draft_topk_logits(const void *logits, int32_t dtype, int64_t rows, int32_t V, int32_t k,
+                                         float temperature, float *topk_p, int32_t *topk_id, void *ws,
+                                         size_t ws_bytes, void *stream) {
+  clear_error();
+  SDV_REQUIRE(dtype == SDV_DTYPE_F32 || dtype == SDV_DTYPE_BF16, SDV_E_UNSUPPORTED,
+              "draft_topk_logits: dtype %d not fp32 or bf16", dtype);
+  SDV_REQUIRE(temperature > 0.f && std::isfinite(temperature), SDV_E_SHAPE,
+              "draft_topk_logits: temperature must be positive");
+  const float c2 = 1.4426950408889634f / temperature;
+  return run_topk("draft_topk_logits", dtype == SDV_DTYPE_BF16 ? kInLogitsBf16 : kInLogitsF32, logits, rows, V,
+                  k, c2, topk_p, topk_id, ws, ws_bytes, stream);
 }

@@ -18,7 +18,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     names = declared_symbols()
-    for must in ("sdv_draft_topk", "sdv_build_tree", "sdv_tree_verify_attention", "sdv_verify_accept",
+    for must in ("sdv_draft_topk", "sdv_draft_topk_logits", "sdv_build_tree", "sdv_tree_verify_attention", "sdv_verify_accept",
                  "sdv_compact_kv", "sdv_tli_lm_head", "sdv_tli_map_ids", "sdv_tli_constrain_draft_logits",
                  "sdv_tli_q_scatter", "sdv_tli_build_maps", "sdv_last_error"):
         assert must in names
@@ -49,6 +49,9 @@ def test_host_side_validation_without_a_device():
     args = [None] * 15
     assert lib.sdv_build_tree(sh, *args, None) == -2
     assert lib.sdv_draft_topk(None, 0, 10, 2, None, None, None, 0, None) == 0         # empty is fine
+    assert lib.sdv_draft_topk_logits(None, 2, 4, 10, 2, 1.0, None, None, None, 0, None) == -3   # unknown dtype
+    assert lib.sdv_draft_topk_logits(None, 1, 4, 10, 2, 0.0, None, None, None, 0, None) == -2   # temperature 0
+    assert lib.sdv_draft_topk_logits(None, 0, 4, 10, 11, 1.0, None, None, None, 0, None) == -2  # k > V
     ash = _lib.AttnShape(1, 4, 6, 4, 128, 1, 10, 10)                                  # Hq % Hkv != 0
     assert lib.sdv_tree_verify_attention(ash, ctypes.c_float(0.0), *([None] * 8), None, 0, None) == -2
     ash = _lib.AttnShape(1, 4, 8, 4, 96, 1, 10, 10)                                   # D not in {64,128}

@@ -54,6 +54,40 @@ def test_topk_bit_exact(rows, V, k, coarse):
     assert np.array_equal(host(gp), op)
 
 
+# Fused softmax + top-k from logits.  Ids must match bit for bit (the order
+# is that of the logits); probabilities within 1e-4 relative: the exponent
+# (x - m) * log2(e) / T rounds once in fp32 (|x - m| < 64 here: < 1e-5
+# relative in p) and the normaliser sums about V / (256 * splits) terms per
+# lane in fp32 before a fixed-order tree (< 512 * 2^-24 = 3e-5 relative).
+@pytest.mark.parametrize("rows,V,k,T,bf16,kind", [
+    (10, 1000, 2, 1.0, False, "normal"), (64, 4099, 8, 0.7, False, "normal"), (33, 128256, 8, 1.0, True, "normal"),
+    (1056, 128256, 8, 1.0, True, "normal"), (300, 128256, 8, 0.7, False, "normal"), (5, 64, 32, 1.3, True, "ties"),
+    (200, 5000, 13, 1.0, False, "ties"), (3, 7, 7, 2.0, True, "normal"), (1, 1, 1, 1.0, False, "normal"),
+    (17, 40003, 4, 0.5, True, "masked"), (40, 9000, 16, 1.0, False, "masked"), (2, 131072, 32, 1.0, True, "ties")])
+def test_topk_from_logits(rows, V, k, T, bf16, kind):
+    rng = np.random.default_rng(rows * 7 + V + k)
+    if kind == "ties":
+        x = (rng.integers(-12, 4, size=(rows, V)) / 4.0).astype(np.float32)
+    else:
+        x = (rng.standard_normal((rows, V)) * 3.0).astype(np.float32)
+    if kind == "masked":
+        x[rng.random((rows, V)) < 0.9] = -np.inf
+        x[:, 0] = 0.5                                          # every row keeps a finite entry
+    if bf16:
+        bits = workloads.to_bf16_bits(x)
+        g = dev(bits).view(torch.bfloat16)
+        ov, oi = otopk.draft_topk_from_logits(bits, k, T, bf16=True)
+    else:
+        g = dev(x)
+        ov, oi = otopk.draft_topk_from_logits(x, k, T)
+    say("topk_logits", rows, V, k, T, "bf16" if bf16 else "f32", kind)
+    gp, gi = sdv.sdv_draft_topk_logits(g, k, T)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gi), oi)
+    got = host(gp).astype(np.float64)
+    assert np.all(np.abs(got - ov) <= 1e-4 * ov + 1e-37)
+
+
 # -------------------------------------------------------------------- A2-A4
 
 TREE_KEYS = ("tokens", "parent", "depth", "positions", "score", "q_row", "mask", "mask_bits", "retrieve_index",

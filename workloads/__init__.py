@@ -236,11 +236,13 @@ def _paged_layout(cfg: Config, rng: np.random.Generator, prefix_len: np.ndarray,
     return table, total
 
 
-def generate(cfg: Config, *, with_attention: bool = True, with_rows: bool = True) -> Dict[str, np.ndarray]:
+def generate(cfg: Config, *, with_attention: bool = True, with_rows: bool = True,
+             with_logits: bool = False) -> Dict[str, np.ndarray]:
     """Draw every input of ``cfg``.  Large configs take seconds.
 
     Keys (present when the config has the stage):
       draft_probs [B,R,V] f32 -- processed draft distributions (A1 input, q rows)
+      draft_logits [B,R,V] f32 -- the logits they are softmax(. / T) of (with_logits)
       target      [B,N,V] f32 -- greedy: raw logits; stochastic: processed p
       root_token [B] i32, prefix_len [B] i32
       u_accept, u_draw [B,N] f32 (stochastic)
@@ -269,6 +271,8 @@ def generate(cfg: Config, *, with_attention: bool = True, with_rows: bool = True
         else:
             dl = _normal_f32(rs["draft_logits"], (B, R, V), cfg.logit_std)
             out["draft_probs"] = softmax_rows(dl, cfg.temperature)
+            if with_logits:
+                out["draft_logits"] = dl
             del dl
         tl = _normal_f32(rs["target_logits"], (B, N, V), cfg.logit_std)
         if cfg.mode == "greedy":
