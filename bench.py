@@ -247,8 +247,8 @@ MEASURED_TRAFFIC = {
         "workload": "c3",
         "sources": ["speculative_decoding_eagle_amd/csrc/attn_wide.hip",
                     "speculative_decoding_eagle_amd/csrc/attn_common.hpp"],
-        "sha256": "8bf14e274c37619e26f5bcb275d23f8cf643592f516690ab45c01edc80917a16",
-        "fetch_kib": 206285.5, "fetch_factor": 1.99996,
+        "sha256": "1474d20878c645eb0d00eb191903cc15da22383fa9b28e2b8ab8b1535cb05243",
+        "fetch_kib": 206288.1, "fetch_factor": 1.99996,
         "write_kib": 63016.0, "write_factor": 1.0,
     },
 }
