@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--draft-input", default="probs", choices=["probs", "logits_f32", "logits_bf16"],
                     help="what the draft top-k reads: the processed probability rows, or the draft logits "
                          "(fp32 or bf16) with the softmax fused into the top-k (non-TLI workloads)")
+    ap.add_argument("--extend-prep", action="store_true",
+                    help="add the index preparation of the draft extend after the accept walk to the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -71,7 +73,7 @@ def log(msg):
 class Pipeline:
     """Preallocated device buffers and the per-stage calls of one step."""
 
-    def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs"):
+    def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs", extend_prep=False):
         import torch
         import speculative_decoding_eagle_amd as sdv
         self.torch, self.sdv, self.cfg = torch, sdv, cfg
@@ -92,6 +94,8 @@ class Pipeline:
         else:
             self.draft_rows = d["draft_probs"]
         self.draft_input = draft_input
+        self.extend_prep = extend_prep
+        self.ext = {}
         if draft_input != "probs":
             # the fused path reads logits; the stochastic accept still reads
             # the probability rows of the draft distribution
@@ -184,6 +188,11 @@ class Pipeline:
                                 cfg.N, cfg.S, cfg.page, pools[0], pools[1], new_len=self.new_len, freed=self.freed,
                                 num_freed=self.num_freed)
 
+    def s_extend(self):
+        self.ext = self.sdv.sdv_draft_extend_prep(self.d["prefix_len"], self.acc["commit_len"],
+                                                  self.acc["commit_tokens"], self.acc["accept_path"], self.cfg.N,
+                                                  t2d=self.t2d if self.cfg.is_tli else None, out=self.ext)
+
     def s_remap(self):
         self.sdv.sdv_tli_map_ids(self.t2d, self.acc["commit_tokens"], out=self.remap_out)
 
@@ -200,6 +209,8 @@ class Pipeline:
             st.append(("compact_kv", lambda: self.s_compact(i)))
         if cfg.is_tli:
             st.append(("t2d_remap", self.s_remap))
+        if self.extend_prep:
+            st.append(("extend_prep", self.s_extend))
         return st
 
     def run_all(self, i):
@@ -359,7 +370,7 @@ def main():
     inp = workloads.generate(cfg, with_logits=args.draft_input != "probs")
     t_gen = time.perf_counter() - t_gen
     log("inputs ready in %.1f s; uploading and warming up" % t_gen)
-    pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept, args.draft_input)
+    pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept, args.draft_input, args.extend_prep)
     stages = [name for name, _ in pipe.stages(0)]
 
     for i in range(args.warmup):
@@ -416,7 +427,8 @@ def main():
         "dtype": "f32+bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[cfg.name], "name": cfg.name, "batch": cfg.B, "tree_tokens": cfg.N,
-                   "accept": args.accept, "draft_input": args.draft_input},
+                   "accept": args.accept, "draft_input": args.draft_input,
+                   "extend_prep": args.extend_prep},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_gbs": {k: round(work[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9, 1) for k in stages if k in work},
         "accepted_tokens": work["accept"]["accepted"],

@@ -309,6 +309,43 @@ int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, const float
                           const int32_t *tgt_ids, float *q_target, void *ws, size_t ws_bytes,
                           void *stream);
 
+/* ------------------------------------------------------------------------
+ * Draft extend after a verify step: index preparation.
+ * "EAGLE speculative decoding in four parts", "Self-test" answer 1 (after
+ * verification the draft model runs one extend over the accepted tokens to
+ * prepare the next round); zero-to-sglang ch.10 section 3.1 (draft, verify,
+ * then the draft-side extend for the next round); sglang PR #22883
+ * "Modifications" (under TLI the accepted tokens are mapped target -> draft
+ * for that extend; the target ids themselves are left as they are).
+ *
+ * Inputs, as sdv_verify_accept writes them (device): commit_len [B],
+ * commit_tokens [B, S+1], accept_path [B, S+1]; prefix_len [B] as given to
+ * the tree build.  Committed token j of request b was chosen at node
+ * accept_path[b, j].  t2d: device [V_target] target -> draft map (as
+ * sdv_tli_build_maps writes it), or NULL for no mapping.
+ * Outputs (device, int32), requests packed in batch order:
+ *   extend_start [B+1]: extend_start[b] = sum of commit_len over requests
+ *     before b; extend_start[B] = total rows;
+ *   for row = extend_start[b] + j, j < commit_len[b]:
+ *     input_ids[row]    = commit_tokens[b, j], through t2d when given;
+ *     positions[row]    = prefix_len[b] + 1 + j;
+ *     hidden_index[row] = b * N + accept_path[b, j] (the verify output row
+ *                         of the node that chose the token);
+ *   last_index [B] = extend_start[b] + commit_len[b] - 1 (-1 if none);
+ *   seq_len [B] = prefix_len[b] + 1 + commit_len[b].
+ * input_ids, positions, hidden_index need room for B * (S+1) rows; rows past
+ * the total are not written.  A commit_len outside [0, S+1] is clamped into
+ * it; a negative token, or one outside [0, V_target) when t2d is given,
+ * gives input_id -1, and a node outside [0, N) gives hidden_index -1.
+ * Limits: B * N < 2^31.
+ * ---------------------------------------------------------------------- */
+int32_t sdv_draft_extend_prep(int32_t B, int32_t N, int32_t S, const int32_t *prefix_len,
+                              const int32_t *commit_len, const int32_t *commit_tokens,
+                              const int32_t *accept_path, const int32_t *t2d, int32_t V_target,
+                              int32_t *extend_start, int32_t *input_ids, int32_t *positions,
+                              int32_t *hidden_index, int32_t *last_index, int32_t *seq_len,
+                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,10 +25,13 @@ Modules and the passages they follow:
                    verification and slots"; zero-to-sglang ch.10 section 5.2).
 * ``tli``       -- Token-Level Intersection remaps, logit masking and the pruned
                    LM head (sglang PR #22883, "Modifications").
+* ``extend``    -- index preparation of the draft extend after a verify step
+                   ("EAGLE speculative decoding in four parts", "Self-test";
+                   zero-to-sglang ch.10 section 3.1; PR #22883 hooks).
 
 Every function that no test pins to something outside itself says
 "parity unpinned" in its docstring.
 """
-from . import topk, tree, attention, accept, compact, tli  # noqa: F401
+from . import topk, tree, attention, accept, compact, tli, extend  # noqa: F401
 
-__all__ = ["topk", "tree", "attention", "accept", "compact", "tli"]
+__all__ = ["topk", "tree", "attention", "accept", "compact", "tli", "extend"]

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     SdvError,
     sdv_build_tree,
     sdv_compact_kv,
+    sdv_draft_extend_prep,
     sdv_draft_topk,
     sdv_draft_topk_logits,
     sdv_tli_build_maps,

@@ -235,6 +235,33 @@ def sdv_verify_accept(mode: int, tree, target, S: int, eos_id: int = -1, remaini
     return out
 
 
+# ------------------------------------------------- draft extend index prep
+
+EXTEND_OUTPUTS = ("extend_start", "input_ids", "positions", "hidden_index", "last_index", "seq_len")
+
+
+def sdv_draft_extend_prep(prefix_len, commit_len, commit_tokens, accept_path, N: int, t2d=None, out=None):
+    """Packed rows of the draft extend after a verify step.  Returns a dict of
+    EXTEND_OUTPUTS; input_ids / positions / hidden_index hold B * (S+1) rows
+    of which extend_start[B] are written."""
+    B, S1 = commit_tokens.shape
+    dev = commit_tokens.device
+    out = {} if out is None else out
+    sizes = {"extend_start": B + 1, "input_ids": B * S1, "positions": B * S1, "hidden_index": B * S1,
+             "last_index": B, "seq_len": B}
+    for name in EXTEND_OUTPUTS:
+        if out.get(name) is None:
+            out[name] = torch.empty(sizes[name], dtype=torch.int32, device=dev)
+    vt = 0 if t2d is None else t2d.numel()
+    _check(_lib.lib().sdv_draft_extend_prep(
+        B, N, S1 - 1, _ptr(prefix_len, torch.int32, "prefix_len"), _ptr(commit_len, torch.int32, "commit_len"),
+        _ptr(commit_tokens, torch.int32, "commit_tokens"), _ptr(accept_path, torch.int32, "accept_path"),
+        _ptr(t2d, torch.int32, "t2d", allow_none=True), vt,
+        *[_ptr(out[name], torch.int32, name) for name in EXTEND_OUTPUTS], _stream(dev)),
+        "sdv_draft_extend_prep")
+    return out
+
+
 # ---------------------------------------------------------------------- A8
 
 def sdv_compact_kv(page_table, prefix_len, accept_len, accept_path, N: int, S: int, page: int,

@@ -13,6 +13,7 @@ import workloads
 from oracle import accept as oacc
 from oracle import attention as oatt
 from oracle import compact as ocmp
+from oracle import extend as oext
 from oracle import tli as otli
 from oracle import topk as otopk
 from oracle import tree as otree
@@ -279,6 +280,85 @@ def test_compaction_bit_exact(page, layers, B, N, S):
     if page > 1:
         for x, y in zip(gk + gv, k2 + v2):
             assert np.array_equal(host(x).view(np.uint16), y)
+
+
+# ------------------------------------------------- draft extend index prep
+
+def _extend_case(prefix_len, commit_len, commit_tokens, accept_path, N, t2d=None):
+    B = commit_tokens.shape[0]
+    g = sdv.sdv_draft_extend_prep(dev(prefix_len.astype(np.int32)), dev(commit_len.astype(np.int32)),
+                                  dev(commit_tokens.astype(np.int32)), dev(accept_path.astype(np.int32)), N,
+                                  t2d=None if t2d is None else dev(t2d))
+    torch.cuda.synchronize()
+    o = oext.draft_extend_prep(prefix_len, commit_len, commit_tokens, accept_path, N, t2d=t2d)
+    total = int(o["extend_start"][-1])
+    assert np.array_equal(host(g["extend_start"]), o["extend_start"])
+    for key in ("input_ids", "positions", "hidden_index"):
+        assert np.array_equal(host(g[key])[:total], o[key]), key
+    for key in ("last_index", "seq_len"):
+        assert np.array_equal(host(g[key]), o[key]), key
+    assert B == 0 or total <= B * commit_tokens.shape[1]
+
+
+@pytest.mark.parametrize("seed,tli", [(0, False), (1, True)])
+def test_extend_prep_after_accept(seed, tli):
+    """The accept walk's outputs (oracle, on a c3-shaped tree with planted
+    acceptance and budgets) through the GPU and oracle index preparation."""
+    cfg = workloads.get_config("c3", V=3000, B=24)
+    inp = workloads.generate(cfg, with_attention=False)
+    tree = oracle_tree(inp, cfg)
+    rng = np.random.default_rng(seed)
+    target = plant_greedy(inp["target"], tree, rng, cfg.S)
+    rem = rng.integers(0, cfg.S + 2, size=cfg.B).astype(np.int32)
+    r = oacc.verify_greedy(tree, target, cfg.S, remaining=rem)
+    t2d = None
+    if tli:
+        K = 1200
+        inter = np.sort(rng.choice(4000, K, replace=False)).astype(np.int32)
+        tgt = rng.choice(cfg.V, K, replace=False).astype(np.int32)
+        t2d = otli.build_maps(inter, tgt, 4000, cfg.V, int(np.setdiff1d(np.arange(4000), inter)[0]))[1]
+    say("extend prep after accept", seed, tli)
+    _extend_case(inp["prefix_len"], r["commit_len"], r["commit_tokens"], r["accept_path"], cfg.N, t2d)
+
+
+@pytest.mark.parametrize("B,S,N", [(0, 4, 8), (1, 0, 1), (37, 5, 64), (1500, 4, 32), (3000, 63, 256)])
+def test_extend_prep_shapes(B, S, N):
+    """Synthetic batches: empty, single, several scan chunks, the largest S;
+    about a fifth of the requests commit nothing."""
+    rng = np.random.default_rng(B + S)
+    S1 = S + 1
+    commit_len = np.where(rng.random(B) < 0.2, 0, rng.integers(1, S1 + 1, size=B)).astype(np.int32)
+    tokens = np.full((B, S1), -1, np.int32)
+    path = np.full((B, S1), -1, np.int32)
+    for b in range(B):
+        c = commit_len[b]
+        tokens[b, :c] = rng.integers(0, 50000, size=c)
+        path[b, :c] = np.sort(rng.choice(N, size=c, replace=False)) if c <= N else 0
+    prefix = rng.integers(0, 100000, size=B).astype(np.int32)
+    t2d = rng.integers(0, 30000, size=50000).astype(np.int32)
+    say("extend prep shapes", B, S, N)
+    _extend_case(prefix, commit_len, tokens, path, N)
+    _extend_case(prefix, commit_len, tokens, path, N, t2d)
+
+
+def test_extend_prep_clamps_out_of_range_inputs():
+    """Documented handling of inputs outside the contract: commit lengths are
+    clamped into [0, S+1]; bad tokens and nodes give -1 in their row."""
+    S, N = 3, 6
+    commit_len = np.array([9, -2, 2, 4], np.int32)
+    tokens = np.array([[1, 2, 3, 4], [5, 6, 7, 8], [-5, 70, 0, 0], [1, 2, 3, 4]], np.int32)
+    path = np.array([[0, 1, 2, 3], [0, 1, 2, 3], [0, 9, 0, 0], [0, 1, 2, 3]], np.int32)
+    prefix = np.array([10, 20, 30, 40], np.int32)
+    t2d = np.arange(60, dtype=np.int32) * 2
+    say("extend prep clamps")
+    g = sdv.sdv_draft_extend_prep(dev(prefix), dev(commit_len), dev(tokens), dev(path), N, t2d=dev(t2d))
+    torch.cuda.synchronize()
+    assert host(g["extend_start"]).tolist() == [0, 4, 4, 6, 10]
+    assert host(g["input_ids"])[:10].tolist() == [2, 4, 6, 8, -1, -1, 2, 4, 6, 8]
+    assert host(g["hidden_index"])[:10].tolist() == [0, 1, 2, 3, 12, -1, 18, 19, 20, 21]
+    assert host(g["positions"])[:10].tolist() == [11, 12, 13, 14, 31, 32, 41, 42, 43, 44]
+    assert host(g["last_index"]).tolist() == [3, -1, 5, 9]
+    assert host(g["seq_len"]).tolist() == [15, 21, 33, 45]
 
 
 # ---------------------------------------------------------------------- A5
