@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--draft-input", default="probs", choices=["probs", "logits_f32", "logits_bf16"],
                     help="what the draft top-k reads: the processed probability rows, or the draft logits "
                          "(fp32 or bf16) with the softmax fused into the top-k (non-TLI workloads)")
+    ap.add_argument("--chain", action="store_true",
+                    help="k = 1 workloads: build the draft as a multi-layer chain (sdv_build_chain) instead of "
+                         "through the tree builder")
     ap.add_argument("--extend-prep", action="store_true",
                     help="add the index preparation of the draft extend after the accept walk to the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -73,7 +76,7 @@ def log(msg):
 class Pipeline:
     """Preallocated device buffers and the per-stage calls of one step."""
 
-    def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs", extend_prep=False):
+    def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs", extend_prep=False, chain=False):
         import torch
         import speculative_decoding_eagle_amd as sdv
         self.torch, self.sdv, self.cfg = torch, sdv, cfg
@@ -95,6 +98,7 @@ class Pipeline:
             self.draft_rows = d["draft_probs"]
         self.draft_input = draft_input
         self.extend_prep = extend_prep
+        self.chain = chain
         self.ext = {}
         if draft_input != "probs":
             # the fused path reads logits; the stochastic accept still reads
@@ -164,6 +168,10 @@ class Pipeline:
 
     def s_tree(self):
         cfg = self.cfg
+        if self.chain:
+            self.tree = self.sdv.sdv_build_chain(self.topk_p, self.topk_id, self.d["root_token"],
+                                                 self.d["prefix_len"], out=self.tree)
+            return
         self.tree = self.sdv.sdv_build_tree(self.topk_p, self.topk_id, self.d["root_token"], self.d["prefix_len"],
                                             cfg.k, cfg.S, cfg.N, out=self.tree)
 
@@ -370,7 +378,11 @@ def main():
     inp = workloads.generate(cfg, with_logits=args.draft_input != "probs")
     t_gen = time.perf_counter() - t_gen
     log("inputs ready in %.1f s; uploading and warming up" % t_gen)
-    pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept, args.draft_input, args.extend_prep)
+    if args.chain and (cfg.k != 1 or cfg.N != cfg.S + 1):
+        print("--chain needs a k = 1 workload whose tree keeps every step (N = S + 1)", file=sys.stderr)
+        sys.exit(2)
+    pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept, args.draft_input, args.extend_prep,
+                    args.chain)
     stages = [name for name, _ in pipe.stages(0)]
 
     for i in range(args.warmup):
@@ -428,7 +440,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[cfg.name], "name": cfg.name, "batch": cfg.B, "tree_tokens": cfg.N,
                    "accept": args.accept, "draft_input": args.draft_input,
-                   "extend_prep": args.extend_prep},
+                   "extend_prep": args.extend_prep, "chain": args.chain},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_gbs": {k: round(work[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9, 1) for k in stages if k in work},
         "accepted_tokens": work["accept"]["accepted"],

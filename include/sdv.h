@@ -134,6 +134,28 @@ int32_t sdv_build_tree(sdv_tree_shape shape, const float *topk_p, const int32_t 
                        int32_t *retrieve_next_sibling, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Multi-layer draft chain.  "[SGLang] Multi-Layer EAGLE", sections 2-3:
+ * each draft step runs its own layer and takes its top-k; the per-step
+ * lists are concatenated along the step dimension, and the draft slices them
+ * by step -- step i gives one node whose parent is the node of step i-1 (the
+ * root for step 0) and whose score is step i's own probability.
+ *
+ * Inputs (device): topk_p / topk_id [B, S] (each step's top-1; the tree
+ * layout [B, S, 1] is the same memory), root_token [B], prefix_len [B].
+ * Outputs as sdv_build_tree with N = S + 1: node i+1 = step i's token,
+ * parent[i] = i - 1, depth = i, positions = prefix_len + i, score = 1.0 for
+ * the root and topk_p[b, i-1] otherwise (not a product), q_row[i] = i
+ * (the draft row of step i) and -1 for the last node, mask = the lower
+ * triangle, retrieve_next_token[i] = i + 1 (-1 last), no siblings.
+ * mask and mask_bits may be NULL.  Limits: 1 <= S <= 255.
+ * ---------------------------------------------------------------------- */
+int32_t sdv_build_chain(int32_t B, int32_t S, const float *topk_p, const int32_t *topk_id,
+                        const int32_t *root_token, const int32_t *prefix_len, int32_t *tokens,
+                        int32_t *parent, int32_t *depth, int32_t *positions, float *score,
+                        int32_t *q_row, uint8_t *mask, uint32_t *mask_bits, int32_t *retrieve_index,
+                        int32_t *retrieve_next_token, int32_t *retrieve_next_sibling, void *stream);
+
+/* ------------------------------------------------------------------------
  * A5  Tree-verify attention.
  * "EAGLE speculative decoding in four parts": verification is one target
  * forward over 1 + candidates tokens per request with a tree attention mask

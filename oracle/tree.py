@@ -186,3 +186,41 @@ def build_tree(topk_p, topk_id, root_token, prefix_len, k: int, S: int, N: int):
             tb.expand([topk_p[b, r] for r in rows], [topk_id[b, r] for r in rows])
         per.append(tb.finalize(N, int(root_token[b]), int(prefix_len[b]), b))
     return {key: np.stack([d[key] for d in per]) for key in per[0]}
+
+
+def build_chain(topk_p, topk_id, root_token, prefix_len):
+    """Multi-layer (MTP) draft chain: one token per draft step.
+
+    "[SGLang] Multi-Layer EAGLE", sections 2-3: each step runs its own draft
+    layer and takes its top-k; the per-step lists are concatenated along the
+    step dimension, and with several steps the draft slices ``tree_info`` by
+    step: step i contributes the score and token of column i, step 0's parent
+    is the root and step i's parent is index i, the token of the step before.
+    The tree is the chain root -> step 0 -> ... -> step S-1 (N = S + 1 nodes)
+    and each node keeps its own step's score (no product along the path).
+
+    ``topk_p`` / ``topk_id``: [B, S] (or [B, S, 1]) top-1 of each step.
+    Readings: node i+1 is step i's token; its children come from draft row
+    i + 1 (the next step), the last node is never expanded (q_row -1), the
+    root's children come from row 0; positions, mask and retrieve arrays as for
+    the tree (``verify_arrays``).  Returns the same keys as ``build_tree``.
+    """
+    topk_p = np.asarray(topk_p, np.float32)
+    topk_id = np.asarray(topk_id, np.int32)
+    if topk_p.ndim == 3:
+        if topk_p.shape[2] != 1:
+            raise ValueError("a chain takes one token per step")
+        topk_p, topk_id = topk_p[:, :, 0], topk_id[:, :, 0]
+    B, S = topk_p.shape
+    if S < 1:
+        raise ValueError("need S >= 1")
+    N = S + 1
+    per = []
+    for b in range(B):
+        tokens = np.array([int(root_token[b])] + [int(x) for x in topk_id[b]], np.int32)
+        parent = np.array([-1] + list(range(S)), np.int32)
+        depth = np.arange(N, dtype=np.int32)
+        score = np.array([1.0] + [float(x) for x in topk_p[b]], np.float32)
+        q_row = np.array(list(range(S)) + [-1], np.int32)
+        per.append(verify_arrays(tokens, parent, depth, score, q_row, int(prefix_len[b]), b))
+    return {key: np.stack([d[key] for d in per]) for key in per[0]}

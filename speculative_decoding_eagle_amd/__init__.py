@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     GREEDY,
     STOCHASTIC,
     SdvError,
+    sdv_build_chain,
     sdv_build_tree,
     sdv_compact_kv,
     sdv_draft_extend_prep,

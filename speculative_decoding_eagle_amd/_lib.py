@@ -52,6 +52,7 @@ SIGNATURES = {
     "sdv_tli_lm_head": (c_i32, [c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),
     "sdv_tli_build_maps": (c_i32, [c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p]),
     "sdv_tli_map_ids": (c_i32, [c_p, c_i32, c_p, c_i64, c_p, c_p]),
+    "sdv_build_chain": (c_i32, [c_i32, c_i32] + [c_p] * 15 + [c_p]),
     "sdv_draft_extend_prep": (c_i32, [c_i32, c_i32, c_i32] + [c_p] * 5 + [c_i32] + [c_p] * 7),
     "sdv_tli_constrain_draft_logits": (c_i32, [c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),
     "sdv_tli_q_scatter_workspace_size": (c_sz, [c_i32]),

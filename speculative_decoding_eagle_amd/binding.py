@@ -119,38 +119,54 @@ TREE_OUTPUTS = ("tokens", "parent", "depth", "positions", "score", "q_row", "mas
                 "retrieve_index", "next_token", "next_sibling")
 
 
+def _tree_outputs(B: int, N: int, dev, out, with_mask: bool):
+    out = dict(out or {})
+    W = (N + 31) // 32
+    i32 = torch.int32
+    shapes = {"tokens": ((B, N), i32), "parent": ((B, N), i32), "depth": ((B, N), i32),
+              "positions": ((B, N), i32), "score": ((B, N), torch.float32), "q_row": ((B, N), i32),
+              "mask_bits": ((B, N, W), i32), "retrieve_index": ((B, N), i32), "next_token": ((B, N), i32),
+              "next_sibling": ((B, N), i32)}
+    if with_mask:
+        shapes["mask"] = ((B, N, N), torch.uint8)
+    for name, (shape, dtype) in shapes.items():
+        if name not in out:
+            out[name] = torch.empty(shape, dtype=dtype, device=dev)
+    return out
+
+
+def _tree_output_ptrs(out):
+    return [_ptr(out[n]) for n in ("tokens", "parent", "depth", "positions", "score", "q_row")] + [
+        _ptr(out.get("mask"), torch.uint8, "mask", allow_none=True),
+        _ptr(out["mask_bits"], (torch.int32, torch.uint32), "mask_bits"),
+        _ptr(out["retrieve_index"]), _ptr(out["next_token"]), _ptr(out["next_sibling"])]
+
+
 def sdv_build_tree(topk_p, topk_id, root_token, prefix_len, k: int, S: int, N: int, out=None,
                    with_mask: bool = True):
     """Candidate tree and verify arrays; returns a dict of device tensors."""
     B = topk_p.shape[0]
-    dev = topk_p.device
-    out = dict(out or {})
-    W = (N + 31) // 32
-
-    def get(name, shape, dtype):
-        if name not in out:
-            out[name] = torch.empty(shape, dtype=dtype, device=dev)
-        return out[name]
-
+    out = _tree_outputs(B, N, topk_p.device, out, with_mask)
     i32 = torch.int32
-    tokens = get("tokens", (B, N), i32)
-    parent = get("parent", (B, N), i32)
-    depth = get("depth", (B, N), i32)
-    positions = get("positions", (B, N), i32)
-    score = get("score", (B, N), torch.float32)
-    q_row = get("q_row", (B, N), i32)
-    mask = get("mask", (B, N, N), torch.uint8) if with_mask else None
-    bits = get("mask_bits", (B, N, W), torch.int32)
-    ri = get("retrieve_index", (B, N), i32)
-    nt = get("next_token", (B, N), i32)
-    ns = get("next_sibling", (B, N), i32)
-    shape = TreeShape(B, k, S, N)
     _check(_lib.lib().sdv_build_tree(
-        shape, _ptr(topk_p, torch.float32, "topk_p"), _ptr(topk_id, i32, "topk_id"),
-        _ptr(root_token, i32, "root_token"), _ptr(prefix_len, i32, "prefix_len"),
-        _ptr(tokens), _ptr(parent), _ptr(depth), _ptr(positions), _ptr(score), _ptr(q_row),
-        _ptr(mask, torch.uint8, "mask", allow_none=True), _ptr(bits, (torch.int32, torch.uint32), "mask_bits"),
-        _ptr(ri), _ptr(nt), _ptr(ns), _stream(dev)), "sdv_build_tree")
+        TreeShape(B, k, S, N), _ptr(topk_p, torch.float32, "topk_p"), _ptr(topk_id, i32, "topk_id"),
+        _ptr(root_token, i32, "root_token"), _ptr(prefix_len, i32, "prefix_len"), *_tree_output_ptrs(out),
+        _stream(topk_p.device)), "sdv_build_tree")
+    return out
+
+
+def sdv_build_chain(topk_p, topk_id, root_token, prefix_len, out=None, with_mask: bool = True):
+    """Multi-layer draft chain from each step's top-1 ([B, S] or [B, S, 1]);
+    returns the same dict as sdv_build_tree with N = S + 1."""
+    B, S = topk_p.shape[0], topk_p.shape[1]
+    if topk_p.dim() == 3 and topk_p.shape[2] != 1:
+        raise ValueError("a chain takes one token per step")
+    out = _tree_outputs(B, S + 1, topk_p.device, out, with_mask)
+    i32 = torch.int32
+    _check(_lib.lib().sdv_build_chain(
+        B, S, _ptr(topk_p, torch.float32, "topk_p"), _ptr(topk_id, i32, "topk_id"),
+        _ptr(root_token, i32, "root_token"), _ptr(prefix_len, i32, "prefix_len"), *_tree_output_ptrs(out),
+        _stream(topk_p.device)), "sdv_build_chain")
     return out
 
 

@@ -223,6 +223,49 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
   }
 }
 
+// Multi-layer draft chain ("[SGLang] Multi-Layer EAGLE", sections 2-3: one
+// draft layer per step, the per-step top-1 lists concatenated, step i's
+// parent the token of step i-1): every output is closed-form, so one
+// 256-thread block per request writes them, thread i for node i (and mask
+// row i).
+constexpr int kChainThreads = 256;
+
+__global__ void __launch_bounds__(kChainThreads)
+build_chain_kernel(int S, const float *__restrict__ topk_p, const int32_t *__restrict__ topk_id,
+                   const int32_t *__restrict__ root_token, const int32_t *__restrict__ prefix_len,
+                   int32_t *__restrict__ tokens, int32_t *__restrict__ parent, int32_t *__restrict__ depth,
+                   int32_t *__restrict__ positions, float *__restrict__ score, int32_t *__restrict__ q_row,
+                   uint8_t *__restrict__ mask, uint32_t *__restrict__ mask_bits,
+                   int32_t *__restrict__ retrieve_index, int32_t *__restrict__ next_token,
+                   int32_t *__restrict__ next_sibling) {
+  const int b = blockIdx.x;
+  const int N = S + 1;
+  const int W = (N + 31) / 32;
+  const int64_t o = static_cast<int64_t>(b) * N;
+  for (int i = threadIdx.x; i < N; i += kChainThreads) {
+    tokens[o + i] = i == 0 ? root_token[b] : topk_id[static_cast<int64_t>(b) * S + i - 1];
+    parent[o + i] = i - 1;
+    depth[o + i] = i;
+    positions[o + i] = prefix_len[b] + i;
+    score[o + i] = i == 0 ? 1.0f : topk_p[static_cast<int64_t>(b) * S + i - 1];
+    q_row[o + i] = i < S ? i : -1;
+    retrieve_index[o + i] = static_cast<int32_t>(o + i);
+    next_token[o + i] = i < S ? i + 1 : -1;
+    next_sibling[o + i] = -1;
+    if (mask) {
+      uint8_t *row = mask + (o + i) * N;
+      for (int j = 0; j < N; ++j) row[j] = j <= i ? 1 : 0;
+    }
+    if (mask_bits) {
+      uint32_t *row = mask_bits + (o + i) * W;
+      for (int w = 0; w < W; ++w) {
+        const int full = i + 1 - 32 * w;     // columns 32w .. i are set
+        row[w] = full >= 32 ? 0xFFFFFFFFu : (full <= 0 ? 0u : (1u << full) - 1u);
+      }
+    }
+  }
+}
+
 }  // namespace
 }  // namespace sdv
 
@@ -255,4 +298,22 @@ extern "C" int32_t sdv_build_tree(sdv_tree_shape sh, const float *topk_p, const 
                      positions, score, q_row, mask, mask_bits, retrieve_index, retrieve_next_token,
                      retrieve_next_sibling);
   return check_launch("build_tree_kernel");
+}
+
+extern "C" int32_t sdv_build_chain(int32_t B, int32_t S, const float *topk_p, const int32_t *topk_id,
+                                   const int32_t *root_token, const int32_t *prefix_len, int32_t *tokens,
+                                   int32_t *parent, int32_t *depth, int32_t *positions, float *score,
+                                   int32_t *q_row, uint8_t *mask, uint32_t *mask_bits, int32_t *retrieve_index,
+                                   int32_t *retrieve_next_token, int32_t *retrieve_next_sibling, void *stream) {
+  clear_error();
+  SDV_REQUIRE(B >= 0 && S >= 1, SDV_E_SHAPE, "build_chain: need B >= 0 and S >= 1");
+  SDV_REQUIRE(S + 1 <= kMaxNodes, SDV_E_UNSUPPORTED, "build_chain: N=%d above %d", S + 1, kMaxNodes);
+  if (B == 0) return SDV_OK;
+  SDV_REQUIRE(topk_p && topk_id && root_token && prefix_len && tokens && parent && depth && positions &&
+                  score && q_row && retrieve_index && retrieve_next_token && retrieve_next_sibling,
+              SDV_E_NULL, "build_chain: NULL pointer");
+  hipLaunchKernelGGL(build_chain_kernel, dim3(B), dim3(kChainThreads), 0, as_stream(stream), S, topk_p, topk_id,
+                     root_token, prefix_len, tokens, parent, depth, positions, score, q_row, mask, mask_bits,
+                     retrieve_index, retrieve_next_token, retrieve_next_sibling);
+  return check_launch("build_chain_kernel");
 }

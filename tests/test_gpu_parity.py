@@ -135,6 +135,49 @@ def test_build_tree_ties_and_shapes(k, S, N):
     _assert_tree_equal(g, o)
 
 
+# Multi-layer draft chain: bit-exact against the oracle, then through the
+# same accept kernels as the tree.
+@pytest.mark.parametrize("B,S", [(1, 1), (7, 4), (300, 12), (3, 255)])
+def test_build_chain_bit_exact(B, S):
+    rng = np.random.default_rng(B * 1000 + S)
+    tp = rng.random((B, S)).astype(np.float32)
+    ti = rng.integers(0, 128256, size=(B, S)).astype(np.int32)
+    root = rng.integers(0, 128256, size=B).astype(np.int32)
+    plen = rng.integers(0, 50000, size=B).astype(np.int32)
+    say("build chain", B, S)
+    t = sdv.sdv_build_chain(dev(tp), dev(ti), dev(root), dev(plen))
+    torch.cuda.synchronize()
+    g = {key: host(v) for key, v in t.items()}
+    g["mask_bits"] = g["mask_bits"].view(np.uint32)
+    _assert_tree_equal(g, otree.build_chain(tp, ti, root, plen))
+
+
+@pytest.mark.parametrize("planted", [False, True])
+def test_chain_through_stochastic_accept(planted):
+    """A k=1 workload (4 draft steps) drafted as a multi-layer chain: the
+    GPU chain equals the oracle's, and the stochastic accept walk over it
+    agrees bit for bit."""
+    cfg = workloads.get_config("c2", V=3001)
+    inp = workloads.generate(cfg, with_attention=False)
+    tp, ti = otopk.draft_topk(inp["draft_probs"], 1)
+    chain = otree.build_chain(tp, ti, inp["root_token"], inp["prefix_len"])
+    say("chain accept", planted)
+    t = sdv.sdv_build_chain(dev(tp), dev(ti), dev(inp["root_token"]), dev(inp["prefix_len"]))
+    torch.cuda.synchronize()
+    g = {key: host(v) for key, v in t.items()}
+    g["mask_bits"] = g["mask_bits"].view(np.uint32)
+    _assert_tree_equal(g, chain)
+    p = inp["target"]
+    if planted:
+        p = plant_stochastic(p, inp["draft_probs"], chain, workloads.extra_rng(cfg, 7), cfg.S)
+    ga = _gpu_accept(sdv.STOCHASTIC, chain, p, cfg.S, draft_probs=inp["draft_probs"], u_accept=inp["u_accept"],
+                     u_draw=inp["u_draw"])
+    o = oacc.verify_stochastic(chain, p, inp["draft_probs"], inp["u_accept"], inp["u_draw"], cfg.S)
+    _assert_accept_equal(ga, o)
+    if planted:
+        assert o["accept_len"].max() > 0
+
+
 # -------------------------------------------------------------------- A6-A7
 
 def _gpu_accept(mode, tree, target, S, **kw):

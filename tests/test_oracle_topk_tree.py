@@ -200,6 +200,59 @@ def test_k1_is_a_chain():
         assert t["q_row"][b].tolist() == list(range(S)) + [-1]
 
 
+def _chain_inputs(seed, B=3, S=6, V=120):
+    rng = np.random.default_rng(seed)
+    probs = workloads.softmax_rows(rng.standard_normal((B, S, V)).astype(np.float32))
+    tp, ti = otopk.draft_topk(probs, 1)
+    root = rng.integers(0, V, size=B).astype(np.int32)
+    prefix = rng.integers(0, 500, size=B).astype(np.int32)
+    return probs, tp, ti, root, prefix
+
+
+def test_multilayer_chain_follows_the_step_slicing():
+    """Multi-layer draft (per-step layers, per-step top-1 concatenated): node
+    i+1 is step i's token, its parent is node i (the root for step 0), and it
+    keeps its own step's probability as its score; the mask is the lower
+    triangle and every node has one child."""
+    probs, tp, ti, root, prefix = _chain_inputs(7)
+    B, S = tp.shape[:2]
+    N = S + 1
+    c = otree.build_chain(tp[:, :, 0], ti[:, :, 0], root, prefix)
+    for b in range(B):
+        assert c["parent"][b].tolist() == [-1] + list(range(S))
+        assert c["tokens"][b].tolist() == [int(root[b])] + [int(np.argmax(probs[b, i])) for i in range(S)]
+        assert c["score"][b, 0] == 1.0 and np.array_equal(c["score"][b, 1:], tp[b, :, 0])
+        assert np.array_equal(c["mask"][b], np.tril(np.ones((N, N), np.uint8)))
+        assert c["next_token"][b].tolist() == list(range(1, N)) + [-1]
+        assert (c["next_sibling"][b] == -1).all()
+        assert c["positions"][b].tolist() == [int(prefix[b]) + d for d in range(N)]
+        assert c["retrieve_index"][b].tolist() == [b * N + i for i in range(N)]
+
+
+@pytest.mark.parametrize("seed,S", [(8, 1), (9, 5), (10, 12)])
+def test_multilayer_chain_is_the_k1_tree_with_step_scores(seed, S):
+    """The same per-step lists read in the tree layout [B, R=S, k=1] build
+    the same tree; the tree's scores are the running fp32 products of the
+    chain's step scores, root first."""
+    probs, tp, ti, root, prefix = _chain_inputs(seed, S=S)
+    c = otree.build_chain(tp, ti, root, prefix)
+    t = otree.build_tree(tp, ti, root, prefix, 1, S, S + 1)
+    for key in t:
+        if key != "score":
+            assert np.array_equal(c[key], t[key]), key
+    for b in range(tp.shape[0]):
+        run = [np.float32(1.0)]
+        for x in c["score"][b, 1:]:
+            run.append(np.float32(run[-1] * x))
+        assert np.array_equal(np.array(run, np.float32), t["score"][b])
+
+
+def test_multilayer_chain_rejects_wider_lists():
+    _, tp, ti, root, prefix = _chain_inputs(11)
+    with pytest.raises(ValueError):
+        otree.build_chain(np.repeat(tp, 2, axis=2), np.repeat(ti, 2, axis=2), root, prefix)
+
+
 def _brute_tree(tp, ti, k, S, N):
     """Independent restatement on paths: a candidate carries the list of draft
     probabilities along its path from the root; its score is the left fold of
