@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--chain", action="store_true",
                     help="k = 1 workloads: build the draft as a multi-layer chain (sdv_build_chain) instead of "
                          "through the tree builder")
+    ap.add_argument("--kv-alloc", action="store_true",
+                    help="workloads with attention: add the draft-side KV allocation (backup, per-branch "
+                         "regions with the partial-page copies, rollback) to the step")
     ap.add_argument("--extend-prep", action="store_true",
                     help="add the index preparation of the draft extend after the accept walk to the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -76,7 +79,8 @@ def log(msg):
 class Pipeline:
     """Preallocated device buffers and the per-stage calls of one step."""
 
-    def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs", extend_prep=False, chain=False):
+    def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs", extend_prep=False, chain=False,
+                 kv_alloc=False):
         import torch
         import speculative_decoding_eagle_amd as sdv
         self.torch, self.sdv, self.cfg = torch, sdv, cfg
@@ -99,6 +103,23 @@ class Pipeline:
         self.draft_input = draft_input
         self.extend_prep = extend_prep
         self.chain = chain
+        self.kv_alloc = kv_alloc and cfg.has_attention
+        if self.kv_alloc:
+            # room for every branch of every request past the workload's own
+            # pages; the allocator hands out exactly those pages
+            P = cfg.page
+            extra = B * k * sdv.sdv_kv_branch_pages(P, S)
+            num_pages = d["k_pool"].shape[0] // P
+            for key in ("k_pool", "v_pool"):
+                old = d[key]
+                grown = torch.empty(((num_pages + extra) * P,) + tuple(old.shape[1:]), dtype=old.dtype, device="cuda")
+                grown[:old.shape[0]].copy_(old)
+                d[key] = grown
+            self.kv = sdv.sdv_kv_alloc_init(extra)
+            self.kv.free_ids.copy_(torch.arange(num_pages + extra - 1, num_pages - 1, -1, dtype=torch.int32))
+            self.kv_backup = torch.empty(2, dtype=torch.int32, device="cuda")
+            self.kv_pages = torch.empty((B, k, sdv.sdv_kv_branch_pages(P, S)), dtype=torch.int32, device="cuda")
+            self.kv_loc = torch.empty((B, k, S), dtype=torch.int32, device="cuda")
         self.ext = {}
         if draft_input != "probs":
             # the fused path reads logits; the stochastic accept still reads
@@ -196,6 +217,14 @@ class Pipeline:
                                 cfg.N, cfg.S, cfg.page, pools[0], pools[1], new_len=self.new_len, freed=self.freed,
                                 num_freed=self.num_freed)
 
+    def s_kv_draft(self, i):
+        cfg, sdv = self.cfg, self.sdv
+        pools = ([self.d["k_pool"]], [self.d["v_pool"]]) if cfg.page > 1 else ([], [])
+        sdv.sdv_kv_alloc_backup(self.kv, self.kv_backup)
+        sdv.sdv_kv_alloc_branches(self.kv, cfg.page, cfg.k, cfg.S, self.tables[i], self.d["prefix_len"], *pools,
+                                  branch_pages=self.kv_pages, out_loc=self.kv_loc)
+        sdv.sdv_kv_alloc_restore(self.kv, self.kv_backup)
+
     def s_extend(self):
         self.ext = self.sdv.sdv_draft_extend_prep(self.d["prefix_len"], self.acc["commit_len"],
                                                   self.acc["commit_tokens"], self.acc["accept_path"], self.cfg.N,
@@ -207,6 +236,8 @@ class Pipeline:
     def stages(self, i):
         cfg = self.cfg
         st = []
+        if self.kv_alloc:
+            st.append(("kv_alloc_draft", lambda: self.s_kv_draft(i)))
         if cfg.is_tli:
             st.append(("tli_head_mask_scatter", self.s_tli))
         st += [("draft_topk", self.s_topk), ("build_tree", self.s_tree)]
@@ -382,7 +413,7 @@ def main():
         print("--chain needs a k = 1 workload whose tree keeps every step (N = S + 1)", file=sys.stderr)
         sys.exit(2)
     pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept, args.draft_input, args.extend_prep,
-                    args.chain)
+                    args.chain, args.kv_alloc)
     stages = [name for name, _ in pipe.stages(0)]
 
     for i in range(args.warmup):
@@ -440,7 +471,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[cfg.name], "name": cfg.name, "batch": cfg.B, "tree_tokens": cfg.N,
                    "accept": args.accept, "draft_input": args.draft_input,
-                   "extend_prep": args.extend_prep, "chain": args.chain},
+                   "extend_prep": args.extend_prep, "chain": args.chain,
+                   "kv_alloc": args.kv_alloc},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_gbs": {k: round(work[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9, 1) for k in stages if k in work},
         "accepted_tokens": work["accept"]["accepted"],

@@ -285,6 +285,67 @@ int32_t sdv_compact_kv(sdv_kv_shape shape, uint16_t *const *k_pools, uint16_t *c
                        int32_t *num_freed, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * KV slot / page allocation around a speculative step.
+ * "EAGLE speculative decoding in four parts", "Drafting, verification and
+ * slots": with page size 1 the draft reserves batch x topk x steps slots at
+ * once with the allocator's state backed up, rolled back after the step;
+ * with page size > 1, topk = 1 extends each request's own sequence and
+ * topk > 1 duplicates the last partial page, every branch holding a copy of
+ * the prefix's partial page followed by its draft tokens; "Design
+ * trade-offs": allocate first, roll back after.  "[SGLang] Multi-Layer
+ * EAGLE" section 6: draft and target share one allocator.
+ *
+ * Units are slots (page == 1) or pages (page > 1).  Allocator (device,
+ * caller-owned): free_ids [capacity] int32 and state [4] int32 = {top,
+ * pushes, error, 0}; the free units are free_ids[0 .. top), free_ids[top-1]
+ * is handed out first.  error is a sticky bit set: 1 no room (or a table
+ * row would overflow), 2 restore refused, 4 release overflow, 8 corrupt
+ * state, 16 partial-page slot outside the pool.  A failed call changes no
+ * allocator or table entry (its position outputs read -1).
+ *   init: free_ids = capacity-1 .. 0 (units come out ascending), top =
+ *     capacity, pushes = error = 0.  A caller may instead fill free_ids
+ *     with any distinct unit ids itself and set state = {count, 0, 0, 0}.
+ *   backup: backup [2] (device) = {top, pushes}.
+ *   restore: top = backup top, allowed only if nothing was released since
+ *     the backup (pushes unchanged) and backup top >= top -- it undoes the
+ *     allocations made since.
+ *   free: pushes ids[0 .. *num_ids) (num_ids on the device, at most
+ *     max_ids), e.g. sdv_compact_kv's freed list; pushes += 1.
+ *   extend: request b of length L = seq_len[b] takes positions L .. L+n-1
+ *     of its own chain, requests in batch order.  page == 1: page_table is a
+ *     slot map [B, max_pages] and gets one slot per position; page > 1: the
+ *     partial last page is continued and pages ceil(L/P) .. ceil((L+n)/P)-1
+ *     are appended to the row.  out_loc [B, n] = slot of position L+i.
+ *   branches: with r = L mod P, branch j of request b takes
+ *     ceil((r + S) / P) pages of its own (requests, branches, pages in
+ *     order): branch_pages [B, topk, sdv_kv_branch_pages(page, S)], -1
+ *     padded; the K and V rows of the r partial-page positions (every layer,
+ *     pools as in sdv_compact_kv) are copied into the first r slots of each
+ *     branch; out_loc [B, topk, S] = slot of draft step i of branch j =
+ *     branch_pages[b][j][(r+i)/P]*P + (r+i) mod P.  page == 1 gives one slot
+ *     per (request, branch, step); page_table is read only; layers may be 0
+ *     (no copy).
+ * Limits: B <= 8192.  Calls on one allocator must be stream ordered.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t B, page, topk, S, Hkv, D, layers, max_pages;
+  int64_t num_slots;
+} sdv_branch_shape;
+
+int32_t sdv_kv_branch_pages(int32_t page, int32_t S);
+int32_t sdv_kv_alloc_init(int32_t capacity, int32_t *free_ids, int32_t *state, void *stream);
+int32_t sdv_kv_alloc_backup(const int32_t *state, int32_t *backup, void *stream);
+int32_t sdv_kv_alloc_restore(int32_t capacity, int32_t *state, const int32_t *backup, void *stream);
+int32_t sdv_kv_alloc_free(int32_t capacity, int32_t *free_ids, int32_t *state, const int32_t *ids,
+                          const int32_t *num_ids, int32_t max_ids, void *stream);
+int32_t sdv_kv_alloc_extend(int32_t capacity, int32_t *free_ids, int32_t *state, int32_t B, int32_t page,
+                            int32_t n, int32_t *page_table, int32_t max_pages, const int32_t *seq_len,
+                            int32_t *out_loc, void *stream);
+int32_t sdv_kv_alloc_branches(int32_t capacity, int32_t *free_ids, int32_t *state, sdv_branch_shape shape,
+                              uint16_t *const *k_pools, uint16_t *const *v_pools, const int32_t *page_table,
+                              const int32_t *seq_len, int32_t *branch_pages, int32_t *out_loc, void *stream);
+
+/* ------------------------------------------------------------------------
  * A9  TLI pruned draft LM head.
  * sglang PR #22883 "TLI (Token-Level Intersection)", "Modifications": the
  * draft LM head becomes a compact [intersection_size x hidden_dim] matrix,

@@ -25,6 +25,10 @@ Modules and the passages they follow:
                    verification and slots"; zero-to-sglang ch.10 section 5.2).
 * ``tli``       -- Token-Level Intersection remaps, logit masking and the pruned
                    LM head (sglang PR #22883, "Modifications").
+* ``alloc``     -- KV slot / page allocation with backup and rollback, and the
+                   duplicated partial page of the page > 1, topk > 1 draft
+                   ("EAGLE speculative decoding in four parts", "Drafting,
+                   verification and slots", "Design trade-offs").
 * ``extend``    -- index preparation of the draft extend after a verify step
                    ("EAGLE speculative decoding in four parts", "Self-test";
                    zero-to-sglang ch.10 section 3.1; PR #22883 hooks).
@@ -32,6 +36,6 @@ Modules and the passages they follow:
 Every function that no test pins to something outside itself says
 "parity unpinned" in its docstring.
 """
-from . import topk, tree, attention, accept, compact, tli, extend  # noqa: F401
+from . import topk, tree, attention, accept, compact, tli, extend, alloc  # noqa: F401
 
-__all__ = ["topk", "tree", "attention", "accept", "compact", "tli", "extend"]
+__all__ = ["topk", "tree", "attention", "accept", "compact", "tli", "extend", "alloc"]

@@ -9,6 +9,7 @@ not been built.
 """
 from .binding import (  # noqa: F401
     GREEDY,
+    KVAlloc,
     STOCHASTIC,
     SdvError,
     sdv_build_chain,
@@ -17,6 +18,13 @@ from .binding import (  # noqa: F401
     sdv_draft_extend_prep,
     sdv_draft_topk,
     sdv_draft_topk_logits,
+    sdv_kv_alloc_backup,
+    sdv_kv_alloc_branches,
+    sdv_kv_alloc_extend,
+    sdv_kv_alloc_free,
+    sdv_kv_alloc_init,
+    sdv_kv_alloc_restore,
+    sdv_kv_branch_pages,
     sdv_tli_build_maps,
     sdv_tli_constrain_draft_logits,
     sdv_tli_lm_head,

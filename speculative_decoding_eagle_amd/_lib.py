@@ -34,6 +34,11 @@ class KVShape(ctypes.Structure):
                 ("layers", c_i32), ("max_pages", c_i32), ("num_slots", c_i64)]
 
 
+class BranchShape(ctypes.Structure):
+    _fields_ = [("B", c_i32), ("page", c_i32), ("topk", c_i32), ("S", c_i32), ("Hkv", c_i32), ("D", c_i32),
+                ("layers", c_i32), ("max_pages", c_i32), ("num_slots", c_i64)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "sdv_last_error": (ctypes.c_char_p, []),
@@ -53,6 +58,13 @@ SIGNATURES = {
     "sdv_tli_build_maps": (c_i32, [c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p]),
     "sdv_tli_map_ids": (c_i32, [c_p, c_i32, c_p, c_i64, c_p, c_p]),
     "sdv_build_chain": (c_i32, [c_i32, c_i32] + [c_p] * 15 + [c_p]),
+    "sdv_kv_branch_pages": (c_i32, [c_i32, c_i32]),
+    "sdv_kv_alloc_init": (c_i32, [c_i32, c_p, c_p, c_p]),
+    "sdv_kv_alloc_backup": (c_i32, [c_p, c_p, c_p]),
+    "sdv_kv_alloc_restore": (c_i32, [c_i32, c_p, c_p, c_p]),
+    "sdv_kv_alloc_free": (c_i32, [c_i32, c_p, c_p, c_p, c_p, c_i32, c_p]),
+    "sdv_kv_alloc_extend": (c_i32, [c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_p, c_i32, c_p, c_p, c_p]),
+    "sdv_kv_alloc_branches": (c_i32, [c_i32, c_p, c_p, BranchShape] + [c_p] * 7),
     "sdv_draft_extend_prep": (c_i32, [c_i32, c_i32, c_i32] + [c_p] * 5 + [c_i32] + [c_p] * 7),
     "sdv_tli_constrain_draft_logits": (c_i32, [c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),
     "sdv_tli_q_scatter_workspace_size": (c_sz, [c_i32]),

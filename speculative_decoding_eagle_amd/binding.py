@@ -251,6 +251,91 @@ def sdv_verify_accept(mode: int, tree, target, S: int, eos_id: int = -1, remaini
     return out
 
 
+# ------------------------------------------------------- KV allocation
+
+class KVAlloc:
+    """Device allocator state: free_ids [capacity] and state [4] int32
+    ({top, pushes, error, 0}); see sdv_kv_alloc_* in include/sdv.h."""
+
+    def __init__(self, capacity: int, device="cuda"):
+        self.capacity = capacity
+        self.free_ids = torch.empty(max(1, capacity), dtype=torch.int32, device=device)
+        self.state = torch.empty(4, dtype=torch.int32, device=device)
+
+    def ptrs(self):
+        return self.capacity, _ptr(self.free_ids, torch.int32, "free_ids"), _ptr(self.state, torch.int32, "state")
+
+
+def sdv_kv_alloc_init(capacity: int, device="cuda") -> KVAlloc:
+    a = KVAlloc(capacity, device)
+    _check(_lib.lib().sdv_kv_alloc_init(*a.ptrs(), _stream(a.state.device)), "sdv_kv_alloc_init")
+    return a
+
+
+def sdv_kv_alloc_backup(a: KVAlloc, backup=None):
+    if backup is None:
+        backup = torch.empty(2, dtype=torch.int32, device=a.state.device)
+    _check(_lib.lib().sdv_kv_alloc_backup(_ptr(a.state, torch.int32, "state"), _ptr(backup, torch.int32, "backup"),
+                                          _stream(a.state.device)), "sdv_kv_alloc_backup")
+    return backup
+
+
+def sdv_kv_alloc_restore(a: KVAlloc, backup):
+    _check(_lib.lib().sdv_kv_alloc_restore(a.capacity, _ptr(a.state, torch.int32, "state"),
+                                           _ptr(backup, torch.int32, "backup"), _stream(a.state.device)),
+           "sdv_kv_alloc_restore")
+
+
+def sdv_kv_alloc_free(a: KVAlloc, ids, num_ids):
+    """Releases ids[0 .. num_ids[0]) (num_ids a device int32 tensor)."""
+    _check(_lib.lib().sdv_kv_alloc_free(*a.ptrs(), _ptr(ids, torch.int32, "ids"), _ptr(num_ids, torch.int32, "num_ids"),
+                                        ids.numel(), _stream(a.state.device)), "sdv_kv_alloc_free")
+
+
+def sdv_kv_alloc_extend(a: KVAlloc, page: int, n: int, page_table, seq_len, out_loc=None):
+    B, max_pages = page_table.shape
+    if out_loc is None:
+        out_loc = torch.empty((B, n), dtype=torch.int32, device=page_table.device)
+    _check(_lib.lib().sdv_kv_alloc_extend(*a.ptrs(), B, page, n, _ptr(page_table, torch.int32, "page_table"),
+                                          max_pages, _ptr(seq_len, torch.int32, "seq_len"),
+                                          _ptr(out_loc, torch.int32, "out_loc"), _stream(page_table.device)),
+           "sdv_kv_alloc_extend")
+    return out_loc
+
+
+def sdv_kv_branch_pages(page: int, S: int) -> int:
+    return int(_lib.lib().sdv_kv_branch_pages(page, S))
+
+
+def sdv_kv_alloc_branches(a: KVAlloc, page: int, topk: int, S: int, page_table, seq_len,
+                          k_pools: Sequence[torch.Tensor] = (), v_pools: Sequence[torch.Tensor] = (),
+                          branch_pages=None, out_loc=None):
+    """Per-branch draft regions (and the partial-page copies into the pools).
+    Returns (branch_pages [B, topk, maxpb], out_loc [B, topk, S])."""
+    B, max_pages = page_table.shape
+    dev = page_table.device
+    maxpb = sdv_kv_branch_pages(page, S)
+    if branch_pages is None:
+        branch_pages = torch.empty((B, topk, maxpb), dtype=torch.int32, device=dev)
+    if out_loc is None:
+        out_loc = torch.empty((B, topk, S), dtype=torch.int32, device=dev)
+    layers = len(k_pools)
+    if len(v_pools) != layers:
+        raise ValueError("K and V pools must match")
+    Hkv = k_pools[0].shape[1] if layers else 0
+    D = k_pools[0].shape[2] if layers else 0
+    slots = k_pools[0].shape[0] if layers else 0
+    kp = (ctypes.c_void_p * max(1, layers))(*[_ptr(t, BF16, "k_pool") for t in k_pools])
+    vp = (ctypes.c_void_p * max(1, layers))(*[_ptr(t, BF16, "v_pool") for t in v_pools])
+    shape = _lib.BranchShape(B, page, topk, S, Hkv, D, layers, max_pages, slots)
+    _check(_lib.lib().sdv_kv_alloc_branches(
+        *a.ptrs(), shape, ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p),
+        _ptr(page_table, torch.int32, "page_table"), _ptr(seq_len, torch.int32, "seq_len"),
+        _ptr(branch_pages, torch.int32, "branch_pages"), _ptr(out_loc, torch.int32, "out_loc"), _stream(dev)),
+        "sdv_kv_alloc_branches")
+    return branch_pages, out_loc
+
+
 # ------------------------------------------------- draft extend index prep
 
 EXTEND_OUTPUTS = ("extend_start", "input_ids", "positions", "hidden_index", "last_index", "seq_len")

@@ -44,6 +44,13 @@ struct Carver {
 // Number of compute units of the current device (cached per device).
 int num_cus();
 
+// The K and V pools of every layer, passed to a kernel by value.
+constexpr int kMaxLayers = 128;
+struct PoolPtrs {
+  uint16_t *k[kMaxLayers];
+  uint16_t *v[kMaxLayers];
+};
+
 #define SDV_REQUIRE(cond, code, ...)          \
   do {                                        \
     if (!(cond)) return ::sdv::fail((code), __VA_ARGS__); \

@@ -16,13 +16,7 @@ namespace sdv {
 namespace {
 
 constexpr int kCmpThreads = 256;
-constexpr int kMaxLayers = 128;
 constexpr int kCopyBatch = 4;     // 16-byte vectors per thread per batch
-
-struct PoolPtrs {
-  uint16_t *k[kMaxLayers];
-  uint16_t *v[kMaxLayers];
-};
 
 __device__ __forceinline__ int clamp_accept(int a, int S, int N) {
   const int hi = min(S, N - 1);

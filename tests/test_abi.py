@@ -20,7 +20,9 @@ def test_header_declares_the_entry_points():
     names = declared_symbols()
     for must in ("sdv_draft_topk", "sdv_draft_topk_logits", "sdv_build_tree", "sdv_tree_verify_attention", "sdv_verify_accept",
                  "sdv_compact_kv", "sdv_tli_lm_head", "sdv_tli_map_ids", "sdv_tli_constrain_draft_logits",
-                 "sdv_tli_q_scatter", "sdv_tli_build_maps", "sdv_draft_extend_prep", "sdv_build_chain", "sdv_last_error"):
+                 "sdv_tli_q_scatter", "sdv_tli_build_maps", "sdv_draft_extend_prep", "sdv_build_chain", "sdv_kv_alloc_init",
+                 "sdv_kv_alloc_backup", "sdv_kv_alloc_restore", "sdv_kv_alloc_free", "sdv_kv_alloc_extend",
+                 "sdv_kv_alloc_branches", "sdv_kv_branch_pages", "sdv_last_error"):
         assert must in names
 
 

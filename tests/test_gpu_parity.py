@@ -11,6 +11,7 @@ import torch
 import speculative_decoding_eagle_amd as sdv
 import workloads
 from oracle import accept as oacc
+from oracle import alloc as oal
 from oracle import attention as oatt
 from oracle import compact as ocmp
 from oracle import extend as oext
@@ -323,6 +324,173 @@ def test_compaction_bit_exact(page, layers, B, N, S):
     if page > 1:
         for x, y in zip(gk + gv, k2 + v2):
             assert np.array_equal(host(x).view(np.uint16), y)
+
+
+# ------------------------------------------------------- KV allocation
+
+def _alloc_equal(g, o):
+    torch.cuda.synchronize()
+    st = host(g.state)
+    assert st[:3].tolist() == [o.top, o.pushes, o.error]
+    assert np.array_equal(host(g.free_ids)[:o.capacity], o.free_ids)
+
+
+def _alloc_pair(capacity):
+    """A fresh GPU allocator and its oracle twin."""
+    g = sdv.sdv_kv_alloc_init(capacity)
+    o = oal.KVAllocator(capacity)
+    return g, o
+
+
+@pytest.mark.parametrize("B,topk,S", [(5, 4, 3), (1, 1, 1), (300, 8, 5)])
+def test_kv_alloc_page1_draft_and_rollback(B, topk, S):
+    cap = B * topk * S + 77
+    g, o = _alloc_pair(cap)
+    seq = np.random.default_rng(B).integers(0, 500, size=B).astype(np.int32)
+    table = np.zeros((B, 1), np.int32)
+    say("kv alloc page 1", B, topk, S)
+    bk = sdv.sdv_kv_alloc_backup(g)
+    obk = o.backup()
+    gp, gl = sdv.sdv_kv_alloc_branches(g, 1, topk, S, dev(table), dev(seq))
+    op, ol, _, _ = oal.alloc_branches(o, table, seq, topk, S, 1)
+    _alloc_equal(g, o)
+    assert np.array_equal(host(gp), op) and np.array_equal(host(gl), ol)
+    sdv.sdv_kv_alloc_restore(g, bk)
+    o.restore(obk)
+    _alloc_equal(g, o)
+    assert o.top == cap and o.error == 0
+
+
+@pytest.mark.parametrize("P,topk,S", [(4, 3, 3), (16, 4, 5), (16, 8, 20), (8, 2, 9)])
+def test_kv_alloc_duplicated_partial_pages(P, topk, S):
+    """Branch layout with the partial-page copies, every layer, K and V."""
+    rng = np.random.default_rng(P * 100 + topk * 10 + S)
+    B, layers, Hkv, D = 6, 3, 2, 64
+    cap = 400
+    g, o = _alloc_pair(cap)
+    seq = rng.integers(0, 5 * P, size=B).astype(np.int32)
+    seq[0] = 2 * P                                          # page aligned: no copy
+    max_pages = 8
+    table = np.full((B, max_pages), -1, np.int32)
+    gt = dev(table)
+    sdv.sdv_kv_alloc_extend(g, P, 0, gt, dev(np.zeros(B, np.int32)))      # n = 0: nothing taken
+    table, _ = oal.alloc_extend(o, table, np.zeros(B, np.int32), 0, P)
+    gt = dev(table)
+    gseq0 = dev(np.zeros(B, np.int32))
+    sdv.sdv_kv_alloc_extend(g, P, int(seq.max()), gt, gseq0)               # give every request pages
+    table, _ = oal.alloc_extend(o, table, np.zeros(B, np.int32), int(seq.max()), P)
+    _alloc_equal(g, o)
+    assert np.array_equal(host(gt), table)
+    slots = cap * P
+    kp = [rng.integers(0, 65536, size=(slots, Hkv, D)).astype(np.uint16) for _ in range(layers)]
+    vp = [rng.integers(0, 65536, size=(slots, Hkv, D)).astype(np.uint16) for _ in range(layers)]
+    gk, gv = [dev(x) for x in kp], [dev(x) for x in vp]
+    say("kv alloc branches", P, topk, S)
+    gp, gl = sdv.sdv_kv_alloc_branches(g, P, topk, S, gt, dev(seq), gk, gv)
+    op, ol, ok2, ov2 = oal.alloc_branches(o, table, seq, topk, S, P, kp, vp)
+    _alloc_equal(g, o)
+    assert np.array_equal(host(gp), op) and np.array_equal(host(gl), ol)
+    for a, b in zip(gk + gv, ok2 + ov2):
+        assert np.array_equal(host(a).view(np.uint16), b)
+
+
+@pytest.mark.parametrize("P,n", [(1, 7), (4, 5), (16, 64), (16, 1)])
+def test_kv_alloc_extend(P, n):
+    rng = np.random.default_rng(P + n)
+    B, max_pages, cap = 40, 64, 3000
+    g, o = _alloc_pair(cap)
+    seq = np.zeros(B, np.int32)
+    table = np.full((B, max_pages), -1, np.int32)
+    gt = dev(table)
+    say("kv alloc extend", P, n)
+    for _ in range(3):
+        grow = rng.integers(0, 3, size=B).astype(np.int32) * n // 2
+        gl = sdv.sdv_kv_alloc_extend(g, P, n, gt, dev(seq))
+        table, ol = oal.alloc_extend(o, table, seq, n, P)
+        _alloc_equal(g, o)
+        assert np.array_equal(host(gt), table) and np.array_equal(host(gl), ol)
+        seq = seq + np.minimum(grow, n).astype(np.int32)
+
+
+def test_kv_alloc_errors_change_nothing():
+    g, o = _alloc_pair(10)
+    table = np.full((2, 4), -1, np.int32)
+    gt = dev(table)
+    say("kv alloc errors")
+    gl = sdv.sdv_kv_alloc_extend(g, 1, 6, gt, dev(np.zeros(2, np.int32)))          # 12 > 10
+    t2, ol = oal.alloc_extend(o, table, np.zeros(2, np.int32), 6, 1)
+    _alloc_equal(g, o)
+    assert (host(gl) == -1).all() and np.array_equal(host(gt), table) and o.error == 1
+    gp, gl = sdv.sdv_kv_alloc_branches(g, 1, 3, 4, gt, dev(np.zeros(2, np.int32)))  # 24 > 10
+    oal.alloc_branches(o, table, np.zeros(2, np.int32), 3, 4, 1)
+    _alloc_equal(g, o)
+    assert (host(gp) == -1).all() and (host(gl) == -1).all()
+    bk, obk = sdv.sdv_kv_alloc_backup(g), o.backup()
+    sdv.sdv_kv_alloc_extend(g, 1, 2, gt, dev(np.zeros(2, np.int32)))
+    table, _ = oal.alloc_extend(o, table, np.zeros(2, np.int32), 2, 1)
+    ids = np.array([table[0, 0]], np.int32)
+    sdv.sdv_kv_alloc_free(g, dev(ids), dev(np.array([1], np.int32)))
+    o.push(ids)
+    sdv.sdv_kv_alloc_restore(g, bk)                                                  # refused: a push since
+    o.restore(obk)
+    _alloc_equal(g, o)
+    assert o.error & 2
+    many = np.arange(20, dtype=np.int32)
+    sdv.sdv_kv_alloc_free(g, dev(many), dev(np.array([20], np.int32)))               # overflow
+    o.push(many)
+    _alloc_equal(g, o)
+    assert o.error & 4
+
+
+@pytest.mark.parametrize("page", [1, 4])
+def test_kv_alloc_speculative_rounds_with_compaction(page):
+    """Rounds of: backup, draft branches, rollback, verify-tree extend,
+    compaction (GPU and oracle each on their own state), release of the freed
+    units.  The allocator, tables and pools agree after every round."""
+    rng = np.random.default_rng(page)
+    B, N, S, topk = 8, 12, 4, 3
+    Hkv, D, layers = 2, 64, 2
+    max_pages = 256 // page
+    cap = B * max_pages
+    g, o = _alloc_pair(cap)
+    seq = rng.integers(1, 40, size=B).astype(np.int32)
+    table = np.full((B, max_pages), -1, np.int32)
+    gt = dev(table)
+    sdv.sdv_kv_alloc_extend(g, page, int(seq.max()), gt, dev(np.zeros(B, np.int32)))
+    table, _ = oal.alloc_extend(o, table, np.zeros(B, np.int32), int(seq.max()), page)
+    # page 1 moves no KV bytes (slot maps only); page 4 copies partial pages
+    # and compacts rows in the pools
+    nl = layers if page > 1 else 0
+    kp = [rng.integers(0, 65536, size=(cap * page, Hkv, D)).astype(np.uint16) for _ in range(nl)]
+    vp = [rng.integers(0, 65536, size=(cap * page, Hkv, D)).astype(np.uint16) for _ in range(nl)]
+    gk, gv = [dev(x) for x in kp], [dev(x) for x in vp]
+    gseq = dev(seq)
+    for rnd in range(4):
+        say("kv alloc round", page, rnd)
+        bk, obk = sdv.sdv_kv_alloc_backup(g), o.backup()
+        gp, gl = sdv.sdv_kv_alloc_branches(g, page, topk, S, gt, gseq, gk, gv)
+        op, ol, kp, vp = oal.alloc_branches(o, table, seq, topk, S, page, kp, vp)
+        assert np.array_equal(host(gp), op) and np.array_equal(host(gl), ol)
+        sdv.sdv_kv_alloc_restore(g, bk)
+        o.restore(obk)
+        sdv.sdv_kv_alloc_extend(g, page, N, gt, gseq)
+        table, _ = oal.alloc_extend(o, table, seq, N, page)
+        _alloc_equal(g, o)
+        acc = rng.integers(0, S + 1, size=B).astype(np.int32)
+        path = np.full((B, S + 1), -1, np.int32)
+        for b in range(B):
+            path[b, :acc[b] + 1] = np.sort(np.concatenate([[0], rng.choice(np.arange(1, N), acc[b], replace=False)]))
+        new_len, freed, num_freed = sdv.sdv_compact_kv(gt, gseq, dev(acc), dev(path), N, S, page, gk, gv)
+        table, kp, vp, onew, ofreed = ocmp.compact_kv(table, kp, vp, seq, acc, path, N, page)
+        sdv.sdv_kv_alloc_free(g, freed, num_freed)
+        o.push(ofreed)
+        _alloc_equal(g, o)
+        assert np.array_equal(host(gt), table) and np.array_equal(host(new_len), onew)
+        for a, b in zip(gk + gv, kp + vp):
+            assert np.array_equal(host(a).view(np.uint16), b)
+        seq = onew.astype(np.int32)
+        gseq = new_len
+        assert o.error == 0
 
 
 # ------------------------------------------------- draft extend index prep
