@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--extend-prep", action="store_true",
                     help="add the index preparation of the draft extend after the accept walk to the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 5 times (scales the HBM counters)")
     return ap.parse_args()
