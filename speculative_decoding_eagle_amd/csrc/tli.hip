@@ -4,10 +4,12 @@
 // of the draft distribution into the target vocabulary.
 //
 // The pruned LM head is a skinny GEMM (B ~ 64 rows) that streams the
-// [K, H] bf16 weight once from HBM: each 4-wave block owns 64 weight rows,
-// each wave 16 of them, and runs bf16 MFMA 16x16x32 with fp32 accumulators
-// over all B rows; the small hidden matrix is re-read from L1/L2.  The remap
-// kernels are coalesced gathers/scatters.
+// [K, H] bf16 weight once from HBM: each 4-wave block owns 256 weight rows,
+// each wave 64 of them, and runs bf16 MFMA 16x16x32 with fp32 accumulators
+// over all B rows; the small hidden matrix is re-read from L1/L2, each
+// fragment serving four weight fragments.  The constraint and the scatter
+// write 16 bytes per thread and row over eight rows per block, their gathers
+// all in flight; the id maps are coalesced gathers/scatters.
 #include <cmath>
 
 #include "common.hpp"
@@ -17,9 +19,13 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+constexpr int kRowsPerScatter = 8;   // rows per block of the 4-wide scatter and constraint kernels
+constexpr int kXcdCount = 8;
 
 constexpr int kGemmThreads = 256;
-constexpr int kRowsPerBlock = 64;   // weight rows (output columns) per block
+constexpr int kNBlocks = 4;         // 16-row weight blocks per wave
+constexpr int kRowsPerBlock = kGemmThreads / 64 * 16 * kNBlocks;   // weight rows (output columns) per block
 constexpr int kMaxMBlocks = 8;      // hidden rows handled per pass: 8 x 16 = 128
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
@@ -29,45 +35,60 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
   return r;
 }
 
-// logits[b, j] = sum_h hidden[b, h] * weight[j, h]
-template <int MB>
+// logits[b, j] = sum_h hidden[b, h] * weight[j, h].  Wave w of a block owns
+// NB blocks of 16 weight rows; per 32-column step it loads NB weight and MB
+// hidden fragments (16 bytes per lane each) and runs NB * MB MFMAs, so each
+// hidden fragment read from L1/L2 serves NB weight fragments.
+template <int MB, int NB>
 __global__ void __launch_bounds__(kGemmThreads)
 lm_head_kernel(int B, int H, int K, const uint16_t *__restrict__ hidden,
                const uint16_t *__restrict__ weight, float *__restrict__ logits) {
   const int wave = threadIdx.x / kWave;
   const int l = lane_id();
-  const int n0 = blockIdx.x * kRowsPerBlock + wave * 16;        // first weight row of this wave
-  const int m0 = blockIdx.y * (MB * 16);                         // first hidden row of this pass
-  const int nrow = min(n0 + (l & 15), K - 1);                     // clamp the tail (never stored)
+  const int n0 = (blockIdx.x * (kGemmThreads / kWave) + wave) * (16 * NB);   // first weight row of this wave
+  const int m0 = blockIdx.y * (MB * 16);                                     // first hidden row of this pass
   const int kofs = 8 * (l >> 4);
-  const uint16_t *wp = weight + static_cast<int64_t>(nrow) * H + kofs;
+  const uint16_t *wp[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int nrow = min(n0 + nb * 16 + (l & 15), K - 1);                   // clamp the tail (never stored)
+    wp[nb] = weight + static_cast<int64_t>(nrow) * H + kofs;
+  }
   const uint16_t *hp[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int mrow = min(m0 + mb * 16 + (l & 15), B - 1);
     hp[mb] = hidden + static_cast<int64_t>(mrow) * H + kofs;
   }
-  f32x4 acc[MB];
+  f32x4 acc[MB][NB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int k0 = 0; k0 < H; k0 += 32) {
-    const bf16x8 bw = load_bf16x8(wp + k0);
+    bf16x8 bw[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) bw[nb] = load_bf16x8(wp[nb] + k0);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const bf16x8 ah = load_bf16x8(hp[mb] + k0);
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[mb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[nb], acc[mb][nb], 0, 0, 0);
     }
   }
   // D[m][n]: lane l holds rows 4*(l/16)+i of the 16x16 block, column l%16
-  const int ncol = n0 + (l & 15);
-  if (ncol < K) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int ncol = n0 + nb * 16 + (l & 15);
+    if (ncol >= K) continue;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = m0 + mb * 16 + 4 * (l >> 4) + i;
-        if (m < B) logits[static_cast<int64_t>(m) * K + ncol] = acc[mb][i];
+        if (m < B) logits[static_cast<int64_t>(m) * K + ncol] = acc[mb][nb][i];
       }
   }
 }
@@ -104,6 +125,42 @@ __device__ __forceinline__ int find_sorted(const int *__restrict__ a, int n, int
   return (lo < n && a[lo] == v) ? lo : -1;
 }
 
+// Four consecutive draft ids per thread: one search finds the first, the
+// sorted list gives the other three by stepping; kRowsPerScatter rows per
+// block, 16-byte non-temporal stores.  Needs Vd % 4 == 0 and a 16-byte
+// aligned output.
+__global__ void __launch_bounds__(256)
+constrain4_kernel(int B, int K, int Vd, const float *__restrict__ pruned, const int *__restrict__ inter,
+                  float *__restrict__ full) {
+  const int v = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (v >= Vd) return;
+  int lo = 0, hi = K;                    // first position with inter[pos] >= v
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (inter[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  int j[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool hit = lo < K && inter[lo] == v + q;
+    j[q] = hit ? lo : -1;
+    lo += hit ? 1 : 0;
+  }
+  const int b0 = blockIdx.y * kRowsPerScatter;
+#pragma unroll
+  for (int bb = 0; bb < kRowsPerScatter; ++bb) {
+    const int b = b0 + bb;
+    if (b >= B) break;
+    const float *pr = pruned + static_cast<int64_t>(b) * K;
+    f32x4v o;
+    o.x = j[0] >= 0 ? pr[j[0]] : -INFINITY;
+    o.y = j[1] >= 0 ? pr[j[1]] : -INFINITY;
+    o.z = j[2] >= 0 ? pr[j[2]] : -INFINITY;
+    o.w = j[3] >= 0 ? pr[j[3]] : -INFINITY;
+    __builtin_nontemporal_store(o, reinterpret_cast<f32x4v *>(full + static_cast<int64_t>(b) * Vd + v));
+  }
+}
+
 __global__ void constrain_kernel(int B, int K, int Vd, const float *__restrict__ pruned,
                                  const int *__restrict__ inter, float *__restrict__ full) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
@@ -118,6 +175,36 @@ __global__ void inverse_kernel(int K, const int *__restrict__ tgt, int Vt, int *
   if (j >= K) return;
   const int t = tgt[j];
   if (t >= 0 && t < Vt) inv[t] = j;
+}
+
+// Four consecutive target ids per thread (one 16-byte inverse load, one
+// 16-byte non-temporal store per row) over kRowsPerScatter rows, whose
+// gathers are independent and all in flight.  The gathers land anywhere in
+// their q rows, so every block of a row group runs on the XCD that owns the
+// group (hardware block h runs on XCD h % 8): each row is then fetched into
+// one L2 only, where the group's blocks find it.  Needs Vt % 4 == 0 and a
+// 16-byte aligned output.
+__global__ void __launch_bounds__(256)
+q_scatter4_kernel(int64_t rows, int K, int Vt, int nchunks, const float *__restrict__ q,
+                  const int *__restrict__ inv, float *__restrict__ out) {
+  const int xcd = blockIdx.x % kXcdCount, slot = blockIdx.x / kXcdCount;
+  const int64_t group = static_cast<int64_t>(slot / nchunks) * kXcdCount + xcd;
+  const int v = ((slot % nchunks) * 256 + static_cast<int>(threadIdx.x)) * 4;
+  const int64_t r0 = group * kRowsPerScatter;
+  if (v >= Vt || r0 >= rows) return;
+  const int4 j = *reinterpret_cast<const int4 *>(inv + v);
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerScatter; ++rr) {
+    const int64_t r = r0 + rr;
+    if (r >= rows) break;
+    const float *qr = q + r * K;
+    f32x4v o;
+    o.x = j.x >= 0 ? qr[j.x] : 0.0f;
+    o.y = j.y >= 0 ? qr[j.y] : 0.0f;
+    o.z = j.z >= 0 ? qr[j.z] : 0.0f;
+    o.w = j.w >= 0 ? qr[j.w] : 0.0f;
+    __builtin_nontemporal_store(o, reinterpret_cast<f32x4v *>(out + r * Vt + v));
+  }
 }
 
 __global__ void q_scatter_kernel(int64_t rows, int K, int Vt, const float *__restrict__ q,
@@ -153,16 +240,16 @@ extern "C" int32_t sdv_tli_lm_head(int32_t B, int32_t H, int32_t K, const uint16
   const int mpass = kMaxMBlocks * 16;
   dim3 grid(nblk(K, kRowsPerBlock), nblk(B, mpass));
   if (B <= 16) {
-    hipLaunchKernelGGL(lm_head_kernel<1>, grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
+    hipLaunchKernelGGL((lm_head_kernel<1, kNBlocks>), grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
                        weight, logits);
   } else if (B <= 32) {
-    hipLaunchKernelGGL(lm_head_kernel<2>, grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
+    hipLaunchKernelGGL((lm_head_kernel<2, kNBlocks>), grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
                        weight, logits);
   } else if (B <= 64) {
-    hipLaunchKernelGGL(lm_head_kernel<4>, grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
+    hipLaunchKernelGGL((lm_head_kernel<4, kNBlocks>), grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K, hidden,
                        weight, logits);
   } else {
-    hipLaunchKernelGGL(lm_head_kernel<kMaxMBlocks>, grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K,
+    hipLaunchKernelGGL((lm_head_kernel<kMaxMBlocks, kNBlocks>), grid, dim3(kGemmThreads), 0, as_stream(stream), B, H, K,
                        hidden, weight, logits);
   }
   return check_launch("lm_head_kernel");
@@ -202,6 +289,11 @@ extern "C" int32_t sdv_tli_constrain_draft_logits(int32_t B, int32_t K, int32_t 
   SDV_REQUIRE(B >= 0 && K >= 0 && V_draft >= 1 && K <= V_draft, SDV_E_SHAPE, "tli_constrain: bad sizes");
   if (B == 0) return SDV_OK;
   SDV_REQUIRE(full && (K == 0 || (pruned && inter_ids)), SDV_E_NULL, "tli_constrain: NULL pointer");
+  if (V_draft % 4 == 0 && reinterpret_cast<uintptr_t>(full) % 16 == 0) {
+    hipLaunchKernelGGL(constrain4_kernel, dim3(nblk(V_draft / 4, 256), nblk(B, kRowsPerScatter)), dim3(256), 0,
+                       as_stream(stream), B, K, V_draft, pruned, inter_ids, full);
+    return check_launch("constrain4_kernel");
+  }
   hipLaunchKernelGGL(constrain_kernel, dim3(nblk(V_draft, 256)), dim3(256), 0, as_stream(stream), B, K, V_draft,
                      pruned, inter_ids, full);
   return check_launch("constrain_kernel");
@@ -227,6 +319,14 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
                      static_cast<int64_t>(V_target), -1);
   if (K > 0)
     hipLaunchKernelGGL(inverse_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, tgt_ids, V_target, inv);
+  if (V_target % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0) {
+    const int nchunks = static_cast<int>(nblk(V_target / 4, 256));
+    const int64_t groups = nblk(rows, kRowsPerScatter);
+    const int64_t per_xcd = (groups + kXcdCount - 1) / kXcdCount;     // row groups per XCD
+    hipLaunchKernelGGL(q_scatter4_kernel, dim3(static_cast<unsigned>(per_xcd * nchunks * kXcdCount)), dim3(256), 0,
+                       st, rows, K, V_target, nchunks, q_pruned, inv, q_target);
+    return check_launch("q_scatter4_kernel");
+  }
   hipLaunchKernelGGL(q_scatter_kernel, dim3(nblk(V_target, 256), static_cast<unsigned>(rows)), dim3(256), 0, st,
                      rows, K, V_target, q_pruned, inv, q_target);
   return check_launch("q_scatter_kernel");
