@@ -7,9 +7,10 @@
 // [K, H] bf16 weight once from HBM: each 4-wave block owns 256 weight rows,
 // each wave 64 of them, and runs bf16 MFMA 16x16x32 with fp32 accumulators
 // over all B rows; the small hidden matrix is re-read from L1/L2, each
-// fragment serving four weight fragments.  The constraint and the scatter
-// write 16 bytes per thread and row over eight rows per block, their gathers
-// all in flight; the id maps are coalesced gathers/scatters.
+// fragment serving four weight fragments.  The constraint writes 16 bytes
+// per thread and row over eight rows per block, its gathers all in flight;
+// the scatter stages most of each q row in LDS so that its random gathers
+// read LDS; the id maps are coalesced gathers/scatters.
 #include <cmath>
 
 #include "common.hpp"
@@ -207,6 +208,37 @@ q_scatter4_kernel(int64_t rows, int K, int Vt, int nchunks, const float *__restr
   }
 }
 
+// One 1024-thread block per row: the first kScatterLds entries of the q row
+// are staged in LDS (16-byte loads), so most of the random gathers read
+// LDS; the rest read the row from L2.  Each thread then writes four target
+// ids per iteration with one 16-byte non-temporal store.  Needs Vt % 4 ==
+// 0, K % 4 == 0 and 16-byte aligned rows.
+constexpr int kScatterLds = 36864;     // floats of a q row staged in LDS (144 KB)
+constexpr int kScatterThreads = 1024;
+
+__global__ void __launch_bounds__(kScatterThreads)
+q_scatter_lds_kernel(int K, int Vt, const float *__restrict__ q, const int *__restrict__ inv,
+                     float *__restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) float s_q[];
+  const int64_t r = blockIdx.x;
+  const float *qr = q + r * K;
+  const int nl = min(K, kScatterLds);
+  for (int i = 4 * static_cast<int>(threadIdx.x); i < nl; i += 4 * kScatterThreads)
+    *reinterpret_cast<float4 *>(s_q + i) = *reinterpret_cast<const float4 *>(qr + i);
+  __syncthreads();
+  auto pick = [&](int j) { return j < 0 ? 0.0f : (j < nl ? s_q[j] : qr[j]); };
+#pragma unroll 2
+  for (int v = 4 * static_cast<int>(threadIdx.x); v < Vt; v += 4 * kScatterThreads) {
+    const int4 j = *reinterpret_cast<const int4 *>(inv + v);
+    f32x4v o;
+    o.x = pick(j.x);
+    o.y = pick(j.y);
+    o.z = pick(j.z);
+    o.w = pick(j.w);
+    __builtin_nontemporal_store(o, reinterpret_cast<f32x4v *>(out + r * Vt + v));
+  }
+}
+
 __global__ void q_scatter_kernel(int64_t rows, int K, int Vt, const float *__restrict__ q,
                                  const int *__restrict__ inv, float *__restrict__ out) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
@@ -319,6 +351,22 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
                      static_cast<int64_t>(V_target), -1);
   if (K > 0)
     hipLaunchKernelGGL(inverse_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, tgt_ids, V_target, inv);
+  if (V_target % 4 == 0 && K % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0 &&
+      reinterpret_cast<uintptr_t>(q_pruned) % 16 == 0) {
+    const size_t lds = static_cast<size_t>(kScatterLds) * sizeof(float);
+    static thread_local int configured_dev = -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "tli_q_scatter: no device");
+    if (configured_dev != dev) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q_scatter_lds_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return fail(SDV_E_HIP, "tli_q_scatter: LDS attribute: %s", hipGetErrorString(e));
+      configured_dev = dev;
+    }
+    hipLaunchKernelGGL(q_scatter_lds_kernel, dim3(static_cast<unsigned>(rows)), dim3(kScatterThreads), lds, st, K,
+                       V_target, q_pruned, inv, q_target);
+    return check_launch("q_scatter_lds_kernel");
+  }
   if (V_target % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0) {
     const int nchunks = static_cast<int>(nblk(V_target / 4, 256));
     const int64_t groups = nblk(rows, kRowsPerScatter);
