@@ -96,6 +96,7 @@ class Pipeline:
             self.d2t, self.t2d = sdv.sdv_tli_build_maps(d["inter_ids"], d["tgt_ids"], cfg.V_draft, cfg.V,
                                                         self.fallback)
             self.scatter_ws = torch.empty(cfg.V * 4 + 256, dtype=torch.uint8, device="cuda")
+            sdv.sdv_tli_q_scatter(d["q_pruned"], d["tgt_ids"], cfg.V, q_target=self.q_target, ws=self.scatter_ws)
             self.remap_out = torch.empty((B, S + 1), dtype=torch.int32, device="cuda")
             self.draft_rows = self.q_target
         else:
@@ -177,7 +178,8 @@ class Pipeline:
         sdv, d, cfg = self.sdv, self.d, self.cfg
         sdv.sdv_tli_lm_head(d["hidden"][0], d["weight"], logits=self.logits)
         sdv.sdv_tli_constrain_draft_logits(self.logits, d["inter_ids"], cfg.V_draft, full=self.full)
-        sdv.sdv_tli_q_scatter(d["q_pruned"], d["tgt_ids"], cfg.V, q_target=self.q_target, ws=self.scatter_ws)
+        # the target -> intersection inverse was built at set-up (the maps are static)
+        sdv.sdv_tli_q_scatter(d["q_pruned"], None, cfg.V, q_target=self.q_target, ws=self.scatter_ws)
 
     def s_topk(self):
         if self.draft_input == "probs":

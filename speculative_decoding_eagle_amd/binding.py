@@ -444,6 +444,7 @@ def sdv_tli_constrain_draft_logits(pruned, inter_ids, V_draft: int, full=None):
 
 
 def sdv_tli_q_scatter(q_pruned, tgt_ids, V_target: int, q_target=None, ws=None):
+    """tgt_ids None: reuse the inverse an earlier call left in ``ws``."""
     K = q_pruned.shape[-1]
     rows = q_pruned.numel() // K
     dev = q_pruned.device
@@ -452,6 +453,7 @@ def sdv_tli_q_scatter(q_pruned, tgt_ids, V_target: int, q_target=None, ws=None):
     L = _lib.lib()
     wp, wb = _workspace(L.sdv_tli_q_scatter_workspace_size(V_target), dev, ws)
     _check(L.sdv_tli_q_scatter(rows, K, V_target, _ptr(q_pruned, torch.float32, "q_pruned"),
-                               _ptr(tgt_ids, torch.int32, "tgt_ids"), _ptr(q_target, torch.float32, "q_target"),
+                               _ptr(tgt_ids, torch.int32, "tgt_ids", allow_none=True),
+                               _ptr(q_target, torch.float32, "q_target"),
                                wp, wb, _stream(dev)), "sdv_tli_q_scatter")
     return q_target

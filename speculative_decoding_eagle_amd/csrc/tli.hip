@@ -342,15 +342,17 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
   SDV_REQUIRE(rows >= 0 && K >= 0 && V_target >= 1 && K <= V_target, SDV_E_SHAPE, "tli_q_scatter: bad sizes");
   SDV_REQUIRE(rows <= 65535, SDV_E_UNSUPPORTED, "tli_q_scatter: rows above 65535");
   if (rows == 0) return SDV_OK;
-  SDV_REQUIRE(q_target && (K == 0 || (q_pruned && tgt_ids)), SDV_E_NULL, "tli_q_scatter: NULL pointer");
+  SDV_REQUIRE(q_target && (K == 0 || q_pruned), SDV_E_NULL, "tli_q_scatter: NULL pointer");
   const size_t need = sdv_tli_q_scatter_workspace_size(V_target);
   SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "tli_q_scatter: workspace of %zu bytes needed", need);
   int *inv = static_cast<int *>(ws);
   hipStream_t st = as_stream(stream);
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(V_target, 256)), dim3(256), 0, st, inv,
-                     static_cast<int64_t>(V_target), -1);
-  if (K > 0)
-    hipLaunchKernelGGL(inverse_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, tgt_ids, V_target, inv);
+  if (tgt_ids) {                         // else: the inverse an earlier call left in ws
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(V_target, 256)), dim3(256), 0, st, inv,
+                       static_cast<int64_t>(V_target), -1);
+    if (K > 0)
+      hipLaunchKernelGGL(inverse_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, tgt_ids, V_target, inv);
+  }
   if (V_target % 4 == 0 && K % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0 &&
       reinterpret_cast<uintptr_t>(q_pruned) % 16 == 0) {
     const size_t lds = static_cast<size_t>(kScatterLds) * sizeof(float);

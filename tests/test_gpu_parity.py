@@ -708,6 +708,31 @@ def test_tli_constrain_and_scatter_bit_exact():
     assert np.array_equal(host(qt), want)
 
 
+@pytest.mark.parametrize("Vd,Vt,K,rows", [(1001, 999, 300, 5), (1000, 1000, 301, 13), (2048, 4096, 512, 17),
+                                          (50000, 60000, 40000, 9)])
+def test_tli_constrain_and_scatter_shapes(Vd, Vt, K, rows):
+    """Every kernel path: scalar (odd sizes), 16-byte with row groups per XCD
+    (K not a multiple of 4), LDS-staged with the whole q row in LDS, and with
+    a row longer than the LDS copy; then a second scatter that reuses the
+    inverse left in the workspace."""
+    rng = np.random.default_rng(Vd + Vt + K)
+    inter = np.sort(rng.choice(Vd, K, replace=False)).astype(np.int32)
+    tgt = rng.choice(Vt, K, replace=False).astype(np.int32)
+    pruned = rng.standard_normal((rows, K)).astype(np.float32)
+    say("tli constrain/scatter shapes", Vd, Vt, K, rows)
+    full = sdv.sdv_tli_constrain_draft_logits(dev(pruned), dev(inter), Vd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(full), otli.constrain_logits(pruned, inter, Vd))
+    ws = torch.empty(sdv._lib.lib().sdv_tli_q_scatter_workspace_size(Vt), dtype=torch.uint8, device="cuda")
+    q1 = rng.random((rows, K)).astype(np.float32)
+    q2 = rng.random((rows, K)).astype(np.float32)
+    g1 = sdv.sdv_tli_q_scatter(dev(q1), dev(tgt), Vt, ws=ws)
+    g2 = sdv.sdv_tli_q_scatter(dev(q2), None, Vt, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(g1), otli.q_scatter(q1, tgt, Vt))
+    assert np.array_equal(host(g2), otli.q_scatter(q2, tgt, Vt))
+
+
 @pytest.mark.parametrize("B,H,K", [(64, 896, 60000), (5, 64, 1000), (17, 96, 77), (130, 32, 513)])
 def test_tli_lm_head_within_tolerance(B, H, K):
     rng = np.random.default_rng(B + H + K)
