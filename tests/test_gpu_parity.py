@@ -763,3 +763,67 @@ def test_tli_pipeline_c5():
     o = oacc.verify_stochastic(ot, inp["target"], q_host, inp["u_accept"], inp["u_draw"], cfg.S)
     for key in o:
         assert np.array_equal(host(r[key]), o[key]), key
+
+
+# ------------------------------------------------------- degenerate cases
+
+def test_empty_batches_return_without_work():
+    """Every stage with an empty batch: success, empty outputs, no launch
+    that touches memory."""
+    say("empty batches")
+    f32, i32 = torch.float32, torch.int32
+    e = lambda *s, dt=i32: torch.empty(s, dtype=dt, device="cuda")
+    p, i = sdv.sdv_draft_topk(e(0, 100, dt=f32), 4)
+    assert p.shape == (0, 4) and i.shape == (0, 4)
+    p, i = sdv.sdv_draft_topk_logits(e(0, 100, dt=torch.bfloat16), 4)
+    assert p.shape == (0, 4)
+    t = sdv.sdv_build_tree(e(0, 9, 2, dt=f32), e(0, 9, 2), e(0), e(0), 2, 5, 8)
+    assert t["tokens"].shape == (0, 8)
+    c = sdv.sdv_build_chain(e(0, 4, dt=f32), e(0, 4), e(0), e(0))
+    assert c["tokens"].shape == (0, 5)
+    pool = torch.zeros((64, 2, 64), dtype=torch.bfloat16, device="cuda")
+    out, _ = sdv.sdv_tree_verify_attention(e(0, 8, 4, 64, dt=torch.bfloat16), pool, pool, e(0, 16), e(0),
+                                           e(0, 8, 1))
+    assert out.shape == (0, 8, 4, 64)
+    acc = sdv.sdv_verify_accept(sdv.GREEDY, {"tokens": e(0, 8), "next_token": e(0, 8), "next_sibling": e(0, 8),
+                                             "q_row": e(0, 8)}, e(0, 8, 100, dt=f32), 5)
+    assert acc["accept_len"].shape == (0,)
+    new_len, freed, num_freed = sdv.sdv_compact_kv(e(0, 16), e(0), e(0), e(0, 6), 8, 5, 1)
+    assert new_len.shape == (0,)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", ["greedy", "stochastic"])
+def test_single_node_trees_through_every_stage(mode):
+    """N = 1: the tree is the root alone; attention sees the prefix and the
+    root; the walk commits only the bonus token (argmax, or a draw from p);
+    compaction keeps the root and frees nothing."""
+    name = "c3" if mode == "greedy" else "c4"
+    cfg = workloads.get_config(name, V=300, B=3, N=1, S=1, k=2, L_min=5, L_max=50)
+    inp = workloads.generate(cfg)
+    t = oracle_tree(inp, cfg)
+    say("single node", mode)
+    tp, ti = otopk.draft_topk(inp["draft_probs"], cfg.k)
+    g = _gpu_tree(tp, ti, inp["root_token"], inp["prefix_len"], cfg.k, cfg.S, cfg.N)
+    _assert_tree_equal(g, t)
+    _attn_case(cfg, inp)
+    if mode == "greedy":
+        ga = _gpu_accept(sdv.GREEDY, t, inp["target"], cfg.S)
+        o = oacc.verify_greedy(t, inp["target"], cfg.S)
+    else:
+        ga = _gpu_accept(sdv.STOCHASTIC, t, inp["target"], cfg.S, draft_probs=inp["draft_probs"],
+                         u_accept=inp["u_accept"], u_draw=inp["u_draw"])
+        o = oacc.verify_stochastic(t, inp["target"], inp["draft_probs"], inp["u_accept"], inp["u_draw"], cfg.S)
+    _assert_accept_equal(ga, o)
+    assert (o["commit_len"] == 1).all() and (o["accept_len"] == 0).all()
+    table = inp["page_table"]
+    gt = dev(table)
+    pools = ([dev(inp["k_pool"])], [dev(inp["v_pool"])]) if cfg.page > 1 else ([], [])
+    new_len, freed, num_freed = sdv.sdv_compact_kv(gt, dev(inp["prefix_len"]), dev(o["accept_len"]),
+                                                   dev(o["accept_path"]), cfg.N, cfg.S, cfg.page, *pools)
+    torch.cuda.synchronize()
+    ot, _, _, onew, ofreed = ocmp.compact_kv(table, [inp["k_pool"]] if cfg.page > 1 else [],
+                                             [inp["v_pool"]] if cfg.page > 1 else [], inp["prefix_len"],
+                                             o["accept_len"], o["accept_path"], cfg.N, cfg.page)
+    assert np.array_equal(host(gt), ot) and np.array_equal(host(new_len), onew)
+    assert int(host(num_freed)[0]) == len(ofreed)
