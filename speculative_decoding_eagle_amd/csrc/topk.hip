@@ -20,6 +20,32 @@ constexpr int kLoads = 4;        // 16-byte loads per lane in flight per window
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// The wave sort below replaces K rounds of wave-wide best-of selection
+// (six exchange steps each) from this K on, where it is the cheaper of the
+// two.
+constexpr int kSortNetK = 8;
+
+// Sorts one (value, id) pair per lane across the wave under the strict
+// order, best first: lane 0 ends with the best pair.  A bitonic network of
+// 21 compare-exchange stages between lanes l and l ^ stride; equal pairs
+// (only the (-inf, INT_MAX) padding can be equal) never swap.
+__device__ __forceinline__ void wave_sort_best_first(float &v, int &i) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      const float ov = __shfl_xor(v, stride, kWave);
+      const int oi = __shfl_xor(i, stride, kWave);
+      const bool best_first = (lane & size) == 0;            // this block's direction
+      const bool lower = (lane & stride) == 0;                // this lane's place in the pair
+      const bool take = (lower == best_first) ? better(ov, oi, v, i) : better(v, i, ov, oi);
+      v = take ? ov : v;
+      i = take ? oi : i;
+    }
+  }
+}
+
 template <int K>
 struct SortedK {
   float v[K];
@@ -93,8 +119,30 @@ struct WaveFilter {
   }
 
   // Folds the buffered candidates into the best-K list.
-  __device__ void fold() {
+  __device__ __forceinline__ void fold() {
     __builtin_amdgcn_wave_barrier();   // candidate stores of every lane precede the reads
+    if (K >= kSortNetK && cnt + K <= kWave) {
+      // one candidate (or list entry) per lane: a wave sort gives the new list
+      const int x = lane_id();
+      float v = -INFINITY;
+      int i = INT_MAX;
+      if (x < K) {
+        v = tv[x];
+        i = ti[x];
+      } else if (x < K + cnt) {
+        v = cv[x - K];
+        i = ci[x - K];
+      }
+      wave_sort_best_first(v, i);
+      if (x < K) {
+        tv[x] = v;
+        ti[x] = i;
+      }
+      thr_v = __shfl(v, K - 1, kWave);
+      thr_i = __shfl(i, K - 1, kWave);
+      cnt = 0;
+      return;
+    }
     SortedK<K> L;
     L.init();
     const int n = cnt + K;
@@ -387,24 +435,34 @@ topk_slice_kernel(const void *__restrict__ rows_in, int64_t rows, int V, int spl
 #pragma unroll
       for (int x = 0; x < NW; ++x) tot.merge(s_norm[x].x, s_norm[x].y, c2);
     }
-    SortedK<K> L;
-    L.init();
-    for (int x = lane_id(); x < NW * K; x += kWave) L.insert(s_tv[x / K][x % K], s_ti[x / K][x % K]);
-    for (int r = 0; r < K; ++r) {
-      float bv = L.v[0];
-      int bi = L.i[0];
-      wave_best(bv, bi);
-      if (L.i[0] == bi && L.v[0] == bv && bi != INT_MAX) L.pop_front();
-      if (lane_id() == 0) {
-        if (splits == 1) {
-          if (r < k) {
-            out_v[row * k + r] = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
-            out_i[row * k + r] = bi;
-          }
-        } else {
-          part_v[bid * K + r] = bv;
-          part_i[bid * K + r] = bi;
+    auto emit = [&](int r, float bv, int bi) {
+      if (splits == 1) {
+        if (r < k) {
+          out_v[row * k + r] = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
+          out_i[row * k + r] = bi;
         }
+      } else {
+        part_v[bid * K + r] = bv;
+        part_i[bid * K + r] = bi;
+      }
+    };
+    if constexpr (K >= kSortNetK && NW * K <= kWave) {
+      // the four lists fit one per lane: one wave sort, lanes 0 .. K-1 emit
+      const int x = lane_id();
+      float bv = x < NW * K ? s_tv[x / K][x % K] : -INFINITY;
+      int bi = x < NW * K ? s_ti[x / K][x % K] : INT_MAX;
+      wave_sort_best_first(bv, bi);
+      if (x < K) emit(x, bv, bi);
+    } else {
+      SortedK<K> L;
+      L.init();
+      for (int x = lane_id(); x < NW * K; x += kWave) L.insert(s_tv[x / K][x % K], s_ti[x / K][x % K]);
+      for (int r = 0; r < K; ++r) {
+        float bv = L.v[0];
+        int bi = L.i[0];
+        wave_best(bv, bi);
+        if (L.i[0] == bi && L.v[0] == bv && bi != INT_MAX) L.pop_front();
+        if (lane_id() == 0) emit(r, bv, bi);
       }
     }
     if (LOGITS && splits > 1 && lane_id() == 0) part_n[bid] = make_float2(tot.m, tot.s);
@@ -430,6 +488,18 @@ topk_merge_kernel(int64_t rows, int splits, int k, float c2, const float *__rest
       tot.merge(t.x, t.y, c2);
     }
   }
+  auto emit = [&](int r, float bv, int bi) {
+    out_v[row * k + r] = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
+    out_i[row * k + r] = bi;
+  };
+  if (K >= kSortNetK && n <= kWave) {
+    const int x = lane_id();
+    float bv = x < n ? pv[x] : -INFINITY;
+    int bi = x < n ? pi[x] : INT_MAX;
+    wave_sort_best_first(bv, bi);
+    if (x < k) emit(x, bv, bi);
+    return;
+  }
   SortedK<K> L;
   L.init();
   for (int c = lane_id(); c < n; c += kWave) L.insert(pv[c], pi[c]);
@@ -438,10 +508,7 @@ topk_merge_kernel(int64_t rows, int splits, int k, float c2, const float *__rest
     int bi = L.i[0];
     wave_best(bv, bi);
     if (L.i[0] == bi && L.v[0] == bv && bi != INT_MAX) L.pop_front();
-    if (lane_id() == 0) {
-      out_v[row * k + r] = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
-      out_i[row * k + r] = bi;
-    }
+    if (lane_id() == 0) emit(r, bv, bi);
   }
 }
 
