@@ -135,7 +135,7 @@ class Pipeline:
         self.topk_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
         self.tree = {}
         self.acc = {}
-        self.acc_ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+        self.acc_ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")   # calls leave it zero-filled
         self.mode = sdv.STOCHASTIC if cfg.mode == "stochastic" else sdv.GREEDY
         if cfg.has_attention:
             self.attn_out = torch.empty((B, N, cfg.Hq, cfg.D), dtype=torch.bfloat16, device="cuda")

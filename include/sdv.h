@@ -232,7 +232,10 @@ int32_t sdv_tree_verify_attention(sdv_attn_shape shape, float sm_scale, const ui
  * first, -1 padded); commit_tokens [B, S+1] (-1 padded); commit_len [B];
  * next_root [B] (last committed token, -1 if none).
  * Limits: V < 2^31 - 4, N <= 256, S + 1 <= 64.  The walk runs as one
- * cooperative launch; calls that share a workspace must not overlap.
+ * cooperative launch; calls that share a workspace must not overlap.  The
+ * workspace must be zero-filled before its first use; every call leaves it
+ * zero-filled (whatever its shape), so one zero-filled buffer of the largest
+ * size query's bytes serves every later call.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t B, N, S, V, R, mode;

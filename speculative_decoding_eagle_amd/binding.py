@@ -173,17 +173,24 @@ def sdv_build_chain(topk_p, topk_id, root_token, prefix_len, out=None, with_mask
 # ---------------------------------------------------------------------- A5
 
 _ATTN_WS = {}
+_ACC_WS = {}
+
+
+def _zeroed_workspace(cache, nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace kept per (device, stream) for entry points whose
+    calls leave it zero-filled: cleared once, when (re)allocated."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        cache[key] = ws
+    return ws
 
 
 def _attn_workspace(nbytes: int, device) -> torch.Tensor:
     """Zero-filled attention workspace, one per (device, stream): every call
     leaves it zero-filled again, so it is cleared once, when allocated."""
-    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
-    buf = _ATTN_WS.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
-        _ATTN_WS[key] = buf
-    return buf
+    return _zeroed_workspace(_ATTN_WS, nbytes, device)
 
 
 def sdv_tree_verify_attention(q, k_pool, v_pool, page_table, prefix_len, mask_bits, page: int = 1,
@@ -238,7 +245,10 @@ def sdv_verify_accept(mode: int, tree, target, S: int, eos_id: int = -1, remaini
             out[name] = torch.empty(shape, dtype=i32, device=dev)
     shape = AcceptShape(B, N, S, V, R, mode)
     L = _lib.lib()
-    wp, wb = _workspace(L.sdv_verify_accept_workspace_size(shape), dev, ws)
+    need = L.sdv_verify_accept_workspace_size(shape)
+    if ws is None and need:
+        ws = _zeroed_workspace(_ACC_WS, need, dev)
+    wp, wb = _workspace(need, dev, ws)
     _check(L.sdv_verify_accept(
         shape, eos_id, _ptr(remaining, i32, "remaining", allow_none=True), _ptr(tokens, i32, "tokens"),
         _ptr(tree["next_token"], i32, "next_token"), _ptr(tree["next_sibling"], i32, "next_sibling"),

@@ -36,6 +36,10 @@
 // exchange n+2 after every workgroup has published exchange n+1, which each
 // does only after reading exchange n.  Every poll is bounded; on timeout the
 // kernel records an error flag and carries on, so every wave always exits.
+// The words start at zero and every call leaves them zero: when a
+// workgroup has read its last word it bumps the request's counter, and the
+// group's last workgroup clears the request's words and the counter, so no
+// clearing launch precedes the walk.
 #include <atomic>
 #include <climits>
 #include <cmath>
@@ -59,7 +63,8 @@ struct AcceptArgs {
   const int *tokens, *next_token, *next_sibling, *q_row;
   const float *target, *draft, *u_accept, *u_draw;
   int *accept_len, *accept_path, *commit_tokens, *commit_len, *next_root;
-  unsigned long long *part;            // [B][2][kMaxGroup] tagged partials (zeroed before the launch)
+  unsigned long long *part;            // [B][2][kMaxGroup] tagged partials (zero at the start, left zero)
+  unsigned *done;                      // [B] workgroups of the request that have finished
   unsigned *err;                       // [1] timeout flag
 };
 
@@ -565,11 +570,22 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
 
   __syncthreads();
   if (writer) write_outputs(a, b, s_path, s_out, path_len, n_out);
-}
-
-__global__ void zero_u32_kernel(unsigned *p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  // Every wave of this workgroup is past its last read of the ring (the
+  // barrier above: the values read have been used); the group's last
+  // workgroup to get here clears it, one word per thread.  No fence is
+  // needed: no read of the ring is outstanding in any workgroup that has
+  // counted itself, and the clearing stores need only land before the next
+  // call's launch.
+  __shared__ int s_last;
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.done + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == static_cast<unsigned>(a.W - 1);
+  }
+  __syncthreads();
+  if (s_last) {
+    if (tid < 2 * kMaxGroup) store_part(ring + tid, 0ull);
+    if (tid == 0) __hip_atomic_store(a.done + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 struct AcceptPlan {
@@ -650,6 +666,7 @@ extern "C" size_t sdv_verify_accept_workspace_size(sdv_accept_shape sh) {
   if (sh.B <= 0) return 0;
   Carver c(nullptr);
   c.take<unsigned long long>(static_cast<size_t>(sh.B) * 2 * kMaxGroup + 1);
+  c.take<unsigned>(static_cast<size_t>(sh.B));
   return c.bytes();
 }
 
@@ -687,12 +704,8 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
   Carver cv(ws);
   const size_t words = static_cast<size_t>(sh.B) * 2 * kMaxGroup + 1;
   unsigned long long *part = cv.take<unsigned long long>(words);
+  unsigned *done = cv.take<unsigned>(static_cast<size_t>(sh.B));
   hipStream_t st = as_stream(stream);
-  const int nz = static_cast<int>(words * 2);
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, st, reinterpret_cast<unsigned *>(part),
-                     nz);
-  rc = check_launch("zero_u32_kernel");
-  if (rc != SDV_OK) return rc;
 
   AcceptArgs a;
   a.B = sh.B; a.N = sh.N; a.S = sh.S; a.V = sh.V; a.R = sh.R; a.mode = sh.mode; a.eos = eos_id;
@@ -703,6 +716,7 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
   a.accept_len = accept_len; a.accept_path = accept_path; a.commit_tokens = commit_tokens;
   a.commit_len = commit_len; a.next_root = next_root;
   a.part = part;
+  a.done = done;
   a.err = reinterpret_cast<unsigned *>(part + words - 1);
   const void *fn = accept_kernel_for(p.E, sh.mode == SDV_ACCEPT_STOCHASTIC, vec);
   for (int b0 = 0; b0 < sh.B; b0 += p.per_launch) {

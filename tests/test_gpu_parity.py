@@ -187,6 +187,8 @@ def _gpu_accept(mode, tree, target, S, **kw):
     for key in ("draft_probs", "u_accept", "u_draw", "remaining"):
         if kw.get(key) is not None:
             args[key] = dev(kw[key])
+    if kw.get("ws") is not None:
+        args["ws"] = kw["ws"]
     r = sdv.sdv_verify_accept(mode, gt, dev(target), S, eos_id=kw.get("eos_id", -1), **args)
     torch.cuda.synchronize()
     return {key: host(v) for key, v in r.items()}
@@ -255,6 +257,28 @@ def test_accept_stochastic_bit_exact(name, V, B, planted):
                     u_draw=inp["u_draw"])
     o = oacc.verify_stochastic(tree, p, inp["draft_probs"], inp["u_accept"], inp["u_draw"], cfg.S)
     _assert_accept_equal(g, o)
+
+
+def test_accept_leaves_its_workspace_zero():
+    """The exchange words and counters are cleared by each call's last
+    workgroup per request: one explicit zero-filled workspace serves calls
+    of both modes and several batch sizes, and is all zero after each."""
+    cfg = workloads.get_config("c4", V=4096, B=16)
+    inp = workloads.generate(cfg, with_attention=False)
+    tree = oracle_tree(inp, cfg)
+    p = plant_stochastic(inp["target"], inp["draft_probs"], tree, workloads.extra_rng(cfg, 8), cfg.S)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    say("accept workspace reset")
+    for sub in (16, 5, 16):
+        t = {key: v[:sub] for key, v in tree.items()}
+        g = _gpu_accept(sdv.STOCHASTIC, t, p[:sub], cfg.S, draft_probs=inp["draft_probs"][:sub],
+                        u_accept=inp["u_accept"][:sub], u_draw=inp["u_draw"][:sub], ws=ws)
+        _assert_accept_equal(g, oacc.verify_stochastic(t, p[:sub], inp["draft_probs"][:sub], inp["u_accept"][:sub],
+                                                       inp["u_draw"][:sub], cfg.S))
+        assert int(torch.count_nonzero(ws)) == 0
+        g = _gpu_accept(sdv.GREEDY, t, p[:sub], cfg.S, ws=ws)
+        _assert_accept_equal(g, oacc.verify_greedy(t, p[:sub], cfg.S))
+        assert int(torch.count_nonzero(ws)) == 0
 
 
 def test_accept_stochastic_degenerate_rows():
