@@ -132,7 +132,7 @@ class Pipeline:
         self.topk_id = torch.empty((B, cfg.R, k), dtype=torch.int32, device="cuda")
         ws = max(sdv._lib.lib().sdv_draft_topk_workspace_size(rows, cfg.V, k),
                  sdv._lib.lib().sdv_draft_topk_logits_workspace_size(rows, cfg.V, k))
-        self.topk_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+        self.topk_ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device="cuda")   # calls leave it zeroed
         self.tree = {}
         self.acc = {}
         self.acc_ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")   # calls leave it zero-filled

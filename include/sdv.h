@@ -64,6 +64,17 @@ int32_t sdv_version(void);
  * largest values in descending order to topk_p (device, [rows, k] fp32) and
  * their column ids to topk_id (device, [rows, k] int32).  Equal values are
  * ordered by ascending id.  1 <= k <= 32, k <= V, V < 2^31.
+ *
+ * Workspace (device, the size query's bytes; 0 when the rows are a multiple
+ * of the device's compute units, or short): with rows = q * CUs + r, the
+ * first q * CUs rows are scanned one workgroup each, and the r others are
+ * cut into equal pieces spread over the compute units; a cut row is merged
+ * by the workgroup that finishes it last, through per-row counters at the
+ * start of the workspace.  The caller
+ * zero-fills the workspace once before its first use; every call leaves the
+ * counters at zero again, so the same workspace serves later calls of any
+ * shape.  Calls that share a workspace must not run concurrently.  Results
+ * do not depend on the split (the k best under the order above are unique).
  * ---------------------------------------------------------------------- */
 size_t sdv_draft_topk_workspace_size(int64_t rows, int32_t V, int32_t k);
 int32_t sdv_draft_topk(const float *probs, int64_t rows, int32_t V, int32_t k,
@@ -84,8 +95,10 @@ int32_t sdv_draft_topk(const float *probs, int64_t rows, int32_t V, int32_t k,
  * exact probabilities, i.e. of the logits, lower id first among equal
  * logits (fp32 rounding of p never reorders).  p is computed in fp32 with
  * the row's normaliser accumulated in a fixed order (deterministic).
- * temperature > 0; 1 <= k <= 32, k <= V, V < 2^31.  Scratch: the size query's
- * bytes (0 when rows alone fill the GPU).
+ * temperature > 0; 1 <= k <= 32, k <= V, V < 2^31.  Workspace: as for
+ * sdv_draft_topk (zero-filled once, left zero-filled by every call); the
+ * segments' normalisers are merged in segment order, so the values are
+ * deterministic for a given device and shape.
  * ---------------------------------------------------------------------- */
 enum { SDV_DTYPE_F32 = 0, SDV_DTYPE_BF16 = 1 };
 

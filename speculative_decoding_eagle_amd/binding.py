@@ -69,8 +69,14 @@ def _keep(*_):
 
 # ---------------------------------------------------------------------- A1
 
+_TOPK_WS = {}
+
+
 def sdv_draft_topk(probs: torch.Tensor, k: int, topk_p=None, topk_id=None, ws=None):
-    """Top-k of every row of ``probs`` [..., V] fp32 -> (topk_p, topk_id) [..., k]."""
+    """Top-k of every row of ``probs`` [..., V] fp32 -> (topk_p, topk_id) [..., k].
+
+    ``ws``: a zero-filled workspace of the size query's bytes (the calls keep
+    it zero-filled); by default a cached one per (device, stream)."""
     V = probs.shape[-1]
     rows = probs.numel() // V if V else 0
     dev = probs.device
@@ -80,6 +86,8 @@ def sdv_draft_topk(probs: torch.Tensor, k: int, topk_p=None, topk_id=None, ws=No
         topk_id = torch.empty(probs.shape[:-1] + (k,), dtype=torch.int32, device=dev)
     L = _lib.lib()
     need = L.sdv_draft_topk_workspace_size(rows, V, k)
+    if need and ws is None:
+        ws = _zeroed_workspace(_TOPK_WS, need, dev)
     wp, wb = _workspace(need, dev, ws)
     _check(L.sdv_draft_topk(_ptr(probs, torch.float32, "probs"), rows, V, k, _ptr(topk_p, torch.float32, "topk_p"),
                             _ptr(topk_id, torch.int32, "topk_id"), wp, wb, _stream(dev)), "sdv_draft_topk")
@@ -105,6 +113,8 @@ def sdv_draft_topk_logits(logits: torch.Tensor, k: int, temperature: float = 1.0
         topk_id = torch.empty(logits.shape[:-1] + (k,), dtype=torch.int32, device=dev)
     L = _lib.lib()
     need = L.sdv_draft_topk_logits_workspace_size(rows, V, k)
+    if need and ws is None:
+        ws = _zeroed_workspace(_TOPK_WS, need, dev)
     wp, wb = _workspace(need, dev, ws)
     _check(L.sdv_draft_topk_logits(_ptr(logits, (torch.float32, torch.bfloat16), "logits"), dtype, rows, V, k,
                                    float(temperature), _ptr(topk_p, torch.float32, "topk_p"),

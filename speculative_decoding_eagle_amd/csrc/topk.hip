@@ -2,11 +2,13 @@
 // softmax, "[SGLang] Multi-Layer EAGLE" section 3).
 //
 // HBM-bound streaming reduction under the strict order (value desc, id asc).
-// Each 256-thread block scans one slice of one row in contiguous 16 KB
-// windows (16-byte non-temporal loads, four in flight per lane); every wave
-// runs a threshold filter (below) over its share, and wave 0 merges the four
-// per-wave lists.  Short-row batches are split over several blocks per
-// row, and a one-wave kernel merges the per-slice lists.
+// Each 256-thread block scans its segments in contiguous 16 KB windows
+// (16-byte non-temporal loads, four per lane, the next window's in flight
+// while this one is processed); every wave runs a threshold filter (below)
+// over its share, and wave 0 merges the four per-wave lists.  With many rows
+// per CU a block scans one row; otherwise every block scans the same number
+// of elements of the rows laid end to end, and the last segment of a row to
+// finish merges the row's lists (no second launch).
 #include <climits>
 #include <cmath>
 
@@ -94,7 +96,7 @@ struct SortedK {
 // and the buffer is folded into the best-K list whenever it fills up.  After
 // the first fold the threshold is high enough that almost no element passes,
 // so the scan is one compare and one ballot per 16-byte load.
-template <int K, int CAP>
+template <int K, int CAP, int FOLD_AT>
 struct WaveFilter {
   float *cv;            // [CAP] candidate values (this wave's slice of LDS)
   int *ci;              // [CAP] candidate ids
@@ -217,7 +219,7 @@ struct WaveFilter {
       if (!EACH || __ballot(valid && xs[j] >= thr_v) != 0ull)
         push(valid && better(xs[j], e + j, thr_v, thr_i), xs[j], e + j);
     }
-    if (cnt > CAP - n * kWave) fold();
+    if (cnt >= FOLD_AT || cnt > CAP - n * kWave) fold();
   }
 };
 
@@ -261,21 +263,111 @@ struct Norm {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// One slice [lo, hi) of one row.  IN: what the row holds (above).
+// Candidates buffered before a fold: low enough that the threshold keeps up
+// with the running K-th best (a threshold left at its seed lets hundreds of
+// elements per wave through), and for K >= kSortNetK low enough that the
+// fold is one wave sort.
+template <int K>
+constexpr int fold_at() {
+  return K >= kSortNetK ? (kWave - 2 * K > 16 ? kWave - 2 * K : 16) : 48;
+}
+
+// Counters at the start of the workspace, one per cut row (fewer than the
+// CUs), for any shape: what one call leaves there (zeros) is what the next
+// expects.
+constexpr int64_t kTopkRowsMax = 16384;
+constexpr unsigned kTopkSpin = 1u << 20;   // polls of a published word before giving up
+
+// A published entry is one 64-bit word, written and read with single
+// relaxed atomics at device scope: the value's bits, then id + 1, so that
+// no entry is zero and zero means "not yet visible".  (A normaliser (m, s)
+// is never zero either: s >= 1 whenever m is finite.)  The flag is the
+// value itself, so no fence is needed: a device-scope release or acquire
+// would write back or invalidate a whole L2 per segment.
+__device__ __forceinline__ unsigned long long pack_entry(float v, int i) {
+  return (static_cast<unsigned long long>(__float_as_uint(v)) << 32) | (static_cast<unsigned>(i) + 1u);
+}
+__device__ __forceinline__ unsigned long long pack_norm(float m, float s) {
+  return (static_cast<unsigned long long>(__float_as_uint(m)) << 32) | __float_as_uint(s);
+}
+__device__ __forceinline__ void put_word(unsigned long long *p, unsigned long long w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The word at p once its writer's store is visible (bounded wait; late is
+// set if it never became so).
+__device__ __forceinline__ unsigned long long await_word(unsigned long long *p, bool &late) {
+  unsigned long long w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (unsigned spins = 0; w == 0ull; ++spins) {
+    if (spins >= kTopkSpin) {
+      late = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return w;
+}
+
+// The K best of n (value, id) pairs, best first, into lanes 0 .. K-1 (other
+// lanes: padding).  get(c, v, i) yields pair c.  One wave.
+template <int K, typename Get>
+__device__ __forceinline__ void wave_best_k(int n, Get &&get, float &bv, int &bi) {
+  const int x = lane_id();
+  if (K >= kSortNetK && n <= kWave) {
+    bv = -INFINITY;
+    bi = INT_MAX;
+    if (x < n) get(x, bv, bi);
+    wave_sort_best_first(bv, bi);
+    return;
+  }
+  SortedK<K> L;
+  L.init();
+  for (int c = x; c < n; c += kWave) {
+    float v;
+    int i;
+    get(c, v, i);
+    L.insert(v, i);
+  }
+  bv = -INFINITY;
+  bi = INT_MAX;
+  for (int r = 0; r < K; ++r) {
+    float v = L.v[0];
+    int i = L.i[0];
+    wave_best(v, i);
+    if (L.i[0] == i && L.v[0] == v && i != INT_MAX) L.pop_front();
+    if (x == r) {
+      bv = v;
+      bi = i;
+    }
+  }
+}
+
+// Block j < nwhole scans row j whole.  The rows after those (fewer than
+// one per CU) are laid end to end and cut into pieces of per < V elements:
+// block nwhole + j scans piece j, part of one row or the tail of one row
+// and the head of the next, so that with rows = q * CUs + r each CU gets q
+// whole rows and an equal share of the r others.  A whole-row segment
+// writes its result.  A row cut into several segments (at most maxseg) has
+// each segment publish its K best (and, for logits, its normaliser) to the
+// workspace as flagged words and count itself on the row's counter; the
+// segment that counts last merges the lists as their words land (the K
+// best under the strict order do not depend on the merge order;
+// normalisers are merged in segment order) and sets the words and the
+// counter back to zero.  IN: what the rows hold (above).
 template <int K, int IN>
 __global__ void __launch_bounds__(kTopkThreads)
-topk_slice_kernel(const void *__restrict__ rows_in, int64_t rows, int V, int splits, int chunk,
-                  int k, bool vec, float c2, float *__restrict__ out_v, int *__restrict__ out_i,
-                  float *__restrict__ part_v, int *__restrict__ part_i, float2 *__restrict__ part_n) {
+topk_kernel(const void *__restrict__ rows_in, int64_t rows, int V, int64_t nwhole, int64_t per, int maxseg, int k,
+            bool vec,
+            float c2, float *__restrict__ out_v, int *__restrict__ out_i, unsigned *__restrict__ cnt,
+            unsigned long long *__restrict__ part, unsigned long long *__restrict__ part_n) {
   constexpr int NW = kTopkThreads / kWave;
   constexpr bool LOGITS = IN != kInProbs;
   constexpr int EPL = IN == kInLogitsBf16 ? 8 : 4;          // elements per 16-byte load
-  // Software pipelined windows (the next window's loads issued before this
-  // one is processed), filtered element by element (see offer) with a
-  // larger candidate buffer: for bf16 rows, which carry twice the elements
-  // per byte, and for K <= 4, where the second set of load registers still
-  // leaves six workgroups per CU.  Otherwise one window at a time.
-  constexpr bool PIPE = EPL == 8 || K <= 4;
+  // Software pipelined windows (the next window's loads are issued before
+  // this one is processed), filtered element by element (see offer) with a
+  // larger candidate buffer, up to K = 8 (bf16: 16); larger K keep one
+  // window at a time, whose registers the K-lists need.
+  constexpr bool PIPE = K <= 8 || (EPL == 8 && K <= 16);
   constexpr int CAP = PIPE ? 768 : 512;                     // candidate slots per wave
   __shared__ float s_cv[NW][CAP];
   __shared__ int s_ci[NW][CAP];
@@ -283,276 +375,287 @@ topk_slice_kernel(const void *__restrict__ rows_in, int64_t rows, int V, int spl
   __shared__ int s_ti[NW][K];
   __shared__ float2 s_norm[NW];
   const int64_t bid = blockIdx.x;
-  const int64_t row = bid / splits;
-  const int split = static_cast<int>(bid % splits);
-  if (row >= rows) return;
-  const int lo = split * chunk;
-  const int hi = min(V, lo + chunk);
   const int tid = threadIdx.x;
   const int w = tid / kWave;
-  const float *rp32 = static_cast<const float *>(rows_in) + row * static_cast<int64_t>(V);
-  const uint16_t *rp16 = static_cast<const uint16_t *>(rows_in) + row * static_cast<int64_t>(V);
+  const int x = lane_id();
 
-  WaveFilter<K, CAP> F;
-  F.init(s_cv[w], s_ci[w], s_tv[w], s_ti[w]);
-  Norm nm;
-  // one 16-byte load: EPL elements starting at element e
-  auto load = [&](int e) {
-    return IN == kInLogitsBf16 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(rp16 + e))
-                               : __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(rp32 + e));
-  };
-  auto unpack = [&](const f32x4v &u, float *x) {
-    if constexpr (IN == kInLogitsBf16) {
-      const uint32_t wd[4] = {__float_as_uint(u.x), __float_as_uint(u.y), __float_as_uint(u.z),
-                              __float_as_uint(u.w)};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[2 * j] = bf16_to_f32(wd[j] & 0xffffu);
-        x[2 * j + 1] = __uint_as_float(wd[j] & 0xffff0000u);
-      }
-    } else {
-      x[0] = u.x;
-      x[1] = u.y;
-      x[2] = u.z;
-      x[3] = u.w;
-    }
-  };
-  if (vec) {
-    // The block reads one contiguous window of kLoads * 4 KB per iteration:
-    // load u of wave w covers 1 KB chunk 4*u + w of the window.  One stream per row
-    // (rather than one per wave) and non-temporal loads (the rows are read
-    // once) keep HBM efficient when a thousand rows stream at once.  The
-    // loads are all in flight before the first is used, one ballot
-    // tests the lane maxima of the window against the threshold, and the
-    // normaliser takes the window in one update.
-    constexpr int step = EPL * kWave;             // elements per 1 KB chunk
-    constexpr int win = kLoads * NW * step;       // elements per window
-    // the window at base, its loads in r
-    auto window = [&](int base, const f32x4v (&r)[kLoads]) {
-      const int e = base + w * step + EPL * lane_id();
-      float x[kLoads * EPL];
-#pragma unroll
-      for (int u = 0; u < kLoads; ++u) unpack(r[u], x + u * EPL);
-      float lmx[kLoads];
-#pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        lmx[u] = x[u * EPL];
-#pragma unroll
-        for (int j = 1; j < EPL; ++j) lmx[u] = vmax(lmx[u], x[u * EPL + j]);
-      }
-      float mx = lmx[0];
-#pragma unroll
-      for (int u = 1; u < kLoads; ++u) mx = vmax(mx, lmx[u]);
-      if (base == lo) F.seed(mx);                 // the first window's lane maxima
-      if (__ballot(mx >= F.thr_v) != 0ull) {
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) F.template offer<EPL, PIPE>(x + u * EPL, lmx[u], e + u * NW * step, true);
-      }
-      if constexpr (LOGITS) nm.add(x, mx, c2);
+  // Segment [lo, hi) of one row.  Called at most twice per block (per < V),
+  // without a loop: a loop back edge keeps hoisted per-lane values live
+  // across the window loop and costs a workgroup per CU.
+  auto segment = [&](const int64_t row, const int lo, const int hi) __attribute__((always_inline)) {
+    const float *rp32 = static_cast<const float *>(rows_in) + row * static_cast<int64_t>(V);
+    const uint16_t *rp16 = static_cast<const uint16_t *>(rows_in) + row * static_cast<int64_t>(V);
+
+    WaveFilter<K, CAP, fold_at<K>()> F;
+    F.init(s_cv[w], s_ci[w], s_tv[w], s_ti[w]);
+    Norm nm;
+    // one 16-byte load: EPL elements starting at element e
+    auto load = [&](int e) {
+      return IN == kInLogitsBf16 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(rp16 + e))
+                                 : __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(rp32 + e));
     };
-    auto issue = [&](int base, f32x4v (&r)[kLoads]) {
-      const int e = base + w * step + EPL * lane_id();
+    auto unpack = [&](const f32x4v &u, float *xs) {
+      if constexpr (IN == kInLogitsBf16) {
+        const uint32_t wd[4] = {__float_as_uint(u.x), __float_as_uint(u.y), __float_as_uint(u.z),
+                                __float_as_uint(u.w)};
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) r[u] = load(e + u * NW * step);
+        for (int j = 0; j < 4; ++j) {
+          xs[2 * j] = bf16_to_f32(wd[j] & 0xffffu);
+          xs[2 * j + 1] = __uint_as_float(wd[j] & 0xffff0000u);
+        }
+      } else {
+        xs[0] = u.x;
+        xs[1] = u.y;
+        xs[2] = u.z;
+        xs[3] = u.w;
+      }
     };
-    int base = lo;
-    if constexpr (PIPE) {
-      if (base + win <= hi) {
-        // the next window's loads are in flight while this one is processed
-        f32x4v cur[kLoads], nxt[kLoads];
-        issue(base, cur);
-        for (; base + 2 * win <= hi; base += win) {
-          issue(base + win, nxt);
+    if (vec) {
+      // The block reads one contiguous window of kLoads * 4 KB per
+      // iteration: load u of wave w covers 1 KB chunk 4*u + w of the window.
+      // One stream per segment (rather than one per wave) and non-temporal
+      // loads (the rows are read once) keep HBM efficient when a thousand
+      // segments stream at once.  One ballot tests the lane maxima of the
+      // window against the threshold, and the normaliser takes the window
+      // in one update.
+      constexpr int step = EPL * kWave;             // elements per 1 KB chunk
+      constexpr int win = kLoads * NW * step;       // elements per window
+      // the window at base, its loads in r
+      auto window = [&](int base, const f32x4v (&r)[kLoads]) {
+        const int e = base + w * step + EPL * x;
+        float xs[kLoads * EPL];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) unpack(r[u], xs + u * EPL);
+        float lmx[kLoads];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+          lmx[u] = xs[u * EPL];
+#pragma unroll
+          for (int j = 1; j < EPL; ++j) lmx[u] = vmax(lmx[u], xs[u * EPL + j]);
+        }
+        float mx = lmx[0];
+#pragma unroll
+        for (int u = 1; u < kLoads; ++u) mx = vmax(mx, lmx[u]);
+        if (base == lo) F.seed(mx);                 // the first window's lane maxima
+        if (__ballot(mx >= F.thr_v) != 0ull) {
+#pragma unroll
+          for (int u = 0; u < kLoads; ++u)
+            F.template offer<EPL, PIPE>(xs + u * EPL, lmx[u], e + u * NW * step, true);
+        }
+        if constexpr (LOGITS) nm.add(xs, mx, c2);
+      };
+      auto issue = [&](int base, f32x4v (&r)[kLoads]) {
+        const int e = base + w * step + EPL * x;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) r[u] = load(e + u * NW * step);
+      };
+      int base = lo;
+      if constexpr (PIPE) {
+        if (base + win <= hi) {
+          // the next window's loads are in flight while this one is processed
+          f32x4v cur[kLoads], nxt[kLoads];
+          issue(base, cur);
+          for (; base + 2 * win <= hi; base += win) {
+            issue(base + win, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            window(base, cur);
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) cur[u] = nxt[u];
+          }
+          window(base, cur);
+          base += win;
+        }
+      } else {
+        for (; base + win <= hi; base += win) {
+          f32x4v cur[kLoads];
+          issue(base, cur);
           __builtin_amdgcn_sched_barrier(0);
           window(base, cur);
-#pragma unroll
-          for (int u = 0; u < kLoads; ++u) cur[u] = nxt[u];
         }
-        window(base, cur);
-        base += win;
+      }
+      for (int e = base + w * step + EPL * x; e - EPL * x < hi; e += NW * step) {
+        const bool in = e < hi;
+        float xs[EPL];
+        if (in) {
+          unpack(load(e), xs);
+        } else {
+#pragma unroll
+          for (int j = 0; j < EPL; ++j) xs[j] = -INFINITY;
+        }
+        float mx = xs[0];
+#pragma unroll
+        for (int j = 1; j < EPL; ++j) mx = vmax(mx, xs[j]);
+        F.template offer<EPL, PIPE>(xs, mx, e, in);
+        if constexpr (LOGITS) {
+          if (in) nm.add(xs, mx, c2);
+        }
       }
     } else {
-      for (; base + win <= hi; base += win) {
-        f32x4v cur[kLoads];
-        issue(base, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        window(base, cur);
+      for (int e0 = lo + w * kWave; e0 < hi; e0 += NW * kWave) {
+        const int e = e0 + x;
+        const bool in = e < hi;
+        float xs[1] = {-INFINITY};
+        if (in) xs[0] = IN == kInLogitsBf16 ? bf16_to_f32(rp16[e]) : rp32[e];
+        F.template offer<1, false>(xs, xs[0], e, in);
+        if constexpr (LOGITS) {
+          if (in) nm.add(xs, xs[0], c2);
+        }
       }
     }
-    for (int e = base + w * step + EPL * lane_id(); e - EPL * lane_id() < hi; e += NW * step) {
-      const bool in = e < hi;
-      float x[EPL];
-      if (in) {
-        unpack(load(e), x);
-      } else {
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) x[j] = -INFINITY;
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int j = 1; j < EPL; ++j) mx = vmax(mx, x[j]);
-      F.template offer<EPL, PIPE>(x, mx, e, in);
-      if constexpr (LOGITS) {
-        if (in) nm.add(x, mx, c2);
-      }
-    }
-  } else {
-    for (int e0 = lo + w * kWave; e0 < hi; e0 += NW * kWave) {
-      const int e = e0 + lane_id();
-      const bool in = e < hi;
-      float x[1] = {-INFINITY};
-      if (in) x[0] = IN == kInLogitsBf16 ? bf16_to_f32(rp16[e]) : rp32[e];
-      F.template offer<1, false>(x, x[0], e, in);
-      if constexpr (LOGITS) {
-        if (in) nm.add(x, x[0], c2);
-      }
-    }
-  }
-  F.fold();
-  if constexpr (LOGITS) {
-    // the wave's lanes in butterfly order, then the waves in order
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const float om = __shfl_xor(nm.m, off, kWave), os = __shfl_xor(nm.s, off, kWave);
-      if (lane_id() & off) {
-        Norm t;
-        t.m = om;
-        t.s = os;
-        t.merge(nm.m, nm.s, c2);
-        nm = t;
-      } else {
-        nm.merge(om, os, c2);
-      }
-    }
-    if (lane_id() == 0) s_norm[w] = make_float2(nm.m, nm.s);
-  }
-  __syncthreads();
-
-  // wave 0 merges the four per-wave lists
-  if (w == 0) {
-    Norm tot;
+    F.fold();
     if constexpr (LOGITS) {
+      // the wave's lanes in butterfly order, then the waves in order
 #pragma unroll
-      for (int x = 0; x < NW; ++x) tot.merge(s_norm[x].x, s_norm[x].y, c2);
-    }
-    auto emit = [&](int r, float bv, int bi) {
-      if (splits == 1) {
-        if (r < k) {
-          out_v[row * k + r] = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
-          out_i[row * k + r] = bi;
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float om = __shfl_xor(nm.m, off, kWave), os = __shfl_xor(nm.s, off, kWave);
+        if (x & off) {
+          Norm t;
+          t.m = om;
+          t.s = os;
+          t.merge(nm.m, nm.s, c2);
+          nm = t;
+        } else {
+          nm.merge(om, os, c2);
         }
-      } else {
-        part_v[bid * K + r] = bv;
-        part_i[bid * K + r] = bi;
       }
-    };
-    if constexpr (K >= kSortNetK && NW * K <= kWave) {
-      // the four lists fit one per lane: one wave sort, lanes 0 .. K-1 emit
-      const int x = lane_id();
-      float bv = x < NW * K ? s_tv[x / K][x % K] : -INFINITY;
-      int bi = x < NW * K ? s_ti[x / K][x % K] : INT_MAX;
-      wave_sort_best_first(bv, bi);
-      if (x < K) emit(x, bv, bi);
-    } else {
-      SortedK<K> L;
-      L.init();
-      for (int x = lane_id(); x < NW * K; x += kWave) L.insert(s_tv[x / K][x % K], s_ti[x / K][x % K]);
-      for (int r = 0; r < K; ++r) {
-        float bv = L.v[0];
-        int bi = L.i[0];
-        wave_best(bv, bi);
-        if (L.i[0] == bi && L.v[0] == bv && bi != INT_MAX) L.pop_front();
-        if (lane_id() == 0) emit(r, bv, bi);
-      }
+      if (x == 0) s_norm[w] = make_float2(nm.m, nm.s);
     }
-    if (LOGITS && splits > 1 && lane_id() == 0) part_n[bid] = make_float2(tot.m, tot.s);
-  }
-}
+    __syncthreads();
 
-// One wave per row merges splits*K candidates (and, for logits, the splits'
-// normalisers in split order).
-template <int K, bool LOGITS>
-__global__ void __launch_bounds__(kWave)
-topk_merge_kernel(int64_t rows, int splits, int k, float c2, const float *__restrict__ part_v,
-                  const int *__restrict__ part_i, const float2 *__restrict__ part_n, float *__restrict__ out_v,
-                  int *__restrict__ out_i) {
-  const int64_t row = blockIdx.x;
-  if (row >= rows) return;
-  const int n = splits * K;
-  const float *pv = part_v + row * n;
-  const int *pi = part_i + row * n;
-  Norm tot;
-  if constexpr (LOGITS) {
-    for (int x = 0; x < splits; ++x) {
-      const float2 t = part_n[row * splits + x];
-      tot.merge(t.x, t.y, c2);
+    // wave 0 merges the four per-wave lists: lane r < K holds the r-th best
+    if (w == 0) {
+      Norm tot;
+      if constexpr (LOGITS) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) tot.merge(s_norm[j].x, s_norm[j].y, c2);
+      }
+      float bv;
+      int bi;
+      wave_best_k<K>(NW * K, [&](int c, float &v, int &i) {
+        v = (&s_tv[0][0])[c];
+        i = (&s_ti[0][0])[c];
+      }, bv, bi);
+      bool emit = lo == 0 && hi == V;                 // a whole row: no other segment
+      bool late = false;
+      if (!emit) {
+        const int64_t trow = row - nwhole;            // the row among the cut ones
+        const int64_t first = trow * V / per;         // pieces holding the row's first and last elements
+        const int64_t last = (trow * V + V - 1) / per;
+        const int nseg = static_cast<int>(last - first + 1);
+        const int64_t s0 = trow * maxseg;
+        const int64_t slot = s0 + (bid - nwhole - first);
+        // publish the segment's list (lane r its r-th entry), then count
+        // the segment on the row's counter: a relaxed count, since the
+        // words carry their own flags
+        if (x < K) put_word(part + slot * K + x, pack_entry(bv, bi));
+        if (LOGITS && x == 0) put_word(part_n + slot, pack_norm(tot.m, tot.s));
+        unsigned ticket = 0;
+        if (x == 0) ticket = __hip_atomic_fetch_add(cnt + trow, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ticket = __shfl(ticket, 0, kWave);
+        if (ticket + 1 == static_cast<unsigned>(nseg)) {
+          // the last segment: every other one has counted itself and its
+          // words are on their way; read them as they land, then set them
+          // and the counter back to zero for the next call
+          unsigned long long *words = part + s0 * K;
+          wave_best_k<K>(nseg * K, [&](int c, float &v, int &i) {
+            const unsigned long long wd = await_word(words + c, late);
+            v = __uint_as_float(static_cast<unsigned>(wd >> 32));
+            i = static_cast<int>(static_cast<unsigned>(wd) - 1u);
+          }, bv, bi);
+          if constexpr (LOGITS) {
+            tot = Norm();
+            for (int j = 0; j < nseg; ++j) {
+              const unsigned long long wd = await_word(part_n + s0 + j, late);
+              tot.merge(__uint_as_float(static_cast<unsigned>(wd >> 32)), __uint_as_float(static_cast<unsigned>(wd)),
+                        c2);
+            }
+          }
+          for (int c = x; c < nseg * K; c += kWave) put_word(words + c, 0ull);
+          if (LOGITS)
+            for (int j = x; j < nseg; j += kWave) put_word(part_n + s0 + j, 0ull);
+          if (x == 0) __hip_atomic_store(cnt + trow, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          late = __any(late);
+          emit = true;
+        }
+      }
+      if (emit && x < k) {
+        const float pv = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
+        out_v[row * k + x] = late ? __builtin_nanf("") : pv;    // a published list never arrived
+        out_i[row * k + x] = late ? -1 : bi;
+      }
     }
-  }
-  auto emit = [&](int r, float bv, int bi) {
-    out_v[row * k + r] = LOGITS ? __builtin_amdgcn_exp2f((bv - tot.m) * c2) / tot.s : bv;
-    out_i[row * k + r] = bi;
+    __syncthreads();                                  // the LDS lists are reused by the next segment
   };
-  if (K >= kSortNetK && n <= kWave) {
-    const int x = lane_id();
-    float bv = x < n ? pv[x] : -INFINITY;
-    int bi = x < n ? pi[x] : INT_MAX;
-    wave_sort_best_first(bv, bi);
-    if (x < k) emit(x, bv, bi);
+  if (bid < nwhole) {
+    segment(bid, 0, V);
     return;
   }
-  SortedK<K> L;
-  L.init();
-  for (int c = lane_id(); c < n; c += kWave) L.insert(pv[c], pi[c]);
-  for (int r = 0; r < k; ++r) {
-    float bv = L.v[0];
-    int bi = L.i[0];
-    wave_best(bv, bi);
-    if (L.i[0] == bi && L.v[0] == bv && bi != INT_MAX) L.pop_front();
-    if (lane_id() == 0) emit(r, bv, bi);
-  }
+  // piece bid - nwhole of the cut rows: elements [t0, t1) counted from row nwhole
+  const int64_t t0 = (bid - nwhole) * per;
+  const int64_t t1 = min((rows - nwhole) * V, t0 + per);
+  const int64_t r0 = t0 / V;
+  segment(nwhole + r0, static_cast<int>(t0 - r0 * V), static_cast<int>(min<int64_t>(t1 - r0 * V, V)));
+  if (t1 > (r0 + 1) * V) segment(nwhole + r0 + 1, 0, static_cast<int>(t1 - (r0 + 1) * V));
 }
 
 struct TopkPlan {
-  int K, splits, chunk;
+  int K;
+  int64_t nwhole;    // rows scanned whole, one block each
+  int64_t per;       // elements per piece of the other rows (0: none)
+  int64_t blocks;
+  int maxseg;        // segments per cut row at most
+  int64_t cut;       // rows cut into pieces
 };
+
+// rows = q * CUs + r: the first q * CUs rows whole, the r others in pieces,
+// one per CU (four per CU when q = 0), each at least a window and less than
+// a row; a whole block per row when r = 0 or the pieces would not be
+// shorter than a row.  Pieces cross row boundaries at most once.
+constexpr int kTopkPiecesPerCuAlone = 4;
 
 TopkPlan plan_topk(int64_t rows, int V, int k) {
   TopkPlan p;
   p.K = 1;
   while (p.K < k) p.K <<= 1;
-  const int64_t target = 4LL * num_cus();
-  int64_t splits = rows >= target ? 1 : (target + rows - 1) / rows;
-  const int64_t max_splits = V / 4096 > 0 ? V / 4096 : 1;
-  if (splits > max_splits) splits = max_splits;
-  int64_t chunk = (V + splits - 1) / splits;
-  chunk = (chunk + 7) / 8 * 8;                       // whole 16-byte loads of fp32 and bf16
-  splits = (V + chunk - 1) / chunk;
-  p.splits = static_cast<int>(splits);
-  p.chunk = static_cast<int>(chunk);
+  p.nwhole = rows;
+  p.per = 0;
+  p.blocks = rows;
+  p.maxseg = 0;
+  p.cut = 0;
+  const int64_t cus = num_cus();
+  const int64_t q = rows / cus, r = rows % cus;
+  if (r == 0 || r > kTopkRowsMax) return p;
+  const int64_t tail = r * static_cast<int64_t>(V);
+  const int64_t pieces = (q == 0 ? kTopkPiecesPerCuAlone : 1) * cus;
+  int64_t per = (tail + pieces - 1) / pieces;
+  per = (per + 7) / 8 * 8;                            // whole 16-byte loads of fp32 and bf16
+  if (per < 4096) per = 4096;                         // at least a window (fp32) per piece
+  if (per >= V) return p;
+  p.nwhole = q * cus;
+  p.per = per;
+  p.cut = r;
+  p.blocks = p.nwhole + (tail + per - 1) / per;
+  p.maxseg = static_cast<int>((V - 1) / per + 2);
   return p;
 }
 
 size_t topk_workspace(int64_t rows, int V, int k, bool logits) {
   const TopkPlan p = plan_topk(rows, V, k);
-  if (p.splits == 1) return 0;
+  if (p.per == 0) return 0;
   Carver c(nullptr);
-  c.take<float>(static_cast<size_t>(rows) * p.splits * p.K);
-  c.take<int>(static_cast<size_t>(rows) * p.splits * p.K);
-  if (logits) c.take<float2>(static_cast<size_t>(rows) * p.splits);
+  c.take<unsigned>(kTopkRowsMax);
+  c.take<unsigned long long>(static_cast<size_t>(p.cut) * p.maxseg * p.K);
+  if (logits) c.take<unsigned long long>(static_cast<size_t>(p.cut) * p.maxseg);
   return c.bytes();
 }
 
 template <int K, int IN>
 int32_t launch_topk(const void *rows_in, int64_t rows, int V, int k, const TopkPlan &p, bool vec, float c2,
-                    float *out_v, int *out_i, float *part_v, int *part_i, float2 *part_n, hipStream_t st) {
-  const int64_t blocks = rows * p.splits;
-  hipLaunchKernelGGL((topk_slice_kernel<K, IN>), dim3(static_cast<unsigned>(blocks)), dim3(kTopkThreads), 0,
-                     st, rows_in, rows, V, p.splits, p.chunk, k, vec, c2, out_v, out_i, part_v, part_i, part_n);
-  int32_t rc = check_launch("topk_slice_kernel");
-  if (rc != SDV_OK || p.splits == 1) return rc;
-  hipLaunchKernelGGL((topk_merge_kernel<K, IN != kInProbs>), dim3(static_cast<unsigned>(rows)), dim3(kWave), 0,
-                     st, rows, p.splits, k, c2, part_v, part_i, part_n, out_v, out_i);
-  return check_launch("topk_merge_kernel");
+                    float *out_v, int *out_i, unsigned *cnt, unsigned long long *part,
+                    unsigned long long *part_n, hipStream_t st) {
+  hipLaunchKernelGGL((topk_kernel<K, IN>), dim3(static_cast<unsigned>(p.blocks)), dim3(kTopkThreads), 0, st,
+                     rows_in, rows, V, p.nwhole, p.per, p.maxseg, k, vec, c2, out_v, out_i, cnt, part, part_n);
+  return check_launch("topk_kernel");
 }
 
 // Common checks and dispatch of both entry points.
@@ -570,20 +673,24 @@ int32_t run_topk(const char *what, int IN, const void *rows_in, int64_t rows, in
   const size_t need = topk_workspace(rows, V, k, IN != kInProbs);
   SDV_REQUIRE(ws_bytes >= need && (need == 0 || ws), SDV_E_WORKSPACE, "%s: workspace of %zu bytes needed", what,
               need);
-  Carver c(ws);
-  float *part_v = c.take<float>(static_cast<size_t>(rows) * p.splits * p.K);
-  int *part_i = c.take<int>(static_cast<size_t>(rows) * p.splits * p.K);
-  float2 *part_n = IN != kInProbs ? c.take<float2>(static_cast<size_t>(rows) * p.splits) : nullptr;
+  unsigned *cnt = nullptr;
+  unsigned long long *part = nullptr, *part_n = nullptr;
+  if (p.per > 0) {
+    Carver c(ws);
+    cnt = c.take<unsigned>(kTopkRowsMax);
+    part = c.take<unsigned long long>(static_cast<size_t>(p.cut) * p.maxseg * p.K);
+    if (IN != kInProbs) part_n = c.take<unsigned long long>(static_cast<size_t>(p.cut) * p.maxseg);
+  }
   const int epl = IN == kInLogitsBf16 ? 8 : 4;
   const bool vec = (V % epl == 0) && (reinterpret_cast<uintptr_t>(rows_in) % 16 == 0);
   hipStream_t st = as_stream(stream);
 #define SDV_TOPK_IN(KK)                                                                                          \
-  (IN == kInProbs        ? launch_topk<KK, kInProbs>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, part_v,     \
-                                                     part_i, part_n, st)                                         \
-   : IN == kInLogitsF32 ? launch_topk<KK, kInLogitsF32>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, part_v, \
-                                                         part_i, part_n, st)                                     \
-                         : launch_topk<KK, kInLogitsBf16>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id,       \
-                                                          part_v, part_i, part_n, st))
+  (IN == kInProbs        ? launch_topk<KK, kInProbs>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, cnt, part, \
+                                                     part_n, st)                                         \
+   : IN == kInLogitsF32 ? launch_topk<KK, kInLogitsF32>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, cnt, part, \
+                                                         part_n, st)                                     \
+                         : launch_topk<KK, kInLogitsBf16>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, cnt, part, \
+                                                          part_n, st))
   switch (p.K) {
     case 1: return SDV_TOPK_IN(1);
     case 2: return SDV_TOPK_IN(2);

@@ -90,6 +90,68 @@ def test_topk_from_logits(rows, V, k, T, bf16, kind):
     assert np.all(np.abs(got - ov) <= 1e-4 * ov + 1e-37)
 
 
+# Rows beyond a multiple of the compute units are cut into equal pieces
+# of the rows laid end to end: a row may be cut between workgroups, and one
+# workgroup may hold the tail of one row and the head of the next.  Each row
+# gets a group of equal values (its maximum, doubled) at random places, so
+# its k best and their tie order straddle wherever the cuts fall; 2048 rows
+# (a multiple of 256 compute units) take the one-workgroup-per-row path
+# alone.
+@pytest.mark.parametrize("rows,V,k", [(1056, 128256, 8), (300, 128256, 4), (2047, 4104, 8), (2048, 4104, 8),
+                                      (5000, 4104, 2), (129, 65536, 16), (7, 9000, 32)])
+def test_topk_segments(rows, V, k):
+    rng = np.random.default_rng(rows * 17 + V + k)
+    p = workloads.softmax_rows(rng.standard_normal((rows, V)).astype(np.float32) * 3)
+    top = p.max(axis=1) * 2
+    pos = rng.integers(0, V, size=(rows, k + 2))
+    for r in range(rows):
+        p[r, pos[r]] = top[r]
+    say("topk segments", rows, V, k)
+    gp, gi = sdv.sdv_draft_topk(dev(p), k)
+    torch.cuda.synchronize()
+    op, oi = otopk.draft_topk(p, k)
+    assert np.array_equal(host(gi), oi)
+    assert np.array_equal(host(gp), op)
+
+
+# One workspace, zero-filled once, through calls of different shapes and
+# both entry points: every call finds the row counters at zero and leaves
+# them so (the counters sit at the start of the workspace).
+def test_topk_workspace_reuse():
+    lib = sdv._lib.lib()
+    shapes = [(1056, 128256, 8, False), (64, 4099, 8, True), (5, 100000, 4, False), (1056, 128256, 8, True),
+              (33, 128256, 8, False), (1056, 128256, 8, False)]
+    need = max(max(lib.sdv_draft_topk_workspace_size(r, V, k), lib.sdv_draft_topk_logits_workspace_size(r, V, k))
+               for r, V, k, _ in shapes)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    cache = {}
+    for rows, V, k, logits in shapes:
+        key = (rows, V, k, logits)
+        if key not in cache:
+            rng = np.random.default_rng(rows + V + k)
+            x = (rng.standard_normal((rows, V)) * 3.0).astype(np.float32)
+            if logits:
+                cache[key] = (x, otopk.draft_topk_from_logits(x, k, 1.0))
+            else:
+                p = workloads.softmax_rows(x)
+                cache[key] = (p, otopk.draft_topk(p, k))
+        x, (ov, oi) = cache[key]
+        say("topk workspace reuse", rows, V, k, "logits" if logits else "probs")
+        if logits:
+            gp, gi = sdv.sdv_draft_topk_logits(dev(x), k, 1.0, ws=ws)
+        else:
+            gp, gi = sdv.sdv_draft_topk(dev(x), k, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(gi), oi)
+        got = host(gp).astype(np.float64)
+        if logits:
+            assert np.all(np.abs(got - ov) <= 1e-4 * ov + 1e-37)
+        else:
+            assert np.array_equal(host(gp), ov)
+        assert not bool(ws[:65536].any()), "row counters left non-zero"
+
+
 # -------------------------------------------------------------------- A2-A4
 
 TREE_KEYS = ("tokens", "parent", "depth", "positions", "score", "q_row", "mask", "mask_bits", "retrieve_index",
