@@ -85,7 +85,8 @@ tree_attn_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, int64
   const int l16 = l & 15;
   const int g4 = l >> 4;
 
-  const int L = prefix_len[b];
+  // the ranking left the batch's prefix lengths in LDS (one global read fewer on the way to the first tile)
+  const int L = B <= kRankMax ? reinterpret_cast<const int *>(smem)[b] : prefix_len[b];
   const int total = L + N;
   const int *trow = table + static_cast<int64_t>(b) * max_pages;
   const bool req_ok = L >= 0 && static_cast<int64_t>(total) <= (static_cast<int64_t>(max_pages) << pshift);
