@@ -44,7 +44,7 @@ __device__ __forceinline__ void rank_block(const unsigned long long *key, int lo
     int r = 0;
     if (ent < n) {
       const unsigned long long ke = key[lo + ent];
-#pragma unroll 4
+#pragma unroll 16
       for (int o = lo + part; o < lo + n; o += g) r += key[o] > ke;
     }
     for (int off = 1; off < g; off <<= 1) r += __shfl_xor(r, off, kWave);

@@ -182,8 +182,9 @@ def test_build_tree_bit_exact(name, V):
     _assert_tree_equal(g, o)
 
 
+# Tie-heavy scores over k from 1 to 32, pools up to 1056 entries.
 @pytest.mark.parametrize("k,S,N", [(2, 3, 6), (3, 4, 30), (8, 5, 64), (4, 6, 85), (16, 2, 200), (1, 9, 10),
-                                   (2, 1, 3), (5, 3, 1), (8, 5, 256)])
+                                   (2, 1, 3), (5, 3, 1), (8, 5, 256), (7, 4, 100), (9, 3, 120), (32, 2, 256)])
 def test_build_tree_ties_and_shapes(k, S, N):
     rng = np.random.default_rng(k * 100 + S * 10 + N)
     B = 5
