@@ -322,6 +322,44 @@ def test_accept_stochastic_bit_exact(name, V, B, planted):
     _assert_accept_equal(g, o)
 
 
+_FULL_ACCEPT = {}
+
+
+def _full_accept_inputs(name):
+    """Inputs and oracle tree of a workload at its full batch and vocabulary
+    (the launch configuration the bench times), made once per module."""
+    if name not in _FULL_ACCEPT:
+        cfg = workloads.get_config(name)
+        inp = workloads.generate(cfg, with_attention=False)
+        _FULL_ACCEPT[name] = (cfg, inp, oracle_tree(inp, cfg))
+    return _FULL_ACCEPT[name]
+
+
+# The accept walk at the workloads' own sizes: c3 greedy (32 requests, one
+# group of 8 workgroups each, 64 floats per thread) and c4 rejection
+# sampling (64 requests), literal and with planted acceptance.
+@pytest.mark.parametrize("name,planted", [("c3", False), ("c3", True), ("c4", False), ("c4", True)])
+def test_accept_full_config(name, planted):
+    cfg, inp, tree = _full_accept_inputs(name)
+    say("accept full", name, cfg.B, cfg.V, cfg.mode, planted)
+    if cfg.mode == "greedy":
+        target = inp["target"]
+        if planted:
+            target = plant_greedy(target, tree, workloads.extra_rng(cfg, 1), cfg.S)
+        g = _gpu_accept(sdv.GREEDY, tree, target, cfg.S)
+        o = oacc.verify_greedy(tree, target, cfg.S)
+    else:
+        p = inp["target"]
+        if planted:
+            p = plant_stochastic(p, inp["draft_probs"], tree, workloads.extra_rng(cfg, 3), cfg.S)
+        g = _gpu_accept(sdv.STOCHASTIC, tree, p, cfg.S, draft_probs=inp["draft_probs"], u_accept=inp["u_accept"],
+                        u_draw=inp["u_draw"])
+        o = oacc.verify_stochastic(tree, p, inp["draft_probs"], inp["u_accept"], inp["u_draw"], cfg.S)
+    _assert_accept_equal(g, o)
+    if planted:
+        assert o["accept_len"].sum() > 0
+
+
 def test_accept_leaves_its_workspace_zero():
     """The exchange words and counters are cleared by each call's last
     workgroup per request: one explicit zero-filled workspace serves calls
