@@ -417,12 +417,17 @@ def _accept_paths(rng, B, N, S, tree=None):
     return acc_len, acc_path
 
 
-@pytest.mark.parametrize("page,layers,B,N,S", [(1, 1, 6, 12, 4), (1, 1, 32, 64, 5), (16, 3, 9, 32, 4),
-                                               (4, 2, 7, 12, 6), (16, 1, 64, 32, 4), (8, 2, 5, 256, 9)])
-def test_compaction_bit_exact(page, layers, B, N, S):
+# The last case is c4's own shape: 64 requests, page 16, 8 KV heads of 128
+# (2 KB per token and pool), prefixes of 1024 to 8192 tokens; its pools hold
+# a position pattern instead of random bits (600 MB each).
+@pytest.mark.parametrize("page,layers,B,N,S,Hkv,D,Lmax", [
+    (1, 1, 6, 12, 4, 2, 16, 300), (1, 1, 32, 64, 5, 2, 16, 300), (16, 3, 9, 32, 4, 2, 16, 300),
+    (4, 2, 7, 12, 6, 2, 16, 300), (16, 1, 64, 32, 4, 2, 16, 300), (8, 2, 5, 256, 9, 2, 16, 300),
+    (16, 1, 64, 32, 4, 8, 128, 8192)])
+def test_compaction_bit_exact(page, layers, B, N, S, Hkv, D, Lmax):
     rng = np.random.default_rng(page * 1000 + layers * 100 + N)
-    Hkv, D = 2, 16
-    L = rng.integers(0, 300, size=B).astype(np.int32)
+    big = Lmax > 300
+    L = rng.integers(1024 if big else 0, Lmax + (1 if big else 0), size=B).astype(np.int32)
     need = (L + N + page - 1) // page
     total = int(need.sum()) + 5
     perm = rng.permutation(total).astype(np.int32)
@@ -431,10 +436,15 @@ def test_compaction_bit_exact(page, layers, B, N, S):
     for b in range(B):
         table[b, :need[b]] = perm[off:off + need[b]]
         off += need[b]
-    kps = [rng.integers(0, 65535, size=(total * page, Hkv, D)).astype(np.uint16) for _ in range(layers)]
-    vps = [rng.integers(0, 65535, size=(total * page, Hkv, D)).astype(np.uint16) for _ in range(layers)]
+    if big:
+        pattern = (np.arange(total * page * Hkv * D, dtype=np.uint32) * np.uint32(40503) % np.uint32(65521)).astype(np.uint16)
+        kps = [pattern.reshape(total * page, Hkv, D) for _ in range(layers)]
+        vps = [(pattern ^ np.uint16(0x5A5A)).reshape(total * page, Hkv, D) for _ in range(layers)]
+    else:
+        kps = [rng.integers(0, 65535, size=(total * page, Hkv, D)).astype(np.uint16) for _ in range(layers)]
+        vps = [rng.integers(0, 65535, size=(total * page, Hkv, D)).astype(np.uint16) for _ in range(layers)]
     a, path = _accept_paths(rng, B, N, S)
-    say("compact", page, layers, B, N, S)
+    say("compact", page, layers, B, N, S, Hkv, D, Lmax)
     gt = dev(table)
     gk = [dev(x) for x in kps] if page > 1 else []
     gv = [dev(x) for x in vps] if page > 1 else []
