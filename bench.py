@@ -458,8 +458,11 @@ def main():
 
     tokens = cfg.B * cfg.N
     value = tokens / (ms_step * 1e-3)
+    # the headline workload's metric as stated with it; its HBM rate is the
+    # roofline entry's "achieved"
+    METRIC_C3 = "verified draft tokens/sec (build+tree-attn+accept) at B=32 topk=8; HBM GB/s"
     line = {
-        "metric": "verified draft tokens/s (build+tree-attn+accept)",
+        "metric": METRIC_C3 if cfg.name == "c3" else "verified draft tokens/sec (build+tree-attn+accept)",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
