@@ -95,7 +95,8 @@ class Pipeline:
             self.full = torch.empty((B, cfg.V_draft), dtype=torch.float32, device="cuda")
             self.d2t, self.t2d = sdv.sdv_tli_build_maps(d["inter_ids"], d["tgt_ids"], cfg.V_draft, cfg.V,
                                                         self.fallback)
-            self.scatter_ws = torch.empty(cfg.V * 4 + 256, dtype=torch.uint8, device="cuda")
+            self.scatter_ws = torch.empty(sdv._lib.lib().sdv_tli_q_scatter_workspace_size(cfg.V), dtype=torch.uint8,
+                                          device="cuda")
             sdv.sdv_tli_q_scatter(d["q_pruned"], d["tgt_ids"], cfg.V, q_target=self.q_target, ws=self.scatter_ws)
             self.remap_out = torch.empty((B, S + 1), dtype=torch.int32, device="cuda")
             self.draft_rows = self.q_target

@@ -394,9 +394,10 @@ int32_t sdv_tli_lm_head(int32_t B, int32_t H, int32_t K, const uint16_t *hidden,
  * ascending, full device [B, V_draft] fp32.
  * sdv_tli_q_scatter: q_target[r, tgt_ids[j]] = q_pruned[r, j], 0 elsewhere;
  * q_pruned device [rows, K] fp32, q_target device [rows, V_target] fp32;
- * the workspace holds the inverse of tgt_ids.  tgt_ids == NULL reuses the
- * inverse that an earlier call with the same V_target and map left in the
- * same workspace (the maps are static, so a serving loop builds it once).
+ * the workspace holds the inverse of tgt_ids and a copy of tgt_ids.
+ * tgt_ids == NULL reuses what an earlier call with the same K, V_target and
+ * map left in the same workspace (the maps are static, so a serving loop
+ * builds them once).
  * ---------------------------------------------------------------------- */
 int32_t sdv_tli_build_maps(int32_t K, const int32_t *inter_ids, const int32_t *tgt_ids,
                            int32_t V_draft, int32_t V_target, int32_t fallback, int32_t *d2t,

@@ -171,10 +171,14 @@ __global__ void constrain_kernel(int B, int K, int Vd, const float *__restrict__
     full[static_cast<int64_t>(b) * Vd + v] = j >= 0 ? pruned[static_cast<int64_t>(b) * K + j] : -INFINITY;
 }
 
-__global__ void inverse_kernel(int K, const int *__restrict__ tgt, int Vt, int *__restrict__ inv) {
+// inv[tgt[j]] = j (target ids outside [0, Vt) are skipped), and a copy of
+// tgt for the chunked scatter of later calls.
+__global__ void inverse_kernel(int K, const int *__restrict__ tgt, int Vt, int *__restrict__ inv,
+                               int *__restrict__ tcopy) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= K) return;
   const int t = tgt[j];
+  tcopy[j] = t;
   if (t >= 0 && t < Vt) inv[t] = j;
 }
 
@@ -208,35 +212,65 @@ q_scatter4_kernel(int64_t rows, int K, int Vt, int nchunks, const float *__restr
   }
 }
 
-// One 1024-thread block per row: the first kScatterLds entries of the q row
-// are staged in LDS (16-byte loads), so most of the random gathers read
-// LDS; the rest read the row from L2.  Each thread then writes four target
-// ids per iteration with one 16-byte non-temporal store.  Needs Vt % 4 ==
-// 0, K % 4 == 0 and 16-byte aligned rows.
-constexpr int kScatterLds = 36864;     // floats of a q row staged in LDS (144 KB)
+// Scatter form, all accesses coalesced: one 1024-thread workgroup per (q
+// row, chunk of kScatterChunk target ids).  It zero-fills the chunk in LDS,
+// streams the row's (target id, q value) pairs with 16-byte loads and drops
+// those that land in its chunk into LDS, then writes the chunk with 16-byte
+// non-temporal stores.  The chunks of a row run on one XCD (hardware block
+// h runs on XCD h % 8), so the row comes from HBM once and from that L2
+// after.  (The gather form, out[t] = q[inv[t]], moved a 128-byte line per
+// 4-byte entry for the part of each row that did not fit in LDS.)  Needs
+// Vt % 4 == 0, K % 4 == 0 and 16-byte aligned q rows, target ids and
+// output.
+constexpr int kScatterChunk = 32768;   // target ids per workgroup (128 KB of LDS)
 constexpr int kScatterThreads = 1024;
+constexpr int kScatterBatch = 8;
 
 __global__ void __launch_bounds__(kScatterThreads)
-q_scatter_lds_kernel(int K, int Vt, const float *__restrict__ q, const int *__restrict__ inv,
-                     float *__restrict__ out) {
-  extern __shared__ __attribute__((aligned(16))) float s_q[];
-  const int64_t r = blockIdx.x;
-  const float *qr = q + r * K;
-  const int nl = min(K, kScatterLds);
-  for (int i = 4 * static_cast<int>(threadIdx.x); i < nl; i += 4 * kScatterThreads)
-    *reinterpret_cast<float4 *>(s_q + i) = *reinterpret_cast<const float4 *>(qr + i);
+q_scatter_chunk_kernel(int64_t rows, int K, int Vt, int nch, const float *__restrict__ q,
+                       const int *__restrict__ tgt, float *__restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) float s_o[];
+  const int xcd = blockIdx.x % kXcdCount, slot = blockIdx.x / kXcdCount;
+  const int64_t r = static_cast<int64_t>(slot / nch) * kXcdCount + xcd;
+  const int c = slot % nch;
+  if (r >= rows) return;
+  const int base = c * kScatterChunk;
+  const int n = min(kScatterChunk, Vt - base);
+  const int tid = static_cast<int>(threadIdx.x);
+  for (int i = 4 * tid; i < n; i += 4 * kScatterThreads)
+    *reinterpret_cast<float4 *>(s_o + i) = make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();
-  auto pick = [&](int j) { return j < 0 ? 0.0f : (j < nl ? s_q[j] : qr[j]); };
-#pragma unroll 2
-  for (int v = 4 * static_cast<int>(threadIdx.x); v < Vt; v += 4 * kScatterThreads) {
-    const int4 j = *reinterpret_cast<const int4 *>(inv + v);
-    f32x4v o;
-    o.x = pick(j.x);
-    o.y = pick(j.y);
-    o.z = pick(j.z);
-    o.w = pick(j.w);
-    __builtin_nontemporal_store(o, reinterpret_cast<f32x4v *>(out + r * Vt + v));
+  const float *qr = q + r * K;
+  const unsigned ub = static_cast<unsigned>(base), un = static_cast<unsigned>(n);
+  // kScatterBatch pairs of 16-byte loads per lane in flight before their
+  // LDS writes (one workgroup per CU: the loads must overlap)
+  constexpr int kStride = 4 * kScatterThreads;
+  for (int j0 = 4 * tid; j0 < K; j0 += kScatterBatch * kStride) {
+    int4 t[kScatterBatch];
+    float4 v[kScatterBatch];
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u) {
+      const int j = j0 + u * kStride;
+      if (j < K) {
+        t[u] = *reinterpret_cast<const int4 *>(tgt + j);
+        v[u] = *reinterpret_cast<const float4 *>(qr + j);
+      } else {
+        t[u] = make_int4(-1, -1, -1, -1);
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u) {
+      if (static_cast<unsigned>(t[u].x) - ub < un) s_o[t[u].x - base] = v[u].x;
+      if (static_cast<unsigned>(t[u].y) - ub < un) s_o[t[u].y - base] = v[u].y;
+      if (static_cast<unsigned>(t[u].z) - ub < un) s_o[t[u].z - base] = v[u].z;
+      if (static_cast<unsigned>(t[u].w) - ub < un) s_o[t[u].w - base] = v[u].w;
+    }
   }
+  __syncthreads();
+  float *orow = out + r * Vt + base;
+  for (int i = 4 * tid; i < n; i += 4 * kScatterThreads)
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4v *>(s_o + i), reinterpret_cast<f32x4v *>(orow + i));
 }
 
 __global__ void q_scatter_kernel(int64_t rows, int K, int Vt, const float *__restrict__ q,
@@ -331,8 +365,10 @@ extern "C" int32_t sdv_tli_constrain_draft_logits(int32_t B, int32_t K, int32_t 
   return check_launch("constrain_kernel");
 }
 
+// Workspace: the inverse of tgt_ids [V_target], then a copy of tgt_ids (at
+// most V_target entries, since the map is injective).
 extern "C" size_t sdv_tli_q_scatter_workspace_size(int32_t V_target) {
-  return V_target > 0 ? align_up(static_cast<size_t>(V_target) * sizeof(int), 256) : 0;
+  return V_target > 0 ? 2 * align_up(static_cast<size_t>(V_target) * sizeof(int), 256) : 0;
 }
 
 extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, const float *q_pruned,
@@ -346,28 +382,33 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
   const size_t need = sdv_tli_q_scatter_workspace_size(V_target);
   SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "tli_q_scatter: workspace of %zu bytes needed", need);
   int *inv = static_cast<int *>(ws);
+  int *tcopy = inv + align_up(static_cast<size_t>(V_target) * sizeof(int), 256) / sizeof(int);
   hipStream_t st = as_stream(stream);
-  if (tgt_ids) {                         // else: the inverse an earlier call left in ws
+  if (tgt_ids) {                         // else: the inverse and the copy an earlier call left in ws
     hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(V_target, 256)), dim3(256), 0, st, inv,
                        static_cast<int64_t>(V_target), -1);
     if (K > 0)
-      hipLaunchKernelGGL(inverse_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, tgt_ids, V_target, inv);
+      hipLaunchKernelGGL(inverse_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, tgt_ids, V_target, inv, tcopy);
   }
   if (V_target % 4 == 0 && K % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0 &&
       reinterpret_cast<uintptr_t>(q_pruned) % 16 == 0) {
-    const size_t lds = static_cast<size_t>(kScatterLds) * sizeof(float);
+    const size_t lds = static_cast<size_t>(kScatterChunk) * sizeof(float);
     static thread_local int configured_dev = -1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "tli_q_scatter: no device");
     if (configured_dev != dev) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q_scatter_lds_kernel),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q_scatter_chunk_kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return fail(SDV_E_HIP, "tli_q_scatter: LDS attribute: %s", hipGetErrorString(e));
       configured_dev = dev;
     }
-    hipLaunchKernelGGL(q_scatter_lds_kernel, dim3(static_cast<unsigned>(rows)), dim3(kScatterThreads), lds, st, K,
-                       V_target, q_pruned, inv, q_target);
-    return check_launch("q_scatter_lds_kernel");
+    const int nch = static_cast<int>(nblk(V_target, kScatterChunk));
+    const int64_t per_xcd = (rows + kXcdCount - 1) / kXcdCount;       // rows per XCD
+    const int64_t blocks = per_xcd * nch * kXcdCount;
+    SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tli_q_scatter: grid too large");
+    hipLaunchKernelGGL(q_scatter_chunk_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), lds, st,
+                       rows, K, V_target, nch, q_pruned, tcopy, q_target);
+    return check_launch("q_scatter_chunk_kernel");
   }
   if (V_target % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0) {
     const int nchunks = static_cast<int>(nblk(V_target / 4, 256));
