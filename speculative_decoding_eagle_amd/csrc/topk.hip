@@ -610,7 +610,9 @@ struct TopkPlan {
 // rows = q * CUs + r: the first q * CUs rows whole, the r others in pieces,
 // one per CU (four per CU when q = 0), each at least a window and less than
 // a row; a whole block per row when r = 0 or the pieces would not be
-// shorter than a row.  Pieces cross row boundaries at most once.
+// shorter than a row, except that one to three rows per CU (r = 0) are all
+// cut into row-aligned pieces when V allows.  Pieces cross row boundaries
+// at most once.
 constexpr int kTopkPiecesPerCuAlone = 4;
 
 TopkPlan plan_topk(int64_t rows, int V, int k) {
@@ -624,6 +626,20 @@ TopkPlan plan_topk(int64_t rows, int V, int k) {
   p.cut = 0;
   const int64_t cus = num_cus();
   const int64_t q = rows / cus, r = rows % cus;
+  if (r == 0 && q > 0 && q < kTopkPiecesPerCuAlone && rows <= kTopkRowsMax) {
+    // one to three rows per CU: every row in s equal pieces (four workgroups
+    // per CU or more) when V splits into whole 16-byte loads, so that no
+    // piece crosses a row boundary
+    const int64_t sp = (kTopkPiecesPerCuAlone + q - 1) / q;
+    if (V % (8 * sp) == 0 && V / sp >= 4096) {
+      p.nwhole = 0;
+      p.per = V / sp;
+      p.cut = rows;
+      p.blocks = rows * sp;
+      p.maxseg = static_cast<int>((V - 1) / p.per + 2);
+    }
+    return p;
+  }
   if (r == 0 || r > kTopkRowsMax) return p;
   const int64_t tail = r * static_cast<int64_t>(V);
   const int64_t pieces = (q == 0 ? kTopkPiecesPerCuAlone : 1) * cus;

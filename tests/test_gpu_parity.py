@@ -96,9 +96,11 @@ def test_topk_from_logits(rows, V, k, T, bf16, kind):
 # gets a group of equal values (its maximum, doubled) at random places, so
 # its k best and their tie order straddle wherever the cuts fall; 2048 rows
 # (a multiple of 256 compute units) take the one-workgroup-per-row path
-# alone.
+# alone, and 256, 512 and 768 rows (one to three per compute unit) are cut
+# into four or two row-aligned pieces each.
 @pytest.mark.parametrize("rows,V,k", [(1056, 128256, 8), (300, 128256, 4), (2047, 4104, 8), (2048, 4104, 8),
-                                      (5000, 4104, 2), (129, 65536, 16), (7, 9000, 32)])
+                                      (5000, 4104, 2), (129, 65536, 16), (7, 9000, 32), (256, 128256, 1),
+                                      (512, 128256, 8), (768, 65536, 4)])
 def test_topk_segments(rows, V, k):
     rng = np.random.default_rng(rows * 17 + V + k)
     p = workloads.softmax_rows(rng.standard_normal((rows, V)).astype(np.float32) * 3)
