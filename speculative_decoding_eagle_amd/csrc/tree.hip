@@ -52,6 +52,83 @@ __device__ __forceinline__ void rank_block(const unsigned long long *key, int lo
   }
 }
 
+// Lane l's value of lane l ^ S, without LDS: DPP for S <= 8, the row-half
+// swaps for 16 and 32.  Where the builtin's direction could be either
+// (row shifts; which swap output is the partner's), the same instruction
+// moves the lane ids and the copy that came from lane l ^ S is taken.
+template <int S>
+__device__ __forceinline__ unsigned xor_lane(unsigned v, unsigned lane) {
+  if constexpr (S == 1) {
+    return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));   // quad [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true));   // quad [2,3,0,1]
+  } else if constexpr (S == 4) {
+    const unsigned a = static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x104, 0xF, 0xF, true));
+    const unsigned b = static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x114, 0xF, 0xF, true));
+    const unsigned la = static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(lane), 0x104, 0xF, 0xF, true));
+    return la == (lane ^ 4u) ? a : b;                                                                     // row shifts by 4
+  } else if constexpr (S == 8) {
+    return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, true));  // row rotate by 8
+  } else if constexpr (S == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    const auto q = __builtin_amdgcn_permlane16_swap(lane, lane, false, false);
+    return q[0] == (lane ^ 16u) ? p[0] : p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(lane, lane, false, false);
+    return q[0] == (lane ^ 32u) ? p[0] : p[1];
+  }
+}
+
+template <int S>
+__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v, unsigned lane) {
+  const unsigned lo = xor_lane<S>(static_cast<unsigned>(v), lane);
+  const unsigned hi = xor_lane<S>(static_cast<unsigned>(v >> 32), lane);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// One bitonic stage of block size SIZE and stride S, larger keys first.
+template <int SIZE, int S>
+__device__ __forceinline__ unsigned long long sort_stage(unsigned long long key, unsigned lane) {
+  const unsigned long long other = xor_lane64<S>(key, lane);
+  const bool desc = (lane & SIZE) == 0;          // this block's direction
+  const bool lower = (lane & S) == 0;            // this lane's place in the pair
+  const bool keep_max = lower == desc;
+  return keep_max ? (other > key ? other : key) : (other < key ? other : key);
+}
+
+// Sorts one order key per lane across the wave, largest first (a bitonic
+// network of 21 compare-exchange stages, all in registers).
+__device__ __forceinline__ unsigned long long wave_sort_keys_desc(unsigned long long key) {
+  const unsigned lane = static_cast<unsigned>(lane_id());
+  key = sort_stage<2, 1>(key, lane);
+  key = sort_stage<4, 2>(key, lane);
+  key = sort_stage<4, 1>(key, lane);
+  key = sort_stage<8, 4>(key, lane);
+  key = sort_stage<8, 2>(key, lane);
+  key = sort_stage<8, 1>(key, lane);
+  key = sort_stage<16, 8>(key, lane);
+  key = sort_stage<16, 4>(key, lane);
+  key = sort_stage<16, 2>(key, lane);
+  key = sort_stage<16, 1>(key, lane);
+  key = sort_stage<32, 16>(key, lane);
+  key = sort_stage<32, 8>(key, lane);
+  key = sort_stage<32, 4>(key, lane);
+  key = sort_stage<32, 2>(key, lane);
+  key = sort_stage<32, 1>(key, lane);
+  key = sort_stage<64, 32>(key, lane);
+  key = sort_stage<64, 16>(key, lane);
+  key = sort_stage<64, 8>(key, lane);
+  key = sort_stage<64, 4>(key, lane);
+  key = sort_stage<64, 2>(key, lane);
+  key = sort_stage<64, 1>(key, lane);
+  return key;
+}
+
+__device__ __forceinline__ int entry_of_key(unsigned long long key) {
+  return static_cast<int>(~static_cast<unsigned>(key));
+}
+
 // Exclusive block scan of one int per thread.
 __device__ int block_exclusive_scan(int x) {
   __shared__ int s_w[kTreeWaves];
@@ -110,33 +187,73 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
   const int root = root_token[b];
   __syncthreads();
 
-  // step 0: the root's children; their rank order is the first frontier
-  for (int c = tid; c < k; c += kTreeThreads) {
-    s_score[c] = s_tp[c];
-    s_par[c] = -1;
-    s_key[c] = order_key(s_tp[c], c);
-  }
-  __syncthreads();
-  rank_block(s_key, 0, k, [&](int e, int r) { s_front[r] = e; });
-  __syncthreads();
-
-  // steps 1 .. S-1: expand every frontier slot, keep the best k as the next frontier
-  for (int i = 1; i < S; ++i) {
-    const int base = k + (i - 1) * k * k;
-    for (int x = tid; x < k * k; x += kTreeThreads) {
-      const int f = s_front[x / k];
-      const int e = base + x;
-      const float sc = s_score[f] * s_tp[e];
-      s_score[e] = sc;
-      s_par[e] = f;
-      s_key[e] = order_key(sc, e);
+  if (k * k <= kWave) {
+    // Every step's k*k candidates fit one wave: wave 0 runs the steps in
+    // registers, each frontier the first k lanes of a wave sort of the
+    // step's order keys (lanes past the candidates hold 0, below any key).
+    if (tid < kWave) {
+      const int x = tid;
+      // step 0: the root's children
+      unsigned long long key = 0;
+      if (x < k) {
+        key = order_key(s_tp[x], x);
+        s_score[x] = s_tp[x];
+        s_par[x] = -1;
+        s_key[x] = key;
+      }
+      key = wave_sort_keys_desc(key);
+      int fe = entry_of_key(key);                  // lanes j < k: frontier slot j
+      float fs = x < k ? s_tp[fe] : 0.f;           // its score
+      // steps 1 .. S-1: expand every frontier slot, keep the best k
+      for (int i = 1; i < S; ++i) {
+        const int base = k + (i - 1) * k * k;
+        const int f = __shfl(fe, x / k, kWave);
+        const float fsc = __shfl(fs, x / k, kWave);
+        if (x < k) s_row[fe] = 1 + (i - 1) * k + x;
+        key = 0;
+        if (x < k * k) {
+          const int e = base + x;
+          const float sc = fsc * s_tp[e];
+          s_score[e] = sc;
+          s_par[e] = f;
+          key = order_key(sc, e);
+          s_key[e] = key;
+        }
+        key = wave_sort_keys_desc(key);
+        fe = entry_of_key(key);
+        fs = x < k ? s_score[fe] : 0.f;            // written by this wave above (LDS keeps a wave's order)
+      }
     }
-    for (int j = tid; j < k; j += kTreeThreads) s_row[s_front[j]] = 1 + (i - 1) * k + j;
     __syncthreads();
-    rank_block(s_key, base, k * k, [&](int e, int r) {
-      if (r < k) s_front[r] = e;
-    });
+  } else {
+    // step 0: the root's children; their rank order is the first frontier
+    for (int c = tid; c < k; c += kTreeThreads) {
+      s_score[c] = s_tp[c];
+      s_par[c] = -1;
+      s_key[c] = order_key(s_tp[c], c);
+    }
     __syncthreads();
+    rank_block(s_key, 0, k, [&](int e, int r) { s_front[r] = e; });
+    __syncthreads();
+
+    // steps 1 .. S-1: expand every frontier slot, keep the best k as the next frontier
+    for (int i = 1; i < S; ++i) {
+      const int base = k + (i - 1) * k * k;
+      for (int x = tid; x < k * k; x += kTreeThreads) {
+        const int f = s_front[x / k];
+        const int e = base + x;
+        const float sc = s_score[f] * s_tp[e];
+        s_score[e] = sc;
+        s_par[e] = f;
+        s_key[e] = order_key(sc, e);
+      }
+      for (int j = tid; j < k; j += kTreeThreads) s_row[s_front[j]] = 1 + (i - 1) * k + j;
+      __syncthreads();
+      rank_block(s_key, base, k * k, [&](int e, int r) {
+        if (r < k) s_front[r] = e;
+      });
+      __syncthreads();
+    }
   }
 
   // final selection: the best N-1 pool entries, numbered in pool order
