@@ -125,6 +125,27 @@ __device__ __forceinline__ unsigned long long wave_sort_keys_desc(unsigned long 
   return key;
 }
 
+// Largest 64 of two lane-sorted key sets (largest first), largest first:
+// b reversed across the wave (lane l ^ 63) against a, the larger of each
+// pair (a bitonic sequence holding the top 64), then the last six stages.
+__device__ __forceinline__ unsigned long long wave_merge_top(unsigned long long a, unsigned long long b) {
+  const unsigned lane = static_cast<unsigned>(lane_id());
+  b = xor_lane64<32>(b, lane);
+  b = xor_lane64<16>(b, lane);
+  b = xor_lane64<8>(b, lane);
+  b = xor_lane64<4>(b, lane);
+  b = xor_lane64<2>(b, lane);
+  b = xor_lane64<1>(b, lane);
+  unsigned long long key = a > b ? a : b;
+  key = sort_stage<64, 32>(key, lane);
+  key = sort_stage<64, 16>(key, lane);
+  key = sort_stage<64, 8>(key, lane);
+  key = sort_stage<64, 4>(key, lane);
+  key = sort_stage<64, 2>(key, lane);
+  key = sort_stage<64, 1>(key, lane);
+  return key;
+}
+
 __device__ __forceinline__ int entry_of_key(unsigned long long key) {
   return static_cast<int>(~static_cast<unsigned>(key));
 }
@@ -182,11 +203,16 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
     s_tp[e] = tp[e];
     s_tok[e] = ti[e];
     s_row[e] = -1;
+    s_tree[e] = 0;
   }
   const int L = prefix_len[b];
   const int root = root_token[b];
   __syncthreads();
 
+  // With N - 1 <= 64 as well, wave 0 also keeps the best 64 keys of the
+  // pool so far (every step's sorted keys merged in) and marks the final
+  // N - 1 itself.
+  const bool wave_final = k * k <= kWave && N - 1 <= kWave;
   if (k * k <= kWave) {
     // Every step's k*k candidates fit one wave: wave 0 runs the steps in
     // registers, each frontier the first k lanes of a wave sort of the
@@ -202,6 +228,7 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
         s_key[x] = key;
       }
       key = wave_sort_keys_desc(key);
+      unsigned long long best = key;               // best 64 of the pool so far, largest first
       int fe = entry_of_key(key);                  // lanes j < k: frontier slot j
       float fs = x < k ? s_tp[fe] : 0.f;           // its score
       // steps 1 .. S-1: expand every frontier slot, keep the best k
@@ -220,9 +247,11 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
           s_key[e] = key;
         }
         key = wave_sort_keys_desc(key);
+        if (wave_final) best = wave_merge_top(best, key);
         fe = entry_of_key(key);
         fs = x < k ? s_score[fe] : 0.f;            // written by this wave above (LDS keeps a wave's order)
       }
+      if (wave_final && x < N - 1) s_tree[entry_of_key(best)] = 1;   // keys are distinct: the top N-1 entries
     }
     __syncthreads();
   } else {
@@ -257,8 +286,10 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
   }
 
   // final selection: the best N-1 pool entries, numbered in pool order
-  rank_block(s_key, 0, M, [&](int e, int r) { s_tree[e] = r < N - 1 ? 1 : 0; });
-  __syncthreads();
+  if (!wave_final) {
+    rank_block(s_key, 0, M, [&](int e, int r) { s_tree[e] = r < N - 1 ? 1 : 0; });
+    __syncthreads();
+  }
   const int per = (M + kTreeThreads - 1) / kTreeThreads;
   const int e0 = tid * per;
   int cnt = 0;
