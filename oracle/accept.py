@@ -125,6 +125,14 @@ def _rejection_draw_masses(p_u, t, last):
     return last
 
 
+def _leaf_bonus_masses(p_leaf, q_parent):
+    """Masses of the bonus drawn at a leaf: the target's own row at the leaf.
+
+    q_parent (the draft row that proposed the leaf; None at a root without
+    children) is not used: the bonus comes from p alone, not from q."""
+    return masses(p_leaf)
+
+
 def _draw(R, t, u) -> int:
     if int(np.asarray(R, np.uint64).sum(dtype=np.uint64)) == 0:
         return argmax_lowest(t)
@@ -137,6 +145,7 @@ def _stochastic_one(b, tokens, next_token, next_sibling, q_row, p_rows, q_rows,
     if remaining == 0:
         return path, out
     u = 0
+    q_parent = None
     while True:
         p_u = np.asarray(p_rows[u], np.float32)
         t = p_u
@@ -164,8 +173,9 @@ def _stochastic_one(b, tokens, next_token, next_sibling, q_row, p_rows, q_rows,
             if y == eos_id or (remaining is not None and len(out) == remaining):
                 return path, out
             u = accepted
+            q_parent = q
             continue
-        R = _rejection_draw_masses(p_u, t, last) if kids else masses(t)
+        R = _rejection_draw_masses(p_u, t, last) if kids else _leaf_bonus_masses(p_u, q_parent)
         out.append(_draw(R, t, u_draw[u]))
         return path, out
 

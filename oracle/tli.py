@@ -40,8 +40,25 @@ def build_maps(inter_ids, tgt_ids, V_draft: int, V_target: int, fallback: int):
     return d2t, t2d
 
 
+def check_tli_shape(topk: int, num_steps: int, num_draft_tokens: int) -> None:
+    """The TLI validation rules (sglang PR #22883, "Modified files", the
+    validation block added to the server-argument checks): TLI drafts a single
+    candidate per step (topk must be 1) and the draft is a chain with the root,
+    so num_draft_tokens must equal num_steps + 1.  Raises ValueError otherwise."""
+    if int(topk) != 1:
+        raise ValueError("TLI needs topk == 1 (got %d)" % topk)
+    if int(num_steps) < 1 or int(num_draft_tokens) != int(num_steps) + 1:
+        raise ValueError("TLI needs num_draft_tokens == num_steps + 1 (got %d, %d)"
+                         % (num_draft_tokens, num_steps))
+
+
 def map_ids(table, ids):
-    """out[i] = table[ids[i]]; an id outside the table maps to -1."""
+    """out[i] = table[ids[i]]; an id outside [0, len(table)) maps to -1.
+
+    Reading: an id that names no entry of the table (the -1 padding of the
+    accept walk's committed-token array, or any other value out of range) has
+    no image in the other vocabulary and stays the padding value -1, so id
+    arrays can be remapped whole, padding included."""
     ids = np.asarray(ids, np.int64)
     table = np.asarray(table, np.int32)
     out = np.full(ids.shape, -1, np.int32)

@@ -440,3 +440,125 @@ def test_stochastic_invariants_on_configs():
                 assert r["next_root"][b] == r["commit_tokens"][b, a]
             if planted:
                 assert r["accept_len"].mean() > 1
+
+
+# ------------------------------- stochastic: the bonus after full acceptance
+#
+# A one-child chain root -> y, where y is a leaf.  If y is accepted, the walk
+# draws the bonus at y from the target row there, p_leaf (zero-to-sglang ch.10
+# section 5.1: after every draft token is accepted, one more token is sampled
+# from the target distribution).  The enumeration covers every y ~ q, every
+# u_accept, the correction draw at the root and the bonus draw at the leaf, and
+# gives the exact law of the whole committed sequence.
+
+def _walk_chain(p_root, p_leaf, q32, y, ka, kd_root, kd_leaf):
+    V = len(p_root)
+    t = _one_child_tree(y)
+    prow = np.stack([np.asarray(p_root, np.float32), np.asarray(p_leaf, np.float32)])[None]
+    u_acc = np.array([[0.0, ka * 2.0 ** -24]], np.float32)
+    u_draw = np.array([[kd_root * 2.0 ** -24, kd_leaf * 2.0 ** -24]], np.float32)
+    r = oacc.verify_stochastic(t, prow, q32[None, None], u_acc, u_draw, S=1)
+    return tuple(int(x) for x in r["commit_tokens"][0, :r["commit_len"][0]])
+
+
+def _draw_counts(f, n):
+    """Counts of each value of a non-decreasing step function f over [0, n)."""
+    counts, lo = {}, 0
+    while lo < n:
+        v = f(lo)
+        nxt = _first_monotone_change(f, lo, n - 1)
+        counts[v] = counts.get(v, 0) + (nxt - lo)
+        lo = nxt
+    return counts
+
+
+def enumerate_chain_sequences(p_root, p_leaf, q_exact):
+    """Exact law of the committed sequence of the one-child chain, y ~ q."""
+    q32 = np.array([float(x) for x in q_exact], np.float32)
+    n = 1 << 24
+    law = {}
+    for y in range(len(q_exact)):
+        if q_exact[y] == 0:
+            continue
+        acc = lambda ka: len(_walk_chain(p_root, p_leaf, q32, y, ka, 0, 0)) == 2      # noqa: E731
+        n_acc = 0 if not acc(0) else _first_monotone_change(acc, 0, n - 1)
+        w = Fraction(q_exact[y])
+        if n_acc > 0:
+            bonus = _draw_counts(lambda kd: _walk_chain(p_root, p_leaf, q32, y, 0, 0, kd)[1], n)
+            for v, c in bonus.items():
+                law[(y, v)] = law.get((y, v), 0) + w * Fraction(n_acc, n) * Fraction(c, n)
+        if n_acc < n:
+            corr = _draw_counts(lambda kd: _walk_chain(p_root, p_leaf, q32, y, n_acc, kd, 0)[0], n)
+            for v, c in corr.items():
+                law[(v,)] = law.get((v,), 0) + w * Fraction(n - n_acc, n) * Fraction(c, n)
+    return law
+
+
+_BONUS_CASE = dict(
+    p_root=[Fraction(1, 4), Fraction(1, 2), Fraction(1, 8), Fraction(1, 8)],
+    # residual (p_root - q)+ = [0, 1/8, 0, 1/8]: its normalisation is dyadic,
+    # so the 2**-24 uniforms reproduce every probability exactly
+    q=[Fraction(1, 2), Fraction(3, 8), Fraction(1, 8), Fraction(0)],
+    # the leaf's own target row differs from both p_root and q
+    p_leaf=[Fraction(1, 16), Fraction(1, 8), Fraction(5, 16), Fraction(1, 2)],
+)
+
+
+def _expected_chain_law(p_root, q, p_leaf):
+    """Speculative sampling with one candidate: y is committed with probability
+    min(p(y), q(y)) and is followed by a bonus ~ p_leaf; otherwise the single
+    token v is committed with probability p(v) - min(p(v), q(v))."""
+    law = {}
+    for y in range(len(q)):
+        for v in range(len(p_leaf)):
+            if min(p_root[y], q[y]) * p_leaf[v] > 0:
+                law[(y, v)] = min(p_root[y], q[y]) * p_leaf[v]
+    for v in range(len(p_root)):
+        if p_root[v] - min(p_root[v], q[v]) > 0:
+            law[(v,)] = p_root[v] - min(p_root[v], q[v])
+    return law
+
+
+def test_bonus_after_full_acceptance_is_drawn_from_the_leaf_row():
+    c = _BONUS_CASE
+    law = enumerate_chain_sequences([float(x) for x in c["p_root"]], [float(x) for x in c["p_leaf"]], c["q"])
+    assert law == _expected_chain_law(c["p_root"], c["q"], c["p_leaf"])
+    # the marginal of the first token is p_root, and given acceptance of y the
+    # second token is distributed as p_leaf
+    first = {}
+    for seq, w in law.items():
+        first[seq[0]] = first.get(seq[0], 0) + w
+    assert [first.get(v, 0) for v in range(4)] == c["p_root"]
+
+
+@pytest.mark.parametrize("plant", ["from_q", "from_parent_p"])
+def test_planted_bonus_source_is_caught(monkeypatch, plant):
+    """Planting a wrong bonus source in the oracle -- the draft row that
+    proposed the leaf, or the parent's target row -- changes the exact law."""
+    c = _BONUS_CASE
+    p_root32 = np.array([float(x) for x in c["p_root"]], np.float32)
+    if plant == "from_q":
+        monkeypatch.setattr(oacc, "_leaf_bonus_masses", lambda p_leaf, q_parent: oacc.masses(q_parent))
+    else:
+        monkeypatch.setattr(oacc, "_leaf_bonus_masses", lambda p_leaf, q_parent: oacc.masses(p_root32))
+    law = enumerate_chain_sequences([float(x) for x in c["p_root"]], [float(x) for x in c["p_leaf"]], c["q"])
+    assert law != _expected_chain_law(c["p_root"], c["q"], c["p_leaf"])
+
+
+def test_bonus_at_a_childless_root_is_drawn_from_p():
+    """A root with no children (N = 1) commits one token drawn from its p row;
+    every u_draw value is enumerated."""
+    p = [Fraction(3, 8), Fraction(1, 8), Fraction(1, 2)]
+    tree = otree.verify_arrays(np.array([0], np.int32), np.array([-1], np.int32), np.array([0], np.int32),
+                               np.ones(1, np.float32), np.array([-1], np.int32), 0, 0)
+    tree = {k: v[None] for k, v in tree.items()}
+    prow = np.array([[float(x) for x in p]], np.float32)[None]
+
+    def tok(kd):
+        r = oacc.verify_stochastic(tree, prow, np.full((1, 1, 3), 1 / 3, np.float32),
+                                   np.zeros((1, 1), np.float32), np.array([[kd * 2.0 ** -24]], np.float32), S=0)
+        assert r["accept_len"][0] == 0 and r["commit_len"][0] == 1
+        return int(r["commit_tokens"][0, 0])
+
+    counts = _draw_counts(tok, 1 << 24)
+    assert [Fraction(counts.get(v, 0), 1 << 24) for v in range(3)] == p

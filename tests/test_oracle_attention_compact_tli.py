@@ -260,3 +260,78 @@ def test_tli_identity_vocab_reduces_to_plain_verify():
     r0 = oacc.verify_stochastic(t0, inp["target"], inp["draft_probs"], inp["u_accept"], inp["u_draw"], S=cfg.S)
     for key in r0:
         assert np.array_equal(r0[key], r1[key])
+
+
+def test_tli_small_pairing_golden(golden_dir):
+    import json
+    import os
+    with open(os.path.join(golden_dir, "tli_small_pairing.json")) as f:
+        g = json.load(f)
+    d2t, t2d = otli.build_maps(g["inter_ids"], g["tgt_ids"], g["V_draft"], g["V_target"], g["fallback"])
+    assert d2t.tolist() == g["expected_d2t"]
+    assert t2d.tolist() == g["expected_t2d"]
+    q = otli.q_scatter(np.array([g["q_pruned"]], np.float32), g["tgt_ids"], g["V_target"])
+    assert q[0].tolist() == g["expected_q_target"]
+
+
+def _q_target_semantics_hold(q_target, q_dense, d2t, t2d):
+    """Target id t carries the draft probability of its draft counterpart
+    t2d[t] when that is an intersection token (d2t[t2d[t]] == t), else 0."""
+    Vt = q_target.shape[1]
+    for t in range(Vt):
+        d = int(t2d[t])
+        want = q_dense[:, d] if 0 <= d < len(d2t) and d2t[d] == t else np.zeros(q_dense.shape[0], np.float32)
+        if not np.array_equal(q_target[:, t], want):
+            return False
+    return True
+
+
+def _q_scatter_case():
+    rng = np.random.default_rng(34)
+    Vd, Vt, K = 300, 250, 120
+    inter, tgt, fb = _tli_case(rng, Vd, Vt, K)
+    d2t, t2d = otli.build_maps(inter, tgt, Vd, Vt, fb)
+    # the draft distribution: softmax over the constrained (dense) draft logits
+    pruned = (rng.standard_normal((3, K)) * 2).astype(np.float32)
+    dense = otli.constrain_logits(pruned, inter, Vd)
+    q_dense = torch.softmax(torch.from_numpy(dense.astype(np.float64)), 1).numpy().astype(np.float32)
+    return inter, tgt, d2t, t2d, q_dense, Vt
+
+
+def test_tli_q_scatter_carries_the_draft_distribution_into_target_ids():
+    """A non-identity pairing: the scattered row is the draft distribution
+    expressed in target ids (via the maps, which are pinned on their own), and
+    it keeps the row's mass."""
+    inter, tgt, d2t, t2d, q_dense, Vt = _q_scatter_case()
+    q_target = otli.q_scatter(q_dense[:, inter], tgt, Vt)
+    assert _q_target_semantics_hold(q_target, q_dense, d2t, t2d)
+    for r in range(q_dense.shape[0]):
+        assert sorted(q_target[r][q_target[r] != 0].tolist()) == sorted(q_dense[r][q_dense[r] != 0].tolist())
+        assert abs(q_target[r].astype(np.float64).sum() - 1.0) < 1e-6
+
+
+@pytest.mark.parametrize("plant", ["keyed_by_draft_ids", "keyed_by_column_through_d2t"])
+def test_tli_q_scatter_planted_keys_are_caught(monkeypatch, plant):
+    """Two plausible mistakes planted in the oracle's scatter -- keying it by
+    the draft ids, or treating the column index as a draft id -- break the
+    target-id semantics."""
+    inter, tgt, d2t, t2d, q_dense, Vt = _q_scatter_case()
+    orig = otli.q_scatter
+    if plant == "keyed_by_draft_ids":
+        monkeypatch.setattr(otli, "q_scatter", lambda q, ids, V: orig(q, np.asarray(inter) % V, V))
+    else:
+        cols = d2t[np.arange(len(inter))]
+        monkeypatch.setattr(otli, "q_scatter", lambda q, ids, V: orig(q[:, cols >= 0], cols[cols >= 0], V))
+    q_target = otli.q_scatter(q_dense[:, inter], tgt, Vt)
+    assert not _q_target_semantics_hold(q_target, q_dense, d2t, t2d)
+
+
+def test_tli_validator_follows_the_pages_rules():
+    """The PR's validation block: topk == 1 and num_draft_tokens ==
+    num_steps + 1.  Its benchmark shape (topk 1, 5 draft tokens, so 4 steps)
+    passes; a tree (topk 8) and mismatched chain lengths are refused."""
+    otli.check_tli_shape(1, 4, 5)
+    otli.check_tli_shape(1, 1, 2)
+    for k, S, N in [(8, 5, 64), (2, 4, 5), (1, 4, 4), (1, 4, 6), (1, 0, 1), (0, 4, 5)]:
+        with pytest.raises(ValueError):
+            otli.check_tli_shape(k, S, N)
