@@ -23,6 +23,13 @@
  *   Shape checks run on the host; the kernels additionally clamp or skip
  *   out-of-range indices read from device arrays instead of faulting (the
  *   results of such inputs are unspecified).
+ * - Device-side status: a workspace whose kernels wait on one another
+ *   (sdv_draft_topk*, sdv_tree_verify_attention, sdv_verify_accept) or that
+ *   carries a map between calls (sdv_tli_q_scatter) begins with a 256-byte
+ *   header.  Its first 32-bit word is a sticky set of SDV_STATUS_* bits
+ *   that a kernel sets when a bounded wait gave up (the outputs of that
+ *   call are then unspecified) or when it met an input it could not use.
+ *   sdv_workspace_status() reads it after the stream drains.
  *
  * Notation: B requests, k = topk, S = draft steps, N = tree size (root
  * included), V vocabulary, R = 1 + (S-1)*k draft-distribution rows per
@@ -55,6 +62,44 @@ const char *sdv_last_error(void);
 /* ABI version (major * 100 + minor). */
 int32_t sdv_version(void);
 
+/* Device status bits (workspace header word 0). */
+enum {
+  SDV_STATUS_ACCEPT_WAIT = 1,      /* sdv_verify_accept: an exchange between the workgroups of a
+                                      request gave up (a workgroup of the group was not running) */
+  SDV_STATUS_ATTN_MERGE_WAIT = 2,  /* sdv_tree_verify_attention: the key split's merge gave up
+                                      (the rows of that unit are NaN) */
+  SDV_STATUS_TOPK_MERGE_WAIT = 4,  /* sdv_draft_topk*: a cut row's pieces did not all arrive (the
+                                      row reads NaN / -1) */
+  SDV_STATUS_TLI_REUSE = 8         /* sdv_tli_q_scatter: a call without ids found no map of its
+                                      K and V_target in the workspace (its output is 0) */
+};
+
+/* Reads the status word of a workspace (device, ws_bytes as passed to the
+ * call that used it; NULL or fewer than 256 bytes: status 0) into *status
+ * (host) after draining `stream`, so the word reflects every call enqueued
+ * before.  reset != 0 and a non-zero status: the whole workspace is then
+ * zero-filled on `stream`, which restores the state the calls expect (a
+ * wait that gave up may leave counters or exchange words behind) and clears
+ * the status; the TLI scatter's map must then be built again.
+ * The callers are error checks outside the hot loop: this call synchronises. */
+int32_t sdv_workspace_status(void *ws, size_t ws_bytes, uint32_t *status, int32_t reset, void *stream);
+
+/* Bounded waits between workgroups (the accept walk's exchanges, the
+ * attention merge, the top-k piece merge) poll at most a library-chosen
+ * number of times.  polls != 0xFFFFFFFF replaces that number for every call
+ * enqueued afterwards (0: every such wait gives up at once, without
+ * polling, so tests can drive the give-up paths while every kernel still
+ * exits normally); 0xFFFFFFFF restores the library's choice.  Returns the
+ * previous setting.  Process-wide; meant for tests. */
+uint32_t sdv_set_wait_limit(uint32_t polls);
+
+/* TLI shape validation.  sglang PR #22883, "Modified files": the TLI
+ * validation block of the server-argument checks requires topk == 1 (TLI
+ * does not support multi-candidate trees) and num_draft_tokens ==
+ * num_steps + 1.  Returns SDV_OK, or SDV_E_UNSUPPORTED with a message.
+ * Host only; a TLI pipeline calls it before its first step. */
+int32_t sdv_tli_check(int32_t topk, int32_t num_steps, int32_t num_draft_tokens);
+
 /* ------------------------------------------------------------------------
  * A1  Draft vocabulary top-k.
  * "[SGLang] Multi-Layer EAGLE", section 3 (draft extend): the per-step softmax
@@ -70,11 +115,12 @@ int32_t sdv_version(void);
  * first q * CUs rows are scanned one workgroup each, and the r others are
  * cut into equal pieces spread over the compute units; a cut row is merged
  * by the workgroup that finishes it last, through per-row counters at the
- * start of the workspace.  The caller
+ * start of the workspace (after the status header).  The caller
  * zero-fills the workspace once before its first use; every call leaves the
  * counters at zero again, so the same workspace serves later calls of any
  * shape.  Calls that share a workspace must not run concurrently.  Results
  * do not depend on the split (the k best under the order above are unique).
+ * A merge that gives up sets SDV_STATUS_TOPK_MERGE_WAIT.
  * ---------------------------------------------------------------------- */
 size_t sdv_draft_topk_workspace_size(int64_t rows, int32_t V, int32_t k);
 int32_t sdv_draft_topk(const float *probs, int64_t rows, int32_t V, int32_t k,
@@ -194,10 +240,11 @@ int32_t sdv_build_chain(int32_t B, int32_t S, const float *topk_p, const int32_t
  * Workspace: when N * Hq/Hkv > 128 (and B * Hkv * ceil(N * Hq/Hkv / 256) <=
  * 4096) the size query returns the bytes with which a call may split each
  * unit's keys over two workgroups (few units, many CUs).  ws must then be
- * 256-byte aligned and zero-filled once before its first use: its first
- * 32 KiB hold counters that every call leaves at zero, whatever the shape,
- * and the rest is scratch.  Calls that may overlap need separate
- * workspaces.  ws = NULL (or fewer bytes) runs without the split.
+ * 256-byte aligned and zero-filled once before its first use: after the
+ * 256-byte status header, 32 KiB hold counters that every call leaves at
+ * zero, whatever the shape, and the rest is scratch.  Calls that may overlap
+ * need separate workspaces.  ws = NULL (or fewer bytes) runs without the
+ * split.  A merge that gives up sets SDV_STATUS_ATTN_MERGE_WAIT.
  * Otherwise the size query returns 0 and ws is ignored.
  * ---------------------------------------------------------------------- */
 typedef struct {
@@ -244,11 +291,16 @@ int32_t sdv_tree_verify_attention(sdv_attn_shape shape, float sm_scale, const ui
  * Outputs (device): accept_len [B]; accept_path [B, S+1] (tree indices, root
  * first, -1 padded); commit_tokens [B, S+1] (-1 padded); commit_len [B];
  * next_root [B] (last committed token, -1 if none).
- * Limits: V < 2^31 - 4, N <= 256, S + 1 <= 64.  The walk runs as one
- * cooperative launch; calls that share a workspace must not overlap.  The
- * workspace must be zero-filled before its first use; every call leaves it
- * zero-filled (whatever its shape), so one zero-filled buffer of the largest
- * size query's bytes serves every later call.
+ * p and q entries lie in [0, 1] (rows need not sum to 1).
+ * Limits: V < 2^31 - 4, N <= 256, S + 1 <= 64.  The W workgroups of a
+ * request exchange row-wide values and must run at the same time: the
+ * launch holds no more workgroups than the device keeps resident, and an
+ * exchange that still misses a word after its bounded wait sets
+ * SDV_STATUS_ACCEPT_WAIT (e.g. when other work occupies the device).  Calls
+ * that share a workspace must not overlap.  The workspace must be
+ * zero-filled before its first use; every call leaves it zero-filled
+ * (whatever its shape), so one zero-filled buffer of the largest size
+ * query's bytes serves every later call.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t B, N, S, V, R, mode;
@@ -394,10 +446,15 @@ int32_t sdv_tli_lm_head(int32_t B, int32_t H, int32_t K, const uint16_t *hidden,
  * ascending, full device [B, V_draft] fp32.
  * sdv_tli_q_scatter: q_target[r, tgt_ids[j]] = q_pruned[r, j], 0 elsewhere;
  * q_pruned device [rows, K] fp32, q_target device [rows, V_target] fp32;
- * the workspace holds the inverse of tgt_ids and a copy of tgt_ids.
- * tgt_ids == NULL reuses what an earlier call with the same K, V_target and
- * map left in the same workspace (the maps are static, so a serving loop
- * builds them once).
+ * the workspace holds a header (K and V_target of the map), the inverse of
+ * tgt_ids and a copy of tgt_ids; a call with tgt_ids builds them (whatever
+ * the workspace held, its status word included, is overwritten).  The
+ * workspace needs no zero-fill.  tgt_ids == NULL reuses what an earlier
+ * call with the same K and V_target left in the same workspace (the maps
+ * are static, so a serving loop builds them once); if the header names
+ * another K or V_target (or no map was built), the output is 0 and
+ * SDV_STATUS_TLI_REUSE is set.  Ids and positions read from the workspace
+ * are bounds-checked against K.
  * ---------------------------------------------------------------------- */
 int32_t sdv_tli_build_maps(int32_t K, const int32_t *inter_ids, const int32_t *tgt_ids,
                            int32_t V_draft, int32_t V_target, int32_t fallback, int32_t *d2t,

@@ -12,6 +12,14 @@ from .binding import (  # noqa: F401
     KVAlloc,
     STOCHASTIC,
     SdvError,
+    STATUS_ACCEPT_WAIT,
+    STATUS_ATTN_MERGE_WAIT,
+    STATUS_TLI_REUSE,
+    STATUS_TOPK_MERGE_WAIT,
+    device_status,
+    sdv_set_wait_limit,
+    sdv_tli_check,
+    sdv_workspace_status,
     sdv_build_chain,
     sdv_build_tree,
     sdv_compact_kv,

@@ -43,6 +43,9 @@ class BranchShape(ctypes.Structure):
 SIGNATURES = {
     "sdv_last_error": (ctypes.c_char_p, []),
     "sdv_version": (c_i32, []),
+    "sdv_workspace_status": (c_i32, [c_p, c_sz, ctypes.POINTER(ctypes.c_uint32), c_i32, c_p]),
+    "sdv_set_wait_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
+    "sdv_tli_check": (c_i32, [c_i32, c_i32, c_i32]),
     "sdv_draft_topk_workspace_size": (c_sz, [c_i64, c_i32, c_i32]),
     "sdv_draft_topk": (c_i32, [c_p, c_i64, c_i32, c_i32, c_p, c_p, c_p, c_sz, c_p]),
     "sdv_draft_topk_logits_workspace_size": (c_sz, [c_i64, c_i32, c_i32]),

@@ -67,6 +67,50 @@ def _keep(*_):
     """Holds references until the call returns (workspaces live on the stream)."""
 
 
+# ------------------------------------------------------- status and checks
+
+STATUS_ACCEPT_WAIT, STATUS_ATTN_MERGE_WAIT, STATUS_TOPK_MERGE_WAIT, STATUS_TLI_REUSE = 1, 2, 4, 8
+
+
+def _ws_status(ws: torch.Tensor, stream: int, reset: bool) -> int:
+    st = ctypes.c_uint32(0)
+    nbytes = ws.numel() * ws.element_size()
+    _check(_lib.lib().sdv_workspace_status(_ptr(ws, name="ws"), nbytes, ctypes.byref(st), int(bool(reset)),
+                                           stream), "sdv_workspace_status")
+    return int(st.value)
+
+
+def sdv_workspace_status(ws: torch.Tensor, reset: bool = True) -> int:
+    """Status bits of a workspace (synchronises its device's current stream);
+    with ``reset`` a non-zero status zero-fills the workspace again."""
+    return _ws_status(ws, _stream(ws.device), reset)
+
+
+def device_status(device=None, reset: bool = True) -> int:
+    """OR of the status words of the workspaces this binding keeps for
+    ``device`` (on the stream each belongs to); reset as in
+    ``sdv_workspace_status``."""
+    dev = torch.device(device if device is not None else "cuda")
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    bits = 0
+    for cache in (_TOPK_WS, _ATTN_WS, _ACC_WS):
+        for (d, stream), ws in list(cache.items()):
+            if d == idx:
+                bits |= _ws_status(ws, stream, reset)
+    return bits
+
+
+def sdv_set_wait_limit(polls: int) -> int:
+    """Process-wide poll limit of the bounded waits (0xFFFFFFFF: library
+    default; 0: give up at once).  Returns the previous setting."""
+    return int(_lib.lib().sdv_set_wait_limit(int(polls) & 0xFFFFFFFF))
+
+
+def sdv_tli_check(topk: int, num_steps: int, num_draft_tokens: int) -> None:
+    """Raises SdvError unless topk == 1 and num_draft_tokens == num_steps + 1."""
+    _check(_lib.lib().sdv_tli_check(int(topk), int(num_steps), int(num_draft_tokens)), "sdv_tli_check")
+
+
 # ---------------------------------------------------------------------- A1
 
 _TOPK_WS = {}
@@ -465,6 +509,9 @@ def sdv_tli_constrain_draft_logits(pruned, inter_ids, V_draft: int, full=None):
 
 def sdv_tli_q_scatter(q_pruned, tgt_ids, V_target: int, q_target=None, ws=None):
     """tgt_ids None: reuse the inverse an earlier call left in ``ws``."""
+    if tgt_ids is None and ws is None:
+        raise ValueError("sdv_tli_q_scatter: tgt_ids=None reuses a workspace; pass the workspace of the call "
+                         "that built the map")
     K = q_pruned.shape[-1]
     rows = q_pruned.numel() // K
     dev = q_pruned.device

@@ -35,7 +35,9 @@
 // Partial words form a ring of two per request: a workgroup only publishes
 // exchange n+2 after every workgroup has published exchange n+1, which each
 // does only after reading exchange n.  Every poll is bounded; on timeout the
-// kernel records an error flag and carries on, so every wave always exits.
+// kernel sets SDV_STATUS_ACCEPT_WAIT in the workspace header and carries on
+// with fill values, so every wave always exits (the outputs of that call are
+// then unspecified, and the workspace must be reset before its next use).
 // The words start at zero and every call leaves them zero: when a
 // workgroup has read its last word it bumps the request's counter, and the
 // group's last workgroup clears the request's words and the counter, so no
@@ -54,18 +56,19 @@ constexpr int kAccWaves = kAccThreads / kWave;
 constexpr int kMaxGroup = 64;          // workgroups per request
 constexpr int kMaxE = 64;              // floats per thread per row slice
 constexpr int kMaxLevels = 256;        // rejections at one node (children of one node)
-constexpr unsigned kSpinLimit = 1u << 22;
+constexpr unsigned kSpinLimit = 1u << 22;    // polls of one exchange word before giving up
 
 struct AcceptArgs {
   int B, N, S, V, R, mode, eos;
   int W, b0;                           // group size, first request of this launch
+  unsigned wait_limit;                 // polls per exchange word before giving up
   const int *remaining;
   const int *tokens, *next_token, *next_sibling, *q_row;
   const float *target, *draft, *u_accept, *u_draw;
   int *accept_len, *accept_path, *commit_tokens, *commit_len, *next_root;
   unsigned long long *part;            // [B][2][kMaxGroup] tagged partials (zero at the start, left zero)
   unsigned *done;                      // [B] workgroups of the request that have finished
-  unsigned *err;                       // [1] timeout flag
+  unsigned *status;                    // workspace header status word
 };
 
 // Tagged partial words.
@@ -110,19 +113,17 @@ __device__ __forceinline__ unsigned long long load_part(unsigned long long *p) {
 // other lanes return `fill`.
 template <bool MASS>
 __device__ __forceinline__ unsigned long long await_part(unsigned long long *slot, int W, unsigned tag,
-                                                         unsigned long long fill, unsigned *err) {
+                                                         unsigned long long fill, unsigned limit,
+                                                         unsigned *status) {
   const int x = lane_id();
   if (x >= W) return fill;
-  unsigned spins = 0;
-  for (;;) {
+  for (unsigned spins = 0; spins < limit; ++spins) {
     const unsigned long long w = load_part(slot + x);
     if (MASS ? mass_tag_is(w, tag) : best_tag_is(w, tag)) return w;
     __builtin_amdgcn_s_sleep(1);
-    if (++spins > kSpinLimit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return fill;
-    }
   }
+  raise_status(status, SDV_STATUS_ACCEPT_WAIT);
+  return fill;
 }
 
 // ------------------------------------------------------------ block reductions
@@ -347,7 +348,8 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
     unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
     ++gen;
     if (tid == 0) store_part(slot + c, pack_best(v, i, gen));
-    const unsigned long long w = await_part<false>(slot, a.W, gen, pack_best(-INFINITY, INT_MAX, gen), a.err);
+    const unsigned long long w =
+        await_part<false>(slot, a.W, gen, pack_best(-INFINITY, INT_MAX, gen), a.wait_limit, a.status);
     float gv = unpack_v(w);
     int gi = unpack_i(w);
     wave_best(gv, gi);
@@ -359,7 +361,7 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
     unsigned long long *slot = ring + (gen & 1) * kMaxGroup;
     ++gen;
     if (tid == 0) store_part(slot + c, pack_mass(m, gen));
-    lane_mass = unpack_mass(await_part<true>(slot, a.W, gen, pack_mass(0, gen), a.err));
+    lane_mass = unpack_mass(await_part<true>(slot, a.W, gen, pack_mass(0, gen), a.wait_limit, a.status));
     return wave_sum_u64(lane_mass);
   };
 
@@ -667,7 +669,8 @@ using namespace sdv;
 extern "C" size_t sdv_verify_accept_workspace_size(sdv_accept_shape sh) {
   if (sh.B <= 0) return 0;
   Carver c(nullptr);
-  c.take<unsigned long long>(static_cast<size_t>(sh.B) * 2 * kMaxGroup + 1);
+  c.take<char>(kWsHeaderBytes);
+  c.take<unsigned long long>(static_cast<size_t>(sh.B) * 2 * kMaxGroup);
   c.take<unsigned>(static_cast<size_t>(sh.B));
   return c.bytes();
 }
@@ -704,8 +707,8 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
   if (rc != SDV_OK) return rc;
 
   Carver cv(ws);
-  const size_t words = static_cast<size_t>(sh.B) * 2 * kMaxGroup + 1;
-  unsigned long long *part = cv.take<unsigned long long>(words);
+  unsigned *header = reinterpret_cast<unsigned *>(cv.take<char>(kWsHeaderBytes));
+  unsigned long long *part = cv.take<unsigned long long>(static_cast<size_t>(sh.B) * 2 * kMaxGroup);
   unsigned *done = cv.take<unsigned>(static_cast<size_t>(sh.B));
   hipStream_t st = as_stream(stream);
 
@@ -719,7 +722,8 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
   a.commit_len = commit_len; a.next_root = next_root;
   a.part = part;
   a.done = done;
-  a.err = reinterpret_cast<unsigned *>(part + words - 1);
+  a.status = header + kWsStatus;
+  a.wait_limit = wait_limit(kSpinLimit);
   const void *fn = accept_kernel_for(p.E, sh.mode == SDV_ACCEPT_STOCHASTIC, vec);
   for (int b0 = 0; b0 < sh.B; b0 += p.per_launch) {
     a.b0 = b0;

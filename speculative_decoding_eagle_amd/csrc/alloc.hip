@@ -186,6 +186,7 @@ alloc_branches_kernel(int capacity, int B, int P, int topk, int S, int maxpb, co
     const int q = seq_len[b] % P + i;
     out_loc[x] = free_ids[top - 1 - (s_off[b] + j * pb + q / P)] * P + q % P;
   }
+  __syncthreads();                      // every thread has read the old top
   if (tid == 0) state[kTop] = top - total;
 }
 

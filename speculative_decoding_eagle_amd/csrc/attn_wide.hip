@@ -31,7 +31,9 @@
 //   * The merge protocol: each chunk takes a ticket (an atomic counter per
 //     unit); the first publishes its (m, l, O) in the workspace and bumps a
 //     second counter; the last waits for it (bounded), merges, writes the
-//     output and resets both counters to zero for the next call.
+//     output and resets both counters to zero for the next call.  A wait
+//     that gives up writes NaN rows and sets SDV_STATUS_ATTN_MERGE_WAIT in
+//     the workspace header (the counters must then be reset by the host).
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -67,7 +69,8 @@ tree_attn_wide_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, 
                       const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
                       const int *__restrict__ table, const int *__restrict__ prefix_len,
                       const uint32_t *__restrict__ mask_bits, uint16_t *__restrict__ out, float *__restrict__ lse,
-                      unsigned *__restrict__ sync, char *__restrict__ parts) {
+                      unsigned *__restrict__ sync, char *__restrict__ parts, unsigned *__restrict__ status,
+                      unsigned wait_limit) {
   using C = WideCfg<D>;
   constexpr int RB = C::RB, KB = C::KB, DS = C::DS, NO = C::NO, IPW = C::IPW;
   constexpr int ROW = C::ROW, TILE = C::TILE_BYTES;
@@ -547,15 +550,15 @@ tree_attn_wide_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, 
     }
     // last: wait for the other chunk, then reset both counters for the next call
     if (tid == 0) {
-      unsigned spins = 0;
-      int ok = 1;
-      while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 < static_cast<unsigned>(nch)) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kMergeSpin) {
-          ok = 0;
+      int ok = 0;
+      for (unsigned spins = 0; spins < wait_limit; ++spins) {
+        if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 >= static_cast<unsigned>(nch)) {
+          ok = 1;
           break;
         }
+        __builtin_amdgcn_s_sleep(2);
       }
+      if (!ok) raise_status(status, SDV_STATUS_ATTN_MERGE_WAIT);
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -616,7 +619,7 @@ template <int D, bool BIG>
 int32_t launch_wide(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb,
                     int nch, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                     const int32_t *page_table, const int32_t *prefix_len, const uint32_t *mask_bits, uint16_t *out,
-                    float *lse, unsigned *sync, char *parts) {
+                    float *lse, unsigned *sync, char *parts, unsigned *status) {
   const size_t lds = WideCfg<D>::SMEM;
   static thread_local int configured_dev = -1;
   int dev = 0;
@@ -629,7 +632,8 @@ int32_t launch_wide(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, in
   }
   hipLaunchKernelGGL((tree_attn_wide_kernel<D, BIG>), dim3(static_cast<unsigned>(blocks)), dim3(kAttnThreads), lds, st,
                      sh.B, sh.N, sh.Hq, sh.Hkv, pshift, sh.max_pages, sh.num_slots, scale_log2, nrb, nch,
-                     q, k_pool, v_pool, page_table, prefix_len, mask_bits, out, lse, sync, parts);
+                     q, k_pool, v_pool, page_table, prefix_len, mask_bits, out, lse, sync, parts, status,
+                     wait_limit(kMergeSpin));
   return check_launch("tree_attn_wide_kernel");
 }
 
@@ -638,6 +642,7 @@ int32_t launch_wide(int64_t blocks, hipStream_t st, const sdv_attn_shape &sh, in
 size_t attn_wide_workspace(int64_t slots, int D) {
   if (2 * slots > kAttnSyncWords) return 0;          // the key split is not offered for this many units
   Carver c(nullptr);
+  c.take<char>(kWsHeaderBytes);
   c.take<unsigned>(kAttnSyncWords);
   c.take<char>(static_cast<size_t>(slots) * (D == 64 ? WideCfg<64>::PART : WideCfg<128>::PART));
   return c.bytes();
@@ -651,17 +656,18 @@ int32_t launch_attn_wide(hipStream_t st, const sdv_attn_shape &sh, int pshift, f
   const int64_t units_pad = (units + kXcds - 1) / kXcds * kXcds;
   const int64_t blocks = units_pad * nrb * nch;
   SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tree_verify_attention: grid too large");
-  unsigned *sync = nullptr;
+  unsigned *sync = nullptr, *status = nullptr;
   char *parts = nullptr;
   if (nch > 1) {
     Carver c(ws);
+    status = reinterpret_cast<unsigned *>(c.take<char>(kWsHeaderBytes)) + kWsStatus;
     sync = c.take<unsigned>(kAttnSyncWords);
     parts = c.take<char>(static_cast<size_t>(units * nrb) * (sh.D == 64 ? WideCfg<64>::PART : WideCfg<128>::PART));
   }
   const bool big = static_cast<uint64_t>(sh.num_slots) * sh.Hkv * sh.D * 2 >= (1ull << 32);
 #define SDV_WIDE(DD, BB)                                                                                       \
   launch_wide<DD, BB>(blocks, st, sh, pshift, scale_log2, nrb, nch, q, k_pool, v_pool, page_table, prefix_len, \
-                      mask_bits, out, lse, sync, parts)
+                      mask_bits, out, lse, sync, parts, status)
   if (sh.D == 64) return big ? SDV_WIDE(64, true) : SDV_WIDE(64, false);
   return big ? SDV_WIDE(128, true) : SDV_WIDE(128, false);
 #undef SDV_WIDE

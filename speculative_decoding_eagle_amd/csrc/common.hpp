@@ -44,6 +44,20 @@ struct Carver {
 // Number of compute units of the current device (cached per device).
 int num_cus();
 
+// Workspaces whose kernels wait on one another begin with a 256-byte header;
+// word 0 is the sticky status word (SDV_STATUS_* bits) that
+// sdv_workspace_status reads.  The TLI scatter keeps the (K, V_target) of the
+// call that built its inverse in words 1-3.
+constexpr size_t kWsHeaderBytes = 256;
+constexpr int kWsStatus = 0;
+constexpr int kWsTliK = 1, kWsTliV = 2, kWsTliMagic = 3;
+constexpr unsigned kTliMagic = 0x544C4931u;
+inline unsigned *ws_header(void *ws) { return static_cast<unsigned *>(ws); }
+
+// Polls a bounded wait makes before it gives up: `dflt` unless a test set a
+// limit with sdv_set_wait_limit (0: give up at once, without polling).
+unsigned wait_limit(unsigned dflt);
+
 // The K and V pools of every layer, passed to a kernel by value.
 constexpr int kMaxLayers = 128;
 struct PoolPtrs {
@@ -83,6 +97,12 @@ __device__ __forceinline__ void wave_best(float &v, int &i) {
       i = oi;
     }
   }
+}
+
+// Sets status bits in a workspace header (device scope, relaxed: the word
+// is read by the host after the stream has drained).
+__device__ __forceinline__ void raise_status(unsigned *status, unsigned bits) {
+  __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x) {

@@ -172,14 +172,31 @@ __global__ void constrain_kernel(int B, int K, int Vd, const float *__restrict__
 }
 
 // inv[tgt[j]] = j (target ids outside [0, Vt) are skipped), and a copy of
-// tgt for the chunked scatter of later calls.
+// tgt for the chunked scatter of later calls; the header records K and Vt so
+// that a later call without ids can check it is reusing the same map.
 __global__ void inverse_kernel(int K, const int *__restrict__ tgt, int Vt, int *__restrict__ inv,
-                               int *__restrict__ tcopy) {
+                               int *__restrict__ tcopy, unsigned *__restrict__ hdr) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j == 0) {
+    hdr[kWsStatus] = 0u;                 // a fresh map: no earlier status applies
+    hdr[kWsTliK] = static_cast<unsigned>(K);
+    hdr[kWsTliV] = static_cast<unsigned>(Vt);
+    hdr[kWsTliMagic] = kTliMagic;
+  }
   if (j >= K) return;
   const int t = tgt[j];
   tcopy[j] = t;
   if (t >= 0 && t < Vt) inv[t] = j;
+}
+
+// True when the workspace's inverse was built for this K and Vt; otherwise
+// the call reports SDV_STATUS_TLI_REUSE (once per workgroup) and the caller
+// gets zeros instead of a gather through a foreign map.
+__device__ __forceinline__ bool map_matches(unsigned *hdr, int K, int Vt) {
+  const bool ok = hdr[kWsTliK] == static_cast<unsigned>(K) && hdr[kWsTliV] == static_cast<unsigned>(Vt) &&
+                  hdr[kWsTliMagic] == kTliMagic;
+  if (!ok && threadIdx.x == 0) raise_status(hdr + kWsStatus, SDV_STATUS_TLI_REUSE);
+  return ok;
 }
 
 // Four consecutive target ids per thread (one 16-byte inverse load, one
@@ -191,13 +208,19 @@ __global__ void inverse_kernel(int K, const int *__restrict__ tgt, int Vt, int *
 // 16-byte aligned output.
 __global__ void __launch_bounds__(256)
 q_scatter4_kernel(int64_t rows, int K, int Vt, int nchunks, const float *__restrict__ q,
-                  const int *__restrict__ inv, float *__restrict__ out) {
+                  const int *__restrict__ inv, float *__restrict__ out, unsigned *__restrict__ hdr) {
   const int xcd = blockIdx.x % kXcdCount, slot = blockIdx.x / kXcdCount;
   const int64_t group = static_cast<int64_t>(slot / nchunks) * kXcdCount + xcd;
   const int v = ((slot % nchunks) * 256 + static_cast<int>(threadIdx.x)) * 4;
   const int64_t r0 = group * kRowsPerScatter;
   if (v >= Vt || r0 >= rows) return;
-  const int4 j = *reinterpret_cast<const int4 *>(inv + v);
+  const bool same = map_matches(hdr, K, Vt);
+  int4 j = *reinterpret_cast<const int4 *>(inv + v);
+  const unsigned uk = same ? static_cast<unsigned>(K) : 0u;     // a foreign map: every entry 0
+  j.x = static_cast<unsigned>(j.x) < uk ? j.x : -1;
+  j.y = static_cast<unsigned>(j.y) < uk ? j.y : -1;
+  j.z = static_cast<unsigned>(j.z) < uk ? j.z : -1;
+  j.w = static_cast<unsigned>(j.w) < uk ? j.w : -1;
 #pragma unroll
   for (int rr = 0; rr < kRowsPerScatter; ++rr) {
     const int64_t r = r0 + rr;
@@ -228,7 +251,7 @@ constexpr int kScatterBatch = 8;
 
 __global__ void __launch_bounds__(kScatterThreads)
 q_scatter_chunk_kernel(int64_t rows, int K, int Vt, int nch, const float *__restrict__ q,
-                       const int *__restrict__ tgt, float *__restrict__ out) {
+                       const int *__restrict__ tgt, float *__restrict__ out, unsigned *__restrict__ hdr) {
   extern __shared__ __attribute__((aligned(16))) float s_o[];
   const int xcd = blockIdx.x % kXcdCount, slot = blockIdx.x / kXcdCount;
   const int64_t r = static_cast<int64_t>(slot / nch) * kXcdCount + xcd;
@@ -242,16 +265,17 @@ q_scatter_chunk_kernel(int64_t rows, int K, int Vt, int nch, const float *__rest
   __syncthreads();
   const float *qr = q + r * K;
   const unsigned ub = static_cast<unsigned>(base), un = static_cast<unsigned>(n);
+  const int kk = map_matches(hdr, K, Vt) ? K : 0;             // a foreign map: every entry 0
   // kScatterBatch pairs of 16-byte loads per lane in flight before their
   // LDS writes (one workgroup per CU: the loads must overlap)
   constexpr int kStride = 4 * kScatterThreads;
-  for (int j0 = 4 * tid; j0 < K; j0 += kScatterBatch * kStride) {
+  for (int j0 = 4 * tid; j0 < kk; j0 += kScatterBatch * kStride) {
     int4 t[kScatterBatch];
     float4 v[kScatterBatch];
 #pragma unroll
     for (int u = 0; u < kScatterBatch; ++u) {
       const int j = j0 + u * kStride;
-      if (j < K) {
+      if (j < kk) {
         t[u] = *reinterpret_cast<const int4 *>(tgt + j);
         v[u] = *reinterpret_cast<const float4 *>(qr + j);
       } else {
@@ -274,12 +298,13 @@ q_scatter_chunk_kernel(int64_t rows, int K, int Vt, int nch, const float *__rest
 }
 
 __global__ void q_scatter_kernel(int64_t rows, int K, int Vt, const float *__restrict__ q,
-                                 const int *__restrict__ inv, float *__restrict__ out) {
+                                 const int *__restrict__ inv, float *__restrict__ out, unsigned *__restrict__ hdr) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t r = blockIdx.y;
   if (v >= Vt || r >= rows) return;
   const int j = inv[v];
-  out[r * Vt + v] = j >= 0 ? q[r * K + j] : 0.0f;
+  const unsigned uk = map_matches(hdr, K, Vt) ? static_cast<unsigned>(K) : 0u;
+  out[r * Vt + v] = static_cast<unsigned>(j) < uk ? q[r * K + j] : 0.0f;
 }
 
 inline unsigned nblk(int64_t n, int t) { return static_cast<unsigned>((n + t - 1) / t); }
@@ -365,10 +390,11 @@ extern "C" int32_t sdv_tli_constrain_draft_logits(int32_t B, int32_t K, int32_t 
   return check_launch("constrain_kernel");
 }
 
-// Workspace: the inverse of tgt_ids [V_target], then a copy of tgt_ids (at
-// most V_target entries, since the map is injective).
+// Workspace: the header (status, and the K and V_target of the map), the
+// inverse of tgt_ids [V_target], then a copy of tgt_ids (at most V_target
+// entries, since the map is injective).
 extern "C" size_t sdv_tli_q_scatter_workspace_size(int32_t V_target) {
-  return V_target > 0 ? 2 * align_up(static_cast<size_t>(V_target) * sizeof(int), 256) : 0;
+  return V_target > 0 ? kWsHeaderBytes + 2 * align_up(static_cast<size_t>(V_target) * sizeof(int), 256) : 0;
 }
 
 extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, const float *q_pruned,
@@ -381,14 +407,15 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
   SDV_REQUIRE(q_target && (K == 0 || q_pruned), SDV_E_NULL, "tli_q_scatter: NULL pointer");
   const size_t need = sdv_tli_q_scatter_workspace_size(V_target);
   SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "tli_q_scatter: workspace of %zu bytes needed", need);
-  int *inv = static_cast<int *>(ws);
+  unsigned *hdr = ws_header(ws);
+  int *inv = reinterpret_cast<int *>(static_cast<char *>(ws) + kWsHeaderBytes);
   int *tcopy = inv + align_up(static_cast<size_t>(V_target) * sizeof(int), 256) / sizeof(int);
   hipStream_t st = as_stream(stream);
   if (tgt_ids) {                         // else: the inverse and the copy an earlier call left in ws
     hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(V_target, 256)), dim3(256), 0, st, inv,
                        static_cast<int64_t>(V_target), -1);
-    if (K > 0)
-      hipLaunchKernelGGL(inverse_kernel, dim3(nblk(K, 256)), dim3(256), 0, st, K, tgt_ids, V_target, inv, tcopy);
+    hipLaunchKernelGGL(inverse_kernel, dim3(K > 0 ? nblk(K, 256) : 1), dim3(256), 0, st, K, tgt_ids, V_target, inv,
+                       tcopy, hdr);
   }
   if (V_target % 4 == 0 && K % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0 &&
       reinterpret_cast<uintptr_t>(q_pruned) % 16 == 0) {
@@ -407,7 +434,7 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
     const int64_t blocks = per_xcd * nch * kXcdCount;
     SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tli_q_scatter: grid too large");
     hipLaunchKernelGGL(q_scatter_chunk_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), lds, st,
-                       rows, K, V_target, nch, q_pruned, tcopy, q_target);
+                       rows, K, V_target, nch, q_pruned, tcopy, q_target, hdr);
     return check_launch("q_scatter_chunk_kernel");
   }
   if (V_target % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0) {
@@ -415,10 +442,10 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
     const int64_t groups = nblk(rows, kRowsPerScatter);
     const int64_t per_xcd = (groups + kXcdCount - 1) / kXcdCount;     // row groups per XCD
     hipLaunchKernelGGL(q_scatter4_kernel, dim3(static_cast<unsigned>(per_xcd * nchunks * kXcdCount)), dim3(256), 0,
-                       st, rows, K, V_target, nchunks, q_pruned, inv, q_target);
+                       st, rows, K, V_target, nchunks, q_pruned, inv, q_target, hdr);
     return check_launch("q_scatter4_kernel");
   }
   hipLaunchKernelGGL(q_scatter_kernel, dim3(nblk(V_target, 256), static_cast<unsigned>(rows)), dim3(256), 0, st,
-                     rows, K, V_target, q_pruned, inv, q_target);
+                     rows, K, V_target, q_pruned, inv, q_target, hdr);
   return check_launch("q_scatter_kernel");
 }

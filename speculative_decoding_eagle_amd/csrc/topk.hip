@@ -293,19 +293,16 @@ __device__ __forceinline__ unsigned long long pack_norm(float m, float s) {
 __device__ __forceinline__ void put_word(unsigned long long *p, unsigned long long w) {
   __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// The word at p once its writer's store is visible (bounded wait; late is
-// set if it never became so).
-__device__ __forceinline__ unsigned long long await_word(unsigned long long *p, bool &late) {
-  unsigned long long w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (unsigned spins = 0; w == 0ull; ++spins) {
-    if (spins >= kTopkSpin) {
-      late = true;
-      break;
-    }
+// The word at p once its writer's store is visible (at most `limit` polls;
+// late is set if it never became so, and the word then reads as 0).
+__device__ __forceinline__ unsigned long long await_word(unsigned long long *p, unsigned limit, bool &late) {
+  for (unsigned spins = 0; spins < limit; ++spins) {
+    const unsigned long long w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (w != 0ull) return w;
     __builtin_amdgcn_s_sleep(1);
-    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  return w;
+  late = true;
+  return 0ull;
 }
 
 // The K best of n (value, id) pairs, best first, into lanes 0 .. K-1 (other
@@ -353,13 +350,16 @@ __device__ __forceinline__ void wave_best_k(int n, Get &&get, float &bv, int &bi
 // segment that counts last merges the lists as their words land (the K
 // best under the strict order do not depend on the merge order;
 // normalisers are merged in segment order) and sets the words and the
-// counter back to zero.  IN: what the rows hold (above).
+// counter back to zero.  A wait that gives up (after wait_limit polls)
+// writes NaN / -1 for the row and sets SDV_STATUS_TOPK_MERGE_WAIT in the
+// workspace header.  IN: what the rows hold (above).
 template <int K, int IN>
 __global__ void __launch_bounds__(kTopkThreads)
 topk_kernel(const void *__restrict__ rows_in, int64_t rows, int V, int64_t nwhole, int64_t per, int maxseg, int k,
             bool vec,
             float c2, float *__restrict__ out_v, int *__restrict__ out_i, unsigned *__restrict__ cnt,
-            unsigned long long *__restrict__ part, unsigned long long *__restrict__ part_n) {
+            unsigned long long *__restrict__ part, unsigned long long *__restrict__ part_n,
+            unsigned *__restrict__ status, unsigned wait_limit) {
   constexpr int NW = kTopkThreads / kWave;
   constexpr bool LOGITS = IN != kInProbs;
   constexpr int EPL = IN == kInLogitsBf16 ? 8 : 4;          // elements per 16-byte load
@@ -558,14 +558,14 @@ topk_kernel(const void *__restrict__ rows_in, int64_t rows, int V, int64_t nwhol
           // and the counter back to zero for the next call
           unsigned long long *words = part + s0 * K;
           wave_best_k<K>(nseg * K, [&](int c, float &v, int &i) {
-            const unsigned long long wd = await_word(words + c, late);
+            const unsigned long long wd = await_word(words + c, wait_limit, late);
             v = __uint_as_float(static_cast<unsigned>(wd >> 32));
             i = static_cast<int>(static_cast<unsigned>(wd) - 1u);
           }, bv, bi);
           if constexpr (LOGITS) {
             tot = Norm();
             for (int j = 0; j < nseg; ++j) {
-              const unsigned long long wd = await_word(part_n + s0 + j, late);
+              const unsigned long long wd = await_word(part_n + s0 + j, wait_limit, late);
               tot.merge(__uint_as_float(static_cast<unsigned>(wd >> 32)), __uint_as_float(static_cast<unsigned>(wd)),
                         c2);
             }
@@ -575,6 +575,7 @@ topk_kernel(const void *__restrict__ rows_in, int64_t rows, int V, int64_t nwhol
             for (int j = x; j < nseg; j += kWave) put_word(part_n + s0 + j, 0ull);
           if (x == 0) __hip_atomic_store(cnt + trow, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           late = __any(late);
+          if (late && x == 0) raise_status(status, SDV_STATUS_TOPK_MERGE_WAIT);
           emit = true;
         }
       }
@@ -659,6 +660,7 @@ size_t topk_workspace(int64_t rows, int V, int k, bool logits) {
   const TopkPlan p = plan_topk(rows, V, k);
   if (p.per == 0) return 0;
   Carver c(nullptr);
+  c.take<char>(kWsHeaderBytes);
   c.take<unsigned>(kTopkRowsMax);
   c.take<unsigned long long>(static_cast<size_t>(p.cut) * p.maxseg * p.K);
   if (logits) c.take<unsigned long long>(static_cast<size_t>(p.cut) * p.maxseg);
@@ -668,9 +670,10 @@ size_t topk_workspace(int64_t rows, int V, int k, bool logits) {
 template <int K, int IN>
 int32_t launch_topk(const void *rows_in, int64_t rows, int V, int k, const TopkPlan &p, bool vec, float c2,
                     float *out_v, int *out_i, unsigned *cnt, unsigned long long *part,
-                    unsigned long long *part_n, hipStream_t st) {
+                    unsigned long long *part_n, unsigned *status, hipStream_t st) {
   hipLaunchKernelGGL((topk_kernel<K, IN>), dim3(static_cast<unsigned>(p.blocks)), dim3(kTopkThreads), 0, st,
-                     rows_in, rows, V, p.nwhole, p.per, p.maxseg, k, vec, c2, out_v, out_i, cnt, part, part_n);
+                     rows_in, rows, V, p.nwhole, p.per, p.maxseg, k, vec, c2, out_v, out_i, cnt, part, part_n,
+                     status, wait_limit(kTopkSpin));
   return check_launch("topk_kernel");
 }
 
@@ -689,10 +692,11 @@ int32_t run_topk(const char *what, int IN, const void *rows_in, int64_t rows, in
   const size_t need = topk_workspace(rows, V, k, IN != kInProbs);
   SDV_REQUIRE(ws_bytes >= need && (need == 0 || ws), SDV_E_WORKSPACE, "%s: workspace of %zu bytes needed", what,
               need);
-  unsigned *cnt = nullptr;
+  unsigned *cnt = nullptr, *status = nullptr;
   unsigned long long *part = nullptr, *part_n = nullptr;
   if (p.per > 0) {
     Carver c(ws);
+    status = reinterpret_cast<unsigned *>(c.take<char>(kWsHeaderBytes)) + kWsStatus;
     cnt = c.take<unsigned>(kTopkRowsMax);
     part = c.take<unsigned long long>(static_cast<size_t>(p.cut) * p.maxseg * p.K);
     if (IN != kInProbs) part_n = c.take<unsigned long long>(static_cast<size_t>(p.cut) * p.maxseg);
@@ -702,11 +706,11 @@ int32_t run_topk(const char *what, int IN, const void *rows_in, int64_t rows, in
   hipStream_t st = as_stream(stream);
 #define SDV_TOPK_IN(KK)                                                                                          \
   (IN == kInProbs        ? launch_topk<KK, kInProbs>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, cnt, part, \
-                                                     part_n, st)                                         \
+                                                     part_n, status, st)                                         \
    : IN == kInLogitsF32 ? launch_topk<KK, kInLogitsF32>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, cnt, part, \
-                                                         part_n, st)                                     \
+                                                         part_n, status, st)                                     \
                          : launch_topk<KK, kInLogitsBf16>(rows_in, rows, V, k, p, vec, c2, topk_p, topk_id, cnt, part, \
-                                                          part_n, st))
+                                                          part_n, status, st))
   switch (p.K) {
     case 1: return SDV_TOPK_IN(1);
     case 2: return SDV_TOPK_IN(2);

@@ -22,7 +22,8 @@ def test_header_declares_the_entry_points():
                  "sdv_compact_kv", "sdv_tli_lm_head", "sdv_tli_map_ids", "sdv_tli_constrain_draft_logits",
                  "sdv_tli_q_scatter", "sdv_tli_build_maps", "sdv_draft_extend_prep", "sdv_build_chain", "sdv_kv_alloc_init",
                  "sdv_kv_alloc_backup", "sdv_kv_alloc_restore", "sdv_kv_alloc_free", "sdv_kv_alloc_extend",
-                 "sdv_kv_alloc_branches", "sdv_kv_branch_pages", "sdv_last_error"):
+                 "sdv_kv_alloc_branches", "sdv_kv_branch_pages", "sdv_last_error", "sdv_workspace_status",
+                 "sdv_set_wait_limit", "sdv_tli_check"):
         assert must in names
 
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_symbols():
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
-    assert lib.sdv_version() == 100
+    assert lib.sdv_version() == 101
     assert lib.sdv_last_error() == b""
 
 
@@ -61,3 +62,31 @@ def test_host_side_validation_without_a_device():
     acc = _lib.AcceptShape(1, 4, 3, 100, 4, 7)                                        # unknown mode
     assert lib.sdv_verify_accept(acc, -1, *([None] * 14), None, 0, None) == -2
     assert lib.sdv_tli_lm_head(4, 100, 8, None, None, None, None) == -3               # H % 32 != 0
+
+
+def test_tli_check_enforces_the_pages_validation_rules():
+    """sglang PR #22883, "Modified files": TLI needs topk == 1 and
+    num_draft_tokens == num_steps + 1; anything else is SDV_E_UNSUPPORTED."""
+    from speculative_decoding_eagle_amd import _lib
+    lib = _lib.lib()
+    assert lib.sdv_tli_check(1, 4, 5) == 0
+    assert lib.sdv_tli_check(1, 1, 2) == 0
+    for k, S, N in [(8, 5, 64), (2, 4, 5), (1, 4, 4), (1, 4, 6), (1, 0, 1), (0, 4, 5)]:
+        assert lib.sdv_tli_check(k, S, N) == -3, (k, S, N)
+        assert b"TLI" in lib.sdv_last_error()
+    import speculative_decoding_eagle_amd as sdv
+    with pytest.raises(sdv.SdvError):
+        sdv.sdv_tli_check(2, 4, 5)
+
+
+def test_status_call_and_wait_limit_on_the_host():
+    """Without a workspace the status is 0 and nothing touches a device; the
+    wait limit is a host setting that round-trips."""
+    from speculative_decoding_eagle_amd import _lib
+    lib = _lib.lib()
+    st = ctypes.c_uint32(7)
+    assert lib.sdv_workspace_status(None, 0, ctypes.byref(st), 1, None) == 0 and st.value == 0
+    assert lib.sdv_workspace_status(None, 4096, None, 1, None) == -1
+    prev = lib.sdv_set_wait_limit(0)
+    assert prev == 0xFFFFFFFF
+    assert lib.sdv_set_wait_limit(0xFFFFFFFF) == 0

@@ -479,7 +479,7 @@ def _alloc_pair(capacity):
     return g, o
 
 
-@pytest.mark.parametrize("B,topk,S", [(5, 4, 3), (1, 1, 1), (300, 8, 5)])
+@pytest.mark.parametrize("B,topk,S", [(5, 4, 3), (1, 1, 1), (300, 8, 5), (8191, 2, 3), (8192, 1, 1)])
 def test_kv_alloc_page1_draft_and_rollback(B, topk, S):
     cap = B * topk * S + 77
     g, o = _alloc_pair(cap)
@@ -751,20 +751,59 @@ def test_attention_paged_small():
     _attn_case(cfg, workloads.generate(cfg))
 
 
+def _attn_gpu(cfg, inp, t, split_keys):
+    say("attention", cfg.name, cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.page, "split" if split_keys else "whole")
+    out, lse = sdv.sdv_tree_verify_attention(dev(inp["q"]), dev(inp["k_pool"]), dev(inp["v_pool"]),
+                                             dev(inp["page_table"]), dev(inp["prefix_len"]),
+                                             dev(t["mask_bits"].view(np.int32)), page=cfg.page, want_lse=True,
+                                             split_keys=split_keys)
+    torch.cuda.synchronize()
+    return bf16_to_f64(out), host(lse)
+
+
 @pytest.mark.parametrize("name", ["c3", "c4"])
-def test_attention_full_config_sampled(name):
+def test_attention_full_config_every_request(name):
+    """The workloads' own shapes, every request (c3: 32 units of 256 rows with
+    the longest-first ranking, the XCD dealing and the key split; c4: 64
+    requests of 514 pages at most), with and without the key split."""
     cfg = workloads.get_config(name, V=256)
     inp = workloads.generate(cfg)
-    _attn_case(cfg, inp, requests=[0, cfg.B // 2, cfg.B - 1])
+    t = oracle_tree(inp, cfg)
+    ro, rl = oatt.tree_verify_attention(inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                                        inp["prefix_len"], t["mask"], page=cfg.page)
+    for split in (True, False):
+        got, lse = _attn_gpu(cfg, inp, t, split)
+        assert_attention_close(got, ro)
+        assert np.abs(lse - rl).max() < 4e-3
 
 
-def test_attention_c3_whole_units_sampled():
-    """c3 without the key split: one workgroup streams all of a unit's keys
-    (the longest prefixes also cross a page-window refresh)."""
+def test_attention_c3_tree_keys_carry_the_output():
+    """c3's shape with every prefix V row zero: each output row is then made of
+    its node's own visible tree keys only (depth + 1 of them), so a single wrong
+    mask bit moves that row by a large fraction of itself.  Checked row by row
+    (relative to the row's norm) on every request, split and unsplit."""
     cfg = workloads.get_config("c3", V=256)
     inp = workloads.generate(cfg)
-    L = inp["prefix_len"]
-    _attn_case(cfg, inp, requests=[int(np.argmax(L)), int(np.argmin(L)), 7], split_keys=False)
+    t = oracle_tree(inp, cfg)
+    keep = np.zeros(inp["v_pool"].shape[0], bool)
+    for b in range(cfg.B):
+        L = int(inp["prefix_len"][b])
+        keep[oatt.slot_of(inp["page_table"], b, np.arange(L, L + cfg.N), cfg.page)] = True
+    v = inp["v_pool"].copy()
+    v[~keep] = 0
+    inp = dict(inp, v_pool=v)
+    ro, _ = oatt.tree_verify_attention(inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                                       inp["prefix_len"], t["mask"], page=cfg.page)
+    ref_rows = ro.reshape(-1, cfg.D)
+    nrm = np.linalg.norm(ref_rows, axis=1)
+    assert nrm.min() > 0
+    for split in (True, False):
+        got, _ = _attn_gpu(cfg, inp, t, split)
+        assert_attention_close(got, ro)
+        rel = np.linalg.norm(got.reshape(-1, cfg.D) - ref_rows, axis=1) / nrm
+        # bf16 weights and output: a few 2^-9 relative per row; one wrong
+        # mask bit moves a row by about 1 / sqrt(depth + 1) of itself
+        assert rel.max() < 3e-2, "row %d off by %.3g of its norm" % (int(np.argmax(rel)), rel.max())
 
 
 # More than 128 query rows per (request, KV head): the wide kernel, with and
@@ -807,7 +846,7 @@ def test_attention_wide_split_is_deterministic_and_resets_workspace():
     from speculative_decoding_eagle_amd import binding
     key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
     ws = binding._ATTN_WS[key]
-    assert not host(ws[: 32768]).any(), "counters not reset"
+    assert not host(ws[: 256 + 32768]).any(), "status or counters not reset"
 
 
 # ------------------------------------------------------------------- A9-A10
@@ -875,6 +914,21 @@ def test_tli_constrain_and_scatter_shapes(Vd, Vt, K, rows):
     torch.cuda.synchronize()
     assert np.array_equal(host(g1), otli.q_scatter(q1, tgt, Vt))
     assert np.array_equal(host(g2), otli.q_scatter(q2, tgt, Vt))
+    assert sdv.sdv_workspace_status(ws) == 0
+    # a reuse call whose K differs from the map's: zeros and a status bit,
+    # never a gather past the row
+    if K > 4:
+        g3 = sdv.sdv_tli_q_scatter(dev(q2[:, :K - 4].copy()), None, Vt, ws=ws)
+        torch.cuda.synchronize()
+        assert (host(g3) == 0).all()
+        assert sdv.sdv_workspace_status(ws, reset=True) == sdv.STATUS_TLI_REUSE
+        assert sdv.sdv_workspace_status(ws) == 0
+        g4 = sdv.sdv_tli_q_scatter(dev(q2), None, Vt, ws=ws)          # the reset wiped the map too
+        torch.cuda.synchronize()
+        assert (host(g4) == 0).all() and sdv.sdv_workspace_status(ws, reset=True) == sdv.STATUS_TLI_REUSE
+        g5 = sdv.sdv_tli_q_scatter(dev(q2), dev(tgt), Vt, ws=ws)       # rebuilt
+        torch.cuda.synchronize()
+        assert np.array_equal(host(g5), otli.q_scatter(q2, tgt, Vt)) and sdv.sdv_workspace_status(ws) == 0
 
 
 @pytest.mark.parametrize("B,H,K", [(64, 896, 60000), (5, 64, 1000), (17, 96, 77), (130, 32, 513)])
@@ -971,3 +1025,56 @@ def test_single_node_trees_through_every_stage(mode):
                                              o["accept_len"], o["accept_path"], cfg.N, cfg.page)
     assert np.array_equal(host(gt), ot) and np.array_equal(host(new_len), onew)
     assert int(host(num_freed)[0]) == len(ofreed)
+
+
+# ------------------------------------------------------- device status
+
+def test_status_reports_given_up_waits_and_reset_restores():
+    """With the wait limit at 0 every bounded wait between workgroups gives
+    up at once (every kernel still exits normally): the top-k piece merge,
+    the attention key-split merge and the accept walk's exchanges.  Their
+    status bits appear in the workspaces, a reset clears them, and with the
+    library's limit the same workspaces give the oracle's results again."""
+    rng = np.random.default_rng(4242)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    rows, V = ncu + 5, 20000                      # rows = CUs + 5: five rows cut into pieces
+    p = workloads.softmax_rows(rng.standard_normal((rows, V)).astype(np.float32) * 3)
+    cfg = workloads.get_config("c3", B=4)
+    inp = workloads.generate(cfg)
+    t = oracle_tree(inp, cfg)
+    accept_tree = {k: dev(t[k]) for k in ("tokens", "next_token", "next_sibling")}
+    bits_dev = dev(t["mask_bits"].view(np.int32))
+
+    def run_all():
+        tk = sdv.sdv_draft_topk(dev(p), 8)
+        att = sdv.sdv_tree_verify_attention(dev(inp["q"]), dev(inp["k_pool"]), dev(inp["v_pool"]),
+                                            dev(inp["page_table"]), dev(inp["prefix_len"]),
+                                            bits_dev, page=cfg.page)[0]
+        acc = sdv.sdv_verify_accept(sdv.GREEDY, accept_tree, dev(inp["target"]), cfg.S)
+        torch.cuda.synchronize()
+        return tk, att, acc
+
+    sdv.device_status(reset=True)
+    say("status: wait limit 0")
+    prev = sdv.sdv_set_wait_limit(0)
+    try:
+        run_all()
+    finally:
+        sdv.sdv_set_wait_limit(prev)
+    bits = sdv.device_status(reset=False)
+    assert bits & sdv.STATUS_TOPK_MERGE_WAIT
+    assert bits & sdv.STATUS_ATTN_MERGE_WAIT
+    assert bits & sdv.STATUS_ACCEPT_WAIT
+    assert sdv.device_status(reset=True) == bits
+    assert sdv.device_status(reset=False) == 0
+    say("status: library limit, after the reset")
+    (gp, gi), att, acc = run_all()
+    assert sdv.device_status(reset=False) == 0
+    op, oi = otopk.draft_topk(p, 8)
+    assert np.array_equal(host(gi), oi) and np.array_equal(host(gp), op)
+    ref, _ = oatt.tree_verify_attention(inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                                        inp["prefix_len"], t["mask"], cfg.page)
+    assert_attention_close(bf16_to_f64(att), ref)
+    want = oacc.verify_greedy(t, inp["target"], S=cfg.S)
+    for key in want:
+        assert np.array_equal(host(acc[key]), want[key]), key
