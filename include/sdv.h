@@ -316,6 +316,27 @@ int32_t sdv_verify_accept(sdv_accept_shape shape, int32_t eos_id, const int32_t 
                           void *stream);
 
 /* ------------------------------------------------------------------------
+ * The accept walk for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, semantics and outputs as sdv_verify_accept, without the
+ * workspace: the exchange words of up to 1024 requests live in a static
+ * device array of the library (1,052,928 bytes per device, held until the
+ * process ends).  Each call zero-fills the part it uses with a kernel on
+ * `stream` (no memset node) before the walk, so it calls no allocator and no
+ * hipMemset.  B > 1024 returns SDV_E_UNSUPPORTED.  Every call on one device
+ * shares that array: calls that may overlap on one device (different
+ * streams, host threads) race and must be serialised by the caller.  The
+ * status word of a wait that gave up is cleared by the next call; callers
+ * that need it use sdv_verify_accept with their own workspace.
+ * ---------------------------------------------------------------------- */
+int32_t sdv_verify_accept_noalloc(sdv_accept_shape shape, int32_t eos_id, const int32_t *remaining,
+                                  const int32_t *tokens, const int32_t *next_token,
+                                  const int32_t *next_sibling, const int32_t *q_row, const float *target,
+                                  const float *draft_probs, const float *u_accept, const float *u_draw,
+                                  int32_t *accept_len, int32_t *accept_path, int32_t *commit_tokens,
+                                  int32_t *commit_len, int32_t *next_root, void *stream);
+
+/* ------------------------------------------------------------------------
  * A8  KV compaction of the accepted path and release of the rest.
  * "EAGLE speculative decoding in four parts": slots for every candidate are
  * reserved before drafting; after verification only the accepted path's

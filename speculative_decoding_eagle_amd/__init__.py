@@ -40,4 +40,5 @@ from .binding import (  # noqa: F401
     sdv_tli_q_scatter,
     sdv_tree_verify_attention,
     sdv_verify_accept,
+    sdv_verify_accept_noalloc,
 )

@@ -55,6 +55,7 @@ SIGNATURES = {
     "sdv_tree_verify_attention": (c_i32, [AttnShape, c_f32] + [c_p] * 8 + [c_p, c_sz, c_p]),
     "sdv_verify_accept_workspace_size": (c_sz, [AcceptShape]),
     "sdv_verify_accept": (c_i32, [AcceptShape, c_i32] + [c_p] * 14 + [c_p, c_sz, c_p]),
+    "sdv_verify_accept_noalloc": (c_i32, [AcceptShape, c_i32] + [c_p] * 14 + [c_p]),
     "sdv_compact_kv_workspace_size": (c_sz, [KVShape]),
     "sdv_compact_kv": (c_i32, [KVShape] + [c_p] * 9 + [c_p, c_sz, c_p]),
     "sdv_tli_lm_head": (c_i32, [c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),

@@ -315,6 +315,30 @@ def sdv_verify_accept(mode: int, tree, target, S: int, eos_id: int = -1, remaini
     return out
 
 
+def sdv_verify_accept_noalloc(mode: int, tree, target, S: int, eos_id: int = -1, remaining=None,
+                              draft_probs=None, u_accept=None, u_draw=None, out=None):
+    """The accept walk without a workspace (the library's static scratch, at
+    most 1024 requests).  Outputs must be passed in ``out`` (this entry point
+    is for callers that allocate nothing); returns ``out``."""
+    tokens = tree["tokens"]
+    B, N = tokens.shape
+    V = target.shape[-1]
+    R = draft_probs.shape[1] if draft_probs is not None else 0
+    i32 = torch.int32
+    shape = AcceptShape(B, N, S, V, R, mode)
+    _check(_lib.lib().sdv_verify_accept_noalloc(
+        shape, eos_id, _ptr(remaining, i32, "remaining", allow_none=True), _ptr(tokens, i32, "tokens"),
+        _ptr(tree["next_token"], i32, "next_token"), _ptr(tree["next_sibling"], i32, "next_sibling"),
+        _ptr(tree.get("q_row"), i32, "q_row", allow_none=True), _ptr(target, torch.float32, "target"),
+        _ptr(draft_probs, torch.float32, "draft_probs", allow_none=True),
+        _ptr(u_accept, torch.float32, "u_accept", allow_none=True),
+        _ptr(u_draw, torch.float32, "u_draw", allow_none=True),
+        _ptr(out["accept_len"], i32, "accept_len"), _ptr(out["accept_path"], i32, "accept_path"),
+        _ptr(out["commit_tokens"], i32, "commit_tokens"), _ptr(out["commit_len"], i32, "commit_len"),
+        _ptr(out["next_root"], i32, "next_root"), _stream(tokens.device)), "sdv_verify_accept_noalloc")
+    return out
+
+
 # ------------------------------------------------------- KV allocation
 
 class KVAlloc:

@@ -45,6 +45,7 @@
 #include <atomic>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -675,15 +676,14 @@ extern "C" size_t sdv_verify_accept_workspace_size(sdv_accept_shape sh) {
   return c.bytes();
 }
 
-extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const int32_t *remaining,
-                                     const int32_t *tokens, const int32_t *next_token,
-                                     const int32_t *next_sibling, const int32_t *q_row,
-                                     const float *target, const float *draft_probs,
-                                     const float *u_accept, const float *u_draw, int32_t *accept_len,
-                                     int32_t *accept_path, int32_t *commit_tokens,
-                                     int32_t *commit_len, int32_t *next_root, void *ws,
-                                     size_t ws_bytes, void *stream) {
-  clear_error();
+namespace sdv {
+namespace {
+
+int32_t run_accept(sdv_accept_shape sh, int32_t eos_id, const int32_t *remaining, const int32_t *tokens,
+                   const int32_t *next_token, const int32_t *next_sibling, const int32_t *q_row,
+                   const float *target, const float *draft_probs, const float *u_accept, const float *u_draw,
+                   int32_t *accept_len, int32_t *accept_path, int32_t *commit_tokens, int32_t *commit_len,
+                   int32_t *next_root, void *ws, size_t ws_bytes, void *stream) {
   SDV_REQUIRE(sh.B >= 0 && sh.N >= 1 && sh.S >= 0 && sh.V >= 1, SDV_E_SHAPE,
               "verify_accept: need B >= 0, N >= 1, S >= 0, V >= 1");
   SDV_REQUIRE(sh.mode == SDV_ACCEPT_GREEDY || sh.mode == SDV_ACCEPT_STOCHASTIC, SDV_E_SHAPE,
@@ -733,4 +733,91 @@ extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const 
     if (e != hipSuccess) return fail(SDV_E_HIP, "verify_accept: launch: %s", hipGetErrorString(e));
   }
   return SDV_OK;
+}
+
+// ------------------------------------------------ the no-allocation variant
+//
+// The exchange words, counters and header of up to kNoAllocMaxB requests
+// live in a file-scope device array, one copy per device that runs the
+// library, held until the process ends.  In host code `scratch` only names
+// the symbol: its device address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch_addr.
+constexpr int kNoAllocMaxB = 1024;
+constexpr size_t kNoAllocBytes = kWsHeaderBytes + static_cast<size_t>(kNoAllocMaxB) * 2 * kMaxGroup * 8 +
+                                 static_cast<size_t>(kNoAllocMaxB) * 4;
+static_assert(kNoAllocBytes % 256 == 0, "scratch regions are 256-byte aligned");
+
+__device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+__global__ void zero_scratch_kernel(unsigned *p, size_t n) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Device address of this device's copy of `scratch` (looked up on the
+// first call on the device, with that device current).
+int32_t scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "verify_accept_noalloc: no device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SDV_E_UNSUPPORTED, "verify_accept_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(SDV_E_HIP, "verify_accept_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return SDV_OK;
+}
+
+}  // namespace
+}  // namespace sdv
+
+extern "C" int32_t sdv_verify_accept(sdv_accept_shape sh, int32_t eos_id, const int32_t *remaining,
+                                     const int32_t *tokens, const int32_t *next_token,
+                                     const int32_t *next_sibling, const int32_t *q_row,
+                                     const float *target, const float *draft_probs,
+                                     const float *u_accept, const float *u_draw, int32_t *accept_len,
+                                     int32_t *accept_path, int32_t *commit_tokens,
+                                     int32_t *commit_len, int32_t *next_root, void *ws,
+                                     size_t ws_bytes, void *stream) {
+  clear_error();
+  return run_accept(sh, eos_id, remaining, tokens, next_token, next_sibling, q_row, target, draft_probs, u_accept,
+                    u_draw, accept_len, accept_path, commit_tokens, commit_len, next_root, ws, ws_bytes, stream);
+}
+
+extern "C" int32_t sdv_verify_accept_noalloc(sdv_accept_shape sh, int32_t eos_id, const int32_t *remaining,
+                                             const int32_t *tokens, const int32_t *next_token,
+                                             const int32_t *next_sibling, const int32_t *q_row,
+                                             const float *target, const float *draft_probs,
+                                             const float *u_accept, const float *u_draw, int32_t *accept_len,
+                                             int32_t *accept_path, int32_t *commit_tokens, int32_t *commit_len,
+                                             int32_t *next_root, void *stream) {
+  clear_error();
+  SDV_REQUIRE(sh.B <= kNoAllocMaxB, SDV_E_UNSUPPORTED,
+              "verify_accept_noalloc: B=%d above the %d requests its static scratch holds", sh.B, kNoAllocMaxB);
+  if (sh.B <= 0) return run_accept(sh, eos_id, remaining, tokens, next_token, next_sibling, q_row, target,
+                                   draft_probs, u_accept, u_draw, accept_len, accept_path, commit_tokens,
+                                   commit_len, next_root, nullptr, 0, stream);
+  void *ptr = nullptr;
+  int32_t rc = scratch_address(&ptr);
+  if (rc != SDV_OK) return rc;
+  const size_t need = sdv_verify_accept_workspace_size(sh);
+  SDV_REQUIRE(need <= kNoAllocBytes, SDV_E_UNSUPPORTED, "verify_accept_noalloc: %zu scratch bytes needed", need);
+  // the part of the scratch this call uses starts at zero (a wait that gave
+  // up in an earlier call may have left words behind); a fill kernel, no
+  // memset node, so that the call can be captured
+  const size_t words = need / sizeof(unsigned);
+  hipLaunchKernelGGL(zero_scratch_kernel, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0,
+                     as_stream(stream), static_cast<unsigned *>(ptr), words);
+  rc = check_launch("verify_accept_noalloc: clear");
+  if (rc != SDV_OK) return rc;
+  return run_accept(sh, eos_id, remaining, tokens, next_token, next_sibling, q_row, target, draft_probs, u_accept,
+                    u_draw, accept_len, accept_path, commit_tokens, commit_len, next_root, ptr, need, stream);
 }
