@@ -1078,3 +1078,30 @@ def test_status_reports_given_up_waits_and_reset_restores():
     want = oacc.verify_greedy(t, inp["target"], S=cfg.S)
     for key in want:
         assert np.array_equal(host(acc[key]), want[key]), key
+
+
+# ------------------------------------- sampling primitives, device vs host
+
+def test_sampling_primitives_at_their_edges_device_vs_host():
+    """The stochastic walk on requests built to sit on the contract's edges
+    (tests/_sampling_edges.py): equality in the accept test, normalised
+    residuals whose fp64 quotient is an fp32 midpoint or one fp64 ulp off
+    one, S near 2^56 that fp64 cannot hold, draws whose threshold meets a
+    running mass exactly at a vocabulary-slice boundary, masses below 2^-40,
+    kk = 0 and 2^24 - 1, S below 2^24 and near 2^57.  The kernel's u64 -> f64
+    conversion, fp64 divide, fp32 rounding, floor(w * 2^40) and inverse-CDF
+    threshold must reproduce the oracle's bit for bit."""
+    import _sampling_edges as edges
+    inp, cases = edges.build()
+    tree = {k: dev(inp[k]) for k in ("tokens", "next_token", "next_sibling", "q_row")}
+    say("sampling edges", len(cases), "requests")
+    g = sdv.sdv_verify_accept(sdv.STOCHASTIC, tree, dev(inp["target"]), 1, draft_probs=dev(inp["draft_probs"]),
+                              u_accept=dev(inp["u_accept"]), u_draw=dev(inp["u_draw"]))
+    torch.cuda.synchronize()
+    want = oacc.verify_stochastic({k: inp[k] for k in ("tokens", "next_token", "next_sibling", "q_row")},
+                                  inp["target"], inp["draft_probs"], inp["u_accept"], inp["u_draw"], S=1)
+    assert sdv.device_status(reset=True) == 0
+    for key in want:
+        got = host(g[key])
+        bad = [cases[b]["name"] for b in range(len(cases)) if not np.array_equal(got[b], want[key][b])]
+        assert not bad, "%s differs for %s" % (key, bad)

@@ -562,3 +562,61 @@ def test_bonus_at_a_childless_root_is_drawn_from_p():
 
     counts = _draw_counts(tok, 1 << 24)
     assert [Fraction(counts.get(v, 0), 1 << 24) for v in range(3)] == p
+
+
+# ------------------------------------- the sampling contract at its edges
+#
+# tests/_sampling_edges.py builds requests that sit on the edges of the
+# fixed-point contract; each carries a fact derived with exact rational or
+# integer arithmetic (not with the oracle).  The oracle's walk must agree with
+# every fact; the GPU test feeds the same batch to the kernel.
+
+def _edge_batch():
+    import _sampling_edges as edges
+    return edges, *edges.build()
+
+
+def test_sampling_edge_facts_hold_in_exact_arithmetic():
+    """The constructions are sharp: the midpoint cases' S are realised by the
+    rows' masses, and the draw facts follow from T = floor(kk * S / 2^24)."""
+    edges, inp, cases = _edge_batch()
+    for b, c in enumerate(cases):
+        p0 = inp["target"][b, 0].astype(np.float64)
+        if "S" in c:
+            q = inp["draft_probs"][b, 0]
+            r = np.maximum(inp["target"][b, 0] - q, np.float32(0))
+            S = int(np.floor(r.astype(np.float64) * 2.0 ** 40).astype(np.uint64).sum(dtype=np.uint64))
+            assert S == c["S"], c["name"]
+            lo, hi = c["neighbours"]
+            assert c["t_prime"] in (lo, hi) and lo < edges.U_MAX * hi < hi
+        if "token" in c and not c["name"].startswith("masses below"):
+            kk = int(round(float(inp["u_draw"][b, 0]) * (1 << 24)))
+            m = np.floor(p0 * 2.0 ** 40).astype(np.int64)        # q is 0 wherever p is not
+            S = int(sum(int(x) for x in m))
+            T = kk * S >> 24
+            cum = np.cumsum(m.astype(object))
+            assert int(np.argmax(cum > T)) == c["token"], c["name"]
+            if c["name"].startswith("crossing"):
+                assert cum[c["token"] - 1] == T           # the running mass meets T exactly
+
+
+def test_oracle_walk_agrees_with_the_edge_facts():
+    edges, inp, cases = _edge_batch()
+    tree = {k: inp[k] for k in ("tokens", "next_token", "next_sibling", "q_row")}
+    r = oacc.verify_stochastic(tree, inp["target"], inp["draft_probs"], inp["u_accept"], inp["u_draw"], S=1)
+    for b, c in enumerate(cases):
+        name = c["name"]
+        if name == "u*q == t rejects":
+            assert r["accept_path"][b, 1] == 2                    # y1 rejected, y2 accepted
+            assert r["commit_tokens"][b, :2].tolist() == [12, inp["target"].shape[2] - 1]
+        elif name == "largest u accepts t == q":
+            assert r["accept_path"][b, :2].tolist() == [0, 1] and r["commit_tokens"][b, 1] == 5
+        elif "S" in c:
+            q = inp["draft_probs"][b, 0]
+            rr = np.maximum(inp["target"][b, 0] - q, np.float32(0))
+            y2 = int(inp["tokens"][b, 2])
+            assert float(oacc.normalise(rr, c["S"])[y2]) == c["t_prime"], name
+            assert (r["accept_len"][b] == 1) == c["second_accepted"], name
+        else:
+            assert r["accept_len"][b] == 0 and r["commit_len"][b] == 1, name
+            assert r["commit_tokens"][b, 0] == c["token"], name
