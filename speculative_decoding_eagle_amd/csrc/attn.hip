@@ -542,15 +542,13 @@ extern "C" int32_t sdv_tree_verify_attention(sdv_attn_shape sh, float sm_scale, 
   hipStream_t st = as_stream(stream);
   const int wide_nrb = wide_row_blocks(sh);
   if (wide_nrb > 0) {
-    // split each unit's keys over two workgroups when units alone leave CUs
-    // idle and the caller gave the workspace the split needs
-    const int64_t slots = static_cast<int64_t>(sh.B) * sh.Hkv * wide_nrb;
-    const size_t need = attn_wide_workspace(slots, sh.D);
-    const bool has_ws = need > 0 && ws && ws_bytes >= need;
-    const int nch = has_ws && slots < 2LL * num_cus() ? 2 : 1;
-    SDV_REQUIRE(nch == 1 || reinterpret_cast<uintptr_t>(ws) % 256 == 0, SDV_E_WORKSPACE,
+    // the persistent schedule when the caller gave its workspace
+    const int64_t units = static_cast<int64_t>(sh.B) * sh.Hkv * wide_nrb;
+    const size_t need = attn_wide_workspace(units, sh.D);
+    const bool split = need > 0 && ws && ws_bytes >= need;
+    SDV_REQUIRE(!split || reinterpret_cast<uintptr_t>(ws) % 256 == 0, SDV_E_WORKSPACE,
                 "tree_verify_attention: workspace must be 256-byte aligned");
-    return launch_attn_wide(st, sh, pshift, scale_log2, wide_nrb, nch, q, k_pool, v_pool, page_table, prefix_len,
+    return launch_attn_wide(st, sh, pshift, scale_log2, wide_nrb, split, q, k_pool, v_pool, page_table, prefix_len,
                             mask_bits, out, lse, ws);
   }
   const int G = sh.Hq / sh.Hkv;

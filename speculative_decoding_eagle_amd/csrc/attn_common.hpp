@@ -139,20 +139,23 @@ __device__ __forceinline__ int request_of_rank(int r, int B, const int *__restri
   return *s_pick;
 }
 
-// The wide kernel's workspace starts with a fixed region of counters (two
-// per unit), the same for every shape, so that what one call leaves there
-// (zeros) is what any later call expects; the partial results follow.
+// The wide kernel's workspace: the status header, a fixed region of
+// counters (two per unit) that every call leaves at zero, whatever the shape,
+// then two partial-result slots per workgroup of the persistent schedule.
 constexpr int kAttnSyncWords = 8192;
 
-// Workspace of the wide kernel for `slots` (request, KV head, row block)
-// units when its keys are split over two workgroups; 0 when the split is not
-// offered (more than kAttnSyncWords / 2 units).
-size_t attn_wide_workspace(int64_t slots, int D);
+// Workspace of the wide kernel's persistent schedule for `units` (request,
+// KV head, row block) units; 0 when it is not offered (more than
+// kAttnSyncWords / 2 units).
+size_t attn_wide_workspace(int64_t units, int D);
 
-// Launches the wide kernel (query rows per unit above 128).  nch: workgroups
-// per unit that split its keys (1 or 2); ws: attn_wide_workspace bytes,
-// zero-filled before first use (calls leave it zero-filled).
-int32_t launch_attn_wide(hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb, int nch,
+// Launches the wide kernel (query rows per unit above 128).  split: run the
+// persistent schedule (every compute unit streams an equal share of all
+// units' key tiles; units cut between workgroups merge their partial
+// softmax states), which needs ws: attn_wide_workspace bytes, zero-filled
+// before first use (calls leave the counters at zero).  Otherwise one
+// workgroup per (unit, row block).
+int32_t launch_attn_wide(hipStream_t st, const sdv_attn_shape &sh, int pshift, float scale_log2, int nrb, bool split,
                          const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                          const int32_t *page_table, const int32_t *prefix_len, const uint32_t *mask_bits,
                          uint16_t *out, float *lse, void *ws);
