@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+ROTATE = 3                     # input sets the timed steps rotate through
+# read-only inputs that are rotated (outputs, tables and small arrays are not)
+ROTATED = ("draft_probs", "draft_logits_in", "target", "q", "k_pool", "v_pool", "hidden", "weight", "q_pruned",
+           "mask_bits")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
 WORKLOAD_NAMES = {
@@ -63,6 +67,11 @@ def parse():
                          "regions with the partial-page copies, rollback) to the step")
     ap.add_argument("--extend-prep", action="store_true",
                     help="add the index preparation of the draft extend after the accept walk to the step")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="KV layers the compaction moves (page > 1); layer 0 is the attention's pool, the others "
+                         "are pools of the same shape that only the compaction touches")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (side figures)")
+    ap.add_argument("--k-inter", type=int, default=None, help="TLI workloads: override the intersection size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -80,7 +89,7 @@ class Pipeline:
     """Preallocated device buffers and the per-stage calls of one step."""
 
     def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs", extend_prep=False, chain=False,
-                 kv_alloc=False):
+                 kv_alloc=False, layers=1):
         import torch
         import speculative_decoding_eagle_amd as sdv
         self.torch, self.sdv, self.cfg = torch, sdv, cfg
@@ -128,6 +137,7 @@ class Pipeline:
             # the probability rows of the draft distribution
             lg = d.pop("draft_logits")
             self.draft_logits = lg.to(torch.bfloat16) if draft_input == "logits_bf16" else lg
+            d["draft_logits_in"] = self.draft_logits
         rows = B * cfg.R
         self.topk_p = torch.empty((B, cfg.R, k), dtype=torch.float32, device="cuda")
         self.topk_id = torch.empty((B, cfg.R, k), dtype=torch.int32, device="cuda")
@@ -145,11 +155,38 @@ class Pipeline:
             self.freed = torch.empty(B * N, dtype=torch.int32, device="cuda")
             self.num_freed = torch.empty(1, dtype=torch.int32, device="cuda")
         self.target = d["target"]
+        # extra KV layers that only the compaction reads and writes
+        self.extra_k, self.extra_v = [], []
+        self.layers = layers if (cfg.has_attention and cfg.page > 1) else 1
+        if cfg.has_attention and cfg.page > 1:
+            for _ in range(layers - 1):
+                self.extra_k.append(torch.empty_like(d["k_pool"]))
+                self.extra_v.append(torch.empty_like(d["v_pool"]))
         # warm build, used to plant acceptance when asked
         self.run_all(0)
         torch.cuda.synchronize()
         if accept_mode == "planted":
             self._plant()
+        # Input rotation: the read-only inputs of more than 1 MB get ROTATE
+        # copies and step i reads copy i % ROTATE, so at least two other
+        # steps' inputs (GBs at the large workloads) pass through L2 and the
+        # 256 MB MALL before a step's own inputs come back: every stage
+        # starts cold, as it would in a serving loop where the target and
+        # draft models run in between.
+        self.sets = [d]
+        for _ in range(1, ROTATE):
+            self.sets.append({key: (val.clone() if key in ROTATED and val.numel() * val.element_size() > (1 << 20)
+                                    else val) for key, val in d.items()})
+        torch.cuda.synchronize()
+
+    def use(self, i):
+        """Point the stages at input set i % ROTATE."""
+        self.d = self.sets[i % len(self.sets)]
+        self.target = self.d["target"]
+        if not self.cfg.is_tli:
+            self.draft_rows = self.d["draft_probs"]
+        if self.draft_input != "probs":
+            self.draft_logits = self.d["draft_logits_in"]
 
     def _plant(self):
         """Make the target accept a random-length path of first children
@@ -215,7 +252,7 @@ class Pipeline:
 
     def s_compact(self, i):
         cfg, d = self.cfg, self.d
-        pools = ([d["k_pool"]], [d["v_pool"]]) if cfg.page > 1 else ([], [])
+        pools = ([d["k_pool"]] + self.extra_k, [d["v_pool"]] + self.extra_v) if cfg.page > 1 else ([], [])
         self.sdv.sdv_compact_kv(self.tables[i], d["prefix_len"], self.acc["accept_len"], self.acc["accept_path"],
                                 cfg.N, cfg.S, cfg.page, pools[0], pools[1], new_len=self.new_len, freed=self.freed,
                                 num_freed=self.num_freed)
@@ -256,6 +293,8 @@ class Pipeline:
         return st
 
     def run_all(self, i):
+        if hasattr(self, "sets"):
+            self.use(i)
         for _, fn in self.stages(i):
             fn()
 
@@ -279,6 +318,15 @@ def algorithmic_work(cfg, inp, pipe):
     rows = int(np.maximum(commit, 1).sum())     # visited nodes = committed tokens
     per_row = V * 4 * (2 if cfg.mode == "stochastic" else 1)
     out["accept"] = dict(bytes=rows * per_row, flops=0, accepted=int(acc_len.sum()))
+    if cfg.has_attention:
+        # page > 1: K and V rows [Hkv, D] of every moved token, read and
+        # written, every layer; page 1: the slot-map entries of the tree
+        path = pipe.acc["accept_path"].cpu().numpy()
+        moved = int(sum(int((path[b, 1:acc_len[b] + 1] != np.arange(1, acc_len[b] + 1)).sum()) for b in range(B)))
+        if cfg.page > 1:
+            out["compact_kv"] = dict(bytes=moved * 2 * 2 * cfg.Hkv * cfg.D * 2 * pipe.layers, flops=0, moved=moved)
+        else:
+            out["compact_kv"] = dict(bytes=B * N * 4 * 2 + B * 4 * 3, flops=0, moved=moved)
     if cfg.is_tli:
         H = cfg.H_draft
         out["tli_head_mask_scatter"] = dict(
@@ -327,9 +375,21 @@ def measured_traffic(stage, workload):
 
 # --------------------------------------------------------------- CPU oracle
 
-def cpu_baseline(cfg, inp, n_req):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, n_req, threads=1):
     """The oracle, as it stands, on the first n_req requests of the same
-    workload, BLAS pinned to one thread; scaled to verified tokens/s."""
+    workload, BLAS limited to `threads` threads (the tree build and walks are
+    single-threaded Python); scaled to verified tokens/s."""
     from threadpoolctl import threadpool_limits
     import oracle.accept as oacc
     import oracle.attention as oatt
@@ -339,7 +399,7 @@ def cpu_baseline(cfg, inp, n_req):
     import oracle.tree as otree
     n = min(n_req, cfg.B)
     sl = slice(0, n)
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         t0 = time.perf_counter()
         if cfg.is_tli:
             h = inp["hidden"][0][sl]
@@ -365,9 +425,10 @@ def cpu_baseline(cfg, inp, n_req):
                 ocmp.compact_kv(inp["page_table"][sl], [inp["k_pool"]], [inp["v_pool"]], inp["prefix_len"][sl],
                                 acc["accept_len"], acc["accept_path"], cfg.N, cfg.page)
         dt = time.perf_counter() - t0
-    return {"value": n * cfg.N / dt, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "first %d of %d requests of %s, every stage of the step (oracle, numpy, BLAS on 1 thread), "
-                      "%.2f s" % (n, cfg.B, cfg.name, dt)}
+    return {"value": n * cfg.N / dt, "unit": "verified draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d requests of %s, every stage of the step (oracle, numpy, BLAS on %d "
+                      "thread%s), %.2f s" % (n, cfg.B, cfg.name, threads, "" if threads == 1 else "s", dt),
+            "cpu_model": cpu_model()}
 
 
 # ------------------------------------------------------ counter calibration
@@ -402,7 +463,12 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    cfg = workloads.get_config(args.config)
+    over = {}
+    if args.batch is not None:
+        over["B"] = args.batch
+    if args.k_inter is not None:
+        over["K_inter"] = args.k_inter
+    cfg = workloads.get_config(args.config, **over)
     log("generating inputs of %s" % cfg.name)
     t_gen = time.perf_counter()
     if args.draft_input != "probs" and cfg.is_tli:
@@ -416,7 +482,7 @@ def main():
         print("--chain needs a k = 1 workload whose tree keeps every step (N = S + 1)", file=sys.stderr)
         sys.exit(2)
     pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept, args.draft_input, args.extend_prep,
-                    args.chain, args.kv_alloc)
+                    args.chain, args.kv_alloc, args.layers)
     stages = [name for name, _ in pipe.stages(0)]
 
     for i in range(args.warmup):
@@ -435,6 +501,7 @@ def main():
     # per-stage times with HIP events on the launch stream (same work again)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     for i in range(args.steps):
+        pipe.use(base + i)
         st = pipe.stages(base + i)
         ev[i][0].record()
         for j, (_, fn) in enumerate(st):
@@ -478,7 +545,7 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[cfg.name], "name": cfg.name, "batch": cfg.B, "tree_tokens": cfg.N,
                    "accept": args.accept, "draft_input": args.draft_input,
                    "extend_prep": args.extend_prep, "chain": args.chain,
-                   "kv_alloc": args.kv_alloc},
+                   "kv_alloc": args.kv_alloc, "kv_layers": args.layers},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_gbs": {k: round(work[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9, 1) for k in stages if k in work},
         "accepted_tokens": work["accept"]["accepted"],
@@ -487,8 +554,12 @@ def main():
         "input_generation_s": round(t_gen, 2),
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+        log("timing the CPU oracle on a sample (one core, then every core of this process)")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample, threads=1)
+        ncores = len(os.sched_getaffinity(0))
+        if ncores > 1:
+            allc = cpu_baseline(cfg, inp, args.cpu_sample, threads=ncores)
+            line["cpu_baseline"]["all_cores"] = {k: allc[k] for k in ("value", "cores", "sample")}
     print(json.dumps(line), flush=True)
 
 
