@@ -55,7 +55,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--accept", default="literal", choices=["literal", "planted"])
+    ap.add_argument("--accept", default="literal", choices=["literal", "planted", "full"],
+                    help="literal inputs; planted: a seeded accepted path of U{0..S} nodes per request; full: "
+                         "every request accepts S nodes (a stress case for the compaction)")
     ap.add_argument("--draft-input", default="probs", choices=["probs", "logits_f32", "logits_bf16"],
                     help="what the draft top-k reads: the processed probability rows, or the draft logits "
                          "(fp32 or bf16) with the softmax fused into the top-k (non-TLI workloads)")
@@ -165,8 +167,8 @@ class Pipeline:
         # warm build, used to plant acceptance when asked
         self.run_all(0)
         torch.cuda.synchronize()
-        if accept_mode == "planted":
-            self._plant()
+        if accept_mode in ("planted", "full"):
+            self._plant(full=accept_mode == "full")
         # Input rotation: the read-only inputs of more than 1 MB get ROTATE
         # copies and step i reads copy i % ROTATE, so at least two other
         # steps' inputs (GBs at the large workloads) pass through L2 and the
@@ -188,7 +190,7 @@ class Pipeline:
         if self.draft_input != "probs":
             self.draft_logits = self.d["draft_logits_in"]
 
-    def _plant(self):
+    def _plant(self, full=False):
         """Make the target accept a random-length path of first children
         (setup only; the same planted rows are then used by every step)."""
         cfg, torch = self.cfg, self.torch
@@ -198,7 +200,7 @@ class Pipeline:
         qr = self.tree["q_row"].cpu().numpy()
         t = self.target
         for b in range(cfg.B):
-            a = int(rng.integers(0, cfg.S + 1))
+            a = cfg.S if full else int(rng.integers(0, cfg.S + 1))
             u = 0
             for _ in range(a):
                 c = int(nt[b, u])

@@ -360,7 +360,10 @@ int32_t sdv_verify_accept_noalloc(sdv_accept_shape shape, int32_t eos_id, const 
  * [num_slots, Hkv, D] bf16 pools (in/out; unused when page == 1).
  * freed: device [B*N] int32, the freed ids of all requests in batch order;
  * num_freed: device [1] int32.  new_len: device [B].
- * Limits: N <= 256, layers <= 128, (Hkv * D) % 8 == 0 when page > 1.
+ * Workspace (page > 1): the size query's bytes (the moved tokens' slot
+ * pairs), no initialisation needed; page == 1 needs none.
+ * Limits: N <= 256, layers <= 128; page > 1 also S <= 63 and
+ * (Hkv * D) % 8 == 0.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t B, N, S, page, Hkv, D, layers, max_pages;

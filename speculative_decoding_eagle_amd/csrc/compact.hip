@@ -4,12 +4,13 @@
 // section 5.2).
 //
 // page == 1: an index remap of the slot map (one block per request), no KV
-// bytes move.  page > 1: a coalesced copy of the moved K/V rows (16-byte
-// vectors, one block per request x layer x pool, all reads of a batch of
-// rows before its writes, batches in increasing destination order), then a
-// per-request kernel that clears the released tail pages and lists them.
-// The freed lists of all requests are laid out in batch order; each block
-// finds its offset from the accept lengths of the requests before it.
+// bytes move.  page > 1: a per-request kernel reads the moved tokens' source
+// and destination slots once (into the workspace) and then clears and lists
+// the released tail pages; a second kernel copies the moved K/V rows
+// (16-byte vectors, one block per request x layer x pool, one dependent load
+// before its copies).  The freed lists of all requests are laid out in batch
+// order; each block finds its offset from the accept lengths of the requests
+// before it.
 #include "common.hpp"
 
 namespace sdv {
@@ -101,67 +102,54 @@ remap_slots_kernel(int B, int N, int S, int max_pages, int *__restrict__ table,
   if (tid == 0) new_len[b] = L + a + 1;
 }
 
+// page > 1, first kernel (one block per request): the source and
+// destination slots of every moved token (path[d] != d, d = 1..a) go to the
+// workspace as pairs, then the released tail pages are cleared and listed.
+// The table is read and written here only, so reading the moved tokens'
+// slots before the release needs no ordering across blocks.
 __global__ void __launch_bounds__(kCmpThreads)
-copy_rows_kernel(PoolPtrs pools, int layers, int N, int S, int page, int max_pages, int64_t num_slots,
-                 int row16, const int *__restrict__ table, const int *__restrict__ prefix_len,
-                 const int *__restrict__ accept_len, const int *__restrict__ accept_path) {
-  const int b = blockIdx.x / (2 * layers);
-  const int rest = blockIdx.x % (2 * layers);
-  const int layer = rest >> 1;
-  uint4 *pool = reinterpret_cast<uint4 *>((rest & 1) ? pools.v[layer] : pools.k[layer]);
-  const int L = prefix_len[b];
-  const int a = clamp_accept(accept_len[b], S, N);
-  if (a == 0 || L < 0 || L + N > max_pages * page) return;
-  const int *path = accept_path + static_cast<int64_t>(b) * (S + 1);
-  const int *trow = table + static_cast<int64_t>(b) * max_pages;
-  const int items = a * row16;                 // rows d = 1..a
-  for (int first = 0; first < items; first += kCopyBatch * kCmpThreads) {
-    uint4 buf[kCopyBatch];
-    int64_t dst[kCopyBatch];
-#pragma unroll
-    for (int j = 0; j < kCopyBatch; ++j) {
-      const int x = first + j * kCmpThreads + threadIdx.x;
-      dst[j] = -1;
-      if (x < items) {
-        const int d = 1 + x / row16;
-        const int c16 = x % row16;
-        int pd = path[d];
-        pd = pd < 0 ? 0 : (pd >= N ? N - 1 : pd);
-        if (pd != d) {
-          const int ps = L + pd, pdst = L + d;
-          const int64_t ss = static_cast<int64_t>(trow[ps / page]) * page + ps % page;
-          const int64_t sd = static_cast<int64_t>(trow[pdst / page]) * page + pdst % page;
-          if (ss >= 0 && ss < num_slots && sd >= 0 && sd < num_slots) {
-            buf[j] = pool[ss * row16 + c16];
-            dst[j] = sd * row16 + c16;
-          }
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kCopyBatch; ++j)
-      if (dst[j] >= 0) pool[dst[j]] = buf[j];
-    __syncthreads();
-  }
-}
-
-__global__ void __launch_bounds__(kCmpThreads)
-release_pages_kernel(int B, int N, int S, int page, int max_pages, int *__restrict__ table,
-                     const int *__restrict__ prefix_len, const int *__restrict__ accept_len,
-                     int *__restrict__ new_len, int *__restrict__ freed, int *__restrict__ num_freed) {
+prep_pages_kernel(int B, int N, int S, int page, int max_pages, int64_t num_slots, int *__restrict__ table,
+                  const int *__restrict__ prefix_len, const int *__restrict__ accept_len,
+                  const int *__restrict__ accept_path, int2 *__restrict__ pairs, int *__restrict__ counts,
+                  int *__restrict__ new_len, int *__restrict__ freed, int *__restrict__ num_freed) {
+  __shared__ int s_count;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int L = prefix_len[b];
   const int a = clamp_accept(accept_len[b], S, N);
-  const int base = released_before(b, prefix_len, accept_len, S, N, page);
+  const bool ok = L >= 0 && static_cast<int64_t>(L) + N <= static_cast<int64_t>(max_pages) * page;
+  int *row = table + static_cast<int64_t>(b) * max_pages;
+  const int *path = accept_path + static_cast<int64_t>(b) * (S + 1);
+  if (tid == 0) s_count = 0;
+  const int base = released_before(b, prefix_len, accept_len, S, N, page);   // (has barriers)
   if (b == 0) {
     const int tot = released_before(B, prefix_len, accept_len, S, N, page);
     if (tid == 0) *num_freed = tot;
   }
+  // moved tokens: thread d - 1 takes row d (d = 1..a, at most 63 of them,
+  // one wave); the kept ones are packed in increasing d by a ballot
+  if (tid < kWave) {
+    const int d = tid + 1;
+    bool mv = false;
+    int2 pr = make_int2(0, 0);
+    if (ok && d <= a) {
+      int pd = path[d];
+      pd = pd < 0 ? 0 : (pd >= N ? N - 1 : pd);
+      const int ps = L + pd, pdst = L + d;
+      const int64_t ss = static_cast<int64_t>(row[ps / page]) * page + ps % page;
+      const int64_t sd = static_cast<int64_t>(row[pdst / page]) * page + pdst % page;
+      mv = pd != d && ss >= 0 && ss < num_slots && sd >= 0 && sd < num_slots;
+      pr = make_int2(static_cast<int>(ss), static_cast<int>(sd));
+    }
+    const unsigned long long m = __ballot(mv);
+    const int slot = __popcll(m & ((1ull << tid) - 1ull));
+    if (mv) pairs[static_cast<int64_t>(b) * S + slot] = pr;
+    if (tid == 0) s_count = __popcll(m);
+  }
+  __syncthreads();                       // the moved tokens' slots are read before the release below
+  if (tid == 0) counts[b] = s_count;
   const int first_free = (L + a + 1 + page - 1) / page;
   const int last_used = (L + N - 1) / page;
-  int *row = table + static_cast<int64_t>(b) * max_pages;
   for (int pg = first_free + tid; pg <= last_used; pg += kCmpThreads) {
     const bool in = pg >= 0 && pg < max_pages;
     freed[base + pg - first_free] = in ? row[pg] : -1;
@@ -170,20 +158,73 @@ release_pages_kernel(int B, int N, int S, int page, int max_pages, int *__restri
   if (tid == 0) new_len[b] = L + a + 1;
 }
 
+// page > 1, second kernel: one block per (request, group of kLayerGroup
+// layers) copies the request's moved K and V rows [Hkv, D] of those layers,
+// 16-byte vectors.  The count and the pairs load together (pairs past the
+// count are not used); then every read of the block is in flight before its
+// first write, which also makes the copy safe where a row's source is a
+// lower row's destination (the path is increasing and path[d] >= d).
+constexpr int kLayerGroup = 4;
+constexpr int kCopyPer = 16;              // 16-byte vectors per thread per pass
+
+__global__ void __launch_bounds__(kCmpThreads)
+copy_pairs_kernel(PoolPtrs pools, int layers, int S, int row16, const int2 *__restrict__ pairs,
+                  const int *__restrict__ counts) {
+  const int ngroups = (layers + kLayerGroup - 1) / kLayerGroup;
+  const int b = blockIdx.x / ngroups;
+  const int l0 = (blockIdx.x % ngroups) * kLayerGroup;
+  const int nl = min(kLayerGroup, layers - l0);
+  const int2 *pr = pairs + static_cast<int64_t>(b) * S;
+  const int n = counts[b];
+  // item x: pool p = x % 2, layer l0 + (x / 2) % nl, row (x / 2 / nl) / row16, chunk % row16
+  const int items = n * row16 * nl * 2;
+  for (int first = 0; first < items; first += kCopyPer * kCmpThreads) {
+    uint4 buf[kCopyPer];
+    uint4 *dst[kCopyPer];
+#pragma unroll
+    for (int j = 0; j < kCopyPer; ++j) {
+      const int x = first + j * kCmpThreads + static_cast<int>(threadIdx.x);
+      dst[j] = nullptr;
+      if (x < items) {
+        const int c16 = x % row16;
+        const int y = x / row16;
+        const int p = y & 1;
+        const int ly = (y >> 1) % nl;
+        const int r = (y >> 1) / nl;
+        const int2 sd = pr[r];
+        uint4 *pool = reinterpret_cast<uint4 *>(p ? pools.v[l0 + ly] : pools.k[l0 + ly]);
+        buf[j] = pool[static_cast<int64_t>(sd.x) * row16 + c16];
+        dst[j] = pool + static_cast<int64_t>(sd.y) * row16 + c16;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCopyPer; ++j)
+      if (dst[j]) *dst[j] = buf[j];
+    __syncthreads();
+  }
+}
+
 }  // namespace
 }  // namespace sdv
 
 using namespace sdv;
 
-extern "C" size_t sdv_compact_kv_workspace_size(sdv_kv_shape) { return 0; }
+// Workspace (page > 1): the moved tokens' (source, destination) slot pairs,
+// S per request, then one count per request.
+extern "C" size_t sdv_compact_kv_workspace_size(sdv_kv_shape sh) {
+  if (sh.page <= 1 || sh.B <= 0 || sh.S < 0) return 0;
+  Carver c(nullptr);
+  c.take<int2>(static_cast<size_t>(sh.B) * (sh.S > 0 ? sh.S : 1));
+  c.take<int>(static_cast<size_t>(sh.B));
+  return c.bytes();
+}
 
 extern "C" int32_t sdv_compact_kv(sdv_kv_shape sh, uint16_t *const *k_pools, uint16_t *const *v_pools,
                                   int32_t *page_table, const int32_t *prefix_len,
                                   const int32_t *accept_len, const int32_t *accept_path,
                                   int32_t *new_len, int32_t *freed, int32_t *num_freed, void *ws,
                                   size_t ws_bytes, void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   clear_error();
   SDV_REQUIRE(sh.B >= 0 && sh.N >= 1 && sh.S >= 0 && sh.page >= 1 && sh.max_pages >= 1, SDV_E_SHAPE,
               "compact_kv: need B >= 0, N >= 1, S >= 0, page >= 1, max_pages >= 1");
@@ -202,6 +243,7 @@ extern "C" int32_t sdv_compact_kv(sdv_kv_shape sh, uint16_t *const *k_pools, uin
               "compact_kv: layers=%d outside [1, %d]", sh.layers, kMaxLayers);
   SDV_REQUIRE(sh.Hkv >= 1 && sh.D >= 1 && (static_cast<int64_t>(sh.Hkv) * sh.D) % 8 == 0, SDV_E_UNSUPPORTED,
               "compact_kv: Hkv*D must be a multiple of 8");
+  SDV_REQUIRE(sh.S <= 63, SDV_E_UNSUPPORTED, "compact_kv: S=%d above 63 with page > 1", sh.S);
   SDV_REQUIRE(k_pools && v_pools, SDV_E_NULL, "compact_kv: NULL pool array");
   PoolPtrs pp;
   for (int l = 0; l < sh.layers; ++l) {
@@ -214,13 +256,18 @@ extern "C" int32_t sdv_compact_kv(sdv_kv_shape sh, uint16_t *const *k_pools, uin
   }
   for (int l = sh.layers; l < kMaxLayers; ++l) pp.k[l] = pp.v[l] = nullptr;
   const int row16 = static_cast<int>(static_cast<int64_t>(sh.Hkv) * sh.D / 8);
-  const int64_t blocks = static_cast<int64_t>(sh.B) * sh.layers * 2;
-  hipLaunchKernelGGL(copy_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCmpThreads), 0, st, pp,
-                     sh.layers, sh.N, sh.S, sh.page, sh.max_pages, sh.num_slots, row16, page_table,
-                     prefix_len, accept_len, accept_path);
-  int32_t rc = check_launch("copy_rows_kernel");
+  const size_t need = sdv_compact_kv_workspace_size(sh);
+  SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "compact_kv: workspace of %zu bytes needed", need);
+  Carver cv(ws);
+  int2 *pairs = cv.take<int2>(static_cast<size_t>(sh.B) * (sh.S > 0 ? sh.S : 1));
+  int *counts = cv.take<int>(static_cast<size_t>(sh.B));
+  hipLaunchKernelGGL(prep_pages_kernel, dim3(sh.B), dim3(kCmpThreads), 0, st, sh.B, sh.N, sh.S, sh.page,
+                     sh.max_pages, sh.num_slots, page_table, prefix_len, accept_len, accept_path, pairs, counts,
+                     new_len, freed, num_freed);
+  int32_t rc = check_launch("prep_pages_kernel");
   if (rc != SDV_OK) return rc;
-  hipLaunchKernelGGL(release_pages_kernel, dim3(sh.B), dim3(kCmpThreads), 0, st, sh.B, sh.N, sh.S, sh.page,
-                     sh.max_pages, page_table, prefix_len, accept_len, new_len, freed, num_freed);
-  return check_launch("release_pages_kernel");
+  const int64_t blocks = static_cast<int64_t>(sh.B) * ((sh.layers + kLayerGroup - 1) / kLayerGroup);
+  hipLaunchKernelGGL(copy_pairs_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCmpThreads), 0, st, pp,
+                     sh.layers, sh.S, row16, pairs, counts);
+  return check_launch("copy_pairs_kernel");
 }
