@@ -186,12 +186,55 @@ __device__ unsigned long long block_exclusive_scan(unsigned long long x, unsigne
 
 // ------------------------------------------------------- sampling arithmetic
 
-__device__ __forceinline__ unsigned long long mass(float w) {
-  return static_cast<unsigned long long>(floor(static_cast<double>(w) * 0x1p40));
+// The stochastic walk holds its slices in units of 2^-40: X = x * 2^40 for
+// every p, q, t and residual entry x.  The values it weighs stay in [0, 2]:
+// p and q lie in [0, 1], a residual never exceeds the t it came from, and a
+// rescaled residual r / S is at most 2 (S, the floored mass sum, is at least
+// floor(max r * 2^40) * 2^-40 >= max r / 2).  On that range the scaling is
+// exact in fp32 both ways, commutes with the rounding of t - q (a difference
+// too small for a normal fp32 is exact in both units), and leaves the fp64
+// quotient r / S unchanged; the mass floor(fp64(r) * 2^40) of an entry is
+// floor(R), and any 64 masses (each below 2^41) sum exactly in fp64.
+constexpr float kUnit = 0x1p40f;
+
+__device__ __forceinline__ double mass_of(float X) { return floor(static_cast<double>(X)); }
+
+// A non-negative integer below 2^53 held in a double, as a u64.
+__device__ __forceinline__ unsigned long long to_u64(double m) {
+  const double h = floor(m * 0x1p-32);
+  return (static_cast<unsigned long long>(static_cast<unsigned>(h)) << 32) |
+         static_cast<unsigned>(m - h * 0x1p32);
 }
+
+__device__ __forceinline__ unsigned long long mass(float X) { return to_u64(mass_of(X)); }
 
 __device__ __forceinline__ float rescale(float r, double s) {
   return static_cast<float>(static_cast<double>(r) / s);
+}
+
+// T = fp32(fp64(R) / tot) * 2^40 for four entries of a slice (tot the mass
+// sum as fp64, inv = fp64(2^40 / tot), both once per level).  The product
+// fp64(R) * inv lies within two fp64 ulps of the quotient, hence of its
+// correctly rounded value, so both round to the same fp32 unless the product
+// is within a few ulps of an fp32 rounding midpoint (the 29 bits below the
+// fp32 mantissa near 2^28) or t is below the fp32 normal range (the product
+// below 2^-86 here); if any of the four is such a case, all four take the
+// division.  R = 0 gives 0 either way.
+__device__ __forceinline__ void rescale4(const float *R, float *T, double tot, double inv) {
+  unsigned near = 0xFFFFFFFFu, small = 0xFFFFFFFFu;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double qd = static_cast<double>(R[k]) * inv;
+    const unsigned long long bits = __double_as_longlong(qd);
+    T[k] = static_cast<float>(qd);
+    near = min(near, (static_cast<unsigned>(bits) & 0x1FFFFFFFu) - (0x10000000u - 4u));
+    small = min(small, static_cast<unsigned>(bits >> 32) - 1u);   // qd = 0 wraps round
+  }
+  // fp64 high word 0x3A900000 is 2^-86
+  if (__builtin_expect(near <= 8u || small < 0x3A900000u - 1u, 0)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) T[k] = rescale(R[k], tot) * kUnit;
+  }
 }
 
 // t at one vocabulary entry after `lev` rejections at the current node:
@@ -213,23 +256,31 @@ __device__ __forceinline__ float t_at(float p, float q, const unsigned long long
 // lo + 4*(j*T + tid) + x: each load instruction of a wave covers 1 KB of
 // the row, and a thread's entries ascend with (j, x).
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 template <int E, bool VEC>
 __device__ __forceinline__ void load_slice(const float *__restrict__ row, int lo, int hi, float (&v)[E], float fill) {
-  const int tid = threadIdx.x;
+  // recomputed at each call: kept from one call to the next, the offsets
+  // and bounds would hold registers across the whole walk
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   if constexpr (VEC) {
-    float4 x[E / 4];
+    // A raw buffer over the slice: a load past its end returns zeros (hi - lo
+    // is a multiple of 4, so a float4 lies wholly inside or outside), with
+    // no address clamp and no branch, and the loads of a slice stay in
+    // flight together.
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row + lo), 0, (hi - lo) * 4, 0x00020000);
+    u32x4 x[E / 4];
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) x[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (j * kAccThreads + tid), 0, 0);
 #pragma unroll
     for (int j = 0; j < E / 4; ++j) {
-      const int e = lo + 4 * (j * kAccThreads + tid);
-      x[j] = *reinterpret_cast<const float4 *>(row + (e < hi ? e : lo));
-    }
-#pragma unroll
-    for (int j = 0; j < E / 4; ++j) {
-      const bool ok = lo + 4 * (j * kAccThreads + tid) < hi;
-      v[4 * j + 0] = ok ? x[j].x : fill;
-      v[4 * j + 1] = ok ? x[j].y : fill;
-      v[4 * j + 2] = ok ? x[j].z : fill;
-      v[4 * j + 3] = ok ? x[j].w : fill;
+      const bool ok = fill == 0.0f || lo + 4 * (j * kAccThreads + tid) < hi;
+      v[4 * j + 0] = ok ? __uint_as_float(x[j].x) : fill;
+      v[4 * j + 1] = ok ? __uint_as_float(x[j].y) : fill;
+      v[4 * j + 2] = ok ? __uint_as_float(x[j].z) : fill;
+      v[4 * j + 3] = ok ? __uint_as_float(x[j].w) : fill;
     }
   } else {
 #pragma unroll
@@ -242,6 +293,53 @@ __device__ __forceinline__ void load_slice(const float *__restrict__ row, int lo
       }
   }
 }
+
+// Entries 4j .. 4j+3 of this thread's slice (0 past its end), as load_slice
+// places them.
+template <bool VEC>
+__device__ __forceinline__ void load_four(const float *__restrict__ row, int lo, int hi, int j, float *v) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int e = lo + 4 * (j * kAccThreads + tid);
+  if constexpr (VEC) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row + lo), 0, (hi - lo) * 4, 0x00020000);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (e - lo), 0, 0);
+    v[0] = __uint_as_float(x.x);
+    v[1] = __uint_as_float(x.y);
+    v[2] = __uint_as_float(x.z);
+    v[3] = __uint_as_float(x.w);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = e + k < hi ? row[e + k] : 0.0f;
+  }
+}
+
+// This thread's slice of `row` straight into LDS (16 bytes per lane, no
+// registers): float4 j of thread t lands at q_lds[j * kAccThreads + t].  A
+// lane past the slice end reads the slice's first float4 instead: the walk
+// never weighs those entries (their p entry is 0, so their residual is 0
+// whatever q holds there).
+// The copies are issued as inline assembly (dma16), unseen by the
+// compiler's wait placement, which would otherwise hold every LDS access of
+// the kernel until they land; the walk waits for them itself (await_slices)
+// before it first reads q_lds.
+template <int E>
+__device__ __forceinline__ void slice_to_lds(const float *__restrict__ row, int lo, int hi, float4 *q_lds) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const uint32_t wave_lds =
+      lds_offset(q_lds) + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tid) & ~(kWave - 1)) * 16u;
+#pragma unroll
+  for (int j = 0; j < E / 4; ++j) {
+    const int e = lo + 4 * (j * kAccThreads + tid);
+    dma16(row + (e < hi ? e : lo), wave_lds + j * kAccThreads * 16u);
+  }
+}
+
+// Waits for every vector-memory load this wave has in flight, the draft
+// slice's LDS copy included; the memory clobber keeps LDS reads after it.
+__device__ __forceinline__ void await_slices() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
 template <int E>
 __device__ __forceinline__ int slice_index(int lo, int n) {
@@ -284,6 +382,9 @@ __device__ void write_outputs(const AcceptArgs &a, int b, const int *s_path, con
 // Keeps the compiler from interleaving the fp64 divisions of many entries
 // (each holds about ten registers while in flight).
 __device__ __forceinline__ void one_at_a_time() { __builtin_amdgcn_sched_barrier(0); }
+// The same, except that LDS reads may move across (the next four entries'
+// q is read ahead).
+__device__ __forceinline__ void four_at_a_time() { __builtin_amdgcn_sched_barrier(0x0100); }
 
 // The workgroup whose slice holds the crossing T of the running mass (lane x
 // holds workgroup x's mass), and the mass of the slices before it.
@@ -302,7 +403,7 @@ __device__ __forceinline__ int group_owner(unsigned long long px, int W, unsigne
 }
 
 template <int E, bool STOCH, bool VEC>
-__global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
+__global__ void __launch_bounds__(kAccThreads, 2) accept_kernel(AcceptArgs a) {
   const int b = a.b0 + static_cast<int>(blockIdx.x) / a.W;
   const int c = static_cast<int>(blockIdx.x) % a.W;
   if (b >= a.B) return;
@@ -327,18 +428,69 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
   __shared__ float s_py[256], s_qy[256];
   __shared__ int s_nk;
 
-  for (int i = tid; i < N; i += kAccThreads) {
-    const int64_t g = static_cast<int64_t>(b) * N + i;
-    s_tok[i] = a.tokens[g];
-    s_nxt[i] = a.next_token[g];
-    s_sib[i] = a.next_sibling[g];
+  // Slices of node u's rows, loaded where the node is chosen so that they are
+  // in flight while the rest of its step is prepared: r = its target row
+  // (registers); stochastic, its children's draft row goes to LDS (q_lds,
+  // E KB, entry 4j+k of thread t at float4 j * kAccThreads + t): it is read
+  // once per level and would otherwise hold E registers.  A node without
+  // children has no levels and reads no q.
+  extern __shared__ __attribute__((aligned(16))) float4 q_lds[];
+  float r[E];
+  auto load_q = [&](int qr, bool has_kids) {
     if constexpr (STOCH) {
-      s_qr[i] = a.q_row[g];
-      s_ua[i] = a.u_accept[g];
+      if (has_kids) {
+        const float *qrow = a.draft + (static_cast<int64_t>(b) * a.R + qr) * V;
+        if constexpr (VEC) {
+          slice_to_lds<E>(qrow, lo, hi, q_lds);
+        } else {
+#pragma unroll
+          for (int j = 0; j < E / 4; ++j) {
+            float q4[4];
+            load_four<false>(qrow, lo, hi, j, q4);
+            q_lds[j * kAccThreads + tid] = make_float4(q4[0], q4[1], q4[2], q4[3]);
+          }
+        }
+      }
+    }
+  };
+  auto load_p = [&](int node) {
+    load_slice<E, VEC>(a.target + (static_cast<int64_t>(b) * N + node) * V, lo, hi, r, STOCH ? 0.0f : -INFINITY);
+  };
+  // The tree (N <= kAccThreads: one node per thread) and the root's slices
+  // are read together: the root's target row is known before the tree, and
+  // its draft row index is read on its own.  The draft slice's copy goes
+  // first, then the tree, then the target slice: the tree is then waited
+  // for without waiting for the target slice.
+  int rem = a.remaining ? a.remaining[b] : INT_MAX;   // (first: its wait then waits for nothing else)
+  if constexpr (STOCH) {
+    // a root without children has its draft row read all the same (when the
+    // index is valid), and never used
+    const int qr0 = a.q_row[static_cast<int64_t>(b) * N];
+    load_q(qr0, qr0 >= 0 && qr0 < a.R);
+  }
+  int g_tok = 0, g_nxt = 0, g_sib = 0, g_qr = 0;
+  float g_ua = 0.0f;
+  if (tid < N) {
+    const int64_t g = static_cast<int64_t>(b) * N + tid;
+    g_tok = a.tokens[g];
+    g_nxt = a.next_token[g];
+    g_sib = a.next_sibling[g];
+    if constexpr (STOCH) {
+      g_qr = a.q_row[g];
+      g_ua = a.u_accept[g];
+    }
+  }
+  load_p(0);
+  if (tid < N) {
+    s_tok[tid] = g_tok;
+    s_nxt[tid] = g_nxt;
+    s_sib[tid] = g_sib;
+    if constexpr (STOCH) {
+      s_qr[tid] = g_qr;
+      s_ua[tid] = g_ua;
     }
   }
   if (tid == 0) s_path[0] = 0;
-  int rem = a.remaining ? a.remaining[b] : INT_MAX;
   if (rem < 0) rem = 0;
   __syncthreads();
 
@@ -373,11 +525,9 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
   while (rem > 0 && n_out < max_out) {
     const float *prow = a.target + (static_cast<int64_t>(b) * N + u) * V;
     if constexpr (!STOCH) {
-      float p[E];
-      load_slice<E, VEC>(prow, lo, hi, p, -INFINITY);
       float bv;
       int bi;
-      thread_best<E>(p, lo, hi, bv, bi);
+      thread_best<E>(r, lo, hi, bv, bi);
       const int t = group_best(bv, bi);
       int match = -1;
       int cc = s_nxt[u];
@@ -396,6 +546,7 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
       }
       if (t == a.eos || n_out == rem || match < 0) break;
       u = match;
+      load_p(u);
       continue;
     } else {
       // ---------------- stochastic: t is held as (r, s); level 0 is t = p
@@ -419,17 +570,12 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
         s_py[i] = prow[y];
         s_qy[i] = qrow[y];
       }
-      float r[E], q[E];
-      load_slice<E, VEC>(prow, lo, hi, r, 0.0f);
-      if (has_kids) {
-        load_slice<E, VEC>(qrow, lo, hi, q, 0.0f);
-      } else {
-#pragma unroll
-        for (int n = 0; n < E; ++n) q[n] = 0.0f;
-      }
       __syncthreads();
-      bool scaled = false;           // t = r / s (else t = r)
-      double s = 1.0;
+      // r holds t itself (scaled false: the row p, or t rebuilt after a level
+      // of zero mass), or the last residual R in units of 2^-40, with
+      // T = R / tot (scaled true)
+      bool scaled = false;
+      double tot_d = 1.0, inv = 1.0;
       int nlev = 0;
       int accepted = -1;
       unsigned long long last_total = 0;
@@ -443,16 +589,40 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
           break;
         }
         // rejection: r <- max(t - q, 0) and its mass
-        unsigned long long m = 0;
+        if (nlev == 0) await_slices();
+        // (T - q * 2^40 as one fma: the product is exact, so this is the
+        // rounded difference in units of 2^-40)
+        double m = 0.0;
+        if (scaled) {
 #pragma unroll
-        for (int n = 0; n < E; ++n) {
-          const float t = scaled ? rescale(r[n], s) : r[n];
-          r[n] = fmaxf(t - q[n], 0.0f);
-          m += mass(r[n]);
-          one_at_a_time();
+          for (int g = 0; g < E / 4; ++g) {
+            const float4 q4 = q_lds[g * kAccThreads + tid];
+            const float qg[4] = {q4.x, q4.y, q4.z, q4.w};
+            float T[4];
+            rescale4(&r[4 * g], T, tot_d, inv);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              r[4 * g + k] = fmaxf(fmaf(qg[k], -kUnit, T[k]), 0.0f);
+              m += mass_of(r[4 * g + k]);
+            }
+            four_at_a_time();
+          }
+        } else {
+          // t * 2^40 - q * 2^40, both products exact
+#pragma unroll
+          for (int g = 0; g < E / 4; ++g) {
+            const float4 q4 = q_lds[g * kAccThreads + tid];
+            const float qg[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              r[4 * g + k] = fmaxf(fmaf(r[4 * g + k], kUnit, qg[k] * -kUnit), 0.0f);
+              m += mass_of(r[4 * g + k]);
+            }
+            four_at_a_time();
+          }
         }
         unsigned long long lane_mass;
-        const unsigned long long tot = group_mass(m, lane_mass);
+        const unsigned long long tot = group_mass(to_u64(m), lane_mass);
         if (tid == 0) s_Slev[nlev] = tot;
         __syncthreads();
         ++nlev;
@@ -460,14 +630,20 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
         last_lane = lane_mass;
         if (tot > 0) {
           scaled = true;
-          s = static_cast<double>(tot) * 0x1p-40;
+          tot_d = static_cast<double>(tot);
+          inv = 0x1p40 / tot_d;
         } else {
           // A level of zero mass leaves t as it was, but r already holds its
           // residual: rebuild t from the row through the levels so far (rare).
-          load_slice<E, VEC>(prow, lo, hi, r, 0.0f);
+          // (four entries at a time, to hold few registers on this path)
 #pragma unroll
-          for (int n = 0; n < E; ++n) {
-            r[n] = t_at(r[n], q[n], s_Slev, nlev);
+          for (int j = 0; j < E / 4; ++j) {
+            float p4[4];
+            load_four<VEC>(prow, lo, hi, j, p4);
+            const float4 q4 = q_lds[j * kAccThreads + tid];
+            const float qg[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r[4 * j + k] = t_at(p4[k], qg[k], s_Slev, nlev);
             one_at_a_time();
           }
           scaled = false;
@@ -483,6 +659,11 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
         ++path_len;
         if (y == a.eos || n_out == rem) break;
         u = accepted;
+        {
+          const int nqr = s_qr[u];
+          load_q(nqr, s_nxt[u] > 0 && s_nxt[u] < N && nqr >= 0 && nqr < a.R);
+          load_p(u);
+        }
         __syncthreads();             // s_kid / s_py / s_qy are rewritten for the next node
         continue;
       }
@@ -496,22 +677,33 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
         lane_mass = last_lane;
         total = last_total;
       } else {
-        unsigned long long m = 0;
+        // t itself (a leaf's bonus, or every residual of zero mass), to
+        // units of 2^-40
+        if (scaled) {
+#pragma unroll
+          for (int g = 0; g < E / 4; ++g) {
+            float T[4];
+            rescale4(&r[4 * g], T, tot_d, inv);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r[4 * g + k] = T[k];
+            one_at_a_time();
+          }
+          scaled = false;
+        } else {
+#pragma unroll
+          for (int n = 0; n < E; ++n) r[n] *= kUnit;
+        }
+        double m = 0.0;
 #pragma unroll
         for (int n = 0; n < E; ++n) {
-          m += mass(scaled ? rescale(r[n], s) : r[n]);
-          one_at_a_time();
+          m += mass_of(r[n]);
+          if ((n & 3) == 3) one_at_a_time();
         }
-        total = group_mass(m, lane_mass);
+        total = group_mass(to_u64(m), lane_mass);
       }
 
       if (total == 0) {
-        // degenerate: argmax of t, lowest id
-#pragma unroll
-        for (int n = 0; n < E; ++n) {
-          r[n] = scaled ? rescale(r[n], s) : r[n];
-          one_at_a_time();
-        }
+        // degenerate: argmax of t, lowest id (r holds t, in units of 2^-40)
         float bv;
         int bi;
         thread_best<E>(r, lo, hi, bv, bi);
@@ -542,10 +734,9 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(AcceptArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int n = 4 * j + k;
-          const float w = from_residual ? r[n] : (scaled ? rescale(r[n], s) : r[n]);
-          w4[k] = mass(w);
+          w4[k] = mass(r[n]);
           sum += w4[k];
-          one_at_a_time();
+          if (k == 3) one_at_a_time();
         }
         unsigned long long grp_total;
         const unsigned long long before = base + block_exclusive_scan(sum, grp_total);
@@ -614,20 +805,29 @@ const void *accept_kernel_for(int E, bool stoch, bool vec) {
   }
 }
 
-// Resident workgroups per CU of one kernel variant, queried once per device.
+// Dynamic LDS of a variant: the stochastic walk keeps the draft slice there.
+size_t accept_lds(int E, bool stoch) { return stoch ? static_cast<size_t>(E) * kAccThreads * sizeof(float) : 0; }
+
+// Resident workgroups per CU of one kernel variant, queried once per device
+// (which also raises the variant's dynamic LDS limit on that device).
 int32_t blocks_per_cu(int E, bool stoch, bool vec, int &per_cu) {
   constexpr int kDevices = 64;
   static std::atomic<int> cache[kDevices][5][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "verify_accept: no device");
+  if (dev < 0 || dev >= kDevices) return fail(SDV_E_UNSUPPORTED, "verify_accept: device %d", dev);
   int ei = 0;
   while ((4 << ei) < E) ++ei;
-  std::atomic<int> *slot = dev < kDevices ? &cache[dev][ei][stoch][vec] : nullptr;
-  per_cu = slot ? slot->load(std::memory_order_relaxed) : 0;
+  std::atomic<int> *slot = &cache[dev][ei][stoch][vec];
+  per_cu = slot->load(std::memory_order_relaxed);
   if (per_cu > 0) return SDV_OK;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel_for(E, stoch, vec), kAccThreads, 0);
+  const void *fn = accept_kernel_for(E, stoch, vec);
+  const size_t lds = accept_lds(E, stoch);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return fail(SDV_E_HIP, "verify_accept: LDS attribute: %s", hipGetErrorString(e));
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kAccThreads, lds);
   if (e != hipSuccess || per_cu <= 0) return fail(SDV_E_HIP, "verify_accept: occupancy query failed");
-  if (slot) slot->store(per_cu, std::memory_order_relaxed);
+  slot->store(per_cu, std::memory_order_relaxed);
   return SDV_OK;
 }
 
@@ -729,7 +929,8 @@ int32_t run_accept(sdv_accept_shape sh, int32_t eos_id, const int32_t *remaining
     a.b0 = b0;
     const int nb = (sh.B - b0 < p.per_launch ? sh.B - b0 : p.per_launch);
     void *args[] = {&a};
-    hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(nb * p.W)), dim3(kAccThreads), args, 0, st);
+    hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(nb * p.W)), dim3(kAccThreads), args,
+                                   accept_lds(p.E, sh.mode == SDV_ACCEPT_STOCHASTIC), st);
     if (e != hipSuccess) return fail(SDV_E_HIP, "verify_accept: launch: %s", hipGetErrorString(e));
   }
   return SDV_OK;

@@ -60,7 +60,7 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 // 4 bytes per lane from global memory straight into LDS (lane L writes LDS
-// bytes lds_addr + 4*L .. +3); same conventions as dma16 below.
+// bytes lds_addr + 4*L .. +3); same conventions as dma16.
 __device__ __forceinline__ void dma4(const void *gaddr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
 }
@@ -70,15 +70,6 @@ __device__ __forceinline__ void dma4(const void *gaddr, uint32_t lds_addr) {
 __device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory", "m0");
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane L writes LDS
-// bytes lds_addr + 16*L .. +15 (lds_addr is wave-uniform, via M0).  Issued
-// as inline assembly so that the compiler does not add its conservative
-// "wait for every LDS DMA before any LDS read"; the kernels wait explicitly
-// (wait_vmcnt) and the memory clobber keeps LDS reads from moving across.
-__device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
 }
 
 // Lane l's value combined with lane l^16's (l^32's): the row-half swap
@@ -98,17 +89,6 @@ __device__ __forceinline__ float sum_xor16(float x) {
 __device__ __forceinline__ float sum_xor32(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
-}
-
-// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 namespace {

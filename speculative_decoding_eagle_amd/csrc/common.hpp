@@ -111,4 +111,26 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x)
   return x;
 }
 
+// ------------------------------------------------------------ LDS DMA
+
+// 16 bytes per lane from global memory straight into LDS: lane L writes LDS
+// bytes lds_addr + 16*L .. +15 (lds_addr is wave-uniform, via M0).  Issued
+// as inline assembly so that the compiler does not add its conservative
+// "wait for every LDS DMA before any LDS read"; the kernels wait explicitly
+// (wait_vmcnt) and the memory clobber keeps LDS reads from moving across.
+__device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
+}
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 }  // namespace sdv
