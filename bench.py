@@ -349,10 +349,11 @@ MEASURED_TRAFFIC = {
     "tree_attention": {
         "workload": "c3",
         "sources": ["speculative_decoding_eagle_amd/csrc/attn_wide.hip",
-                    "speculative_decoding_eagle_amd/csrc/attn_common.hpp"],
-        "sha256": "1474d20878c645eb0d00eb191903cc15da22383fa9b28e2b8ab8b1535cb05243",
-        "fetch_kib": 206288.1, "fetch_factor": 1.99996,
-        "write_kib": 63016.0, "write_factor": 1.0,
+                    "speculative_decoding_eagle_amd/csrc/attn_common.hpp",
+                    "speculative_decoding_eagle_amd/csrc/common.hpp"],
+        "sha256": "efda36c6397e16e60ca0a7fd6dc19038cef6f5f9377bfab86fcc72a3af05a505",
+        "fetch_kib": 204409.7, "fetch_factor": 1.99996,
+        "write_kib": 47382.6, "write_factor": 1.0,
     },
 }
 

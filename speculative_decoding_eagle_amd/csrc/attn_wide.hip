@@ -5,15 +5,21 @@
 // EAGLE" section 6, TARGET_VERIFY).  Same operation and arguments as the
 // kernel in attn.hip, another work layout.
 //
-// Work layout.  A unit is one (request, KV head) and its N*G query rows (row
-// = node*G + g).  A workgroup of eight waves owns 256 rows of a unit, wave w
-// rows 32w .. 32w+31 against all 64 keys of every tile, so each K/V tile is
-// copied into LDS once for all of those rows (128-row workgroups would copy
-// every tile twice).  When there are few units, a unit's key tiles are split
-// between two workgroups (chunks) so that 256 CUs get enough pieces of equal
-// size; the workgroup that finishes second merges the two partial softmax
-// states (m, l, O), in chunk order, so the result does not depend on which
-// one finished first.
+// Work layout.  A unit is one (request, KV head, block of 256 query rows)
+// (row = node*G + g).  A workgroup of eight waves works on 256 rows of a
+// unit, wave w rows 32w .. 32w+31 against all 64 keys of every tile, so
+// each K/V tile is copied into LDS once for all of those rows (128-row
+// workgroups would copy every tile twice).
+//   * Schedule.  With a workspace, the grid is persistent (one workgroup per
+//     CU at most): every unit weighs a fixed piece cost plus a cost per key
+//     tile, the units of the length-ranked requests form one weighted
+//     sequence, and workgroup ri takes the tiles whose start falls in the
+//     ri-th of equal ranges of it (stream-K).  A unit cut between ranges
+//     runs as several pieces; each piece keeps its partial softmax state
+//     (m, l, O), and the piece that takes the unit's last ticket merges all
+//     of them in range order, so the result does not depend on which piece
+//     finished last.  The ranges of one XCD are consecutive, so a unit's
+//     pieces share an L2.  Without a workspace, one workgroup per unit.
 //   * K and V tiles move from the paged pool into LDS by DMA
 //     (global_load_lds_dwordx4) through a ring of four K tiles and a ring of
 //     four V tiles, the K stream one tile ahead; the chunk swizzle keeps the
@@ -28,12 +34,13 @@
 //     ring; a key's slot is clamped into the pool, and positions past the
 //     request read its last token (finite data that the mask turns into a
 //     zero weight), so every DMA reads real pool rows.
-//   * The merge protocol: each chunk takes a ticket (an atomic counter per
-//     unit); the first publishes its (m, l, O) in the workspace and bumps a
-//     second counter; the last waits for it (bounded), merges, writes the
-//     output and resets both counters to zero for the next call.  A wait
-//     that gives up writes NaN rows and sets SDV_STATUS_ATTN_MERGE_WAIT in
-//     the workspace header (the counters must then be reset by the host).
+//   * The merge protocol: each piece takes a ticket (an atomic counter per
+//     unit); the others publish their (m, l, O) in their workspace slots and
+//     count themselves on a second counter after an agent-scope release; the
+//     last waits for that count (bounded), merges, writes the output and
+//     resets both counters to zero for the next call.  A wait that gives up
+//     writes NaN rows and sets SDV_STATUS_ATTN_MERGE_WAIT in the workspace
+//     header (the counters must then be reset by the host).
 #include <type_traits>
 
 #include "attn_common.hpp"
