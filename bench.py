@@ -33,7 +33,7 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE = 3                     # input sets the timed steps rotate through
 # read-only inputs that are rotated (outputs, tables and small arrays are not)
-ROTATED = ("draft_probs", "draft_logits_in", "target", "q", "k_pool", "v_pool", "hidden", "weight", "q_pruned",
+ROTATED = ("draft_probs", "draft_logits_in", "draft_logits", "target_logits", "target", "q", "k_pool", "v_pool", "hidden", "weight", "q_pruned",
            "mask_bits")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--accept", default="literal", choices=["literal", "planted", "full"],
                     help="literal inputs; planted: a seeded accepted path of U{0..S} nodes per request; full: "
                          "every request accepts S nodes (a stress case for the compaction)")
+    ap.add_argument("--logits", action="store_true",
+                    help="stochastic workloads: read the draft and target logits and compute both processed "
+                         "distributions softmax(logits / T) on the GPU inside the step (two more stages)")
     ap.add_argument("--draft-input", default="probs", choices=["probs", "logits_f32", "logits_bf16"],
                     help="what the draft top-k reads: the processed probability rows, or the draft logits "
                          "(fp32 or bf16) with the softmax fused into the top-k (non-TLI workloads)")
@@ -91,7 +94,7 @@ class Pipeline:
     """Preallocated device buffers and the per-stage calls of one step."""
 
     def __init__(self, cfg, inp, n_tables, accept_mode, draft_input="probs", extend_prep=False, chain=False,
-                 kv_alloc=False, layers=1):
+                 kv_alloc=False, layers=1, logits=False):
         import torch
         import speculative_decoding_eagle_amd as sdv
         self.torch, self.sdv, self.cfg = torch, sdv, cfg
@@ -114,6 +117,13 @@ class Pipeline:
         else:
             self.draft_rows = d["draft_probs"]
         self.draft_input = draft_input
+        self.logits = logits
+        if logits:
+            # the processed rows are this step's outputs: the stages below
+            # write them from the logits
+            d["draft_probs"] = torch.empty_like(d["draft_logits"])
+            d["target"] = torch.empty_like(d["target_logits"])
+            self.draft_rows = d["draft_probs"]
         self.extend_prep = extend_prep
         self.chain = chain
         self.kv_alloc = kv_alloc and cfg.has_attention
@@ -178,12 +188,16 @@ class Pipeline:
         self.sets = [d]
         for _ in range(1, ROTATE):
             self.sets.append({key: (val.clone() if key in ROTATED and val.numel() * val.element_size() > (1 << 20)
-                                    else val) for key, val in d.items()})
+                                    and not (logits and key in ("draft_probs", "target")) else val)
+                              for key, val in d.items()})
         torch.cuda.synchronize()
 
     def use(self, i):
         """Point the stages at input set i % ROTATE."""
         self.d = self.sets[i % len(self.sets)]
+        if self.logits:
+            # the outputs of the softmax stages are shared by every set
+            self.d["draft_probs"], self.d["target"] = self.sets[0]["draft_probs"], self.sets[0]["target"]
         self.target = self.d["target"]
         if not self.cfg.is_tli:
             self.draft_rows = self.d["draft_probs"]
@@ -208,6 +222,9 @@ class Pipeline:
                     break
                 if self.mode == self.sdv.GREEDY:
                     t[b, u, int(tok[b, c])] = t[b, u].max() + 1.0
+                elif self.logits:
+                    # equal logits at the same temperature give p = q bit for bit
+                    self.d["target_logits"][b, u] = self.d["draft_logits"][b, int(qr[b, u])]
                 else:
                     t[b, u] = self.draft_rows[b, int(qr[b, u])]
                 u = c
@@ -220,6 +237,12 @@ class Pipeline:
         sdv.sdv_tli_constrain_draft_logits(self.logits, d["inter_ids"], cfg.V_draft, full=self.full)
         # the target -> intersection inverse was built at set-up (the maps are static)
         sdv.sdv_tli_q_scatter(d["q_pruned"], None, cfg.V, q_target=self.q_target, ws=self.scatter_ws)
+
+    def s_softmax_draft(self):
+        self.sdv.sdv_softmax_rows(self.d["draft_logits"], self.cfg.temperature, out=self.d["draft_probs"])
+
+    def s_softmax_target(self):
+        self.sdv.sdv_softmax_rows(self.d["target_logits"], self.cfg.temperature, out=self.d["target"])
 
     def s_topk(self):
         if self.draft_input == "probs":
@@ -282,9 +305,13 @@ class Pipeline:
             st.append(("kv_alloc_draft", lambda: self.s_kv_draft(i)))
         if cfg.is_tli:
             st.append(("tli_head_mask_scatter", self.s_tli))
+        if self.logits:
+            st.append(("softmax_draft", self.s_softmax_draft))
         st += [("draft_topk", self.s_topk), ("build_tree", self.s_tree)]
         if cfg.has_attention:
             st.append(("tree_attention", lambda: self.s_attn(i)))
+        if self.logits:
+            st.append(("softmax_target", self.s_softmax_target))
         st.append(("accept", self.s_accept))
         if cfg.has_attention:
             st.append(("compact_kv", lambda: self.s_compact(i)))
@@ -306,6 +333,10 @@ def algorithmic_work(cfg, inp, pipe):
     B, N, V, R, k = cfg.B, cfg.N, cfg.V, cfg.R, cfg.k
     row_bytes = 2 if pipe.draft_input == "logits_bf16" else 4
     out = {"draft_topk": dict(bytes=B * R * V * row_bytes + B * R * k * 8, flops=0)}
+    if pipe.logits:
+        # every row read once and written once
+        out["softmax_draft"] = dict(bytes=B * R * V * 8, flops=0)
+        out["softmax_target"] = dict(bytes=B * N * V * 8, flops=0)
     if cfg.has_attention:
         L = inp["prefix_len"].astype(np.int64)
         depth = pipe.tree["depth"].cpu().numpy().astype(np.int64)
@@ -389,14 +420,16 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(cfg, inp, n_req, threads=1):
+def cpu_baseline(cfg, inp, n_req, threads=1, logits=False):
     """The oracle, as it stands, on the first n_req requests of the same
     workload, BLAS limited to `threads` threads (the tree build and walks are
-    single-threaded Python); scaled to verified tokens/s."""
+    single-threaded Python); scaled to verified tokens/s.  With `logits`, the
+    step starts from the draft and target logits as the GPU step does."""
     from threadpoolctl import threadpool_limits
     import oracle.accept as oacc
     import oracle.attention as oatt
     import oracle.compact as ocmp
+    import oracle.softmax as osm
     import oracle.tli as otli
     import oracle.topk as otopk
     import oracle.tree as otree
@@ -410,6 +443,8 @@ def cpu_baseline(cfg, inp, n_req, threads=1):
             otli.constrain_logits(logits.astype(np.float32), inp["inter_ids"], cfg.V_draft)
             rows = otli.q_scatter(inp["q_pruned"][sl].reshape(-1, cfg.K_inter), inp["tgt_ids"], cfg.V)
             rows = rows.reshape(n, cfg.R, cfg.V)
+        elif logits:
+            rows = osm.softmax_rows(inp["draft_logits"][sl], cfg.temperature).astype(np.float32)
         else:
             rows = inp["draft_probs"][sl]
         tp, ti = otopk.draft_topk(rows, cfg.k)
@@ -420,8 +455,9 @@ def cpu_baseline(cfg, inp, n_req, threads=1):
         if cfg.mode == "greedy":
             acc = oacc.verify_greedy(tree, inp["target"][sl], cfg.S)
         else:
-            acc = oacc.verify_stochastic(tree, inp["target"][sl], rows, inp["u_accept"][sl], inp["u_draw"][sl],
-                                         cfg.S)
+            target = osm.softmax_rows(inp["target_logits"][sl], cfg.temperature).astype(np.float32) if logits \
+                else inp["target"][sl]
+            acc = oacc.verify_stochastic(tree, target, rows, inp["u_accept"][sl], inp["u_draw"][sl], cfg.S)
         if cfg.has_attention:
             ocmp.compact_kv(inp["page_table"][sl], [], [], inp["prefix_len"][sl], acc["accept_len"],
                             acc["accept_path"], cfg.N, cfg.page) if cfg.page == 1 else \
@@ -478,14 +514,17 @@ def main():
         print("--draft-input %s: the TLI workloads take the draft rows from the pruned head" % args.draft_input,
               file=sys.stderr)
         sys.exit(2)
-    inp = workloads.generate(cfg, with_logits=args.draft_input != "probs")
+    if args.logits and (cfg.mode != "stochastic" or cfg.is_tli or args.draft_input != "probs"):
+        print("--logits: the non-TLI stochastic workloads (c2, c4) with --draft-input probs", file=sys.stderr)
+        sys.exit(2)
+    inp = workloads.generate(cfg, with_logits=args.draft_input != "probs" or args.logits)
     t_gen = time.perf_counter() - t_gen
     log("inputs ready in %.1f s; uploading and warming up" % t_gen)
     if args.chain and (cfg.k != 1 or cfg.N != cfg.S + 1):
         print("--chain needs a k = 1 workload whose tree keeps every step (N = S + 1)", file=sys.stderr)
         sys.exit(2)
     pipe = Pipeline(cfg, inp, args.warmup + args.steps + 1, args.accept, args.draft_input, args.extend_prep,
-                    args.chain, args.kv_alloc, args.layers)
+                    args.chain, args.kv_alloc, args.layers, args.logits)
     stages = [name for name, _ in pipe.stages(0)]
 
     for i in range(args.warmup):
@@ -546,7 +585,7 @@ def main():
         "dtype": "f32+bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[cfg.name], "name": cfg.name, "batch": cfg.B, "tree_tokens": cfg.N,
-                   "accept": args.accept, "draft_input": args.draft_input,
+                   "accept": args.accept, "draft_input": args.draft_input, "logits": args.logits,
                    "extend_prep": args.extend_prep, "chain": args.chain,
                    "kv_alloc": args.kv_alloc, "kv_layers": args.layers},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
@@ -558,10 +597,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample (one core, then every core of this process)")
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample, threads=1)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample, threads=1, logits=args.logits)
         ncores = len(os.sched_getaffinity(0))
         if ncores > 1:
-            allc = cpu_baseline(cfg, inp, args.cpu_sample, threads=ncores)
+            allc = cpu_baseline(cfg, inp, args.cpu_sample, threads=ncores, logits=args.logits)
             line["cpu_baseline"]["all_cores"] = {k: allc[k] for k in ("value", "cores", "sample")}
     print(json.dumps(line), flush=True)
 

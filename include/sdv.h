@@ -154,6 +154,28 @@ int32_t sdv_draft_topk_logits(const void *logits, int32_t dtype, int64_t rows, i
                               size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Processed distributions from logits: p = softmax(logits / T) per row, the
+ * target-side processing the stochastic verify consumes and the draft's
+ * per-step softmax ("[SGLang] Multi-Layer EAGLE", section 3: softmax, then
+ * fast_topk, after each draft pass; zero-to-sglang ch.10 section 5.1: the
+ * acceptance test compares the target's and the draft's probabilities).
+ *
+ * For every row r of logits (device, [rows, V] fp32, rows contiguous;
+ * entries may be -inf, at least one finite per row, no NaN) writes
+ * probs[r] (device, [rows, V] fp32) = exp((x - m) / T) / (sum of the same
+ * over the row), m the row maximum.  Computed in fp32 as
+ * 2^(x * c - m * c) with c = log2(e) / T and the normaliser summed in a
+ * fixed order, so the result is deterministic for a given shape and
+ * device; per entry within 3e-5 of the exact value, relative, for rows whose
+ * finite logits span at most 64 * T.  A -inf entry gives exactly 0.
+ * temperature finite and > 0; V >= 1; rows < 2^31.  probs must not alias
+ * logits.  No workspace; asynchronous on `stream`.  Errors: SDV_E_SHAPE,
+ * SDV_E_NULL, SDV_E_UNSUPPORTED, SDV_E_HIP.
+ * ---------------------------------------------------------------------- */
+int32_t sdv_softmax_rows(const float *logits, int64_t rows, int32_t V, float temperature, float *probs,
+                         void *stream);
+
+/* ------------------------------------------------------------------------
  * A2-A4  Candidate tree, positions, mask and retrieve arrays.
  * "[SGLang] Multi-Layer EAGLE", section 2 (select_top_k_tokens builds
  * tree_info = scores, tokens, parents with cumulative scores);

@@ -12,6 +12,9 @@ Modules and the passages they follow:
 
 * ``topk``      -- per-row draft top-k (``fast_topk`` after the per-step softmax;
                    "[SGLang] Multi-Layer EAGLE", section 3, draft extend).
+* ``softmax``   -- the processed distributions softmax(logits / T) that the
+                   draft's top-k and the stochastic verify consume (same page
+                   section 3; zero-to-sglang ch.10 section 5.1).
 * ``tree``      -- frontier expansion with cumulative scores and the final tree
                    (``select_top_k_tokens`` / ``tree_info``, same page section 2;
                    ``build_eagle_tree`` in "EAGLE speculative decoding in four

@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     sdv_draft_extend_prep,
     sdv_draft_topk,
     sdv_draft_topk_logits,
+    sdv_softmax_rows,
     sdv_kv_alloc_backup,
     sdv_kv_alloc_branches,
     sdv_kv_alloc_extend,

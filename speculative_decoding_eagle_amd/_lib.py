@@ -50,6 +50,7 @@ SIGNATURES = {
     "sdv_draft_topk": (c_i32, [c_p, c_i64, c_i32, c_i32, c_p, c_p, c_p, c_sz, c_p]),
     "sdv_draft_topk_logits_workspace_size": (c_sz, [c_i64, c_i32, c_i32]),
     "sdv_draft_topk_logits": (c_i32, [c_p, c_i32, c_i64, c_i32, c_i32, c_f32, c_p, c_p, c_p, c_sz, c_p]),
+    "sdv_softmax_rows": (c_i32, [c_p, c_i64, c_i32, c_f32, c_p, c_p]),
     "sdv_build_tree": (c_i32, [TreeShape] + [c_p] * 15 + [c_p]),
     "sdv_tree_verify_attention_workspace_size": (c_sz, [AttnShape]),
     "sdv_tree_verify_attention": (c_i32, [AttnShape, c_f32] + [c_p] * 8 + [c_p, c_sz, c_p]),

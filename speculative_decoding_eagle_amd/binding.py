@@ -167,6 +167,22 @@ def sdv_draft_topk_logits(logits: torch.Tensor, k: int, temperature: float = 1.0
     return topk_p, topk_id
 
 
+def sdv_softmax_rows(logits: torch.Tensor, temperature: float = 1.0, out=None):
+    """softmax(logits / temperature) of every row of ``logits`` [..., V] (fp32)
+    -> fp32 tensor of the same shape."""
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V else 0
+    dev = logits.device
+    if out is None:
+        out = torch.empty(logits.shape, dtype=torch.float32, device=dev)
+    if out.shape != logits.shape:
+        raise ValueError("out must have the shape of logits")
+    L = _lib.lib()
+    _check(L.sdv_softmax_rows(_ptr(logits, torch.float32, "logits"), rows, V, float(temperature),
+                              _ptr(out, torch.float32, "out"), _stream(dev)), "sdv_softmax_rows")
+    return out
+
+
 # -------------------------------------------------------------------- A2-A4
 
 TREE_OUTPUTS = ("tokens", "parent", "depth", "positions", "score", "q_row", "mask", "mask_bits",

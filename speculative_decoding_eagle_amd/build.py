@@ -17,7 +17,7 @@ OUT = os.path.join(PKG, "libsdv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["common.hip", "topk.hip", "tree.hip", "attn.hip", "attn_wide.hip", "accept.hip", "compact.hip", "tli.hip", "extend.hip", "alloc.hip"]
+SOURCES = ["common.hip", "topk.hip", "tree.hip", "attn.hip", "attn_wide.hip", "accept.hip", "compact.hip", "tli.hip", "extend.hip", "alloc.hip", "softmax.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
                  "sdv_tli_q_scatter", "sdv_tli_build_maps", "sdv_draft_extend_prep", "sdv_build_chain", "sdv_kv_alloc_init",
                  "sdv_kv_alloc_backup", "sdv_kv_alloc_restore", "sdv_kv_alloc_free", "sdv_kv_alloc_extend",
                  "sdv_kv_alloc_branches", "sdv_kv_branch_pages", "sdv_last_error", "sdv_workspace_status",
-                 "sdv_set_wait_limit", "sdv_tli_check"):
+                 "sdv_set_wait_limit", "sdv_tli_check", "sdv_softmax_rows"):
         assert must in names
 
 
@@ -54,6 +54,12 @@ def test_host_side_validation_without_a_device():
     assert lib.sdv_draft_topk(None, 0, 10, 2, None, None, None, 0, None) == 0         # empty is fine
     assert lib.sdv_draft_topk_logits(None, 2, 4, 10, 2, 1.0, None, None, None, 0, None) == -3   # unknown dtype
     assert lib.sdv_draft_topk_logits(None, 1, 4, 10, 2, 0.0, None, None, None, 0, None) == -2   # temperature 0
+    assert lib.sdv_softmax_rows(None, 4, 10, 0.0, None, None) == -2      # temperature 0
+    assert lib.sdv_softmax_rows(None, 4, 10, float("nan"), None, None) == -2
+    assert lib.sdv_softmax_rows(None, 4, 0, 1.0, None, None) == -2        # V = 0
+    assert lib.sdv_softmax_rows(None, -1, 10, 1.0, None, None) == -2
+    assert lib.sdv_softmax_rows(None, 0, 10, 1.0, None, None) == 0        # nothing to do
+    assert lib.sdv_softmax_rows(None, 4, 10, 1.0, None, None) == -1       # NULL
     assert lib.sdv_draft_topk_logits(None, 0, 4, 10, 11, 1.0, None, None, None, 0, None) == -2  # k > V
     ash = _lib.AttnShape(1, 4, 6, 4, 128, 1, 10, 10)                                  # Hq % Hkv != 0
     assert lib.sdv_tree_verify_attention(ash, ctypes.c_float(0.0), *([None] * 8), None, 0, None) == -2

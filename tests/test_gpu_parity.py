@@ -15,6 +15,7 @@ from oracle import alloc as oal
 from oracle import attention as oatt
 from oracle import compact as ocmp
 from oracle import extend as oext
+from oracle import softmax as osm
 from oracle import tli as otli
 from oracle import topk as otopk
 from oracle import tree as otree
@@ -88,6 +89,41 @@ def test_topk_from_logits(rows, V, k, T, bf16, kind):
     assert np.array_equal(host(gi), oi)
     got = host(gp).astype(np.float64)
     assert np.all(np.abs(got - ov) <= 1e-4 * ov + 1e-37)
+
+
+# Processed distributions softmax(logits / T).  The GPU computes in fp32
+# (exponent 2^(x*c - m*c), c = log2(e)/T, normaliser summed in a fixed
+# order); per entry its error against the float64 definition is the rounding
+# of the exponent's argument, about |x - m| / T * 2^-23 relative (at most 60
+# here, i.e. 7e-6), one ulp of the exponential, the normaliser's fp32 sum
+# of up to a few hundred terms per thread (under 1e-5) and two roundings
+# of the output: 3e-5 relative bounds it with room.  -inf entries are exact
+# zeros.  Shapes: the vector path (V % 4 == 0) at the configs' V and rows,
+# the scalar path (V % 4 != 0, V = 1), masked rows, several temperatures.
+@pytest.mark.parametrize("rows,V,T,kind", [
+    (80, 128256, 1.0, "normal"), (24, 128256, 0.7, "normal"), (5, 128256, 0.5, "normal"), (7, 1000, 0.7, "normal"),
+    (3, 5, 1.0, "normal"), (9, 4099, 2.0, "normal"), (4, 1, 1.0, "normal"), (6, 40000, 0.8, "masked"),
+    (2, 131072, 1.0, "ties"), (0, 128256, 1.0, "normal")])
+def test_softmax_rows_against_the_float64_definition(rows, V, T, kind):
+    rng = np.random.default_rng(rows * 13 + V)
+    if kind == "ties":
+        x = (rng.integers(-12, 4, size=(rows, V)) / 4.0).astype(np.float32)
+    else:
+        x = (rng.standard_normal((rows, V)) * 3.0).astype(np.float32)
+    if kind == "masked":
+        x[rng.random((rows, V)) < 0.7] = -np.inf
+        x[:, 0] = 0.5
+    say("softmax_rows", rows, V, T, kind)
+    got = sdv.sdv_softmax_rows(dev(x), T)
+    again = sdv.sdv_softmax_rows(dev(x), T)
+    torch.cuda.synchronize()
+    g = host(got).astype(np.float64)
+    assert np.array_equal(host(got), host(again))              # deterministic
+    if rows == 0:
+        return
+    ref = osm.softmax_rows(x, T)
+    assert np.all(np.abs(g - ref) <= 3e-5 * ref + 1e-37), float(np.max(np.abs(g - ref) / np.maximum(ref, 1e-37)))
+    assert np.all(g[np.isneginf(x)] == 0.0)
 
 
 # Rows beyond a multiple of the compute units are cut into equal pieces

@@ -243,6 +243,7 @@ def generate(cfg: Config, *, with_attention: bool = True, with_rows: bool = True
     Keys (present when the config has the stage):
       draft_probs [B,R,V] f32 -- processed draft distributions (A1 input, q rows)
       draft_logits [B,R,V] f32 -- the logits they are softmax(. / T) of (with_logits)
+      target_logits [B,N,V] f32 -- stochastic: the logits p is softmax(. / T) of (with_logits)
       target      [B,N,V] f32 -- greedy: raw logits; stochastic: processed p
       root_token [B] i32, prefix_len [B] i32
       u_accept, u_draw [B,N] f32 (stochastic)
@@ -279,6 +280,8 @@ def generate(cfg: Config, *, with_attention: bool = True, with_rows: bool = True
             out["target"] = tl
         else:
             out["target"] = softmax_rows(tl, cfg.temperature)
+            if with_logits:
+                out["target_logits"] = tl
             del tl
         if cfg.mode == "stochastic":
             out["u_accept"] = uniforms24(rs["u_accept"], (B, N))
