@@ -117,7 +117,7 @@ class Pipeline:
         else:
             self.draft_rows = d["draft_probs"]
         self.draft_input = draft_input
-        self.logits = logits
+        self.from_logits = logits
         if logits:
             # the processed rows are this step's outputs: the stages below
             # write them from the logits
@@ -195,7 +195,7 @@ class Pipeline:
     def use(self, i):
         """Point the stages at input set i % ROTATE."""
         self.d = self.sets[i % len(self.sets)]
-        if self.logits:
+        if self.from_logits:
             # the outputs of the softmax stages are shared by every set
             self.d["draft_probs"], self.d["target"] = self.sets[0]["draft_probs"], self.sets[0]["target"]
         self.target = self.d["target"]
@@ -222,7 +222,7 @@ class Pipeline:
                     break
                 if self.mode == self.sdv.GREEDY:
                     t[b, u, int(tok[b, c])] = t[b, u].max() + 1.0
-                elif self.logits:
+                elif self.from_logits:
                     # equal logits at the same temperature give p = q bit for bit
                     self.d["target_logits"][b, u] = self.d["draft_logits"][b, int(qr[b, u])]
                 else:
@@ -305,12 +305,12 @@ class Pipeline:
             st.append(("kv_alloc_draft", lambda: self.s_kv_draft(i)))
         if cfg.is_tli:
             st.append(("tli_head_mask_scatter", self.s_tli))
-        if self.logits:
+        if self.from_logits:
             st.append(("softmax_draft", self.s_softmax_draft))
         st += [("draft_topk", self.s_topk), ("build_tree", self.s_tree)]
         if cfg.has_attention:
             st.append(("tree_attention", lambda: self.s_attn(i)))
-        if self.logits:
+        if self.from_logits:
             st.append(("softmax_target", self.s_softmax_target))
         st.append(("accept", self.s_accept))
         if cfg.has_attention:
@@ -333,7 +333,7 @@ def algorithmic_work(cfg, inp, pipe):
     B, N, V, R, k = cfg.B, cfg.N, cfg.V, cfg.R, cfg.k
     row_bytes = 2 if pipe.draft_input == "logits_bf16" else 4
     out = {"draft_topk": dict(bytes=B * R * V * row_bytes + B * R * k * 8, flops=0)}
-    if pipe.logits:
+    if pipe.from_logits:
         # every row read once and written once
         out["softmax_draft"] = dict(bytes=B * R * V * 8, flops=0)
         out["softmax_target"] = dict(bytes=B * N * V * 8, flops=0)
