@@ -35,16 +35,21 @@ __device__ __forceinline__ int released(int r, const int *prefix_len, const int 
   return last_used >= first_free ? last_used - first_free + 1 : 0;
 }
 
-// Sum of released(r) over r < upto (all threads get it).
+// Sum of released(r) over r < upto (all threads get it): per-thread sums,
+// a wave sum, then the four waves' sums in order.
 __device__ int released_before(int upto, const int *prefix_len, const int *accept_len, int S, int N,
                                int page) {
-  __shared__ int s_part[kCmpThreads];
+  constexpr int kWaves = kCmpThreads / kWave;
+  __shared__ int s_part[kWaves];
   int acc = 0;
   for (int r = threadIdx.x; r < upto; r += kCmpThreads) acc += released(r, prefix_len, accept_len, S, N, page);
-  s_part[threadIdx.x] = acc;
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+  if (lane_id() == 0) s_part[threadIdx.x / kWave] = acc;
   __syncthreads();
   int tot = 0;
-  for (int j = 0; j < kCmpThreads; ++j) tot += s_part[j];
+#pragma unroll
+  for (int j = 0; j < kWaves; ++j) tot += s_part[j];
   __syncthreads();
   return tot;
 }
@@ -56,7 +61,7 @@ remap_slots_kernel(int B, int N, int S, int max_pages, int *__restrict__ table,
                    int *__restrict__ num_freed) {
   __shared__ int s_old[256];
   __shared__ int s_kept[256];
-  __shared__ int s_scan[256];
+  __shared__ int s_scan[kCmpThreads / kWave];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int L = prefix_len[b];
@@ -79,17 +84,15 @@ remap_slots_kernel(int B, int N, int S, int max_pages, int *__restrict__ table,
     s_kept[pj] = 1;
   }
   __syncthreads();
-  // exclusive scan of the not-kept flags gives each released slot its place
-  const int flag = (tid < N && !s_kept[tid]) ? 1 : 0;
-  s_scan[tid] = flag;
+  // exclusive scan of the not-kept flags gives each released slot its
+  // place: a ballot per wave, then the waves before this one
+  const bool flag = tid < N && !s_kept[tid];
+  const unsigned long long m = __ballot(flag);
+  if (lane_id() == 0) s_scan[tid / kWave] = __popcll(m);
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += add;
-    __syncthreads();
-  }
-  if (flag) freed[base + s_scan[tid] - 1] = s_old[tid];
+  int before = __popcll(m & ((1ull << lane_id()) - 1ull));
+  for (int w = 0; w < tid / kWave; ++w) before += s_scan[w];
+  if (flag) freed[base + before] = s_old[tid];
   if (ok && tid < N) {
     int v = -1;
     if (tid <= a) {
