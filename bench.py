@@ -382,9 +382,9 @@ MEASURED_TRAFFIC = {
         "sources": ["speculative_decoding_eagle_amd/csrc/attn_wide.hip",
                     "speculative_decoding_eagle_amd/csrc/attn_common.hpp",
                     "speculative_decoding_eagle_amd/csrc/common.hpp"],
-        "sha256": "efda36c6397e16e60ca0a7fd6dc19038cef6f5f9377bfab86fcc72a3af05a505",
-        "fetch_kib": 204409.7, "fetch_factor": 1.99996,
-        "write_kib": 47382.6, "write_factor": 1.0,
+        "sha256": "bea906d6037b1b958f236de89197049b8d36b811ddc744a1d44e4e7a3e519fcd",
+        "fetch_kib": 198137.7, "fetch_factor": 1.99996,
+        "write_kib": 34438.6, "write_factor": 1.0,
     },
 }
 

@@ -65,7 +65,10 @@ struct WideCfg : KvTile<D> {
   static constexpr int RB = 2;                             // 16-row blocks per wave
   static constexpr int KB = 4;                             // 16-key blocks per tile
   static constexpr int SMEM = KvTile<D>::RINGS;
-  static constexpr size_t PART_O = static_cast<size_t>(kWideRows) * D * 4;   // fp32 partial O
+  // partial O in bf16 (its relative rounding, 2^-9, is far inside the
+  // output tolerance and halves the bytes a piece writes and the merge
+  // reads), then (m, l) per row in fp32
+  static constexpr size_t PART_O = static_cast<size_t>(kWideRows) * D * 2;
   static constexpr size_t PART = PART_O + kWideRows * 8;                      // + (m, l) per row
 };
 
@@ -711,13 +714,15 @@ tree_attn_wide_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, 
     if (tid == 0) s_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_ticket + 1 < static_cast<unsigned>(m_np)) {
-      float4 *pO = reinterpret_cast<float4 *>(slot_ptr(ri));
+      uint2 *pO = reinterpret_cast<uint2 *>(slot_ptr(ri));
       float2 *pml = reinterpret_cast<float2 *>(slot_ptr(ri) + C::PART_O);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int db = 0; db < NO; ++db)
-          pO[((wave * RB + rb) * NO + db) * kWave + l] = make_float4(o[rb][db][0], o[rb][db][1], o[rb][db][2], o[rb][db][3]);
+          pO[((wave * RB + rb) * NO + db) * kWave + l] =
+              make_uint2(f32_to_bf16_rne(o[rb][db][0]) | (static_cast<uint32_t>(f32_to_bf16_rne(o[rb][db][1])) << 16),
+                         f32_to_bf16_rne(o[rb][db][2]) | (static_cast<uint32_t>(f32_to_bf16_rne(o[rb][db][3])) << 16));
       if (g4 == 0) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) pml[wave * 32 + 16 * rb + l16] = make_float2(mfin[rb], lrow[rb]);
@@ -765,20 +770,26 @@ tree_attn_wide_kernel(int B, int N, int Hq, int Hkv, int pshift, int max_pages, 
           float mp, lp;
           f32x4 xo[NO];
           if (pp == ri) {
+            // its own partial as the others see it (rounded to bf16), so
+            // that the merged bits do not depend on which piece merges
             mp = mfin[rb];
             lp = lrow[rb];
 #pragma unroll
-            for (int db = 0; db < NO; ++db) xo[db] = o[rb][db];
+            for (int db = 0; db < NO; ++db)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                xo[db][i] = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_rne(o[rb][db][i])) << 16);
           } else {
             const char *base = slot_ptr(pp);
             const float2 ml = reinterpret_cast<const float2 *>(base + C::PART_O)[wave * 32 + 16 * rb + l16];
             mp = ml.x;
             lp = ml.y;
-            const float4 *pO = reinterpret_cast<const float4 *>(base);
+            const uint2 *pO = reinterpret_cast<const uint2 *>(base);
 #pragma unroll
             for (int db = 0; db < NO; ++db) {
-              const float4 x = pO[((wave * RB + rb) * NO + db) * kWave + l];
-              xo[db] = f32x4{x.x, x.y, x.z, x.w};
+              const uint2 x = pO[((wave * RB + rb) * NO + db) * kWave + l];
+              xo[db] = f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                             __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
             }
           }
           const float f = exp2f(mp - Mu);
