@@ -5,10 +5,15 @@
 // (zero-to-sglang ch.10 section 5.2).
 //
 // Latency-bound integer work: one 1024-thread block per request keeps its
-// top-k lists and the whole candidate pool in LDS.  Every selection (each step's frontier and the
-// final best N-1) is a rank computation under the strict order
-// (score desc, pool index asc): an entry's rank is the number of entries that
-// beat it, so ranks are unique and the result is deterministic.
+// top-k lists and the whole candidate pool in LDS.  Every selection (each
+// step's frontier and the final best N-1) follows the strict order (score
+// desc, pool index asc) of 64-bit order keys, so the result is deterministic.
+// When a step's k*k candidates fit one wave (k <= 8), wave 0 runs the steps
+// with sorting networks in registers and, for N - 1 <= 64, keeps the running
+// best 64; otherwise a selection is a rank computation over the block (an
+// entry's rank is the number of entries that beat it).  The per-node arrays
+// (first child, next sibling, mask rows) then take all waves, a group of
+// lanes per node.
 #include <climits>
 
 #include "common.hpp"
@@ -29,6 +34,12 @@ __device__ __forceinline__ unsigned long long order_key(float score, int e) {
   const unsigned u = __float_as_uint(score + 0.0f);
   const unsigned su = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (static_cast<unsigned long long>(su) << 32) | static_cast<unsigned>(~e);
+}
+
+// The score a key was made from (a -0 score comes back as +0).
+__device__ __forceinline__ float score_of_key(unsigned long long key) {
+  const unsigned su = static_cast<unsigned>(key >> 32);
+  return __uint_as_float((su & 0x80000000u) ? (su & 0x7FFFFFFFu) : ~su);
 }
 
 // Ranks the n entries [lo, lo + n) among themselves (rank = how many beat
@@ -87,63 +98,92 @@ __device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v, u
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
-// One bitonic stage of block size SIZE and stride S, larger keys first.
-template <int SIZE, int S>
-__device__ __forceinline__ unsigned long long sort_stage(unsigned long long key, unsigned lane) {
+// One move of a 64-bit value across the wave by a DPP pattern.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(v >> 32), CTRL, 0xF, 0xF, true);
+  return (static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo);
+}
+
+// Lane l's value of lane l ^ (SIZE - 1): the mirror image within aligned
+// blocks of SIZE lanes (quad and row mirrors by DPP, then the row-half swaps).
+template <int SIZE>
+__device__ __forceinline__ unsigned long long mirror64(unsigned long long v, unsigned lane) {
+  if constexpr (SIZE == 2) {
+    return xor_lane64<1>(v, lane);
+  } else if constexpr (SIZE == 4) {
+    return dpp64<0x1B>(v);                                        // quad [3,2,1,0]
+  } else if constexpr (SIZE == 8) {
+    return dpp64<0x141>(v);                                       // half-row mirror
+  } else if constexpr (SIZE == 16) {
+    return dpp64<0x140>(v);                                       // row mirror
+  } else if constexpr (SIZE == 32) {
+    return xor_lane64<16>(dpp64<0x140>(v), lane);
+  } else {
+    return xor_lane64<32>(xor_lane64<16>(dpp64<0x140>(v), lane), lane);
+  }
+}
+
+// Compare-exchange with the lane at stride S: within each pair the lower
+// lane keeps the larger key when DESC, the smaller otherwise.  One
+// comparison decides both lanes (equal keys, only the zero fill, swap
+// harmlessly).
+template <int S, bool DESC>
+__device__ __forceinline__ unsigned long long half_stage(unsigned long long key, unsigned lane) {
   const unsigned long long other = xor_lane64<S>(key, lane);
-  const bool desc = (lane & SIZE) == 0;          // this block's direction
-  const bool lower = (lane & S) == 0;            // this lane's place in the pair
-  const bool keep_max = lower == desc;
-  return keep_max ? (other > key ? other : key) : (other < key ? other : key);
+  const bool keep_max = ((lane & S) == 0) == DESC;
+  return (other > key) == keep_max ? other : key;
 }
 
-// Sorts one order key per lane across the wave, largest first (a bitonic
-// network of 21 compare-exchange stages, all in registers).
-__device__ __forceinline__ unsigned long long wave_sort_keys_desc(unsigned long long key) {
-  const unsigned lane = static_cast<unsigned>(lane_id());
-  key = sort_stage<2, 1>(key, lane);
-  key = sort_stage<4, 2>(key, lane);
-  key = sort_stage<4, 1>(key, lane);
-  key = sort_stage<8, 4>(key, lane);
-  key = sort_stage<8, 2>(key, lane);
-  key = sort_stage<8, 1>(key, lane);
-  key = sort_stage<16, 8>(key, lane);
-  key = sort_stage<16, 4>(key, lane);
-  key = sort_stage<16, 2>(key, lane);
-  key = sort_stage<16, 1>(key, lane);
-  key = sort_stage<32, 16>(key, lane);
-  key = sort_stage<32, 8>(key, lane);
-  key = sort_stage<32, 4>(key, lane);
-  key = sort_stage<32, 2>(key, lane);
-  key = sort_stage<32, 1>(key, lane);
-  key = sort_stage<64, 32>(key, lane);
-  key = sort_stage<64, 16>(key, lane);
-  key = sort_stage<64, 8>(key, lane);
-  key = sort_stage<64, 4>(key, lane);
-  key = sort_stage<64, 2>(key, lane);
-  key = sort_stage<64, 1>(key, lane);
-  return key;
+// Half-cleaners at strides S, S/2, .., 1: sort every aligned block of 2S
+// lanes that holds a bitonic sequence.
+template <int S, bool DESC>
+__device__ __forceinline__ unsigned long long cleaners(unsigned long long key, unsigned lane) {
+  if constexpr (S >= 1) {
+    key = half_stage<S, DESC>(key, lane);
+    return cleaners<S / 2, DESC>(key, lane);
+  } else {
+    return key;
+  }
 }
 
-// Largest 64 of two lane-sorted key sets (largest first), largest first:
-// b reversed across the wave (lane l ^ 63) against a, the larger of each
-// pair (a bitonic sequence holding the top 64), then the last six stages.
-__device__ __forceinline__ unsigned long long wave_merge_top(unsigned long long a, unsigned long long b) {
-  const unsigned lane = static_cast<unsigned>(lane_id());
-  b = xor_lane64<32>(b, lane);
-  b = xor_lane64<16>(b, lane);
-  b = xor_lane64<8>(b, lane);
-  b = xor_lane64<4>(b, lane);
-  b = xor_lane64<2>(b, lane);
-  b = xor_lane64<1>(b, lane);
-  unsigned long long key = a > b ? a : b;
-  key = sort_stage<64, 32>(key, lane);
-  key = sort_stage<64, 16>(key, lane);
-  key = sort_stage<64, 8>(key, lane);
-  key = sort_stage<64, 4>(key, lane);
-  key = sort_stage<64, 2>(key, lane);
-  key = sort_stage<64, 1>(key, lane);
-  return key;
+// Sorts largest first, assuming every aligned block of LO / 2 lanes already
+// is: the levels LO, 2 LO, .., HI each merge two sorted halves of a block by
+// comparing every lane of the lower half with its mirror image in the upper
+// half (lower keeps the larger) and then sorting both bitonic halves.  Lanes
+// past HI must already be in order with the rest (zero fill).
+template <int LO, int HI>
+__device__ __forceinline__ unsigned long long merge_sort_desc(unsigned long long key, unsigned lane) {
+  if constexpr (LO <= HI) {
+    const unsigned long long other = mirror64<LO>(key, lane);
+    const bool keep_max = (lane & (LO / 2)) == 0;
+    key = (other > key) == keep_max ? other : key;
+    key = cleaners<LO / 4, true>(key, lane);
+    return merge_sort_desc<LO * 2, HI>(key, lane);
+  } else {
+    return key;
+  }
+}
+
+// Largest 64 of a (lane-sorted smallest first) and b (largest first),
+// smallest first: the lane-wise maxima form a bitonic sequence that holds
+// the top 64, and the six half-cleaner stages of a 64-lane merge sort it.
+__device__ __forceinline__ unsigned long long merge_top_asc(unsigned long long a, unsigned long long b,
+                                                             unsigned lane) {
+  return cleaners<32, false>(a > b ? a : b, lane);
+}
+
+// Minimum over aligned groups of g lanes (g a power of two, at most 64,
+// uniform across the wave, every lane active).
+__device__ __forceinline__ unsigned group_min(unsigned v, int g, unsigned lane) {
+  if (g > 1) v = min(v, xor_lane<1>(v, lane));
+  if (g > 2) v = min(v, xor_lane<2>(v, lane));
+  if (g > 4) v = min(v, xor_lane<4>(v, lane));
+  if (g > 8) v = min(v, xor_lane<8>(v, lane));
+  if (g > 16) v = min(v, xor_lane<16>(v, lane));
+  if (g > 32) v = min(v, xor_lane<32>(v, lane));
+  return v;
 }
 
 __device__ __forceinline__ int entry_of_key(unsigned long long key) {
@@ -166,6 +206,65 @@ __device__ int block_exclusive_scan(int x) {
   for (int j = 0; j < w; ++j) before += s_w[j];
   __syncthreads();
   return before + inc - x;
+}
+
+// The draft steps in wave 0 when every step's k*k candidates fit one wave
+// (k <= 8).  Candidate c of frontier slot j sits in lane j * K2 + c (K2 = k
+// rounded up to a power of two; lanes without a candidate hold key 0, below
+// every key).  With RUNS (every top-k row sorted largest first, entries in
+// [0, 1]) each slot's children are already in order -- their scores are one
+// non-negative factor times a falling sequence and ties go to the smaller
+// pool index -- so each step's sort starts from runs of K2; otherwise it
+// sorts from scratch.  Each step's keys end largest first (frontier slot j
+// in lane j).  With FINAL the best 64 keys of the pool so far are kept
+// smallest first and every step's keys merge into them one step late, in
+// the same straight-line code as the next step's sort.  The candidates'
+// scores, parents, keys and the frontier's draft rows go to LDS; a frontier
+// entry's score comes back from its key.
+template <int K2, bool RUNS, bool FINAL>
+__device__ unsigned long long wave_steps(int k, int S, const float *s_tp, float *s_score, int *s_par,
+                                         unsigned long long *s_key, int *s_row) {
+  constexpr int LO = RUNS ? 2 * K2 : 2;
+  const int x = static_cast<int>(threadIdx.x);
+  const unsigned lane = static_cast<unsigned>(x);
+  unsigned long long key = 0;
+  if (x < k) {                      // step 0: the root's children
+    key = order_key(s_tp[x], x);
+    s_score[x] = s_tp[x];
+    s_par[x] = -1;
+    s_key[x] = key;
+  }
+  key = merge_sort_desc<LO, RUNS ? K2 : kWave>(key, lane);
+  unsigned long long best = 0, pend = key;
+  const int j = x / K2, c = x % K2;   // the frontier slot and child this lane expands
+  for (int i = 1; i < S; ++i) {
+    if (x < k) s_row[entry_of_key(key)] = 1 + (i - 1) * k + x;
+    const unsigned long long fk = __shfl(key, j, kWave);
+    unsigned long long ck = 0;
+    if (j < k && c < k) {
+      const int e = k + (i - 1) * k * k + j * k + c;
+      const float sc = score_of_key(fk) * s_tp[e];
+      s_score[e] = sc;
+      s_par[e] = entry_of_key(fk);
+      ck = order_key(sc, e);
+      s_key[e] = ck;
+    }
+    key = merge_sort_desc<LO, RUNS ? K2 * K2 : kWave>(ck, lane);
+    if constexpr (FINAL) best = merge_top_asc(best, pend, lane);
+    pend = key;
+  }
+  if constexpr (FINAL) best = merge_top_asc(best, pend, lane);
+  return best;
+}
+
+template <bool FINAL>
+__device__ unsigned long long wave_steps_for(int k, int S, bool runs, const float *s_tp, float *s_score, int *s_par,
+                                             unsigned long long *s_key, int *s_row) {
+  if (!runs) return wave_steps<8, false, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
+  if (k == 1) return wave_steps<1, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
+  if (k == 2) return wave_steps<2, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
+  if (k <= 4) return wave_steps<4, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
+  return wave_steps<8, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
 }
 
 // Pool entry e of a request coincides with entry e of its row-major [R, k]
@@ -192,66 +291,83 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
   int *s_tree = s_row + M;                               // tree index, -1 if not selected
   __shared__ int s_front[32];
   __shared__ int s_tpar[kMaxNodes];
-  __shared__ int s_fc[kMaxNodes], s_ns[kMaxNodes];
-  __shared__ uint32_t s_bits[kMaxNodes][kMaxWords];
+  __shared__ __align__(16) int s_sel[kWave];
+  __shared__ int s_bad[kTreeWaves];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const float *tp = topk_p + static_cast<int64_t>(b) * M;
   const int *ti = topk_id + static_cast<int64_t>(b) * M;
+  bool runs = true;                  // every top-k row falls, entries in [0, 1]
   for (int e = tid; e < M; e += kTreeThreads) {
-    s_tp[e] = tp[e];
+    const float v = tp[e];
+    s_tp[e] = v;
     s_tok[e] = ti[e];
     s_row[e] = -1;
-    s_tree[e] = 0;
+    s_tree[e] = -1;
+    runs = runs && v >= 0.0f && v <= 1.0f && ((e + 1) % k == 0 || v >= tp[e + 1]);   // rows are blocks of k
   }
+  const unsigned long long bad = __ballot(!runs);
+  if (lane_id() == 0) s_bad[tid / kWave] = bad != 0;
   const int L = prefix_len[b];
   const int root = root_token[b];
+  const int64_t ob = static_cast<int64_t>(b) * N;
+  if (tid == 0) {
+    o_tokens[ob] = root;
+    o_parent[ob] = -1;
+    o_depth[ob] = 0;
+    o_positions[ob] = L;
+    o_score[ob] = 1.0f;
+    o_qrow[ob] = 0;
+    s_tpar[0] = -1;
+  }
   __syncthreads();
 
   // With N - 1 <= 64 as well, wave 0 also keeps the best 64 keys of the
-  // pool so far (every step's sorted keys merged in) and marks the final
-  // N - 1 itself.
+  // pool so far (every step's sorted keys merged in) and then numbers and
+  // writes the final N - 1 itself.
   const bool wave_final = k * k <= kWave && N - 1 <= kWave;
   if (k * k <= kWave) {
-    // Every step's k*k candidates fit one wave: wave 0 runs the steps in
-    // registers, each frontier the first k lanes of a wave sort of the
-    // step's order keys (lanes past the candidates hold 0, below any key).
     if (tid < kWave) {
       const int x = tid;
-      // step 0: the root's children
-      unsigned long long key = 0;
-      if (x < k) {
-        key = order_key(s_tp[x], x);
-        s_score[x] = s_tp[x];
-        s_par[x] = -1;
-        s_key[x] = key;
-      }
-      key = wave_sort_keys_desc(key);
-      unsigned long long best = key;               // best 64 of the pool so far, largest first
-      int fe = entry_of_key(key);                  // lanes j < k: frontier slot j
-      float fs = x < k ? s_tp[fe] : 0.f;           // its score
-      // steps 1 .. S-1: expand every frontier slot, keep the best k
-      for (int i = 1; i < S; ++i) {
-        const int base = k + (i - 1) * k * k;
-        const int f = __shfl(fe, x / k, kWave);
-        const float fsc = __shfl(fs, x / k, kWave);
-        if (x < k) s_row[fe] = 1 + (i - 1) * k + x;
-        key = 0;
-        if (x < k * k) {
-          const int e = base + x;
-          const float sc = fsc * s_tp[e];
-          s_score[e] = sc;
-          s_par[e] = f;
-          key = order_key(sc, e);
-          s_key[e] = key;
+      runs = true;
+#pragma unroll
+      for (int w = 0; w < kTreeWaves; ++w) runs = runs && !s_bad[w];
+      const unsigned long long best = wave_final
+                                          ? wave_steps_for<true>(k, S, runs, s_tp, s_score, s_par, s_key, s_row)
+                                          : wave_steps_for<false>(k, S, runs, s_tp, s_score, s_par, s_key, s_row);
+      if (wave_final) {
+        // lanes 65 - N .. 63 hold the best N - 1 entries; an entry's tree
+        // index is 1 + the number of the others with a smaller pool index.
+        // The LDS writes of this wave land before its later reads.
+        const bool sel = x >= kWave - (N - 1);
+        const int e = sel ? entry_of_key(best) : INT_MAX;
+        s_sel[x] = e;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        int below = 0;
+#pragma unroll
+        for (int y = 0; y < kWave; y += 4) {
+          const int4 v = *reinterpret_cast<const int4 *>(&s_sel[y]);
+          below += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
         }
-        key = wave_sort_keys_desc(key);
-        if (wave_final) best = wave_merge_top(best, key);
-        fe = entry_of_key(key);
-        fs = x < k ? s_score[fe] : 0.f;            // written by this wave above (LDS keeps a wave's order)
+        const int te = 1 + below;
+        if (sel) s_tree[e] = te;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (sel) {
+          const int pe = s_par[e];
+          const int tpar = pe < 0 ? 0 : s_tree[pe];   // -1 only if scores broke monotonicity
+          const int step = e < k ? 0 : 1 + (e - k) / (k * k);
+          o_tokens[ob + te] = s_tok[e];
+          o_parent[ob + te] = tpar;
+          o_depth[ob + te] = step + 1;
+          o_positions[ob + te] = L + step + 1;
+          o_score[ob + te] = s_score[e];
+          o_qrow[ob + te] = s_row[e];
+          s_tpar[te] = tpar;
+        }
       }
-      if (wave_final && x < N - 1) s_tree[entry_of_key(best)] = 1;   // keys are distinct: the top N-1 entries
     }
     __syncthreads();
   } else {
@@ -285,88 +401,95 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
     }
   }
 
-  // final selection: the best N-1 pool entries, numbered in pool order
+  // final selection by ranks over the whole pool: the best N-1 entries,
+  // numbered in pool order
   if (!wave_final) {
     rank_block(s_key, 0, M, [&](int e, int r) { s_tree[e] = r < N - 1 ? 1 : 0; });
     __syncthreads();
-  }
-  const int per = (M + kTreeThreads - 1) / kTreeThreads;
-  const int e0 = tid * per;
-  int cnt = 0;
-  for (int e = e0; e < min(M, e0 + per); ++e) cnt += s_tree[e];
-  int t = 1 + block_exclusive_scan(cnt);   // tree index of this thread's first selected entry
-  for (int e = e0; e < min(M, e0 + per); ++e) s_tree[e] = s_tree[e] ? t++ : -1;
-  __syncthreads();
-
-  const int64_t ob = static_cast<int64_t>(b) * N;
-  if (tid == 0) {
-    o_tokens[ob] = root;
-    o_parent[ob] = -1;
-    o_depth[ob] = 0;
-    o_positions[ob] = L;
-    o_score[ob] = 1.0f;
-    o_qrow[ob] = 0;
-    s_tpar[0] = -1;
-  }
-  for (int e = tid; e < M; e += kTreeThreads) {
-    const int te = s_tree[e];
-    if (te < 0) continue;
-    const int pe = s_par[e];
-    const int tpar = pe < 0 ? 0 : s_tree[pe];   // -1 only if scores broke monotonicity
-    const int step = e < k ? 0 : 1 + (e - k) / (k * k);
-    o_tokens[ob + te] = s_tok[e];
-    o_parent[ob + te] = tpar;
-    o_depth[ob + te] = step + 1;
-    o_positions[ob + te] = L + step + 1;
-    o_score[ob + te] = s_score[e];
-    o_qrow[ob + te] = s_row[e];
-    s_tpar[te] = tpar;
-  }
-  __syncthreads();
-
-  // first child and next sibling: the smallest larger index with the node
-  // as parent / with the same parent, found over all (n, m) pairs
-  for (int n = tid; n < N; n += kTreeThreads) {
-    s_fc[n] = INT_MAX;
-    s_ns[n] = INT_MAX;
-  }
-  __syncthreads();
-  for (int x = tid; x < N * N; x += kTreeThreads) {
-    const int n = x / N, m = x % N;
-    if (m <= n) continue;
-    const int pm = s_tpar[m];
-    if (pm == n) atomicMin(&s_fc[n], m);
-    const int p = s_tpar[n];
-    if (p >= 0 && pm == p) atomicMin(&s_ns[n], m);
-  }
-  const int W = (N + 31) / 32;
-  for (int n = tid; n < N; n += kTreeThreads) {
-    uint32_t bits[kMaxWords];
-#pragma unroll
-    for (int w = 0; w < kMaxWords; ++w) bits[w] = 0;
-    int j = n;
-    for (int hop = 0; hop <= S && j >= 0; ++hop) {
-#pragma unroll
-      for (int w = 0; w < kMaxWords; ++w)
-        if (w == j / 32) bits[w] |= 1u << (j % 32);
-      j = s_tpar[j];
+    const int per = (M + kTreeThreads - 1) / kTreeThreads;
+    const int e0 = tid * per;
+    int cnt = 0;
+    for (int e = e0; e < min(M, e0 + per); ++e) cnt += s_tree[e];
+    int t = 1 + block_exclusive_scan(cnt);   // tree index of this thread's first selected entry
+    for (int e = e0; e < min(M, e0 + per); ++e) s_tree[e] = s_tree[e] ? t++ : -1;
+    __syncthreads();
+    for (int e = tid; e < M; e += kTreeThreads) {
+      const int te = s_tree[e];
+      if (te < 0) continue;
+      const int pe = s_par[e];
+      const int tpar = pe < 0 ? 0 : s_tree[pe];   // -1 only if scores broke monotonicity
+      const int step = e < k ? 0 : 1 + (e - k) / (k * k);
+      o_tokens[ob + te] = s_tok[e];
+      o_parent[ob + te] = tpar;
+      o_depth[ob + te] = step + 1;
+      o_positions[ob + te] = L + step + 1;
+      o_score[ob + te] = s_score[e];
+      o_qrow[ob + te] = s_row[e];
+      s_tpar[te] = tpar;
     }
-#pragma unroll
-    for (int w = 0; w < kMaxWords; ++w) {
-      s_bits[n][w] = bits[w];
-      if (o_bits && w < W) o_bits[(ob + n) * W + w] = bits[w];
+    __syncthreads();
+  }
+
+  // ---- per node, g lanes each (g a power of two, at most 64, g * N <= the
+  // block): the first child and next sibling (the smallest larger index with
+  // the node as parent / with the same parent), the ancestor bits (the mask
+  // row) and the retrieve index.  A group lies inside one wave.
+  int lg = 0;
+  while (lg < 6 && (2 << lg) * N <= kTreeThreads) ++lg;
+  const int g = 1 << lg;
+  const int n = tid >> lg, part = tid & (g - 1);
+  const unsigned lane = static_cast<unsigned>(lane_id());
+  const bool live = n < N;
+  const int p = live ? s_tpar[n] : -1;
+  unsigned fc = UINT_MAX, ns = UINT_MAX;
+  if (live) {
+    for (int m = n + 1 + part; m < N; m += g) {
+      const int pm = s_tpar[m];
+      if (pm == n) fc = min(fc, static_cast<unsigned>(m));
+      if (p >= 0 && pm == p) ns = min(ns, static_cast<unsigned>(m));
     }
-    o_retrieve[ob + n] = static_cast<int>(ob + n);
   }
-  __syncthreads();
-  for (int n = tid; n < N; n += kTreeThreads) {
-    o_next_token[ob + n] = s_fc[n] == INT_MAX ? -1 : s_fc[n];
-    o_next_sibling[ob + n] = s_ns[n] == INT_MAX ? -1 : s_ns[n];
+  fc = group_min(fc, g, lane);
+  ns = group_min(ns, g, lane);
+  uint32_t bits[kMaxWords];
+#pragma unroll
+  for (int w = 0; w < kMaxWords; ++w) bits[w] = 0;
+  int j = live ? n : -1;
+  for (int hop = 0; hop <= S && j >= 0; ++hop) {
+#pragma unroll
+    for (int w = 0; w < kMaxWords; ++w)
+      if (w == j / 32) bits[w] |= 1u << (j % 32);
+    j = s_tpar[j];
   }
-  if (o_mask) {
-    for (int x = tid; x < N * N; x += kTreeThreads) {
-      const int r = x / N, c = x % N;
-      o_mask[ob * N + x] = static_cast<uint8_t>((s_bits[r][c / 32] >> (c % 32)) & 1u);
+  auto word = [&](int wi) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < kMaxWords; ++w)
+      if (w == wi) r = bits[w];
+    return r;
+  };
+  if (live) {
+    const int64_t row = ob + n;
+    if (part == 0) {
+      o_next_token[row] = fc == UINT_MAX ? -1 : static_cast<int>(fc);
+      o_next_sibling[row] = ns == UINT_MAX ? -1 : static_cast<int>(ns);
+      o_retrieve[row] = static_cast<int>(row);
+    }
+    const int W = (N + 31) / 32;
+    if (o_bits)
+      for (int w = part; w < W; w += g) o_bits[row * W + w] = word(w);
+    if (o_mask) {
+      uint8_t *mrow = o_mask + row * N;
+      if (N % 4 == 0 && (reinterpret_cast<uintptr_t>(o_mask) & 3) == 0) {
+        // four columns per store: bit c of the row -> byte c
+        for (int q = part; 4 * q < N; q += g) {
+          const uint32_t nib = (word(q / 8) >> (4 * (q % 8))) & 0xFu;
+          reinterpret_cast<uint32_t *>(mrow)[q] =
+              (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+        }
+      } else {
+        for (int c = part; c < N; c += g) mrow[c] = static_cast<uint8_t>((word(c / 32) >> (c % 32)) & 1u);
+      }
     }
   }
 }

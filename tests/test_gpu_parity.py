@@ -237,6 +237,29 @@ def test_build_tree_ties_and_shapes(k, S, N):
     _assert_tree_equal(g, o)
 
 
+# Top-k rows that are not sorted (columns shuffled) and rows with exact 0 and
+# 1 entries: the builder may not assume the draft top-k's order.
+@pytest.mark.parametrize("k,S,N,shuffle", [(8, 5, 64, True), (4, 4, 32, True), (3, 4, 30, True), (8, 5, 256, True),
+                                           (2, 3, 6, True), (5, 3, 40, True), (1, 5, 6, True), (8, 5, 64, False),
+                                           (4, 4, 32, False)])
+def test_build_tree_unsorted_and_edge_rows(k, S, N, shuffle):
+    rng = np.random.default_rng(k * 1000 + S * 100 + N + (7 if shuffle else 0))
+    B = 6
+    R = 1 + (S - 1) * k
+    probs = (rng.integers(0, 17, size=(B, R, 64)) / 16.0).astype(np.float32)   # 0, 1/16, .., 1: ties, 0s and 1s
+    tp, ti = otopk.draft_topk(probs, k)
+    if shuffle:
+        perm = np.argsort(rng.random((B, R, k)), axis=2)
+        tp = np.take_along_axis(tp, perm, axis=2)
+        ti = np.take_along_axis(ti, perm, axis=2)
+    root = rng.integers(0, 64, size=B).astype(np.int32)
+    plen = rng.integers(0, 1000, size=B).astype(np.int32)
+    say("build_tree unsorted/edge", k, S, N, shuffle)
+    g = _gpu_tree(np.ascontiguousarray(tp), np.ascontiguousarray(ti), root, plen, k, S, N)
+    o = otree.build_tree(tp, ti, root, plen, k, S, N)
+    _assert_tree_equal(g, o)
+
+
 # Multi-layer draft chain: bit-exact against the oracle, then through the
 # same accept kernels as the tree.
 @pytest.mark.parametrize("B,S", [(1, 1), (7, 4), (300, 12), (3, 255)])
