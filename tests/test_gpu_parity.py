@@ -66,7 +66,8 @@ def test_topk_bit_exact(rows, V, k, coarse):
     (10, 1000, 2, 1.0, False, "normal"), (64, 4099, 8, 0.7, False, "normal"), (33, 128256, 8, 1.0, True, "normal"),
     (1056, 128256, 8, 1.0, True, "normal"), (300, 128256, 8, 0.7, False, "normal"), (5, 64, 32, 1.3, True, "ties"),
     (200, 5000, 13, 1.0, False, "ties"), (3, 7, 7, 2.0, True, "normal"), (1, 1, 1, 1.0, False, "normal"),
-    (17, 40003, 4, 0.5, True, "masked"), (40, 9000, 16, 1.0, False, "masked"), (2, 131072, 32, 1.0, True, "ties")])
+    (17, 40003, 4, 0.5, True, "masked"), (40, 9000, 16, 1.0, False, "masked"), (2, 131072, 32, 1.0, True, "ties"),
+    (260, 90000, 8, 1.0, True, "normal"), (257, 100004, 16, 0.7, False, "ties")])
 def test_topk_from_logits(rows, V, k, T, bf16, kind):
     rng = np.random.default_rng(rows * 7 + V + k)
     if kind == "ties":
@@ -132,11 +133,13 @@ def test_softmax_rows_against_the_float64_definition(rows, V, T, kind):
 # gets a group of equal values (its maximum, doubled) at random places, so
 # its k best and their tie order straddle wherever the cuts fall; 2048 rows
 # (a multiple of 256 compute units) take the one-workgroup-per-row path
-# alone, and 256, 512 and 768 rows (one to three per compute unit) are cut
-# into four or two row-aligned pieces each.
+# alone, 256, 512 and 768 rows (one to three per compute unit) are cut into
+# four or two row-aligned pieces each, and V = 82020 and 100004 end in a
+# partial window.
 @pytest.mark.parametrize("rows,V,k", [(1056, 128256, 8), (300, 128256, 4), (2047, 4104, 8), (2048, 4104, 8),
                                       (5000, 4104, 2), (129, 65536, 16), (7, 9000, 32), (256, 128256, 1),
-                                      (512, 128256, 8), (768, 65536, 4)])
+                                      (512, 128256, 8), (768, 65536, 4), (300, 82020, 8), (260, 100004, 3),
+                                      (255, 128256, 8)])
 def test_topk_segments(rows, V, k):
     rng = np.random.default_rng(rows * 17 + V + k)
     p = workloads.softmax_rows(rng.standard_normal((rows, V)).astype(np.float32) * 3)
