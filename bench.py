@@ -439,8 +439,8 @@ def cpu_baseline(cfg, inp, n_req, threads=1, logits=False):
         t0 = time.perf_counter()
         if cfg.is_tli:
             h = inp["hidden"][0][sl]
-            logits = otli.lm_head(h, inp["weight"])
-            otli.constrain_logits(logits.astype(np.float32), inp["inter_ids"], cfg.V_draft)
+            head_logits = otli.lm_head(h, inp["weight"])
+            otli.constrain_logits(head_logits.astype(np.float32), inp["inter_ids"], cfg.V_draft)
             rows = otli.q_scatter(inp["q_pruned"][sl].reshape(-1, cfg.K_inter), inp["tgt_ids"], cfg.V)
             rows = rows.reshape(n, cfg.R, cfg.V)
         elif logits:
