@@ -257,20 +257,18 @@ __device__ unsigned long long wave_steps(int k, int S, const float *s_tp, float 
   return best;
 }
 
-template <bool FINAL>
-__device__ unsigned long long wave_steps_for(int k, int S, bool runs, const float *s_tp, float *s_score, int *s_par,
-                                             unsigned long long *s_key, int *s_row) {
-  if (!runs) return wave_steps<8, false, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
-  if (k == 1) return wave_steps<1, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
-  if (k == 2) return wave_steps<2, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
-  if (k <= 4) return wave_steps<4, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
-  return wave_steps<8, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
-}
+
 
 // Pool entry e of a request coincides with entry e of its row-major [R, k]
 // top-k lists: step 0 holds the root's k children (row 0), and entry
 // k + (i-1)*k*k + j*k + c of step i >= 1 is child c of frontier slot j,
 // drawn from row 1 + (i-1)*k + j.
+// K2 = 0: a step's candidates do not fit one wave (k > 8); otherwise K2 is
+// k rounded up to a power of two and FINAL says N - 1 <= 64.  The host picks
+// both from the shape, so each kernel holds only its own two forms of the
+// steps, sorted runs or not (one kernel with all ten forms took 0.4 us
+// longer over the c3 steps).
+template <int K2, bool FINAL>
 __global__ void __launch_bounds__(kTreeThreads)
 build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
                   const int *__restrict__ topk_id, const int *__restrict__ root_token,
@@ -326,17 +324,16 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
   // With N - 1 <= 64 as well, wave 0 also keeps the best 64 keys of the
   // pool so far (every step's sorted keys merged in) and then numbers and
   // writes the final N - 1 itself.
-  const bool wave_final = k * k <= kWave && N - 1 <= kWave;
-  if (k * k <= kWave) {
+  constexpr bool wave_final = FINAL;
+  if constexpr (K2 > 0) {
     if (tid < kWave) {
       const int x = tid;
       runs = true;
 #pragma unroll
       for (int w = 0; w < kTreeWaves; ++w) runs = runs && !s_bad[w];
-      const unsigned long long best = wave_final
-                                          ? wave_steps_for<true>(k, S, runs, s_tp, s_score, s_par, s_key, s_row)
-                                          : wave_steps_for<false>(k, S, runs, s_tp, s_score, s_par, s_key, s_row);
-      if (wave_final) {
+      const unsigned long long best = runs ? wave_steps<K2, true, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row)
+                                           : wave_steps<8, false, FINAL>(k, S, s_tp, s_score, s_par, s_key, s_row);
+      if constexpr (FINAL) {
         // lanes 65 - N .. 63 hold the best N - 1 entries; an entry's tree
         // index is 1 + the number of the others with a smaller pool index.
         // The LDS writes of this wave land before its later reads.
@@ -403,7 +400,7 @@ build_tree_kernel(int k, int S, int N, const float *__restrict__ topk_p,
 
   // final selection by ranks over the whole pool: the best N-1 entries,
   // numbered in pool order
-  if (!wave_final) {
+  if constexpr (!wave_final) {
     rank_block(s_key, 0, M, [&](int e, int r) { s_tree[e] = r < N - 1 ? 1 : 0; });
     __syncthreads();
     const int per = (M + kTreeThreads - 1) / kTreeThreads;
@@ -564,10 +561,17 @@ extern "C" int32_t sdv_build_tree(sdv_tree_shape sh, const float *topk_p, const 
                   score && q_row && retrieve_index && retrieve_next_token && retrieve_next_sibling,
               SDV_E_NULL, "build_tree: NULL pointer");
   const size_t lds = static_cast<size_t>(M) * (6 * sizeof(int) + sizeof(uint64_t));   // key, tp, tok, score, par, row, tree
-  hipLaunchKernelGGL(build_tree_kernel, dim3(sh.B), dim3(kTreeThreads), lds, as_stream(stream), sh.k,
-                     sh.S, sh.N, topk_p, topk_id, root_token, prefix_len, tokens, parent, depth,
-                     positions, score, q_row, mask, mask_bits, retrieve_index, retrieve_next_token,
-                     retrieve_next_sibling);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(sh.B), dim3(kTreeThreads), lds, as_stream(stream), sh.k, sh.S, sh.N, topk_p,
+                       topk_id, root_token, prefix_len, tokens, parent, depth, positions, score, q_row, mask,
+                       mask_bits, retrieve_index, retrieve_next_token, retrieve_next_sibling);
+  };
+  const bool fin = sh.N - 1 <= kWave;
+  if (sh.k * sh.k > kWave) go(build_tree_kernel<0, false>);
+  else if (sh.k == 1) fin ? go(build_tree_kernel<1, true>) : go(build_tree_kernel<1, false>);
+  else if (sh.k == 2) fin ? go(build_tree_kernel<2, true>) : go(build_tree_kernel<2, false>);
+  else if (sh.k <= 4) fin ? go(build_tree_kernel<4, true>) : go(build_tree_kernel<4, false>);
+  else fin ? go(build_tree_kernel<8, true>) : go(build_tree_kernel<8, false>);
   return check_launch("build_tree_kernel");
 }
 
