@@ -223,9 +223,12 @@ def test_build_tree_bit_exact(name, V):
     _assert_tree_equal(g, o)
 
 
-# Tie-heavy scores over k from 1 to 32, pools up to 1056 entries.
+# Tie-heavy scores over k from 1 to 32, pools up to 1056 entries; every
+# kernel form (k rounded up to 1, 2, 4 or 8 with N - 1 <= 64 or above, and
+# k > 8) appears.
 @pytest.mark.parametrize("k,S,N", [(2, 3, 6), (3, 4, 30), (8, 5, 64), (4, 6, 85), (16, 2, 200), (1, 9, 10),
-                                   (2, 1, 3), (5, 3, 1), (8, 5, 256), (7, 4, 100), (9, 3, 120), (32, 2, 256)])
+                                   (2, 1, 3), (5, 3, 1), (8, 5, 256), (7, 4, 100), (9, 3, 120), (32, 2, 256),
+                                   (1, 80, 81), (2, 20, 70)])
 def test_build_tree_ties_and_shapes(k, S, N):
     rng = np.random.default_rng(k * 100 + S * 10 + N)
     B = 5
@@ -244,7 +247,7 @@ def test_build_tree_ties_and_shapes(k, S, N):
 # 1 entries: the builder may not assume the draft top-k's order.
 @pytest.mark.parametrize("k,S,N,shuffle", [(8, 5, 64, True), (4, 4, 32, True), (3, 4, 30, True), (8, 5, 256, True),
                                            (2, 3, 6, True), (5, 3, 40, True), (1, 5, 6, True), (8, 5, 64, False),
-                                           (4, 4, 32, False)])
+                                           (4, 4, 32, False), (2, 20, 70, True), (1, 80, 81, False)])
 def test_build_tree_unsorted_and_edge_rows(k, S, N, shuffle):
     rng = np.random.default_rng(k * 1000 + S * 100 + N + (7 if shuffle else 0))
     B = 6
