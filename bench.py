@@ -77,6 +77,9 @@ def parse():
                          "are pools of the same shape that only the compaction touches")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (side figures)")
     ap.add_argument("--k-inter", type=int, default=None, help="TLI workloads: override the intersection size")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed steps before the warm-up until the GPU has run this long (ms): it lowers its "
+                         "clocks when idle, and the timed steps should see the clocks of a busy serving loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -321,6 +324,16 @@ class Pipeline:
             st.append(("extend_prep", self.s_extend))
         return st
 
+    def settle_step(self, n):
+        """Untimed step n: the input set of a timed step n (rotating as they
+        do), on page table 0 (restored from the input table first, since the
+        compaction rewrites it)."""
+        if self.cfg.has_attention:
+            self.tables[0].copy_(self.sets[0]["page_table"])
+        self.use(n)
+        for _, fn in self.stages(0):
+            fn()
+
     def run_all(self, i):
         if hasattr(self, "sets"):
             self.use(i)
@@ -527,6 +540,26 @@ def main():
                     args.chain, args.kv_alloc, args.layers, args.logits)
     stages = [name for name, _ in pipe.stages(0)]
 
+    # The GPU lowers its clocks when idle (it has been, during input
+    # generation) and raises them only under uninterrupted load: measured at
+    # c3, 20 timed steps after 5 warm-up steps take 0.27 ms each, after 50
+    # 0.250 and after 200 0.243, while hundreds of untimed steps in bursts of
+    # ten with a host sync between them leave it at 0.27.  So, untimed, one
+    # continuous burst of about settle_ms of steps (their count from the time
+    # of ten).
+    settle_steps, t_settle = 0, time.perf_counter()
+    if args.settle_ms > 0:
+        for _ in range(10):
+            pipe.settle_step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t_settle) / 10
+        for _ in range(int(args.settle_ms * 1e-3 / max(per, 1e-5))):
+            pipe.settle_step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    t_settle = time.perf_counter() - t_settle
+
     for i in range(args.warmup):
         pipe.run_all(1 + i)
     torch.cuda.synchronize()
@@ -578,6 +611,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "ms": round(t_settle * 1e3, 1)},
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
