@@ -325,14 +325,16 @@ class Pipeline:
         return st
 
     def settle_step(self, n):
-        """Untimed step n: the input set of a timed step n (rotating as they
-        do), on page table 0 (restored from the input table first, since the
-        compaction rewrites it)."""
-        if self.cfg.has_attention:
-            self.tables[0].copy_(self.sets[0]["page_table"])
+        """Untimed step n on the input set of a timed step n (rotating as they
+        do): every stage but the two that rewrite the page table (the
+        compaction and the draft-side allocation), so table 0 is only read.
+        (Settle steps that also compacted, on a table restored before each
+        step, were followed by stalls of some 30 ms in later steps of the
+        page-16 and planted workloads; without those stages there were none.)"""
         self.use(n)
-        for _, fn in self.stages(0):
-            fn()
+        for name, fn in self.stages(0):
+            if name not in ("compact_kv", "kv_alloc_draft"):
+                fn()
 
     def run_all(self, i):
         if hasattr(self, "sets"):
