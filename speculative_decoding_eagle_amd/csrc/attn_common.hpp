@@ -65,13 +65,6 @@ __device__ __forceinline__ void dma4(const void *gaddr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
 }
 
-// As dma16, addressed as a 64-bit base in scalar registers plus this
-// lane's 32-bit byte offset.
-__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
-}
-
 // Lane l's value combined with lane l^16's (l^32's): the row-half swap
 // instructions hand every lane the pair {x[l], x[l^16]} ({x[l], x[l^32]}).
 __device__ __forceinline__ float max_xor16(float x) {

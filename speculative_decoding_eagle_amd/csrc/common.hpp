@@ -122,6 +122,13 @@ __device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_addr) : "memory", "m0");
 }
 
+// As dma16, addressed as a 64-bit base in scalar registers plus this
+// lane's 32-bit byte offset.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
 }

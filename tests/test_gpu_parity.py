@@ -101,10 +101,17 @@ def test_topk_from_logits(rows, V, k, T, bf16, kind):
 # of the output: 3e-5 relative bounds it with room.  -inf entries are exact
 # zeros.  Shapes: the vector path (V % 4 == 0) at the configs' V and rows,
 # the scalar path (V % 4 != 0, V = 1), masked rows, several temperatures.
+# Rows of 65536 to 135168 entries stay on chip between the passes (one
+# workgroup per row, one per CU at a time): more rows than CUs (517, 300,
+# 260), rows whose last register chunks lie past the row (V = 70004), the
+# largest such row (135168, nine LDS chunks) next to the smallest read
+# twice above it (135172), and both sides of the lower end (65536, 65532).
 @pytest.mark.parametrize("rows,V,T,kind", [
     (80, 128256, 1.0, "normal"), (24, 128256, 0.7, "normal"), (5, 128256, 0.5, "normal"), (7, 1000, 0.7, "normal"),
     (3, 5, 1.0, "normal"), (9, 4099, 2.0, "normal"), (4, 1, 1.0, "normal"), (6, 40000, 0.8, "masked"),
-    (2, 131072, 1.0, "ties"), (0, 128256, 1.0, "normal")])
+    (2, 131072, 1.0, "ties"), (0, 128256, 1.0, "normal"), (517, 70004, 0.9, "normal"),
+    (300, 128256, 0.7, "masked"), (260, 135168, 1.0, "normal"), (7, 135172, 1.0, "normal"),
+    (11, 65532, 1.0, "normal"), (13, 65536, 1.0, "ties")])
 def test_softmax_rows_against_the_float64_definition(rows, V, T, kind):
     rng = np.random.default_rng(rows * 13 + V)
     if kind == "ties":
