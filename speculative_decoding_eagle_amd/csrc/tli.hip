@@ -4,10 +4,17 @@
 // of the draft distribution into the target vocabulary.
 //
 // The pruned LM head is a skinny GEMM (B ~ 64 rows) that streams the
-// [K, H] bf16 weight once from HBM: each 4-wave block owns 256 weight rows,
-// each wave 64 of them, and runs bf16 MFMA 16x16x32 with fp32 accumulators
-// over all B rows; the small hidden matrix is re-read from L1/L2, each
-// fragment serving four weight fragments.  The constraint writes 16 bytes
+// [K, H] bf16 weight once from HBM with bf16 MFMA 16x16x32 and fp32
+// accumulators over all B rows.  Where the hidden rows of a pass fit in LDS
+// (B <= 64 and up to about 160 KB), a block of 15 waves stages them there
+// once and each wave streams 16 weight rows, reading its hidden fragments
+// from LDS: 240 weight rows per block, 250 blocks at K = 60000 (a CU each).
+// Otherwise each 4-wave block owns 256 weight rows, each wave 64 of them,
+// and the hidden fragments come from L1/L2, each serving four weight
+// fragments.  (Measured at B=64, H=896, K=60000 on MI355X: 25.5 us staged
+// against 35 us; without the LDS, more waves per CU ran slower -- 44 us with
+// 32 weight rows per wave, 67 with 16 -- since every wave re-reads the
+// hidden matrix per weight fragment.)  The constraint writes 16 bytes
 // per thread and row over eight rows per block, its gathers all in flight;
 // the scatter stages most of each q row in LDS so that its random gathers
 // read LDS; the id maps are coalesced gathers/scatters.
@@ -92,6 +99,69 @@ lm_head_kernel(int B, int H, int K, const uint16_t *__restrict__ hidden,
         if (m < B) logits[static_cast<int64_t>(m) * K + ncol] = acc[mb][nb][i];
       }
   }
+}
+
+// The same product with the pass's hidden rows staged in LDS: NW waves of 16
+// weight rows each; the rows of the stage are padded by kHPad bf16 so that
+// the 16 rows of one fragment read fall in distinct banks.  The first kPre
+// k-steps of weight fragments are issued before the staging so that the
+// weight stream starts at once.  Dynamic LDS: MB * 16 * (H + kHPad) * 2
+// bytes.
+constexpr int kHPad = 8;
+constexpr int kLdsWaves = 15;                  // 240 weight rows per block
+constexpr int kLdsMax = 160 * 1024;            // staged hidden rows at most (bytes)
+template <int MB, int NW>
+__global__ void __launch_bounds__(NW * 64)
+lm_head_lds_kernel(int B, int H, int K, const uint16_t *__restrict__ hidden,
+                   const uint16_t *__restrict__ weight, float *__restrict__ logits) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_h[];
+  const int wave = threadIdx.x / kWave;
+  const int l = lane_id();
+  const int tid = threadIdx.x;
+  const int HP = H + kHPad;
+  const int n0 = (blockIdx.x * NW + wave) * 16;            // first weight row of this wave
+  const int m0 = blockIdx.y * (MB * 16);                   // first hidden row of this pass
+  const int kofs = 8 * (l >> 4);
+  const uint16_t *wp = weight + static_cast<int64_t>(min(n0 + (l & 15), K - 1)) * H + kofs;   // tail rows clamped, never stored
+  constexpr int kPre = 8;
+  bf16x8 pre[kPre];
+#pragma unroll
+  for (int p = 0; p < kPre; ++p) pre[p] = load_bf16x8(wp + min(32 * p, H - 32));
+  for (int i = 8 * tid; i < MB * 16 * H; i += NW * 64 * 8) {
+    const int r = i / H, col = i - r * H;                  // H % 32 == 0: a chunk stays in its row
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (m0 + r < B) u = *reinterpret_cast<const uint4 *>(hidden + static_cast<int64_t>(m0 + r) * H + col);
+    *reinterpret_cast<uint4 *>(s_h + r * HP + col) = u;
+  }
+  __syncthreads();
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t *hl = s_h + (l & 15) * HP + kofs;
+  auto kstep = [&](int k0, const bf16x8 &bw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      bf16x8 ah;
+      const uint4 u = *reinterpret_cast<const uint4 *>(hl + mb * 16 * HP + k0);
+      __builtin_memcpy(&ah, &u, 16);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[mb], 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < kPre; ++p)
+    if (32 * p < H) kstep(32 * p, pre[p]);
+#pragma unroll 4
+  for (int k0 = 32 * kPre; k0 < H; k0 += 32) kstep(k0, load_bf16x8(wp + k0));
+  // D[m][n]: lane l holds rows 4*(l/16)+i of the 16x16 block, column l%16
+  const int ncol = n0 + (l & 15);
+  if (ncol >= K) return;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + mb * 16 + 4 * (l >> 4) + i;
+      if (m < B) logits[static_cast<int64_t>(m) * K + ncol] = acc[mb][i];
+    }
 }
 
 __global__ void fill_i32_kernel(int *p, int64_t n, int v) {
@@ -327,6 +397,29 @@ extern "C" int32_t sdv_tli_lm_head(int32_t B, int32_t H, int32_t K, const uint16
     hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(static_cast<int64_t>(B) * K, 256)), dim3(256), 0,
                        as_stream(stream), reinterpret_cast<int *>(logits), static_cast<int64_t>(B) * K, 0);
     return check_launch("fill_i32_kernel");
+  }
+  // hidden rows staged in LDS: one pass of MB 16-row blocks covering B
+  const int mb_lds = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
+  const size_t lds = static_cast<size_t>(mb_lds) * 16 * (H + kHPad) * 2;
+  if (B <= 64 && lds <= static_cast<size_t>(kLdsMax)) {
+    auto run = [&](auto kernel, int mb) -> int32_t {
+      static thread_local int configured_dev[3] = {-1, -1, -1};
+      const int slot = mb == 1 ? 0 : (mb == 2 ? 1 : 2);
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "tli_lm_head: no device");
+      if (configured_dev[slot] != dev) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+        if (e != hipSuccess) return fail(SDV_E_HIP, "tli_lm_head: LDS attribute: %s", hipGetErrorString(e));
+        configured_dev[slot] = dev;
+      }
+      hipLaunchKernelGGL(kernel, dim3(nblk(K, kLdsWaves * 16)), dim3(kLdsWaves * 64), lds, as_stream(stream), B, H, K,
+                         hidden, weight, logits);
+      return check_launch("lm_head_lds_kernel");
+    };
+    if (mb_lds == 1) return run(lm_head_lds_kernel<1, kLdsWaves>, 1);
+    if (mb_lds == 2) return run(lm_head_lds_kernel<2, kLdsWaves>, 2);
+    return run(lm_head_lds_kernel<4, kLdsWaves>, 4);
   }
   const int mpass = kMaxMBlocks * 16;
   dim3 grid(nblk(K, kRowsPerBlock), nblk(B, mpass));

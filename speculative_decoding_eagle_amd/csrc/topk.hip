@@ -21,10 +21,10 @@ constexpr int kTopkThreads = 256;
 // 16-byte loads per lane in flight per window.  HBM serves a full chip of
 // streams fastest with about 6-8 MB in flight: with five blocks per CU, two
 // loads per lane per window (four with the next window's) measured 92 us
-// against 95-97 with four for 1056 rows of 128256 fp32 probabilities, 94
-// against 109 for fp32 logits and 62-66 against 69-71 for bf16 logits (a
-// plain grid-stride read of the same bytes: 6.9 TB/s with two loads per
-// lane, 5.8 with four, 5.2 with eight).
+// against 95-97 with four and 102-103 with one for 1056 rows of 128256 fp32
+// probabilities, 94 against 109 for fp32 logits and 62-66 against 69-71 for
+// bf16 logits (a plain grid-stride read of the same bytes: 6.9 TB/s with
+// two loads per lane, 5.8 with four, 5.2 with eight).
 constexpr int kLoads = 2;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));

@@ -1003,7 +1003,14 @@ def test_tli_constrain_and_scatter_shapes(Vd, Vt, K, rows):
         assert np.array_equal(host(g5), otli.q_scatter(q2, tgt, Vt)) and sdv.sdv_workspace_status(ws) == 0
 
 
-@pytest.mark.parametrize("B,H,K", [(64, 896, 60000), (5, 64, 1000), (17, 96, 77), (130, 32, 513)])
+# Up to 64 hidden rows whose 16-row blocks fit in LDS (padded rows, at most
+# 160 KB) take the staged kernel (one, two or four blocks: B = 5, 8, 17, 33,
+# 48, 64; H = 1248 is the largest that fits at B = 64); more rows (130) or
+# wider ones (H = 1280 at B = 64) take the kernel that reads them from L1/L2.
+# K = 109569 is the larger intersection of the TLI notes; tails of K below
+# a block (77, 241, 500, 4097).
+@pytest.mark.parametrize("B,H,K", [(64, 896, 60000), (5, 64, 1000), (17, 96, 77), (130, 32, 513), (33, 896, 4097),
+                                   (8, 896, 109569), (64, 1248, 500), (64, 1280, 500), (48, 64, 241)])
 def test_tli_lm_head_within_tolerance(B, H, K):
     rng = np.random.default_rng(B + H + K)
     hidden = workloads.to_bf16_bits(rng.standard_normal((B, H)).astype(np.float32))
