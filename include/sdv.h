@@ -492,8 +492,8 @@ int32_t sdv_tli_lm_head(int32_t B, int32_t H, int32_t K, const uint16_t *hidden,
  * ascending, full device [B, V_draft] fp32.
  * sdv_tli_q_scatter: q_target[r, tgt_ids[j]] = q_pruned[r, j], 0 elsewhere;
  * q_pruned device [rows, K] fp32, q_target device [rows, V_target] fp32;
- * the workspace holds a header (K and V_target of the map), the inverse of
- * tgt_ids and a copy of tgt_ids; a call with tgt_ids builds them (whatever
+ * the workspace holds a header (K and V_target of the map) and the inverse
+ * of tgt_ids; a call with tgt_ids builds them (whatever
  * the workspace held, its status word included, is overwritten).  The
  * workspace needs no zero-fill.  tgt_ids == NULL reuses what an earlier
  * call with the same K and V_target left in the same workspace (the maps

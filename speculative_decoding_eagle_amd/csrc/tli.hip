@@ -16,8 +16,9 @@
 // 32 weight rows per wave, 67 with 16 -- since every wave re-reads the
 // hidden matrix per weight fragment.)  The constraint writes 16 bytes
 // per thread and row over eight rows per block, its gathers all in flight;
-// the scatter stages most of each q row in LDS so that its random gathers
+// the scatter passes each q row through LDS so that its random gathers
 // read LDS; the id maps are coalesced gathers/scatters.
+#include <algorithm>
 #include <cmath>
 
 #include "common.hpp"
@@ -241,11 +242,11 @@ __global__ void constrain_kernel(int B, int K, int Vd, const float *__restrict__
     full[static_cast<int64_t>(b) * Vd + v] = j >= 0 ? pruned[static_cast<int64_t>(b) * K + j] : -INFINITY;
 }
 
-// inv[tgt[j]] = j (target ids outside [0, Vt) are skipped), and a copy of
-// tgt for the chunked scatter of later calls; the header records K and Vt so
-// that a later call without ids can check it is reusing the same map.
+// inv[tgt[j]] = j (target ids outside [0, Vt) are skipped); the header
+// records K and Vt so that a later call without ids can check it is reusing
+// the same map.
 __global__ void inverse_kernel(int K, const int *__restrict__ tgt, int Vt, int *__restrict__ inv,
-                               int *__restrict__ tcopy, unsigned *__restrict__ hdr) {
+                               unsigned *__restrict__ hdr) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j == 0) {
     hdr[kWsStatus] = 0u;                 // a fresh map: no earlier status applies
@@ -255,7 +256,6 @@ __global__ void inverse_kernel(int K, const int *__restrict__ tgt, int Vt, int *
   }
   if (j >= K) return;
   const int t = tgt[j];
-  tcopy[j] = t;
   if (t >= 0 && t < Vt) inv[t] = j;
 }
 
@@ -305,66 +305,68 @@ q_scatter4_kernel(int64_t rows, int K, int Vt, int nchunks, const float *__restr
   }
 }
 
-// Scatter form, all accesses coalesced: one 1024-thread workgroup per (q
-// row, chunk of kScatterChunk target ids).  It zero-fills the chunk in LDS,
-// streams the row's (target id, q value) pairs with 16-byte loads and drops
-// those that land in its chunk into LDS, then writes the chunk with 16-byte
-// non-temporal stores.  The chunks of a row run on one XCD (hardware block
-// h runs on XCD h % 8), so the row comes from HBM once and from that L2
-// after.  (The gather form, out[t] = q[inv[t]], moved a 128-byte line per
-// 4-byte entry for the part of each row that did not fit in LDS.)  Needs
-// Vt % 4 == 0, K % 4 == 0 and 16-byte aligned q rows, target ids and
-// output.
-constexpr int kScatterChunk = 32768;   // target ids per workgroup (128 KB of LDS)
-constexpr int kScatterThreads = 1024;
-constexpr int kScatterBatch = 8;
+// Gather form through LDS: one 1024-thread workgroup per (q row, chunk of
+// kGatherIds target ids).  Each thread holds 44 of the chunk's target ids
+// (eleven runs of four, coalesced) in registers: their inverse entries
+// inv[t] (the q column of t, or -1) and their outputs, zero to start.  The q
+// row then passes through LDS in slices of at most kQSlice floats (two at K
+// = 60000, copied by DMA), and each thread picks up the entries whose column
+// falls in the slice; finally the chunk is written with 16-byte
+// non-temporal stores.  The chunks of a row run on one XCD (hardware block h
+// runs on XCD h % 8), so the row comes from HBM once and from that L2 after.
+// (A scatter form that streamed every (target id, q value) pair of the row
+// into an LDS chunk of 32768 outputs per workgroup read 480 KB per 128 KB
+// written; a gather from L2 moves a 128-byte line per 4-byte entry.)  Needs
+// Vt % 4 == 0, K % 4 == 0 and 16-byte aligned q rows and output.
+constexpr int kGatherThreads = 1024;
+constexpr int kGatherRuns = 11;                                  // runs of four target ids per thread
+constexpr int kGatherIds = kGatherThreads * 4 * kGatherRuns;      // 45056 target ids per workgroup
+constexpr int kQSlice = 38912;                                   // q floats per LDS slice (152 KB)
 
-__global__ void __launch_bounds__(kScatterThreads)
-q_scatter_chunk_kernel(int64_t rows, int K, int Vt, int nch, const float *__restrict__ q,
-                       const int *__restrict__ tgt, float *__restrict__ out, unsigned *__restrict__ hdr) {
-  extern __shared__ __attribute__((aligned(16))) float s_o[];
-  const int xcd = blockIdx.x % kXcdCount, slot = blockIdx.x / kXcdCount;
-  const int64_t r = static_cast<int64_t>(slot / nch) * kXcdCount + xcd;
-  const int c = slot % nch;
+__global__ void __launch_bounds__(kGatherThreads)
+q_gather_lds_kernel(int64_t rows, int K, int Vt, int nch, int slice, const float *__restrict__ q,
+                    const int *__restrict__ inv, float *__restrict__ out, unsigned *__restrict__ hdr) {
+  extern __shared__ __attribute__((aligned(16))) float s_q[];
+  const int xcd = blockIdx.x % kXcdCount, bslot = blockIdx.x / kXcdCount;
+  const int64_t r = static_cast<int64_t>(bslot / nch) * kXcdCount + xcd;
+  const int c = bslot % nch;
   if (r >= rows) return;
-  const int base = c * kScatterChunk;
-  const int n = min(kScatterChunk, Vt - base);
   const int tid = static_cast<int>(threadIdx.x);
-  for (int i = 4 * tid; i < n; i += 4 * kScatterThreads)
-    *reinterpret_cast<float4 *>(s_o + i) = make_float4(0.f, 0.f, 0.f, 0.f);
-  __syncthreads();
-  const float *qr = q + r * K;
-  const unsigned ub = static_cast<unsigned>(base), un = static_cast<unsigned>(n);
-  const int kk = map_matches(hdr, K, Vt) ? K : 0;             // a foreign map: every entry 0
-  // kScatterBatch pairs of 16-byte loads per lane in flight before their
-  // LDS writes (one workgroup per CU: the loads must overlap)
-  constexpr int kStride = 4 * kScatterThreads;
-  for (int j0 = 4 * tid; j0 < kk; j0 += kScatterBatch * kStride) {
-    int4 t[kScatterBatch];
-    float4 v[kScatterBatch];
+  const int base = c * kGatherIds;
+  const bool same = map_matches(hdr, K, Vt);                        // a foreign map: every entry 0
+  int4 j[kGatherRuns];
+  f32x4v o[kGatherRuns];
 #pragma unroll
-    for (int u = 0; u < kScatterBatch; ++u) {
-      const int j = j0 + u * kStride;
-      if (j < kk) {
-        t[u] = *reinterpret_cast<const int4 *>(tgt + j);
-        v[u] = *reinterpret_cast<const float4 *>(qr + j);
-      } else {
-        t[u] = make_int4(-1, -1, -1, -1);
-        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kScatterBatch; ++u) {
-      if (static_cast<unsigned>(t[u].x) - ub < un) s_o[t[u].x - base] = v[u].x;
-      if (static_cast<unsigned>(t[u].y) - ub < un) s_o[t[u].y - base] = v[u].y;
-      if (static_cast<unsigned>(t[u].z) - ub < un) s_o[t[u].z - base] = v[u].z;
-      if (static_cast<unsigned>(t[u].w) - ub < un) s_o[t[u].w - base] = v[u].w;
-    }
+  for (int g = 0; g < kGatherRuns; ++g) {
+    const int t = base + 4 * (tid + g * kGatherThreads);
+    j[g] = same && t < Vt ? *reinterpret_cast<const int4 *>(inv + t) : make_int4(-1, -1, -1, -1);
+    o[g] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  __syncthreads();
-  float *orow = out + r * Vt + base;
-  for (int i = 4 * tid; i < n; i += 4 * kScatterThreads)
-    __builtin_nontemporal_store(*reinterpret_cast<const f32x4v *>(s_o + i), reinterpret_cast<f32x4v *>(orow + i));
+  const float *qr = q + r * K;
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_offset(s_q) + (tid / kWave) * kWave * 16);
+  for (int lo = 0; same && lo < K; lo += slice) {
+    const int len = min(slice, K - lo);                             // a multiple of 4
+    // the slice into LDS: float4 i of the slice (lane-contiguous per wave)
+    for (int i0 = 0; i0 < len / 4; i0 += kGatherThreads)
+      if (i0 + tid < len / 4) dma16(qr + lo + 4 * (i0 + tid), lds_wave + 16u * i0);
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");              // this wave's copies are in
+    __syncthreads();                                                // and everyone's
+    const unsigned ulen = static_cast<unsigned>(len);
+#pragma unroll
+    for (int g = 0; g < kGatherRuns; ++g) {
+      if (static_cast<unsigned>(j[g].x - lo) < ulen) o[g].x = s_q[j[g].x - lo];
+      if (static_cast<unsigned>(j[g].y - lo) < ulen) o[g].y = s_q[j[g].y - lo];
+      if (static_cast<unsigned>(j[g].z - lo) < ulen) o[g].z = s_q[j[g].z - lo];
+      if (static_cast<unsigned>(j[g].w - lo) < ulen) o[g].w = s_q[j[g].w - lo];
+    }
+    __syncthreads();                                                // read before the next slice lands
+  }
+  float *orow = out + r * Vt;
+#pragma unroll
+  for (int g = 0; g < kGatherRuns; ++g) {
+    const int t = base + 4 * (tid + g * kGatherThreads);
+    if (t < Vt) __builtin_nontemporal_store(o[g], reinterpret_cast<f32x4v *>(orow + t));
+  }
 }
 
 __global__ void q_scatter_kernel(int64_t rows, int K, int Vt, const float *__restrict__ q,
@@ -483,11 +485,10 @@ extern "C" int32_t sdv_tli_constrain_draft_logits(int32_t B, int32_t K, int32_t 
   return check_launch("constrain_kernel");
 }
 
-// Workspace: the header (status, and the K and V_target of the map), the
-// inverse of tgt_ids [V_target], then a copy of tgt_ids (at most V_target
-// entries, since the map is injective).
+// Workspace: the header (status, and the K and V_target of the map), then
+// the inverse of tgt_ids [V_target].
 extern "C" size_t sdv_tli_q_scatter_workspace_size(int32_t V_target) {
-  return V_target > 0 ? kWsHeaderBytes + 2 * align_up(static_cast<size_t>(V_target) * sizeof(int), 256) : 0;
+  return V_target > 0 ? kWsHeaderBytes + align_up(static_cast<size_t>(V_target) * sizeof(int), 256) : 0;
 }
 
 extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, const float *q_pruned,
@@ -502,33 +503,36 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
   SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "tli_q_scatter: workspace of %zu bytes needed", need);
   unsigned *hdr = ws_header(ws);
   int *inv = reinterpret_cast<int *>(static_cast<char *>(ws) + kWsHeaderBytes);
-  int *tcopy = inv + align_up(static_cast<size_t>(V_target) * sizeof(int), 256) / sizeof(int);
   hipStream_t st = as_stream(stream);
-  if (tgt_ids) {                         // else: the inverse and the copy an earlier call left in ws
+  if (tgt_ids) {                         // else: the inverse an earlier call left in ws
     hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(V_target, 256)), dim3(256), 0, st, inv,
                        static_cast<int64_t>(V_target), -1);
     hipLaunchKernelGGL(inverse_kernel, dim3(K > 0 ? nblk(K, 256) : 1), dim3(256), 0, st, K, tgt_ids, V_target, inv,
-                       tcopy, hdr);
+                       hdr);
   }
   if (V_target % 4 == 0 && K % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0 &&
       reinterpret_cast<uintptr_t>(q_pruned) % 16 == 0) {
-    const size_t lds = static_cast<size_t>(kScatterChunk) * sizeof(float);
+    // slices of at most kQSlice floats, equal up to the last, multiples of 4
+    const int nslices = K > 0 ? (K + kQSlice - 1) / kQSlice : 1;
+    const int slice = static_cast<int>(align_up(static_cast<size_t>((K + nslices - 1) / nslices), 4));
+    const size_t lds = static_cast<size_t>(std::max(slice, 4)) * sizeof(float);
     static thread_local int configured_dev = -1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SDV_E_HIP, "tli_q_scatter: no device");
     if (configured_dev != dev) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q_scatter_chunk_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q_gather_lds_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(kQSlice * sizeof(float)));
       if (e != hipSuccess) return fail(SDV_E_HIP, "tli_q_scatter: LDS attribute: %s", hipGetErrorString(e));
       configured_dev = dev;
     }
-    const int nch = static_cast<int>(nblk(V_target, kScatterChunk));
+    const int nch = static_cast<int>(nblk(V_target, kGatherIds));
     const int64_t per_xcd = (rows + kXcdCount - 1) / kXcdCount;       // rows per XCD
     const int64_t blocks = per_xcd * nch * kXcdCount;
     SDV_REQUIRE(blocks < (1LL << 31), SDV_E_UNSUPPORTED, "tli_q_scatter: grid too large");
-    hipLaunchKernelGGL(q_scatter_chunk_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), lds, st,
-                       rows, K, V_target, nch, q_pruned, tcopy, q_target, hdr);
-    return check_launch("q_scatter_chunk_kernel");
+    hipLaunchKernelGGL(q_gather_lds_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kGatherThreads), lds, st,
+                       rows, K, V_target, nch, std::max(slice, 4), q_pruned, inv, q_target, hdr);
+    return check_launch("q_gather_lds_kernel");
   }
   if (V_target % 4 == 0 && reinterpret_cast<uintptr_t>(q_target) % 16 == 0) {
     const int nchunks = static_cast<int>(nblk(V_target / 4, 256));

@@ -957,18 +957,20 @@ def test_tli_constrain_and_scatter_bit_exact():
 
 
 @pytest.mark.parametrize("Vd,Vt,K,rows", [(1001, 999, 300, 5), (1000, 1000, 301, 13), (2048, 4096, 512, 17),
-                                          (50000, 60000, 40000, 9), (151936, 128256, 60000, 11)])
+                                          (50000, 60000, 40000, 9), (151936, 128256, 60000, 11),
+                                          (151936, 128256, 109568, 3)])
 def test_tli_constrain_and_scatter_shapes(Vd, Vt, K, rows):
     """Every kernel path: scalar (odd sizes), 16-byte with row groups per XCD
-    (K not a multiple of 4), and the chunked scatter with one chunk of target
-    ids, two, and four (rows not a multiple of the XCD count; the ids on both
-    sides of every chunk boundary present); then a second scatter that reuses
-    the inverse and the id copy left in the workspace."""
+    (K not a multiple of 4), and the LDS gather with one chunk of target ids,
+    two, and three, its q rows in one LDS slice, two or three (rows not a multiple
+    of the XCD count; the ids on both sides of every chunk and slice boundary
+    present); then a second scatter that reuses the inverse left in the
+    workspace."""
     rng = np.random.default_rng(Vd + Vt + K)
     inter = np.sort(rng.choice(Vd, K, replace=False)).astype(np.int32)
     tgt = rng.choice(Vt, K, replace=False).astype(np.int32)
-    if Vt > 32768:
-        edges = [e for c in range(1, (Vt + 32767) // 32768) for e in (32768 * c - 1, 32768 * c)] + [0, Vt - 1]
+    if Vt > 45056:
+        edges = [e for c in range(1, (Vt + 45055) // 45056) for e in (45056 * c - 1, 45056 * c)] + [0, Vt - 1]
         rest = np.setdiff1d(tgt, edges)
         tgt = np.concatenate([np.array(edges, np.int32), rng.permutation(rest)[:K - len(edges)]]).astype(np.int32)
         tgt = rng.permutation(tgt).astype(np.int32)
