@@ -500,7 +500,8 @@ int32_t sdv_tli_lm_head(int32_t B, int32_t H, int32_t K, const uint16_t *hidden,
  * are static, so a serving loop builds them once); if the header names
  * another K or V_target (or no map was built), the output is 0 and
  * SDV_STATUS_TLI_REUSE is set.  Ids and positions read from the workspace
- * are bounds-checked against K.
+ * are bounds-checked against K.  K == 0 writes zeros and leaves the
+ * workspace as it was.
  * ---------------------------------------------------------------------- */
 int32_t sdv_tli_build_maps(int32_t K, const int32_t *inter_ids, const int32_t *tgt_ids,
                            int32_t V_draft, int32_t V_target, int32_t fallback, int32_t *d2t,

@@ -10,6 +10,7 @@ bf16 tensors may be given as torch.bfloat16 or as int16/uint16 bit patterns.
 from __future__ import annotations
 
 import ctypes
+import math
 from typing import Optional, Sequence
 
 import torch
@@ -553,7 +554,7 @@ def sdv_tli_q_scatter(q_pruned, tgt_ids, V_target: int, q_target=None, ws=None):
         raise ValueError("sdv_tli_q_scatter: tgt_ids=None reuses a workspace; pass the workspace of the call "
                          "that built the map")
     K = q_pruned.shape[-1]
-    rows = q_pruned.numel() // K
+    rows = math.prod(q_pruned.shape[:-1])             # also when K == 0
     dev = q_pruned.device
     if q_target is None:
         q_target = torch.empty(q_pruned.shape[:-1] + (V_target,), dtype=torch.float32, device=dev)

@@ -499,6 +499,13 @@ extern "C" int32_t sdv_tli_q_scatter(int64_t rows, int32_t K, int32_t V_target, 
   SDV_REQUIRE(rows <= 65535, SDV_E_UNSUPPORTED, "tli_q_scatter: rows above 65535");
   if (rows == 0) return SDV_OK;
   SDV_REQUIRE(q_target && (K == 0 || q_pruned), SDV_E_NULL, "tli_q_scatter: NULL pointer");
+  if (K == 0) {                          // nothing to scatter: zeros, the workspace untouched
+    const int64_t n = rows * static_cast<int64_t>(V_target);
+    SDV_REQUIRE((n + 255) / 256 < (1LL << 31), SDV_E_UNSUPPORTED, "tli_q_scatter: output too large");
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(nblk(n, 256)), dim3(256), 0, as_stream(stream),
+                       reinterpret_cast<int *>(q_target), n, 0);
+    return check_launch("fill_i32_kernel");
+  }
   const size_t need = sdv_tli_q_scatter_workspace_size(V_target);
   SDV_REQUIRE(ws && ws_bytes >= need, SDV_E_WORKSPACE, "tli_q_scatter: workspace of %zu bytes needed", need);
   unsigned *hdr = ws_header(ws);

@@ -958,7 +958,7 @@ def test_tli_constrain_and_scatter_bit_exact():
 
 @pytest.mark.parametrize("Vd,Vt,K,rows", [(1001, 999, 300, 5), (1000, 1000, 301, 13), (2048, 4096, 512, 17),
                                           (50000, 60000, 40000, 9), (151936, 128256, 60000, 11),
-                                          (151936, 128256, 109568, 3)])
+                                          (151936, 128256, 109568, 3), (1000, 1000, 0, 3)])
 def test_tli_constrain_and_scatter_shapes(Vd, Vt, K, rows):
     """Every kernel path: scalar (odd sizes), 16-byte with row groups per XCD
     (K not a multiple of 4), and the LDS gather with one chunk of target ids,
@@ -980,7 +980,9 @@ def test_tli_constrain_and_scatter_shapes(Vd, Vt, K, rows):
     full = sdv.sdv_tli_constrain_draft_logits(dev(pruned), dev(inter), Vd)
     torch.cuda.synchronize()
     assert np.array_equal(host(full), otli.constrain_logits(pruned, inter, Vd))
-    ws = torch.empty(sdv._lib.lib().sdv_tli_q_scatter_workspace_size(Vt), dtype=torch.uint8, device="cuda")
+    # (zero-filled only for K = 0, whose calls leave the workspace untouched;
+    # a call that builds the map writes its header itself)
+    ws = torch.zeros(sdv._lib.lib().sdv_tli_q_scatter_workspace_size(Vt), dtype=torch.uint8, device="cuda")
     q1 = rng.random((rows, K)).astype(np.float32)
     q2 = rng.random((rows, K)).astype(np.float32)
     g1 = sdv.sdv_tli_q_scatter(dev(q1), dev(tgt), Vt, ws=ws)
