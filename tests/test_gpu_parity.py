@@ -105,13 +105,15 @@ def test_topk_from_logits(rows, V, k, T, bf16, kind):
 # workgroup per row, one per CU at a time): more rows than CUs (517, 300,
 # 260), rows whose last register chunks lie past the row (V = 70004), the
 # largest such row (135168, nine LDS chunks) next to the smallest read
-# twice above it (135172), and both sides of the lower end (65536, 65532).
+# twice above it (135172), both sides of the lower end (65536, 65532), and
+# rows that just fill the register chunks (98304) or add one float4 in LDS
+# (98308).
 @pytest.mark.parametrize("rows,V,T,kind", [
     (80, 128256, 1.0, "normal"), (24, 128256, 0.7, "normal"), (5, 128256, 0.5, "normal"), (7, 1000, 0.7, "normal"),
     (3, 5, 1.0, "normal"), (9, 4099, 2.0, "normal"), (4, 1, 1.0, "normal"), (6, 40000, 0.8, "masked"),
     (2, 131072, 1.0, "ties"), (0, 128256, 1.0, "normal"), (517, 70004, 0.9, "normal"),
     (300, 128256, 0.7, "masked"), (260, 135168, 1.0, "normal"), (7, 135172, 1.0, "normal"),
-    (11, 65532, 1.0, "normal"), (13, 65536, 1.0, "ties")])
+    (11, 65532, 1.0, "normal"), (13, 65536, 1.0, "ties"), (9, 98304, 1.0, "normal"), (9, 98308, 0.9, "normal")])
 def test_softmax_rows_against_the_float64_definition(rows, V, T, kind):
     rng = np.random.default_rng(rows * 13 + V)
     if kind == "ties":
